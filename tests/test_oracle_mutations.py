@@ -1,0 +1,130 @@
+"""Planted mistakes in the oracle must each fail at least one pin.
+
+Each mutant replaces one oracle function (on the CPU, inside this test only) with
+a plausible wrong version -- a dropped scale, a flipped sign, a wrong head or
+block index, a per-block softmax, a swapped slot decode -- and runs the pin
+tests against it.  A mutant that passes every pin would mean the pins leave that
+part of the oracle unchecked.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.attention as att
+import oracle.cache_ops as cops
+import test_oracle_attention as TA
+import test_oracle_cache_ops as TC
+
+
+def attend_factory(kind):
+    def attend(q, K, V, scale):
+        Hq, D = q.shape
+        L, Hkv, _ = K.shape
+        g = Hq // Hkv
+        out = np.zeros((Hq, D))
+        if L == 0:
+            return out
+        for h in range(Hq):
+            kv = h % Hkv if kind == "head_mod" else h // g
+            sc = 1.0 if kind == "no_scale" else scale
+            s = sc * (K[:, kv, :] @ q[h])
+            if kind == "neg_sign":
+                s = -s
+            if kind == "v_from_k":
+                Vh = K[:, kv, :]
+            else:
+                Vh = V[:, kv, :]
+            p = np.exp(s - s.max())
+            if kind == "no_norm":
+                out[h] = p @ Vh
+            elif kind == "drop_last":
+                out[h] = (p[:-1] @ Vh[:-1]) / p[:-1].sum() if L > 1 else Vh[0]
+            else:
+                out[h] = (p @ Vh) / p.sum()
+        return out
+    return attend
+
+
+def gather_factory(kind):
+    def gather(cache, table_row, seq_len, block_size):
+        t = np.arange(seq_len)
+        table_row = np.asarray(table_row)
+        if kind == "physical_by_index":           # ignores the table
+            return cache[t // block_size, t % block_size]
+        if kind == "swap_div_mod":
+            return cache[table_row[t % block_size % max(1, len(table_row))], t // block_size % block_size]
+        if kind == "off_by_one_block":
+            return cache[table_row[np.minimum((t + 1) // block_size, len(table_row) - 1)], t % block_size]
+        raise AssertionError(kind)
+    return gather
+
+
+def write_factory(kind):
+    orig = cops.write_kv
+
+    def write_kv(k, v, slot_mapping, k_cache, v_cache):
+        if kind == "k_into_v":
+            kc, vc = orig(k, v, slot_mapping, k_cache, v_cache)
+            return kc, orig(k, k, slot_mapping, k_cache, v_cache)[1]
+        B = k_cache.shape[1]
+        kc, vc = k_cache.copy(), v_cache.copy()
+        for i, s in enumerate(slot_mapping):
+            if kind == "no_skip":
+                s = abs(int(s))
+            elif s < 0:
+                continue
+            b, o = (s % k_cache.shape[0], s // k_cache.shape[0]) if kind == "swap_decode" else divmod(int(s), B)
+            kc[b, o % B] = k[i]
+            vc[b, o % B] = v[i]
+        return kc, vc
+    return write_kv
+
+
+ATTN_PINS = [
+    lambda: TA.test_single_token_returns_v_exactly("f32"),
+    lambda: TA.test_single_token_returns_v_exactly("bf16"),
+    lambda: TA.test_zero_query_gives_mean_of_valid_rows(4),
+    TA.test_one_hot_attention_selects_the_constructed_token,
+    TA.test_two_tokens_match_logistic_closed_form,
+    lambda: TA.test_matches_torch_sdpa_float64(8, 2),
+    TA.test_unused_slots_are_never_read,
+]
+
+CACHE_PINS = [
+    TC.test_worked_mapping_slots_and_next_write,
+    TC.test_write_is_a_bit_copy_and_skips_negative_slots,
+]
+
+
+def caught(pins):
+    for pin in pins:
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except (AssertionError, IndexError, ValueError):
+            return True
+    return False
+
+
+@pytest.mark.parametrize("kind", ["no_scale", "neg_sign", "head_mod", "no_norm", "v_from_k",
+                                  "drop_last"])
+def test_attend_mutants_are_caught(monkeypatch, kind):
+    monkeypatch.setattr(att, "attend", attend_factory(kind))
+    assert caught(ATTN_PINS), kind
+
+
+@pytest.mark.parametrize("kind", ["physical_by_index", "swap_div_mod", "off_by_one_block"])
+def test_gather_mutants_are_caught(monkeypatch, kind):
+    monkeypatch.setattr(att, "gather", gather_factory(kind))
+    assert caught(ATTN_PINS), kind
+
+
+@pytest.mark.parametrize("kind", ["swap_decode", "no_skip", "k_into_v"])
+def test_write_mutants_are_caught(monkeypatch, kind):
+    monkeypatch.setattr(oracle, "write_kv", write_factory(kind))
+    assert caught(CACHE_PINS), kind
+
+
+def test_unmutated_oracle_passes_every_pin():
+    assert not caught(ATTN_PINS) and not caught(CACHE_PINS)
