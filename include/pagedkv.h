@@ -1,0 +1,166 @@
+/*
+ * pagedkv.h -- C ABI of libpagedkv, paged decode attention for MI355X (gfx950).
+ *
+ * The operations follow three web pages on PagedAttention, cited as
+ *   [PA-notes]     "LLM 注意力与计算内核精读笔记 · 05 PagedAttention 与 KV 显存管理"
+ *   [vLLM-what]    "vLLM 是什么 PagedAttention 解决了什么"
+ *   [PA-explainer] "PagedAttention：分页注意力——推理引擎的显存革命"
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers.  Every array argument is a DEVICE pointer to contiguous row-major
+ *   memory owned by the caller.  The library allocates no device memory and
+ *   keeps no pointer after a call returns.
+ * Streams.  `stream` is a hipStream_t passed as void* (NULL = the default
+ *   stream).  Calls only enqueue work and return; results are ready when the
+ *   stream reaches that point.  Work issued on one stream runs in order, so
+ *   write -> copy -> decode on one stream needs no extra synchronisation.
+ * Element types.  pa_dtype names the storage type of q, K/V, new tokens and
+ *   the output.  Arithmetic is float32 inside the kernels.
+ * Cache pool layout (both K and V, identical):
+ *     cache[num_blocks][block_size][num_kv_heads][head_dim]
+ *   Each physical block holds block_size consecutive tokens of one sequence
+ *   ([PA-notes] §3; per-block [block_size, heads, head_dim] as in
+ *   [PA-explainer] "Block结构", with KV heads under GQA as in [vLLM-what]
+ *   "1）KV cache 显存估算").  Token t of a sequence is in its logical block
+ *   t / block_size at offset t % block_size.
+ * Slots.  slot = physical_block * block_size + offset, a flat token index
+ *   into the pool.
+ * Errors.  Problems the host can see (null pointers, unsupported sizes,
+ *   inconsistent dimensions, a workspace too small) return a non-PA_OK status
+ *   before anything is enqueued; pa_last_error() then describes it.  Index
+ *   data that lives on the device (block tables, slots, pairs) is the
+ *   caller's contract and is not checked on the hot path: out-of-range ids
+ *   are clamped (decode) or skipped (write, copy) so that no access leaves the
+ *   pool, and the result for such entries is unspecified.  Setting the
+ *   environment variable PA_DEBUG_CHECK=1 makes every call copy its index
+ *   arrays to the host, synchronously, and reject contract violations with
+ *   PA_ERR_INVALID before launching.  A failed launch returns PA_ERR_HIP.
+ * Thread safety.  Calls may come from any host thread; pa_last_error() is per
+ *   thread.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_F32 = 0,  /* float32 */
+  PA_F16 = 1,  /* IEEE binary16 */
+  PA_BF16 = 2  /* bfloat16 */
+} pa_dtype;
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_INVALID = 1,     /* bad argument or (debug mode) bad index data */
+  PA_ERR_UNSUPPORTED = 2, /* valid request outside the compiled kernel set */
+  PA_ERR_WORKSPACE = 3,   /* workspace missing or too small */
+  PA_ERR_HIP = 4          /* the HIP runtime reported an error */
+} pa_status;
+
+/* Library ABI version (incremented on any signature change). */
+int pa_version(void);
+
+/* Message for the last non-PA_OK status returned on the calling thread
+ * ("" if none).  The string stays valid until the next call on that thread. */
+const char* pa_last_error(void);
+
+/* Tokens per context partition that pa_decode uses for these arguments.  A
+ * sequence longer than one partition is split into ceil(len / partition)
+ * pieces, each reduced on its own, and the pieces are merged by a second
+ * kernel.  The size is a multiple of block_size and of 16; PA_PARTITION_TOKENS
+ * in the environment (read once) overrides the default of 512.  Returns 0 for
+ * an unsupported block_size. */
+int pa_decode_partition_tokens(int block_size);
+
+/* Bytes of workspace pa_decode needs for these arguments (0 when no sequence
+ * can need more than one partition).  Returns 0 for invalid arguments. */
+size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_dim,
+                                int block_size, int max_seq_len);
+
+/*
+ * pa_decode -- one decode step of paged attention.
+ *
+ * For every sequence s and query head h (KV head kv = h / (num_heads /
+ * num_kv_heads)), with L = seq_lens[s] tokens:
+ *     out[s][h] = sum_t softmax_t(scale * q[s][h] . K_s[t][kv]) * V_s[t][kv]
+ * where K_s[t] is read from physical block block_tables[s][t / block_size] at
+ * offset t % block_size.  The softmax is normalised over all L tokens of the
+ * sequence, across blocks, by merging a running maximum and running sum block
+ * by block ([PA-notes] §4; the dense formula with 1/sqrt(d) is [vLLM-what]
+ * "2）PagedAttention 算子").  A sequence with L = 0 yields zeros.
+ *
+ *   q            [num_seqs][num_heads][head_dim]            dtype
+ *   k_cache      [num_blocks][block_size][num_kv_heads][head_dim]  dtype
+ *   v_cache      same shape as k_cache
+ *   block_tables [num_seqs][max_blocks_per_seq] int32: physical block ids;
+ *                entries at and past ceil(L / block_size) are never read
+ *   seq_lens     [num_seqs] int32, 0 <= L <= max_seq_len
+ *   out          [num_seqs][num_heads][head_dim] dtype; must not alias inputs
+ *   workspace    device scratch of at least pa_decode_workspace_size(...)
+ *                bytes (may be NULL when that size is 0); its contents on
+ *                entry do not matter and are clobbered
+ *   max_seq_len  caller's upper bound on every seq_lens[s]; must be
+ *                <= max_blocks_per_seq * block_size.  Lengths above it are
+ *                clamped to it.
+ * Supported: head_dim in {64, 128}; block_size in {8, 16, 32}; num_heads a
+ * multiple of num_kv_heads with group size num_heads / num_kv_heads <= 16.
+ * Accumulation is float32; the output is rounded once, to nearest even.
+ * Results are deterministic: the same inputs give the same bits.
+ */
+pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* seq_lens,
+                    int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                    int block_size, int num_blocks, int max_blocks_per_seq,
+                    int max_seq_len, float scale, pa_dtype dtype, void* out,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pa_write_kv -- store new tokens' K and V rows into their slots.
+ *
+ * For every i with 0 <= slot_mapping[i] < num_blocks * block_size:
+ *     k_cache[slot / block_size][slot % block_size] = k[i]   (all KV heads)
+ *     v_cache[slot / block_size][slot % block_size] = v[i]
+ * A negative slot marks a padding token and writes nothing.  This is the
+ * append step of on-demand allocation: a new token goes to the next free slot
+ * of its sequence's last block, and the host takes a new block only when that
+ * one is full ([PA-notes] §5 ②).  The copy is bit-exact.
+ *
+ *   k, v          [num_tokens][num_kv_heads][head_dim] dtype; must not alias
+ *                 the caches
+ *   slot_mapping  [num_tokens] int32; two tokens must not name the same slot
+ *   k_cache, v_cache  pool layout above
+ */
+pa_status pa_write_kv(const void* k, const void* v, const int32_t* slot_mapping,
+                      void* k_cache, void* v_cache, int num_tokens,
+                      int num_kv_heads, int head_dim, int block_size,
+                      int num_blocks, pa_dtype dtype, void* stream);
+
+/*
+ * pa_copy_blocks -- copy-on-write block duplication.
+ *
+ * For every pair (src, dst) = (src_dst_pairs[2i], src_dst_pairs[2i+1]):
+ *     k_cache[dst] = k_cache[src];  v_cache[dst] = v_cache[src]
+ * copying the whole block (every slot and KV head).  Before a sequence writes
+ * into a physical block that other sequences still share, the host picks a
+ * fresh block, repoints the writer's table entry and asks for this copy
+ * ([PA-notes] §6.1 and §12 题4).  All pairs act at once: no dst may be a src
+ * of any pair, and no dst may repeat.  Pairs naming ids outside
+ * [0, num_blocks) are skipped.  The copy is bit-exact.
+ *
+ *   src_dst_pairs  [num_pairs][2] int32, device memory
+ */
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst_pairs,
+                         int num_pairs, int block_size, int num_kv_heads,
+                         int head_dim, int num_blocks, pa_dtype dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,0 +1,297 @@
+// C-ABI entry points of libpagedkv: argument validation, launch planning and
+// dispatch.  The operations themselves are described in include/pagedkv.h.
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+#include <vector>
+
+#include "common.h"
+#include "pagedkv.h"
+
+using namespace pagedkv;
+
+namespace {
+
+thread_local std::string g_err;
+
+pa_status fail(pa_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+pa_status hip_fail(hipError_t e, const char* what) {
+  return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int env_int(const char* name, int dflt) {
+  const char* s = getenv(name);
+  if (!s || !*s) return dflt;
+  char* end = nullptr;
+  long v = strtol(s, &end, 10);
+  return (end && *end == 0 && v > 0 && v < (1L << 30)) ? (int)v : dflt;
+}
+
+bool debug_checks() {
+  static const bool on = env_int("PA_DEBUG_CHECK", 0) == 1;
+  return on;
+}
+
+int requested_partition() {
+  static const int v = env_int("PA_PARTITION_TOKENS", 512);
+  return v;
+}
+
+bool valid_block_size(int bs) { return bs == 8 || bs == 16 || bs == 32; }
+
+// Partition size: a multiple of 16 (the tile) and of the block size, at most
+// 64 blocks (one block id per lane of the wave).
+int partition_tokens(int bs) {
+  if (!valid_block_size(bs)) return 0;
+  const int unit = bs > 16 ? bs : 16;
+  int p = requested_partition() / unit * unit;
+  if (p < unit) p = unit;
+  if (p > 64 * bs) p = 64 * bs;
+  return p;
+}
+
+bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+struct WorkspaceLayout {
+  int max_parts;
+  size_t ml_bytes;
+  size_t acc_offset;
+  size_t total;
+};
+
+WorkspaceLayout plan_workspace(int num_seqs, int num_heads, int head_dim, int bs, int max_seq_len) {
+  WorkspaceLayout w{1, 0, 0, 0};
+  const int P = partition_tokens(bs);
+  w.max_parts = max_seq_len > 0 ? (max_seq_len + P - 1) / P : 1;
+  if (w.max_parts <= 1) return w;
+  const size_t rows = (size_t)num_seqs * num_heads * w.max_parts;
+  w.ml_bytes = rows * 2 * sizeof(float);
+  w.acc_offset = align_up(w.ml_bytes, 256);
+  w.total = w.acc_offset + rows * head_dim * sizeof(float);
+  return w;
+}
+
+template <typename T>
+bool to_host(std::vector<T>& dst, const void* src, size_t n, hipStream_t stream, pa_status* st) {
+  dst.resize(n);
+  if (n == 0) return true;
+  hipError_t e = hipMemcpyAsync(dst.data(), src, n * sizeof(T), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) {
+    *st = hip_fail(e, "PA_DEBUG_CHECK copy");
+    return false;
+  }
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_version(void) { return 1; }
+
+const char* pa_last_error(void) { return g_err.c_str(); }
+
+int pa_decode_partition_tokens(int block_size) { return partition_tokens(block_size); }
+
+size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_dim, int block_size,
+                                int max_seq_len) {
+  if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || max_seq_len < 0 ||
+      !valid_block_size(block_size))
+    return 0;
+  return plan_workspace(num_seqs, num_heads, head_dim, block_size, max_seq_len).total;
+}
+
+pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* seq_lens, int num_seqs,
+                    int num_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                    int max_blocks_per_seq, int max_seq_len, float scale, pa_dtype dtype, void* out,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != PA_F32 && dtype != PA_F16 && dtype != PA_BF16)
+    return fail(PA_ERR_INVALID, "pa_decode: unknown dtype %d", (int)dtype);
+  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
+      max_blocks_per_seq <= 0 || max_seq_len < 0)
+    return fail(PA_ERR_INVALID,
+                "pa_decode: need num_seqs >= 0, num_heads, num_kv_heads, num_blocks, "
+                "max_blocks_per_seq > 0 and max_seq_len >= 0");
+  if (num_heads % num_kv_heads != 0)
+    return fail(PA_ERR_INVALID, "pa_decode: num_heads (%d) is not a multiple of num_kv_heads (%d)",
+                num_heads, num_kv_heads);
+  if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f)
+    return fail(PA_ERR_INVALID, "pa_decode: scale must be finite");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: head_dim %d not in {64, 128}", head_dim);
+  if (!valid_block_size(block_size))
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: block_size %d not in {8, 16, 32}", block_size);
+  const int group = num_heads / num_kv_heads;
+  if (padded_group(group) == 0)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: %d query heads per KV head (at most 16)", group);
+  if (num_seqs > 65535 || num_kv_heads > 65535)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: num_seqs and num_kv_heads must be <= 65535");
+  if ((long long)max_seq_len > (long long)max_blocks_per_seq * block_size)
+    return fail(PA_ERR_INVALID, "pa_decode: max_seq_len %d exceeds max_blocks_per_seq * block_size (%lld)",
+                max_seq_len, (long long)max_blocks_per_seq * block_size);
+  if (num_seqs == 0) return PA_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !out)
+    return fail(PA_ERR_INVALID, "pa_decode: null pointer argument");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return fail(PA_ERR_INVALID, "pa_decode: q, caches and out must be 16-byte aligned");
+
+  const WorkspaceLayout ws = plan_workspace(num_seqs, num_heads, head_dim, block_size, max_seq_len);
+  if (ws.total > 0) {
+    if (!workspace || workspace_bytes < ws.total)
+      return fail(PA_ERR_WORKSPACE, "pa_decode: workspace of %zu bytes needed, %zu given", ws.total,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (((uintptr_t)workspace & 255u) != 0)
+      return fail(PA_ERR_WORKSPACE, "pa_decode: workspace must be 256-byte aligned");
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  if (debug_checks()) {
+    pa_status bad = PA_OK;
+    std::vector<int32_t> lens, tab;
+    if (!to_host(lens, seq_lens, num_seqs, st, &bad)) return bad;
+    if (!to_host(tab, block_tables, (size_t)num_seqs * max_blocks_per_seq, st, &bad)) return bad;
+    for (int s = 0; s < num_seqs; ++s) {
+      if (lens[s] < 0 || lens[s] > max_seq_len)
+        return fail(PA_ERR_INVALID, "pa_decode: seq_lens[%d] = %d outside [0, %d]", s, lens[s], max_seq_len);
+      const int nb = (lens[s] + block_size - 1) / block_size;
+      for (int j = 0; j < nb; ++j) {
+        const int id = tab[(size_t)s * max_blocks_per_seq + j];
+        if (id < 0 || id >= num_blocks)
+          return fail(PA_ERR_INVALID, "pa_decode: block_tables[%d][%d] = %d outside [0, %d)", s, j, id,
+                      num_blocks);
+      }
+    }
+  }
+
+  DecodeParams p;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.block_tables = block_tables;
+  p.seq_lens = seq_lens;
+  p.out = out;
+  p.ws_ml = ws.total ? static_cast<float*>(workspace) : nullptr;
+  p.ws_acc = ws.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.acc_offset) : nullptr;
+  p.num_seqs = num_seqs;
+  p.num_heads = num_heads;
+  p.num_kv_heads = num_kv_heads;
+  p.group = group;
+  p.head_dim = head_dim;
+  p.block_size = block_size;
+  p.num_blocks = num_blocks;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.max_seq_len = max_seq_len;
+  p.part_tokens = partition_tokens(block_size);
+  p.max_parts = ws.max_parts;
+  p.scale_log2e = (float)((double)scale * 1.4426950408889634074);
+
+  hipError_t e;
+  switch (dtype) {
+    case PA_F32: e = launch_decode_f32(p, st); break;
+    case PA_F16: e = launch_decode_f16(p, st); break;
+    default: e = launch_decode_bf16(p, st); break;
+  }
+  if (e != hipSuccess) return hip_fail(e, "pa_decode launch");
+  return PA_OK;
+}
+
+pa_status pa_write_kv(const void* k, const void* v, const int32_t* slot_mapping, void* k_cache,
+                      void* v_cache, int num_tokens, int num_kv_heads, int head_dim, int block_size,
+                      int num_blocks, pa_dtype dtype, void* stream) {
+  if (dtype != PA_F32 && dtype != PA_F16 && dtype != PA_BF16)
+    return fail(PA_ERR_INVALID, "pa_write_kv: unknown dtype %d", (int)dtype);
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_INVALID, "pa_write_kv: need num_tokens >= 0 and positive sizes");
+  const long long row_bytes = (long long)num_kv_heads * head_dim * elem_bytes(dtype);
+  if (row_bytes % 16 != 0 || row_bytes / 16 > (1 << 22))
+    return fail(PA_ERR_UNSUPPORTED, "pa_write_kv: a token row of %lld bytes is not a multiple of 16 "
+                "bytes or exceeds 64 MiB", row_bytes);
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache)
+    return fail(PA_ERR_INVALID, "pa_write_kv: null pointer argument");
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PA_ERR_INVALID, "pa_write_kv: k, v and caches must be 16-byte aligned");
+  const long long pool_slots = (long long)num_blocks * block_size;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (debug_checks()) {
+    pa_status bad = PA_OK;
+    std::vector<int32_t> slots;
+    if (!to_host(slots, slot_mapping, num_tokens, st, &bad)) return bad;
+    std::vector<int32_t> live;
+    for (int i = 0; i < num_tokens; ++i) {
+      if (slots[i] >= pool_slots)
+        return fail(PA_ERR_INVALID, "pa_write_kv: slot_mapping[%d] = %d beyond the pool", i, slots[i]);
+      if (slots[i] >= 0) live.push_back(slots[i]);
+    }
+    std::sort(live.begin(), live.end());
+    for (size_t i = 1; i < live.size(); ++i)
+      if (live[i] == live[i - 1]) return fail(PA_ERR_INVALID, "pa_write_kv: slot %d named twice", live[i]);
+  }
+  hipError_t e = launch_write_kv(k, v, slot_mapping, k_cache, v_cache, num_tokens, (int)row_bytes,
+                                 pool_slots, st);
+  if (e != hipSuccess) return hip_fail(e, "pa_write_kv launch");
+  return PA_OK;
+}
+
+pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst_pairs, int num_pairs,
+                         int block_size, int num_kv_heads, int head_dim, int num_blocks,
+                         pa_dtype dtype, void* stream) {
+  if (dtype != PA_F32 && dtype != PA_F16 && dtype != PA_BF16)
+    return fail(PA_ERR_INVALID, "pa_copy_blocks: unknown dtype %d", (int)dtype);
+  if (num_pairs < 0 || block_size <= 0 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks <= 0)
+    return fail(PA_ERR_INVALID, "pa_copy_blocks: need num_pairs >= 0 and positive sizes");
+  const long long block_bytes = (long long)block_size * num_kv_heads * head_dim * elem_bytes(dtype);
+  if (block_bytes % 16 != 0 || block_bytes / 16 > 65535LL * 1024)
+    return fail(PA_ERR_UNSUPPORTED, "pa_copy_blocks: a block of %lld bytes is not a multiple of 16 "
+                "bytes or exceeds 1 GiB", block_bytes);
+  if (num_pairs == 0) return PA_OK;
+  if (!k_cache || !v_cache || !src_dst_pairs)
+    return fail(PA_ERR_INVALID, "pa_copy_blocks: null pointer argument");
+  if (!aligned16(k_cache) || !aligned16(v_cache))
+    return fail(PA_ERR_INVALID, "pa_copy_blocks: caches must be 16-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (debug_checks()) {
+    pa_status bad = PA_OK;
+    std::vector<int32_t> pr;
+    if (!to_host(pr, src_dst_pairs, (size_t)num_pairs * 2, st, &bad)) return bad;
+    std::vector<int32_t> srcs, dsts;
+    for (int i = 0; i < num_pairs; ++i) {
+      const int s = pr[2 * i], d = pr[2 * i + 1];
+      if (s < 0 || s >= num_blocks || d < 0 || d >= num_blocks)
+        return fail(PA_ERR_INVALID, "pa_copy_blocks: pair %d (%d, %d) outside [0, %d)", i, s, d, num_blocks);
+      if (s == d) return fail(PA_ERR_INVALID, "pa_copy_blocks: pair %d copies block %d onto itself", i, s);
+      srcs.push_back(s);
+      dsts.push_back(d);
+    }
+    std::sort(srcs.begin(), srcs.end());
+    std::sort(dsts.begin(), dsts.end());
+    for (size_t i = 1; i < dsts.size(); ++i)
+      if (dsts[i] == dsts[i - 1]) return fail(PA_ERR_INVALID, "pa_copy_blocks: dst %d repeated", dsts[i]);
+    for (int d : dsts)
+      if (std::binary_search(srcs.begin(), srcs.end(), d))
+        return fail(PA_ERR_INVALID, "pa_copy_blocks: block %d is both a src and a dst", d);
+  }
+  hipError_t e = launch_copy_blocks(k_cache, v_cache, src_dst_pairs, num_pairs, block_bytes,
+                                    num_blocks, st);
+  if (e != hipSuccess) return hip_fail(e, "pa_copy_blocks launch");
+  return PA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,10 @@
+// Decode-attention instantiations for one element type (see decode_kernel.h).
+#include "decode_kernel.h"
+
+namespace pagedkv {
+
+hipError_t launch_decode_f16(const DecodeParams& p, hipStream_t stream) {
+  return dispatch_decode<kF16>(p, stream);
+}
+
+}  // namespace pagedkv

@@ -1,0 +1,140 @@
+"""The C-ABI library on the CPU: it loads, exports every declared entry point, plans
+workspace as documented and rejects host-visible argument errors before launching
+anything.  None of these calls reaches a kernel, so no GPU is needed."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = [os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+           if f.endswith(".h")]
+
+
+@pytest.fixture(scope="module")
+def pk():
+    import paged_kv_cache_351_amd as pk
+    if not os.path.exists(pk.LIB_PATH):
+        from paged_kv_cache_351_amd.build import build
+        build(verbose=False)
+    pk.lib()
+    return pk
+
+
+def declared_functions():
+    names = []
+    for h in HEADERS:
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names += re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(pa_[a-z0-9_]+)\s*\(",
+                            src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["pa_decode", "pa_write_kv", "pa_copy_blocks", "pa_decode_workspace_size",
+              "pa_last_error", "pa_version", "pa_decode_partition_tokens"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(pk):
+    L = ctypes.CDLL(pk.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(L, n), n
+
+
+def test_binding_names_match_the_abi(pk):
+    for n in ["pa_decode", "pa_write_kv", "pa_copy_blocks", "pa_decode_workspace_size",
+              "pa_decode_partition_tokens", "pa_last_error", "pa_version"]:
+        assert callable(getattr(pk, n))
+
+
+def test_version(pk):
+    assert pk.pa_version() == 1
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32])
+def test_partition_size_rules(pk, bs):
+    P = pk.pa_decode_partition_tokens(bs)
+    assert P % bs == 0 and P % 16 == 0 and P <= 64 * bs and P > 0
+    assert pk.pa_decode_partition_tokens(12) == 0
+
+
+@pytest.mark.parametrize("N,H,D,bs,L", [(256, 32, 128, 16, 4096), (32, 64, 128, 8, 32768),
+                                        (4, 4, 64, 16, 41), (64, 32, 128, 32, 2048), (3, 8, 64, 16, 0)])
+def test_workspace_size_formula(pk, N, H, D, bs, L):
+    P = pk.pa_decode_partition_tokens(bs)
+    parts = max(1, math.ceil(L / P))
+    got = pk.pa_decode_workspace_size(N, H, D, bs, L)
+    if parts == 1:
+        assert got == 0
+    else:
+        rows = N * H * parts
+        ml = -(-(rows * 8) // 256) * 256
+        assert got == ml + rows * D * 4
+
+
+def test_workspace_size_rejects_bad_arguments(pk):
+    assert pk.pa_decode_workspace_size(-1, 8, 128, 16, 100) == 0
+    assert pk.pa_decode_workspace_size(4, 8, 128, 12, 100) == 0
+
+
+FAKE = 1 << 20  # a 16-byte aligned, non-null address that is never dereferenced
+
+
+def call_decode(pk, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, lens=FAKE, N=4, H=8, HKV=2, D=128, BS=16, NB=100,
+             MB=10, L=160, scale=0.088, dt=2, out=FAKE, ws=FAKE, wsb=0, stream=None)
+    a.update(over)
+    return pk.lib().pa_decode(a["q"], a["k"], a["v"], a["bt"], a["lens"], a["N"], a["H"], a["HKV"],
+                              a["D"], a["BS"], a["NB"], a["MB"], a["L"], a["scale"], a["dt"],
+                              a["out"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status,words", [
+    (dict(D=96), 2, "head_dim"),
+    (dict(BS=12), 2, "block_size"),
+    (dict(H=9), 1, "multiple"),
+    (dict(H=34, HKV=1), 2, "at most 16"),
+    (dict(dt=7), 1, "dtype"),
+    (dict(L=161), 1, "max_seq_len"),
+    (dict(NB=0), 1, "num_blocks"),
+    (dict(q=None), 1, "null"),
+    (dict(out=FAKE + 4), 1, "aligned"),
+    (dict(scale=float("nan")), 1, "finite"),
+    (dict(L=1000, MB=100, wsb=16), 3, "workspace"),
+    (dict(L=1000, MB=100, ws=None, wsb=1 << 30), 3, "workspace"),
+])
+def test_decode_rejects_host_visible_errors(pk, over, status, words):
+    assert call_decode(pk, **over) == status
+    assert words in pk.pa_last_error()
+
+
+def test_decode_with_no_sequences_is_a_no_op(pk):
+    assert call_decode(pk, N=0, q=None, out=None) == 0
+
+
+def test_write_and_copy_reject_host_visible_errors(pk):
+    L = pk.lib()
+    # write: row of 3 f16 elements x 2 heads = 12 bytes is not a multiple of 16
+    assert L.pa_write_kv(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, 3, 16, 10, 1, None) == 2
+    assert "multiple of 16" in pk.pa_last_error()
+    assert L.pa_write_kv(FAKE, None, FAKE, FAKE, FAKE, 4, 8, 128, 16, 10, 2, None) == 1
+    assert L.pa_write_kv(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 8, 128, 16, 10, 2, None) == 1
+    assert L.pa_write_kv(None, None, None, None, None, 0, 8, 128, 16, 10, 2, None) == 0
+    assert L.pa_copy_blocks(FAKE, FAKE, None, 3, 16, 8, 128, 10, 2, None) == 1
+    assert L.pa_copy_blocks(FAKE, FAKE, FAKE, 3, 16, 8, 128, 10, 9, None) == 1
+    assert L.pa_copy_blocks(None, None, None, 0, 16, 8, 128, 10, 2, None) == 0
+
+
+def test_binding_rejects_cpu_tensors(pk):
+    import torch
+    q = torch.zeros(1, 4, 64)
+    with pytest.raises(ValueError):
+        pk.pa_decode(q, torch.zeros(2, 16, 4, 64), torch.zeros(2, 16, 4, 64),
+                     torch.zeros(1, 1, dtype=torch.int32), torch.ones(1, dtype=torch.int32), 4,
+                     0.125, q, max_seq_len=1)

@@ -1,0 +1,92 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the benchmark
+times.  The oracle recomputes a seeded sample of sequences (always including the
+shortest and the longest); writes and block copies are checked bit for bit over the
+whole pool."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from workloads import as_numpy
+from _gpu import assert_close, bits, gpu_decode, log, oracle_decode, pk, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pk()
+
+
+def sample(b, n, seed=0):
+    lens = b.seq_lens.numpy()
+    rng = np.random.default_rng(seed)
+    pick = set(rng.choice(len(lens), size=min(n, len(lens)), replace=False).tolist())
+    pick |= {int(lens.argmin()), int(lens.argmax())}
+    return sorted(pick)
+
+
+def apply_write_and_check(b, d, with_copy=False):
+    """Run (copy +) write on the GPU, apply the oracle's to the CPU pool, compare all bits,
+    and leave the batch's CPU pool in the written state."""
+    m = pk()
+    kc, vc = as_numpy(b.k_cache), as_numpy(b.v_cache)
+    if with_copy:
+        m.pa_copy_blocks(d.kc, d.vc, d.pairs)
+        kc, vc = oracle.copy_blocks(kc, vc, as_numpy(b.cow_pairs))
+    m.pa_write_kv(d.new_k, d.new_v, d.slots, d.kc, d.vc)
+    kc, vc = oracle.write_kv(as_numpy(b.new_k), as_numpy(b.new_v), as_numpy(b.slot_mapping), kc, vc)
+    torch.cuda.synchronize()
+    ek, ev = torch.from_numpy(kc), torch.from_numpy(vc)
+    assert torch.equal(bits(d.kc), bits(ek).cuda())
+    assert torch.equal(bits(d.vc), bits(ev).cuda())
+    if b.dtype == "bf16":
+        ek, ev = ek.view(torch.bfloat16), ev.view(torch.bfloat16)
+    b.k_cache, b.v_cache = ek, ev
+
+
+def check_sampled(b, d, n, what):
+    seqs = sample(b, n)
+    log(f"{what}: decode, oracle on sequences {seqs}")
+    got = gpu_decode(b, d)
+    ref = oracle_decode(b, seqs=seqs)
+    err = assert_close(got[seqs], ref, b.dtype, what)
+    assert np.isfinite(got).all()
+    log(f"{what}: max abs err {err:.3e}")
+
+
+def test_llama3_8b_full():
+    b = workloads.llama3_8b()
+    d = to_dev(b)
+    log("llama3_8b full: write 256 tokens")
+    apply_write_and_check(b, d)
+    check_sampled(b, d, 14, "llama3_8b full")
+
+
+def test_llama7b_full():
+    b = workloads.llama7b()
+    check_sampled(b, to_dev(b), 10, "llama7b full")
+
+
+def test_opt13b_shared_full():
+    b = workloads.opt13b_shared()
+    check_sampled(b, to_dev(b), 10, "opt13b_shared full")
+
+
+def test_opt13b_cow_full():
+    b = workloads.opt13b_cow()
+    d = to_dev(b)
+    log("opt13b_cow full: copy 224 blocks, write 256 tokens")
+    assert len(b.cow_pairs) == 224
+    apply_write_and_check(b, d, with_copy=True)
+    check_sampled(b, d, 10, "opt13b_cow full")
+
+
+@pytest.mark.parametrize("block_size", [8, 16, 32])
+def test_llama2_70b_full(block_size):
+    b = workloads.llama2_70b(block_size=block_size)
+    check_sampled(b, to_dev(b), 2, f"llama2_70b B={block_size} full")
