@@ -1,0 +1,200 @@
+"""Benchmark: paged decode attention on one MI355X, Llama-3-8B-shaped GQA layer.
+
+One step = pa_write_kv of 256 new tokens (one per sequence) followed by pa_decode
+over all 256 sequences (decode kernel + split-K reduce kernel), on one stream, with
+every input already resident in HBM.  Workload: 256 sequences, 32 query / 8 KV
+heads, head_dim 128, bf16 KV and q, fp32 accumulation, block size 16, lengths
+uniform in [512, 4096] (seed 0), 70,000-block pool with random block placement.
+
+Prints ONE JSON line.  ``value`` is the K/V bytes the decode step must read
+(each (token, KV head) row of K and V once) divided by the measured step time;
+``roofline`` reports the decode call alone, timed with HIP events on the stream it
+runs on; ``cpu_baseline`` times the float64 CPU oracle on the host.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+    python bench.py --copy-calibration   # a block copy of known size, for counter scaling
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import paged_kv_cache_351_amd as pk  # noqa: E402
+import workloads  # noqa: E402
+
+METRIC = "paged-decode KV GB/s read (% of HBM peak) and seqs/s, Llama-3-8B-shaped, 1 GPU"
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, vendor figure
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_llama3_8b_traffic.json")
+KERNEL_SOURCES = ["decode_kernel.h", "decode_bf16.hip", "common.h", "api.hip"]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_sha():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_cache_351_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per decode call from the committed counter runs, or None when they
+    were taken on different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_sha") != kernel_sha():
+        return None
+    return t.get("hbm_bytes_per_call")
+
+
+def copy_calibration(steps):
+    """pa_copy_blocks of 2 x 16384 blocks x 32 KiB: 1 GiB read and 1 GiB written per launch."""
+    dev = torch.device("cuda:0")
+    nb, B, H, D = 32768, 16, 8, 128
+    kc = torch.zeros(nb, B, H, D, dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    half = nb // 2
+    pairs = torch.stack([torch.arange(half), torch.arange(half) + half], 1).int().to(dev)
+    for _ in range(steps):
+        pk.pa_copy_blocks(kc, vc, pairs)
+    torch.cuda.synchronize()
+    per = half * B * H * D * 2 * 2
+    print(json.dumps({"copy_calibration": True, "launches": steps, "read_bytes_per_launch": per,
+                      "write_bytes_per_launch": per}))
+
+
+def cpu_baseline(b, gpu_out, time_cap=25.0):
+    """The float64 oracle on the host: the step's write, then decode over the workload's
+    sequences in order until all are done or the time cap is reached.  Also reports its
+    max abs difference from the GPU output on those sequences."""
+    import oracle
+    from workloads import as_numpy
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads = 1
+    q, bt, lens = as_numpy(b.q), as_numpy(b.block_tables), as_numpy(b.seq_lens)
+    done, err = 0, 0.0
+    t0, c0 = time.time(), time.process_time()
+    # the step's write of the new tokens, then decode sequence by sequence
+    kc, vc = oracle.write_kv(as_numpy(b.new_k), as_numpy(b.new_v), as_numpy(b.slot_mapping),
+                             as_numpy(b.k_cache), as_numpy(b.v_cache))
+    while done < b.num_seqs and time.time() - t0 < time_cap:
+        ref = oracle.paged_decode(q, kc, vc, bt, lens, b.scale, b.dtype, seqs=[done])
+        err = max(err, float(np.abs(gpu_out[done] - ref[0]).max()))
+        done += 1
+    wall, cpu = time.time() - t0, time.process_time() - c0
+    kv = int(lens[:done].astype(np.int64).sum()) * b.num_kv_heads * b.head_dim * 2 * 2
+    return {"value": kv / wall / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"write of all {b.num_seqs} new tokens, then decode of the first {done} of "
+                      f"{b.num_seqs} sequences of the same workload (numpy float64, "
+                      f"{kv / 1e9:.3f} GB of K/V)",
+            "seqs_per_s": done / wall, "wall_s": wall, "cpu_s": cpu,
+            "host_cpus": len(os.sched_getaffinity(0)),
+            "max_abs_err_gpu_vs_oracle": err}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    pk.lib()
+    if args.copy_calibration:
+        copy_calibration(max(1, args.steps))
+        return
+
+    dev = torch.device("cuda:0")
+    log("building the llama3_8b workload (seed 0)")
+    b = workloads.llama3_8b(seed=0)
+    q, kc, vc = b.q.to(dev), b.k_cache.to(dev), b.v_cache.to(dev)
+    bt, lens = b.block_tables.to(dev), b.seq_lens.to(dev)
+    nk, nv, slots = b.new_k.to(dev), b.new_v.to(dev), b.slot_mapping.to(dev)
+    out = torch.empty_like(q)
+    max_len = b.max_seq_len
+    ws = pk.decode_workspace(q, b.block_size, max_len)
+    kv_bytes = b.kv_bytes()
+    stream = torch.cuda.current_stream()
+
+    def step(ev0=None, ev1=None):
+        pk.pa_write_kv(nk, nv, slots, kc, vc)
+        if ev0 is not None:
+            ev0.record(stream)
+        pk.pa_decode(q, kc, vc, bt, lens, b.num_kv_heads, b.scale, out, max_seq_len=max_len,
+                     workspace=ws)
+        if ev1 is not None:
+            ev1.record(stream)
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    log(f"timing {K} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(*ev[i])
+    torch.cuda.synchronize()
+    total = time.perf_counter() - t0
+    dec_ms = np.array([a.elapsed_time(z) for a, z in ev])
+    dec_avg = float(dec_ms.mean())
+
+    ms_per_step = total * 1e3 / K
+    value = kv_bytes / (total / K) / 1e9
+    achieved = kv_bytes / (dec_avg * 1e-3) / 1e9
+    traffic = measured_traffic()
+    res = {
+        "metric": METRIC, "value": value, "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "llama3_8b_gqa_decode", "num_seqs": b.num_seqs, "num_heads": 32,
+                   "num_kv_heads": 8, "head_dim": 128, "block_size": 16,
+                   "seq_len_range": [512, 4096], "num_blocks": b.num_blocks, "write_tokens": 256,
+                   "seed": 0, "kv_bytes_per_step": kv_bytes,
+                   "partition_tokens": pk.pa_decode_partition_tokens(16)},
+        "pct_of_hbm_peak": 100.0 * value / HBM_PEAK_GBS,
+        "seqs_per_s": b.num_seqs / (total / K),
+        "roofline": {"kernel": "pa_decode (decode_kernel + reduce_kernel)", "bound": "hbm",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": kv_bytes,
+                     "avg_launch_us": dec_avg * 1e3, "p10_us": float(np.percentile(dec_ms, 10)) * 1e3,
+                     "p90_us": float(np.percentile(dec_ms, 90)) * 1e3},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline: float64 oracle on the host")
+        torch.cuda.synchronize()
+        res["cpu_baseline"] = cpu_baseline(b, out.float().cpu().double().numpy())
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -153,6 +153,8 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
     return fail(PA_ERR_INVALID, "pa_decode: q, caches and out must be 16-byte aligned");
 
   const WorkspaceLayout ws = plan_workspace(num_seqs, num_heads, head_dim, block_size, max_seq_len);
+  if (ws.max_parts > 65535)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: max_seq_len %d needs more than 65535 partitions", max_seq_len);
   if (ws.total > 0) {
     if (!workspace || workspace_bytes < ws.total)
       return fail(PA_ERR_WORKSPACE, "pa_decode: workspace of %zu bytes needed, %zu given", ws.total,

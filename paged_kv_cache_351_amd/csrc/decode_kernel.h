@@ -10,11 +10,18 @@
 // section "2）PagedAttention 算子").
 //
 // Work decomposition
-//   One 64-lane wave (= one workgroup) per (context partition, KV head,
-//   sequence).  A partition is part_tokens consecutive tokens (a multiple of the
+//   One 64-lane wave (= one workgroup) per (KV head, sequence, context
+//   partition).  A partition is part_tokens consecutive tokens (a multiple of the
 //   block size); the wave walks it in tiles of 16 tokens.  Every query head of
 //   the KV head's group (g = num_heads / num_kv_heads <= GP) is handled by the
 //   same wave, so each K/V row is read from HBM once.
+//   Grid order: x = KV head, y = sequence, z = partition.  Workgroups are handed
+//   to the eight XCDs round-robin in linear order, so consecutive ids must carry
+//   similar work: with the partition index slowest, every XCD gets a fair share
+//   of first partitions (which every sequence has) and of late ones (which only
+//   long sequences have), and the empty tail partitions come last.  With the
+//   partition index fastest instead, partition p would always land on XCD p mod 8
+//   and the chip would run at the speed of its busiest XCD.
 //
 // Lane roles (lane = 16 * grp + col, grp = 0..3, col = 0..15)
 //   q.K^T on the matrix cores: v_mfma_f32_16x16x32_{bf16,f16} (or 16x16x4_f32)
@@ -41,8 +48,9 @@
 // Logits are taken in base 2 (scale * log2 e folded in), so every exponential is
 // one v_exp_f32.  Running maxima start at a finite -1e30 so that a stream with
 // no valid token yet never forms inf - inf.  Tokens past the sequence end in the
-// last tile are excluded by selects, never by multiplying with 0, so a NaN in
-// an unused slot cannot leak into the result.
+// last tile are redirected to the sequence's last token before loading (so no
+// unused slot is ever read) and their scores are replaced by -inf with a select,
+// which makes their weights exactly 0.
 #pragma once
 
 #include <type_traits>
@@ -165,9 +173,9 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
   const int lane = threadIdx.x;
   const int grp = lane >> 4;
   const int col = lane & 15;
-  const int part = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int s = blockIdx.z;
+  const int kvh = blockIdx.x;
+  const int s = blockIdx.y;
+  const int part = blockIdx.z;
   const int g = p.group;
   const int head0 = kvh * g;
   const int P = p.part_tokens;
@@ -222,47 +230,37 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
     uint32_t v[4][VW];
   };
 
-  // Tile tt covers partition tokens [16 tt, 16 tt + 16).  Rows past the sequence
-  // end are still inside an allocated block (or block 0) and are masked later.
+  // Tile tt covers partition tokens [16 tt, 16 tt + 16).  A token index past the
+  // partition's last token is clamped to that token, so every load reads a real
+  // row of this sequence (never an unused slot); such tokens get weight exactly 0
+  // from the score mask below.  Loads are therefore always legal, and the
+  // prefetch of a tile past the end simply re-reads the last one (cache hits).
+  const int last = n_tok - 1;
   auto load_tile = [&](Tile& T, int tt) __attribute__((always_inline)) {
-    int pk, ok;          // K row of this lane: token 16 tt + col
-    int pv[4], ov[4];    // V rows of this lane: tokens 16 tt + 4 grp + j
+    const int t0 = 16 * tt;
+    const int tk = min(t0 + col, last);        // K row of this lane
+    int tv[4];                                 // V rows of this lane
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tv[j] = min(t0 + 4 * grp + j, last);
+    int pk, pv[4];
     if constexpr (BS == 8) {
       const int ida = __builtin_amdgcn_readlane(my_id, 2 * tt);
       const int idb = __builtin_amdgcn_readlane(my_id, 2 * tt + 1);
-      pk = col < 8 ? ida : idb;
-      ok = col & 7;
+      pk = (tk & 8) ? idb : ida;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        pv[j] = grp < 2 ? ida : idb;
-        ov[j] = (4 * grp + j) & 7;
-      }
-    } else if constexpr (BS == 16) {
-      const int id = __builtin_amdgcn_readlane(my_id, tt);
-      pk = id;
-      ok = col;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        pv[j] = id;
-        ov[j] = 4 * grp + j;
-      }
+      for (int j = 0; j < 4; ++j) pv[j] = (tv[j] & 8) ? idb : ida;
     } else {
-      const int id = __builtin_amdgcn_readlane(my_id, tt >> 1);
-      const int base = (tt & 1) * 16;
+      const int id = __builtin_amdgcn_readlane(my_id, t0 / BS);
       pk = id;
-      ok = base + col;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        pv[j] = id;
-        ov[j] = base + 4 * grp + j;
-      }
+      for (int j = 0; j < 4; ++j) pv[j] = id;
     }
-    const char* kp = kbase + (size_t)pk * blk_bytes + (size_t)ok * tok_stride;
+    const char* kp = kbase + (size_t)pk * blk_bytes + (size_t)(tk % BS) * tok_stride;
 #pragma unroll
     for (int c = 0; c < NKC; ++c) T.k[c] = *reinterpret_cast<const u32x4*>(kp + (4 * c + grp) * 16);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
-      load_dwords<VW>(vbase + (size_t)pv[j] * blk_bytes + (size_t)ov[j] * tok_stride, T.v[j]);
+      load_dwords<VW>(vbase + (size_t)pv[j] * blk_bytes + (size_t)(tv[j] % BS) * tok_stride, T.v[j]);
   };
 
   float m = kNegBig;
@@ -274,7 +272,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
     for (int e = 0; e < VE; ++e) acc[h][e] = 0.f;
   const float sl2 = p.scale_log2e;
 
-  auto compute = [&](const Tile& T, int tt, bool masked) __attribute__((always_inline)) {
+  auto compute = [&](const Tile& T, int tt) __attribute__((always_inline)) {
     // S = K q^T on the matrix cores
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -292,14 +290,11 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
                                                     sc, 0, 0, 0);
       }
     }
-    // online softmax, stream (grp, head col)
+    // online softmax, stream (grp, head col); tokens past the end get -inf
+    const int lim = n_tok - 16 * tt - 4 * grp;
     float sv[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      float x = sc[r] * sl2;
-      if (masked && 16 * tt + 4 * grp + r >= n_tok) x = -__builtin_inff();
-      sv[r] = x;
-    }
+    for (int r = 0; r < 4; ++r) sv[r] = r < lim ? sc[r] * sl2 : -__builtin_inff();
     const float mn = fmaxf(m, fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
     const float alpha = fast_exp2(m - mn);
     float pr[4];
@@ -321,11 +316,6 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
     for (int j = 0; j < 4; ++j) {
       float vf[VE];
       unpack<DT, VW>(T.v[j], vf);
-      if (masked) {
-        const bool ok = 16 * tt + 4 * grp + j < n_tok;
-#pragma unroll
-        for (int e = 0; e < VE; ++e) vf[e] = ok ? vf[e] : 0.f;
-      }
       static_for<GP>([&](auto hc) {
         constexpr int h = decltype(hc)::value;
         const float pj = row_bcast<h>(pr[j]);
@@ -335,26 +325,26 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
     }
   };
 
-  // Two tiles in flight: while one is reduced, the next two are being fetched.
-  const int n_full = n_tok >> 4;
-  const int tail = n_tok & 15;
+  // Two tiles in flight: while one is reduced the next two are being fetched.  The
+  // loads are unconditional (clamped tile index) so no tile register is ever
+  // copied, and the scheduling barriers keep a refill after the last use of the
+  // registers it overwrites.
+  const int n_tiles = (n_tok + 15) >> 4;
+  const int lt = n_tiles - 1;
   Tile A, B;
-  if (n_full > 0) load_tile(A, 0);
-  if (n_full > 1) load_tile(B, 1);
-  int tt = 0;
-  for (; tt + 1 < n_full; tt += 2) {
-    compute(A, tt, false);
-    if (tt + 2 < n_full) load_tile(A, tt + 2);
-    compute(B, tt + 1, false);
-    if (tt + 3 < n_full) load_tile(B, tt + 3);
-  }
-  if (tt < n_full) {
-    compute(A, tt, false);
-    ++tt;
-  }
-  if (tail) {
-    load_tile(A, tt);
-    compute(A, tt, true);
+  load_tile(A, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  load_tile(B, min(1, lt));
+  __builtin_amdgcn_sched_barrier(0);
+  for (int tt = 0; tt < n_tiles; tt += 2) {
+    compute(A, tt);
+    __builtin_amdgcn_sched_barrier(0);
+    load_tile(A, min(tt + 2, lt));
+    __builtin_amdgcn_sched_barrier(0);
+    if (tt + 1 < n_tiles) compute(B, tt + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_tile(B, min(tt + 3, lt));
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // Merge the four per-group streams of every head.
@@ -451,7 +441,7 @@ hipError_t launch_one(const DecodeParams& p, hipStream_t stream) {
   DecodeParams args = p;
   void* kargs[] = {&args};
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&decode_kernel<DT, D, BS, GP>),
-                                 dim3(p.max_parts, p.num_kv_heads, p.num_seqs), dim3(64), kargs, 0, stream);
+                                 dim3(p.num_kv_heads, p.num_seqs, p.max_parts), dim3(64), kargs, 0, stream);
   if (e != hipSuccess || p.max_parts == 1) return e;
   return hipLaunchKernel(reinterpret_cast<const void*>(&reduce_kernel<DT, D>),
                          dim3(p.num_heads, p.num_seqs), dim3(64), kargs, 0, stream);
