@@ -13,6 +13,7 @@ runs on; ``cpu_baseline`` times the float64 CPU oracle on the host.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1]
     python bench.py --copy-calibration   # a block copy of known size, for counter scaling
+    python bench.py --record-traffic DEC_FETCH.csv DEC_WRITE.csv COPY_FETCH.csv COPY_WRITE.csv
 """
 
 import argparse
@@ -35,6 +36,7 @@ METRIC = "paged-decode KV GB/s read (% of HBM peak) and seqs/s, Llama-3-8B-shape
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, vendor figure
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_llama3_8b_traffic.json")
 KERNEL_SOURCES = ["decode_kernel.h", "decode_bf16.hip", "common.h", "api.hip"]
+DECODE_KERNELS = ["decode_kernel", "reduce_kernel"]   # kernels one pa_decode call launches
 
 
 def log(msg):
@@ -60,6 +62,55 @@ def measured_traffic():
     if t.get("kernel_sha") != kernel_sha():
         return None
     return t.get("hbm_bytes_per_call")
+
+
+def _pmc_per_dispatch(csv_path, counter, kernel_substr):
+    """Mean value of ``counter`` over the dispatches of kernels whose name contains
+    ``kernel_substr`` in a rocprofv3 ``--pmc ... -f csv`` counter_collection file (one row per
+    dispatch and counter; the value is the sum over hardware instances)."""
+    import csv
+    per = {}
+    with open(csv_path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row.get("Counter_Name") != counter or kernel_substr not in row.get("Kernel_Name", ""):
+                continue
+            key = row.get("Dispatch_Id") or row.get("Correlation_Id")
+            per[key] = per.get(key, 0.0) + float(row["Counter_Value"])
+    if not per:
+        raise SystemExit(f"{csv_path}: no {counter} rows for kernels matching {kernel_substr!r}")
+    return sum(per.values()) / len(per), len(per)
+
+
+def record_traffic(paths):
+    """Turn four rocprofv3 counter files into HBM bytes per decode call and write them to
+    the traffic file, tagged with the hash of the kernel sources they were taken on.
+
+    paths: decode FETCH_SIZE csv, decode WRITE_SIZE csv, calibration-copy FETCH_SIZE csv,
+    calibration-copy WRITE_SIZE csv.  FETCH_SIZE and WRITE_SIZE are in KiB per dispatch;
+    each is scaled by (known bytes / counter bytes) of the calibration copy, which reads
+    and writes exactly 1 GiB per launch."""
+    dec_f, dec_w, cal_f, cal_w = paths
+    known = 16384 * 16 * 8 * 128 * 2 * 2
+    cf, _ = _pmc_per_dispatch(cal_f, "FETCH_SIZE", "copy_blocks_kernel")
+    cw, _ = _pmc_per_dispatch(cal_w, "WRITE_SIZE", "copy_blocks_kernel")
+    fetch_scale, write_scale = known / (cf * 1024), known / (cw * 1024)
+    per_kernel = {}
+    total = 0.0
+    for name in DECODE_KERNELS:
+        f, nf = _pmc_per_dispatch(dec_f, "FETCH_SIZE", name)
+        w, nw = _pmc_per_dispatch(dec_w, "WRITE_SIZE", name)
+        rb, wb = f * 1024 * fetch_scale, w * 1024 * write_scale
+        per_kernel[name] = {"fetch_kib": f, "write_kib": w, "dispatches": [nf, nw],
+                            "read_bytes": rb, "write_bytes": wb}
+        total += rb + wb
+    out = {"kernel_sha": kernel_sha(), "hbm_bytes_per_call": total,
+           "fetch_scale": fetch_scale, "write_scale": write_scale,
+           "calibration_counter_kib": {"fetch": cf, "write": cw, "known_bytes_each": known},
+           "per_kernel": per_kernel}
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out))
 
 
 def copy_calibration(steps):
@@ -117,7 +168,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--record-traffic", nargs=4, metavar="CSV",
+                    help="decode FETCH_SIZE, decode WRITE_SIZE, copy FETCH_SIZE, copy WRITE_SIZE "
+                         "counter files from rocprofv3 --pmc -f csv")
     args = ap.parse_args()
+    if args.record_traffic:
+        record_traffic(args.record_traffic)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
