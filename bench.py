@@ -192,7 +192,7 @@ def main():
     nk, nv, slots = b.new_k.to(dev), b.new_v.to(dev), b.slot_mapping.to(dev)
     out = torch.empty_like(q)
     max_len = b.max_seq_len
-    ws = pk.decode_workspace(q, b.block_size, max_len)
+    ws = pk.decode_workspace(q, b.num_kv_heads, max_len)
     kv_bytes = b.kv_bytes()
     stream = torch.cuda.current_stream()
 
@@ -234,8 +234,7 @@ def main():
         "config": {"workload": "llama3_8b_gqa_decode", "num_seqs": b.num_seqs, "num_heads": 32,
                    "num_kv_heads": 8, "head_dim": 128, "block_size": 16,
                    "seq_len_range": [512, 4096], "num_blocks": b.num_blocks, "write_tokens": 256,
-                   "seed": 0, "kv_bytes_per_step": kv_bytes,
-                   "partition_tokens": pk.pa_decode_partition_tokens(16)},
+                   "seed": 0, "kv_bytes_per_step": kv_bytes},
         "pct_of_hbm_peak": 100.0 * value / HBM_PEAK_GBS,
         "seqs_per_s": b.num_seqs / (total / K),
         "roofline": {"kernel": "pa_decode (decode_kernel + reduce_kernel)", "bound": "hbm",

@@ -70,18 +70,13 @@ int pa_version(void);
  * ("" if none).  The string stays valid until the next call on that thread. */
 const char* pa_last_error(void);
 
-/* Tokens per context partition that pa_decode uses for these arguments.  A
- * sequence longer than one partition is split into ceil(len / partition)
- * pieces, each reduced on its own, and the pieces are merged by a second
- * kernel.  The size is a multiple of block_size and of 16; PA_PARTITION_TOKENS
- * in the environment (read once) overrides the default of 512.  Returns 0 for
- * an unsupported block_size. */
-int pa_decode_partition_tokens(int block_size);
-
-/* Bytes of workspace pa_decode needs for these arguments (0 when no sequence
- * can need more than one partition).  Returns 0 for invalid arguments. */
-size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_dim,
-                                int block_size, int max_seq_len);
+/* Bytes of workspace pa_decode needs for these arguments (0 for invalid
+ * arguments).  It depends only on the shapes: the number of waves a call may
+ * launch is bounded by num_seqs * num_kv_heads * ceil(max_seq_len / 16) / 8
+ * and by 8192, and each wave needs 16 bytes of bookkeeping plus two partial
+ * results of (head_dim + 2) floats per query head of its group. */
+size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                                int max_seq_len);
 
 /*
  * pa_decode -- one decode step of paged attention.
@@ -95,6 +90,12 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_dim,
  * by block ([PA-notes] §4; the dense formula with 1/sqrt(d) is [vLLM-what]
  * "2）PagedAttention 算子").  A sequence with L = 0 yields zeros.
  *
+ * Work split: the step's (sequence, KV head) pairs are cut into 16-token tiles
+ * and the launched waves (as many as the device holds at once) take equal runs
+ * of consecutive tiles, whatever the length mix.  A pair cut by a run boundary
+ * is finished by a second kernel on the same stream, which merges the pieces'
+ * running maxima, sums and accumulators with the same rule.
+ *
  *   q            [num_seqs][num_heads][head_dim]            dtype
  *   k_cache      [num_blocks][block_size][num_kv_heads][head_dim]  dtype
  *   v_cache      same shape as k_cache
@@ -103,15 +104,17 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_dim,
  *   seq_lens     [num_seqs] int32, 0 <= L <= max_seq_len
  *   out          [num_seqs][num_heads][head_dim] dtype; must not alias inputs
  *   workspace    device scratch of at least pa_decode_workspace_size(...)
- *                bytes (may be NULL when that size is 0); its contents on
- *                entry do not matter and are clobbered
+ *                bytes, 256-byte aligned; its contents on entry do not
+ *                matter and are clobbered
  *   max_seq_len  caller's upper bound on every seq_lens[s]; must be
- *                <= max_blocks_per_seq * block_size.  Lengths above it are
- *                clamped to it.
+ *                <= max_blocks_per_seq * block_size and <= 2^24.  Lengths
+ *                above it are clamped to it, negative lengths to 0.
  * Supported: head_dim in {64, 128}; block_size in {8, 16, 32}; num_heads a
  * multiple of num_kv_heads with group size num_heads / num_kv_heads <= 16.
  * Accumulation is float32; the output is rounded once, to nearest even.
- * Results are deterministic: the same inputs give the same bits.
+ * Results are deterministic on a given device: the same inputs give the same
+ * bits (the split depends on the lengths and the device's wave capacity).
+ * The current HIP device must be the stream's device.
  */
 pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
                     const int32_t* block_tables, const int32_t* seq_lens,

@@ -45,10 +45,8 @@ def lib():
     L.pa_version.argtypes = []
     L.pa_last_error.restype = ctypes.c_char_p
     L.pa_last_error.argtypes = []
-    L.pa_decode_partition_tokens.restype = i32
-    L.pa_decode_partition_tokens.argtypes = [i32]
     L.pa_decode_workspace_size.restype = sz
-    L.pa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]
+    L.pa_decode_workspace_size.argtypes = [i32, i32, i32, i32, i32]  # N, Hq, Hkv, D, max_len
     L.pa_decode.restype = i32
     L.pa_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32,
                             vp, vp, sz, vp]
@@ -96,18 +94,15 @@ def _dev(name, t, dtype=None, ndim=None):
         raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
 
 
-def pa_decode_partition_tokens(block_size):
-    return lib().pa_decode_partition_tokens(int(block_size))
+def pa_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, max_seq_len):
+    return int(lib().pa_decode_workspace_size(int(num_seqs), int(num_heads), int(num_kv_heads),
+                                              int(head_dim), int(max_seq_len)))
 
 
-def pa_decode_workspace_size(num_seqs, num_heads, head_dim, block_size, max_seq_len):
-    return int(lib().pa_decode_workspace_size(int(num_seqs), int(num_heads), int(head_dim),
-                                              int(block_size), int(max_seq_len)))
-
-
-def decode_workspace(q, block_size, max_seq_len):
-    """A workspace tensor sized for ``pa_decode`` with these arguments (None if none is needed)."""
-    n = pa_decode_workspace_size(q.shape[0], q.shape[1], q.shape[2], block_size, max_seq_len)
+def decode_workspace(q, num_kv_heads, max_seq_len):
+    """A workspace tensor sized for ``pa_decode`` with these arguments (None if the
+    arguments are invalid; pa_decode then reports why)."""
+    n = pa_decode_workspace_size(q.shape[0], q.shape[1], num_kv_heads, q.shape[2], max_seq_len)
     if n == 0:
         return None
     return torch.empty(n, dtype=torch.uint8, device=q.device)
@@ -123,7 +118,7 @@ def pa_decode(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, scale, 
     block_tables: int32 [num_seqs, max_blocks_per_seq]; seq_lens: int32 [num_seqs];
     max_seq_len: host int bound on seq_lens (no device sync is made);
     workspace: uint8 tensor of at least pa_decode_workspace_size(...) bytes, allocated
-    here if omitted.
+    here if omitted (pass one to keep allocation off the hot path).
     """
     _dev("q", q, ndim=3)
     if q.dtype not in _DTYPE:
@@ -143,7 +138,7 @@ def pa_decode(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, scale, 
     if out.shape != q.shape or block_tables.shape[0] != num_seqs or seq_lens.shape[0] != num_seqs:
         raise ValueError("q, out, block_tables and seq_lens disagree on num_seqs or shape")
     if workspace is None:
-        workspace = decode_workspace(q, block_size, max_seq_len)
+        workspace = decode_workspace(q, num_kv_heads, max_seq_len)
     if workspace is not None:
         _dev("workspace", workspace)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
@@ -190,5 +185,5 @@ def pa_copy_blocks(k_cache, v_cache, src_dst_pairs, *, stream=None):
 
 
 __all__ = ["pa_decode", "pa_write_kv", "pa_copy_blocks", "pa_decode_workspace_size",
-           "pa_decode_partition_tokens", "decode_workspace", "pa_last_error", "pa_version",
+           "decode_workspace", "pa_last_error", "pa_version",
            "PagedKVError", "lib", "LIB_PATH"]

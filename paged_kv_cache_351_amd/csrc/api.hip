@@ -6,11 +6,15 @@
 #include <string.h>
 
 #include <algorithm>
+#include <map>
+#include <mutex>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "common.h"
 #include "pagedkv.h"
+#include "split.h"
 
 using namespace pagedkv;
 
@@ -45,45 +49,70 @@ bool debug_checks() {
   return on;
 }
 
-int requested_partition() {
-  static const int v = env_int("PA_PARTITION_TOKENS", 512);
+// PA_DECODE_WAVES caps the number of decode waves (for tuning sweeps); 0 = no cap.
+int requested_waves() {
+  static const int v = env_int("PA_DECODE_WAVES", 0);
   return v;
 }
 
 bool valid_block_size(int bs) { return bs == 8 || bs == 16 || bs == 32; }
 
-// Partition size: a multiple of 16 (the tile) and of the block size, at most
-// 64 blocks (one block id per lane of the wave).
-int partition_tokens(int bs) {
-  if (!valid_block_size(bs)) return 0;
-  const int unit = bs > 16 ? bs : 16;
-  int p = requested_partition() / unit * unit;
-  if (p < unit) p = unit;
-  if (p > 64 * bs) p = 64 * bs;
-  return p;
-}
-
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+constexpr int kMaxSeqLen = 1 << 24;
+
+// Workspace of one pa_decode call: per launched wave a 16-byte record saying which
+// split pair it owns, and two partial-result slots (running max and sum, and the
+// unnormalised accumulator, for each query head of the group).  It is sized for
+// the most waves the call could launch, a bound that depends only on the shapes
+// (one wave per kMinTilesPerWave tiles of the longest possible batch, at most
+// kMaxWaves); the launch never uses more waves than that.
 struct WorkspaceLayout {
-  int max_parts;
-  size_t ml_bytes;
+  int waves;
+  size_t ml_offset;
   size_t acc_offset;
   size_t total;
 };
 
-WorkspaceLayout plan_workspace(int num_seqs, int num_heads, int head_dim, int bs, int max_seq_len) {
-  WorkspaceLayout w{1, 0, 0, 0};
-  const int P = partition_tokens(bs);
-  w.max_parts = max_seq_len > 0 ? (max_seq_len + P - 1) / P : 1;
-  if (w.max_parts <= 1) return w;
-  const size_t rows = (size_t)num_seqs * num_heads * w.max_parts;
-  w.ml_bytes = rows * 2 * sizeof(float);
-  w.acc_offset = align_up(w.ml_bytes, 256);
-  w.total = w.acc_offset + rows * head_dim * sizeof(float);
+WorkspaceLayout plan_workspace(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                               int max_seq_len) {
+  WorkspaceLayout w{0, 0, 0, 0};
+  const long long t_max = (long long)num_seqs * num_kv_heads * tiles_of(max_seq_len);
+  long long waves = waves_used(t_max, kMaxWaves);
+  if (waves < 1) waves = 1;
+  const size_t g = (size_t)(num_heads / num_kv_heads);
+  w.waves = (int)waves;
+  w.ml_offset = align_up((size_t)waves * 16, 256);
+  w.acc_offset = w.ml_offset + align_up(2 * (size_t)waves * g * 2 * sizeof(float), 256);
+  w.total = w.acc_offset + 2 * (size_t)waves * g * head_dim * sizeof(float);
   return w;
+}
+
+// Waves of `kernel` the current device holds at once (one 64-lane wave per
+// workgroup), cached per device and kernel.
+hipError_t resident_waves(const void* kernel, int* out) {
+  static std::mutex mu;
+  static std::map<std::pair<int, const void*>, int> cache;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find({dev, kernel});
+  if (it != cache.end()) {
+    *out = it->second;
+    return hipSuccess;
+  }
+  int cus = 0, per_cu = 0;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64, 0);
+  if (e != hipSuccess) return e;
+  const int n = std::max(1, cus * per_cu);
+  cache[{dev, kernel}] = n;
+  *out = n;
+  return hipSuccess;
 }
 
 template <typename T>
@@ -103,18 +132,16 @@ bool to_host(std::vector<T>& dst, const void* src, size_t n, hipStream_t stream,
 
 extern "C" {
 
-int pa_version(void) { return 1; }
+int pa_version(void) { return 2; }
 
 const char* pa_last_error(void) { return g_err.c_str(); }
 
-int pa_decode_partition_tokens(int block_size) { return partition_tokens(block_size); }
-
-size_t pa_decode_workspace_size(int num_seqs, int num_heads, int head_dim, int block_size,
+size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
                                 int max_seq_len) {
-  if (num_seqs < 0 || num_heads <= 0 || head_dim <= 0 || max_seq_len < 0 ||
-      !valid_block_size(block_size))
+  if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      num_heads % num_kv_heads != 0 || max_seq_len < 0 || max_seq_len > kMaxSeqLen)
     return 0;
-  return plan_workspace(num_seqs, num_heads, head_dim, block_size, max_seq_len).total;
+  return plan_workspace(num_seqs, num_heads, num_kv_heads, head_dim, max_seq_len).total;
 }
 
 pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
@@ -141,27 +168,36 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
   const int group = num_heads / num_kv_heads;
   if (padded_group(group) == 0)
     return fail(PA_ERR_UNSUPPORTED, "pa_decode: %d query heads per KV head (at most 16)", group);
-  if (num_seqs > 65535 || num_kv_heads > 65535)
-    return fail(PA_ERR_UNSUPPORTED, "pa_decode: num_seqs and num_kv_heads must be <= 65535");
   if ((long long)max_seq_len > (long long)max_blocks_per_seq * block_size)
     return fail(PA_ERR_INVALID, "pa_decode: max_seq_len %d exceeds max_blocks_per_seq * block_size (%lld)",
                 max_seq_len, (long long)max_blocks_per_seq * block_size);
+  if (max_seq_len > kMaxSeqLen)
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: max_seq_len %d above %d", max_seq_len, kMaxSeqLen);
+  if ((long long)num_seqs * num_kv_heads * tiles_of(max_seq_len) >= (1LL << 40))
+    return fail(PA_ERR_UNSUPPORTED, "pa_decode: batch of more than 2^40 tiles");
   if (num_seqs == 0) return PA_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !out)
     return fail(PA_ERR_INVALID, "pa_decode: null pointer argument");
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
     return fail(PA_ERR_INVALID, "pa_decode: q, caches and out must be 16-byte aligned");
 
-  const WorkspaceLayout ws = plan_workspace(num_seqs, num_heads, head_dim, block_size, max_seq_len);
-  if (ws.max_parts > 65535)
-    return fail(PA_ERR_UNSUPPORTED, "pa_decode: max_seq_len %d needs more than 65535 partitions", max_seq_len);
-  if (ws.total > 0) {
-    if (!workspace || workspace_bytes < ws.total)
-      return fail(PA_ERR_WORKSPACE, "pa_decode: workspace of %zu bytes needed, %zu given", ws.total,
-                  workspace ? workspace_bytes : (size_t)0);
-    if (((uintptr_t)workspace & 255u) != 0)
-      return fail(PA_ERR_WORKSPACE, "pa_decode: workspace must be 256-byte aligned");
+  const WorkspaceLayout ws = plan_workspace(num_seqs, num_heads, num_kv_heads, head_dim, max_seq_len);
+  if (!workspace || workspace_bytes < ws.total)
+    return fail(PA_ERR_WORKSPACE, "pa_decode: workspace of %zu bytes needed, %zu given", ws.total,
+                workspace ? workspace_bytes : (size_t)0);
+  if (((uintptr_t)workspace & 255u) != 0)
+    return fail(PA_ERR_WORKSPACE, "pa_decode: workspace must be 256-byte aligned");
+
+  const void* dec = nullptr;
+  const void* red = nullptr;
+  const int gp = padded_group(group);
+  bool found;
+  switch (dtype) {
+    case PA_F32: found = decode_kernels_f32(head_dim, block_size, gp, &dec, &red); break;
+    case PA_F16: found = decode_kernels_f16(head_dim, block_size, gp, &dec, &red); break;
+    default: found = decode_kernels_bf16(head_dim, block_size, gp, &dec, &red); break;
   }
+  if (!found) return fail(PA_ERR_UNSUPPORTED, "pa_decode: no kernel for this shape");
   hipStream_t st = static_cast<hipStream_t>(stream);
 
   if (debug_checks()) {
@@ -182,6 +218,12 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
     }
   }
 
+  int waves = 0;
+  hipError_t e = resident_waves(dec, &waves);
+  if (e != hipSuccess) return hip_fail(e, "pa_decode occupancy query");
+  waves = std::min(waves, ws.waves);
+  if (requested_waves() > 0) waves = std::min(waves, requested_waves());
+
   DecodeParams p;
   p.q = q;
   p.k_cache = k_cache;
@@ -189,8 +231,9 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
   p.block_tables = block_tables;
   p.seq_lens = seq_lens;
   p.out = out;
-  p.ws_ml = ws.total ? static_cast<float*>(workspace) : nullptr;
-  p.ws_acc = ws.total ? reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.acc_offset) : nullptr;
+  p.ws_meta = static_cast<int*>(workspace);
+  p.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.ml_offset);
+  p.ws_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.acc_offset);
   p.num_seqs = num_seqs;
   p.num_heads = num_heads;
   p.num_kv_heads = num_kv_heads;
@@ -200,17 +243,15 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
   p.num_blocks = num_blocks;
   p.max_blocks_per_seq = max_blocks_per_seq;
   p.max_seq_len = max_seq_len;
-  p.part_tokens = partition_tokens(block_size);
-  p.max_parts = ws.max_parts;
   p.scale_log2e = (float)((double)scale * 1.4426950408889634074);
 
-  hipError_t e;
-  switch (dtype) {
-    case PA_F32: e = launch_decode_f32(p, st); break;
-    case PA_F16: e = launch_decode_f16(p, st); break;
-    default: e = launch_decode_bf16(p, st); break;
-  }
+  void* kargs[] = {&p};
+  e = hipLaunchKernel(dec, dim3(waves), dim3(64), kargs, 0, st);
   if (e != hipSuccess) return hip_fail(e, "pa_decode launch");
+  if (waves > 1) {  // with one wave no pair can be split
+    e = hipLaunchKernel(red, dim3(waves, group), dim3(256), kargs, 0, st);
+    if (e != hipSuccess) return hip_fail(e, "pa_decode merge launch");
+  }
   return PA_OK;
 }
 

@@ -20,8 +20,9 @@ struct DecodeParams {
   const int32_t* block_tables;
   const int32_t* seq_lens;
   void* out;
-  float* ws_ml;        // [num_seqs][num_heads][max_parts] x {m, l}
-  float* ws_acc;       // [num_seqs][num_heads][max_parts][head_dim]
+  int* ws_meta;        // [waves][4]: pair a wave owns and how many waves share it
+  float* ws_ml;        // [2 * waves][group][2]: running max and sum of each piece
+  float* ws_acc;       // [2 * waves][group][head_dim]: unnormalised accumulator
   int num_seqs;
   int num_heads;
   int num_kv_heads;
@@ -31,16 +32,14 @@ struct DecodeParams {
   int num_blocks;
   int max_blocks_per_seq;
   int max_seq_len;
-  int part_tokens;     // tokens per context partition
-  int max_parts;       // ceil(max_seq_len / part_tokens), >= 1
   float scale_log2e;   // scale * log2(e): logits are taken in base 2
 };
 
-// Launchers, one translation unit per element type.  They return
-// hipErrorInvalidValue for a shape outside the compiled set.
-hipError_t launch_decode_f32(const DecodeParams& p, hipStream_t stream);
-hipError_t launch_decode_f16(const DecodeParams& p, hipStream_t stream);
-hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream);
+// The decode and merge kernels for one shape, one translation unit per element
+// type; false for a shape outside the compiled set.  `gp` is the padded group.
+bool decode_kernels_f32(int head_dim, int block_size, int gp, const void** dec, const void** red);
+bool decode_kernels_f16(int head_dim, int block_size, int gp, const void** dec, const void** red);
+bool decode_kernels_bf16(int head_dim, int block_size, int gp, const void** dec, const void** red);
 
 hipError_t launch_write_kv(const void* k, const void* v, const int32_t* slots,
                            void* k_cache, void* v_cache, int num_tokens,

@@ -3,8 +3,8 @@
 
 namespace pagedkv {
 
-hipError_t launch_decode_bf16(const DecodeParams& p, hipStream_t stream) {
-  return dispatch_decode<kBF16>(p, stream);
+bool decode_kernels_bf16(int head_dim, int block_size, int gp, const void** dec, const void** red) {
+  return pick_decode_kernels<kBF16>(head_dim, block_size, gp, dec, red);
 }
 
 }  // namespace pagedkv

@@ -1,0 +1,84 @@
+// Even split of one decode step's work over a fixed number of waves.
+//
+// The work of a decode step is cut into tiles of 16 consecutive tokens of one
+// (sequence, KV head) pair.  Pair (s, kv) owns ceil(L_s / 16) tiles, and the
+// tiles are numbered sequence by sequence, KV head by KV head, tile by tile:
+//     pair (s, kv) starts at  Hkv * C_s + kv * n_s,   C_s = sum_{s' < s} n_s'.
+// With T tiles in all and nw waves, wave w takes the tiles
+//     [floor(w T / nw), floor((w + 1) T / nw)),
+// so every wave reads the same number of K/V rows, give or take one tile,
+// whatever the mix of lengths.  A wave's range is a run of "segments", each the
+// part of one pair that falls inside it:
+//   * a segment that covers its whole pair yields that pair's final output;
+//   * otherwise the pair is split over several consecutive waves.  Each piece
+//     yields a partial result (running max, running sum, unnormalised
+//     accumulator): this is the same blockwise merge the softmax uses across
+//     blocks, applied across waves, and a second kernel combines the pieces.
+//     The wave that holds the pair's first tile "owns" the pair; its piece is
+//     its last segment.  Every other piece is the first segment of its wave.
+//
+// Everything here is plain integer arithmetic shared by the kernels and by the
+// host code that sizes the workspace.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace pagedkv {
+
+constexpr int kTileTokens = 16;       // tokens per tile (the MFMA row count)
+constexpr int kMinTilesPerWave = 8;   // fewer tiles per wave would only add partials
+constexpr int kMaxWaves = 8192;       // 256 CUs x 4 SIMDs x 8 waves: the whole chip
+
+__host__ __device__ inline int tiles_of(int len) { return (len + kTileTokens - 1) / kTileTokens; }
+
+// Waves that get tiles when `launched` waves run over T tiles: at most one per
+// kMinTilesPerWave tiles, so each has at least one tile (0 when T == 0).
+__host__ __device__ inline long long waves_used(long long T, long long launched) {
+  const long long want = (T + kMinTilesPerWave - 1) / kMinTilesPerWave;
+  return want < launched ? want : launched;
+}
+
+// First tile of wave w (w = nw gives T).
+__host__ __device__ inline long long wave_begin(long long w, long long T, long long nw) {
+  return w * T / nw;
+}
+
+// The wave whose range holds tile t (0 <= t < T): the largest w with
+// wave_begin(w) <= t, i.e. w T / nw < t + 1.
+__host__ __device__ inline long long wave_of(long long t, long long T, long long nw) {
+  return ((t + 1) * nw + T - 1) / T - 1;
+}
+
+// Walk the tiles [t0, t1) of one wave, starting in pair (s, kv) at tile j of
+// that pair.  len(s) gives the length of sequence s (already clamped); seg(s,
+// kv, jb, je, L) is called for each segment, tiles [jb, je) of pair (s, kv).
+// The caller guarantees that tile t0 is tile j of pair (s, kv) and t1 <= T,
+// so the walk never runs past the last non-empty sequence; it still stops at
+// num_seqs rather than read past the lengths.
+template <class LenFn, class SegFn>
+__host__ __device__ inline void walk_tiles(long long t0, long long t1, int s, int kv, int j,
+                                           int num_seqs, int num_kv_heads, LenFn len, SegFn seg) {
+  int L = len(s);
+  int n = tiles_of(L);
+  long long t = t0;
+  while (t < t1) {
+    const long long left = t1 - t;
+    const int je = left < (long long)(n - j) ? j + (int)left : n;
+    if (je <= j) return;  // cannot happen for a valid start; never loop without progress
+    seg(s, kv, j, je, L);
+    t += je - j;
+    if (t >= t1) break;
+    // je == n here: the pair is done, go to the next one
+    j = 0;
+    if (++kv == num_kv_heads) {
+      kv = 0;
+      do {
+        if (++s >= num_seqs) return;
+        L = len(s);
+      } while (L == 0);
+      n = tiles_of(L);
+    }
+  }
+}
+
+}  // namespace pagedkv

@@ -1,0 +1,152 @@
+// Host check of the even tile split used by the decode kernel (split.h).
+//
+// For seeded random batches (empty sequences, partial tiles, long sequences, more
+// waves than tiles) it replays what every wave does -- locate its first tile,
+// walk its segments -- and checks that:
+//   * every tile of every (sequence, KV head) pair is visited exactly once, and
+//     the waves' ranges cover [0, T) in order;
+//   * a segment never leaves its pair, and segments follow the pair order;
+//   * a split pair has exactly one owner (the piece holding its first tile), which
+//     is its wave's last segment; every other piece is its wave's first segment;
+//   * the pieces the merge step reads for an owned pair (slot 2w+1 of the owner,
+//     then slot 2v of waves v = w+1 .. w+parts-1) are exactly that pair's pieces
+//     and together cover its tiles.
+// Prints "split ok: <cases>" and exits 0, or prints the first failure and exits 1.
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <random>
+#include <vector>
+
+#include "split.h"
+
+using namespace pagedkv;
+
+struct Piece {
+  int s, kv, jb, je;
+};
+
+static int fail(const char* what, int c) {
+  printf("split check failed (case %d): %s\n", c, what);
+  return 1;
+}
+
+int check(const std::vector<int>& lens, int Hkv, long long launched, int c) {
+  const int N = (int)lens.size();
+  std::vector<long long> C(N + 1, 0);  // C[s] = tiles of sequences before s
+  for (int s = 0; s < N; ++s) C[s + 1] = C[s] + tiles_of(lens[s]);
+  const long long T = C[N] * Hkv;
+  const long long nw = waves_used(T, launched);
+  if (T > 0 && (nw < 1 || nw > launched || nw > T)) return fail("waves_used out of range", c);
+  if (T == 0 && nw != 0) return fail("waves for an empty batch", c);
+
+  std::vector<int> seen(T, 0);  // visits of each tile, by its global index
+  std::vector<Piece> first(launched, Piece{-1, -1, -1, -1}), owned(launched, Piece{-1, -1, -1, -1});
+  std::vector<int> parts(launched, 0);
+  long long covered = 0;
+  for (long long w = 0; w < nw; ++w) {
+    const long long t0 = wave_begin(w, T, nw), t1 = wave_begin(w + 1, T, nw);
+    if (t0 != covered || t1 <= t0) return fail("wave ranges do not tile [0, T)", c);
+    // locate tile t0 as the kernel does: the first sequence whose tiles end past t0
+    int s0 = 0;
+    while (C[s0 + 1] * Hkv <= t0) ++s0;
+    const long long off = t0 - C[s0] * Hkv;
+    const int n0 = tiles_of(lens[s0]);
+    int nseg = 0, last_jb = -1, last_je = -1, last_s = -1, last_kv = -1;
+    long long t_seg = t0;
+    bool bad = false;
+    const char* why = "";
+    walk_tiles(t0, t1, s0, (int)(off / n0), (int)(off % n0), N, Hkv,
+               [&](int s) { return lens[s]; },
+               [&](int s, int kv, int jb, int je, int L) {
+                 const int n = tiles_of(L);
+                 if (L != lens[s] || jb < 0 || je > n || jb >= je) { bad = true; why = "segment bounds"; }
+                 if (C[s] * Hkv + (long long)kv * n + jb != t_seg) { bad = true; why = "segment position"; }
+                 for (int j = jb; j < je; ++j) seen[C[s] * Hkv + (long long)kv * n + j]++;
+                 if (jb > 0 && nseg != 0) { bad = true; why = "non-owned piece is not the first segment"; }
+                 if (nseg == 0 && jb > 0) first[w] = Piece{s, kv, jb, je};
+                 if (nseg == 0 && jb == 0 && je < n) first[w] = Piece{-1, -1, -1, -1};
+                 if (jb == 0 && je < n) {
+                   owned[w] = Piece{s, kv, jb, je};
+                   parts[w] = (int)(wave_of(t_seg + n - 1, T, nw) - w + 1);
+                 }
+                 last_jb = jb;
+                 last_je = je;
+                 last_s = s;
+                 last_kv = kv;
+                 t_seg += je - jb;
+                 ++nseg;
+               });
+    if (bad) return fail(why, c);
+    if (t_seg != t1) return fail("walk does not end at the range end", c);
+    if (owned[w].s >= 0 && (owned[w].s != last_s || owned[w].kv != last_kv || last_jb != 0 ||
+                            last_je != owned[w].je))
+      return fail("owned piece is not the last segment", c);
+    if (owned[w].s >= 0 && parts[w] < 2) return fail("owned split pair with fewer than 2 pieces", c);
+    covered = t1;
+  }
+  if (covered != T) return fail("ranges stop before T", c);
+  // every tile exactly once (the position check above maps each visit to its
+  // pair's own index range, so a count of one everywhere means exact coverage)
+  for (long long t = 0; t < T; ++t)
+    if (seen[t] != 1) return fail("tile not visited exactly once", c);
+  // the merge step's reads
+  int owners = 0;
+  for (long long w = 0; w < nw; ++w) {
+    if (owned[w].s < 0) continue;
+    ++owners;
+    const Piece o = owned[w];
+    const int n = tiles_of(lens[o.s]);
+    int next = o.je;
+    for (int i = 1; i < parts[w]; ++i) {
+      const long long v = w + i;
+      if (v >= nw) return fail("merge reads a wave that got no tiles", c);
+      const Piece f = first[v];
+      if (f.s != o.s || f.kv != o.kv || f.jb != next) return fail("merge piece mismatch", c);
+      next = f.je;
+    }
+    if (next != n) return fail("merge pieces do not cover the pair", c);
+  }
+  // every split pair has an owner: count pairs whose tiles span more than one wave
+  int split_pairs = 0;
+  for (int s = 0; s < N; ++s)
+    for (int kv = 0; kv < Hkv; ++kv) {
+      const int n = tiles_of(lens[s]);
+      if (n == 0) continue;
+      const long long a = C[s] * Hkv + (long long)kv * n;
+      if (wave_of(a, T, nw) != wave_of(a + n - 1, T, nw)) ++split_pairs;
+    }
+  if (split_pairs != owners) return fail("split pairs and owners differ", c);
+  return 0;
+}
+
+int main() {
+  std::mt19937 rng(12345);
+  int cases = 0;
+  const long long launched_set[] = {1, 2, 3, 7, 64, 1000, 3072, 8192};
+  const int hkv_set[] = {1, 2, 3, 8};
+  for (int rep = 0; rep < 300; ++rep) {
+    const int kind = rep % 4;
+    const int N = 1 + (int)(rng() % (rep < 150 ? 12 : (kind == 3 ? 40 : 300)));
+    std::vector<int> lens(N);
+    for (int& L : lens) {
+      const unsigned r = rng();
+      if (kind == 0) L = (int)(r % 40);                       // short, many empty and partial
+      else if (kind == 1) L = (r % 5 == 0) ? 0 : (int)(r % 4097);
+      else if (kind == 2) L = 512 + (int)(r % 3585);          // the Llama-3-8B mix
+      else L = (r % 3 == 0) ? (int)(r % 17) : 8192 + (int)(r % 24577);
+    }
+    for (int Hkv : hkv_set)
+      for (long long launched : launched_set) {
+        if (check(lens, Hkv, launched, cases)) return 1;
+        ++cases;
+      }
+  }
+  // all empty, single token, one huge sequence
+  if (check(std::vector<int>(5, 0), 2, 3072, cases++)) return 1;
+  if (check(std::vector<int>{1}, 1, 3072, cases++)) return 1;
+  if (check(std::vector<int>{0, 0, 1, 0}, 8, 3072, cases++)) return 1;
+  if (check(std::vector<int>{32768}, 8, 3072, cases++)) return 1;
+  printf("split ok: %d cases\n", cases);
+  return 0;
+}

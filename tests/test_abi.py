@@ -37,7 +37,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["pa_decode", "pa_write_kv", "pa_copy_blocks", "pa_decode_workspace_size",
-              "pa_last_error", "pa_version", "pa_decode_partition_tokens"]:
+              "pa_last_error", "pa_version"]:
         assert n in names
 
 
@@ -49,38 +49,33 @@ def test_library_exports_every_declared_symbol(pk):
 
 def test_binding_names_match_the_abi(pk):
     for n in ["pa_decode", "pa_write_kv", "pa_copy_blocks", "pa_decode_workspace_size",
-              "pa_decode_partition_tokens", "pa_last_error", "pa_version"]:
+              "pa_last_error", "pa_version"]:
         assert callable(getattr(pk, n))
 
 
 def test_version(pk):
-    assert pk.pa_version() == 1
+    assert pk.pa_version() == 2
 
 
-@pytest.mark.parametrize("bs", [8, 16, 32])
-def test_partition_size_rules(pk, bs):
-    P = pk.pa_decode_partition_tokens(bs)
-    assert P % bs == 0 and P % 16 == 0 and P <= 64 * bs and P > 0
-    assert pk.pa_decode_partition_tokens(12) == 0
-
-
-@pytest.mark.parametrize("N,H,D,bs,L", [(256, 32, 128, 16, 4096), (32, 64, 128, 8, 32768),
-                                        (4, 4, 64, 16, 41), (64, 32, 128, 32, 2048), (3, 8, 64, 16, 0)])
-def test_workspace_size_formula(pk, N, H, D, bs, L):
-    P = pk.pa_decode_partition_tokens(bs)
-    parts = max(1, math.ceil(L / P))
-    got = pk.pa_decode_workspace_size(N, H, D, bs, L)
-    if parts == 1:
-        assert got == 0
-    else:
-        rows = N * H * parts
-        ml = -(-(rows * 8) // 256) * 256
-        assert got == ml + rows * D * 4
+@pytest.mark.parametrize("N,H,HKV,D,L", [(256, 32, 8, 128, 4096), (32, 64, 8, 128, 32768),
+                                         (4, 4, 4, 64, 41), (64, 32, 32, 128, 2048), (3, 8, 2, 64, 0),
+                                         (1, 8, 8, 128, 1)])
+def test_workspace_size_formula(pk, N, H, HKV, D, L):
+    # waves: one per 8 tiles of the longest possible batch, at least 1, at most 8192;
+    # 16 bytes of bookkeeping per wave, then two partial slots of (D + 2) floats per
+    # query head of the group, each region 256-byte aligned
+    up = lambda x: -(-x // 256) * 256
+    waves = min(8192, max(1, -(-(N * HKV * math.ceil(L / 16)) // 8)))
+    g = H // HKV
+    got = pk.pa_decode_workspace_size(N, H, HKV, D, L)
+    assert got == up(waves * 16) + up(2 * waves * g * 2 * 4) + 2 * waves * g * D * 4
 
 
 def test_workspace_size_rejects_bad_arguments(pk):
-    assert pk.pa_decode_workspace_size(-1, 8, 128, 16, 100) == 0
-    assert pk.pa_decode_workspace_size(4, 8, 128, 12, 100) == 0
+    assert pk.pa_decode_workspace_size(-1, 8, 2, 128, 100) == 0
+    assert pk.pa_decode_workspace_size(4, 8, 3, 128, 100) == 0
+    assert pk.pa_decode_workspace_size(4, 8, 2, 128, -1) == 0
+    assert pk.pa_decode_workspace_size(4, 8, 2, 128, (1 << 24) + 1) == 0
 
 
 FAKE = 1 << 20  # a 16-byte aligned, non-null address that is never dereferenced
@@ -108,6 +103,8 @@ def call_decode(pk, **over):
     (dict(scale=float("nan")), 1, "finite"),
     (dict(L=1000, MB=100, wsb=16), 3, "workspace"),
     (dict(L=1000, MB=100, ws=None, wsb=1 << 30), 3, "workspace"),
+    (dict(wsb=1 << 30, ws=FAKE + 16), 3, "256-byte"),
+    (dict(L=(1 << 24) + 16, MB=1 << 21), 2, "above"),
 ])
 def test_decode_rejects_host_visible_errors(pk, over, status, words):
     assert call_decode(pk, **over) == status

@@ -121,10 +121,9 @@ SWEEP = [(dt, D, B, Hq, Hkv)
 
 @pytest.mark.parametrize("dt,D,B,Hq,Hkv", SWEEP)
 def test_shape_sweep(dt, D, B, Hq, Hkv):
-    # lengths: one token, partial tiles, exact tile and block multiples, and beyond one
-    # and two context partitions, with a ragged tail
-    P = pk().pa_decode_partition_tokens(B)
-    lens = [1, 3, 15, 16, 17, B, B + 1, 33, P - 1, P, P + 1, 2 * P + 7]
+    # lengths: one token, partial tiles, exact tile and block multiples, longer ones
+    # with a ragged tail; the batch is small, so its pairs are split over many waves
+    lens = [1, 3, 15, 16, 17, B, B + 1, 33, 511, 512, 513, 1031]
     b = random_batch(100 + SWEEP.index((dt, D, B, Hq, Hkv)), dt, lens, Hq, Hkv, D, B)
     d = to_dev(b)
     log(f"sweep {dt} D={D} B={B} {Hq}/{Hkv}")
