@@ -73,8 +73,9 @@ const char* pa_last_error(void);
 /* Bytes of workspace pa_decode needs for these arguments (0 for invalid
  * arguments).  It depends only on the shapes: the number of waves a call may
  * launch is bounded by num_seqs * num_kv_heads * ceil(max_seq_len / 16) / 8
- * and by 8192, and each wave needs 16 bytes of bookkeeping plus two partial
- * results of (head_dim + 2) floats per query head of its group. */
+ * and by 8192; each wave's work is cut into two chunks, and each chunk needs
+ * 16 bytes of bookkeeping plus two partial results of (head_dim + 2) floats per
+ * query head of its group, after a 256-byte header. */
 size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
                                 int max_seq_len);
 
@@ -92,9 +93,12 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, i
  *
  * Work split: the step's (sequence, KV head) pairs are cut into 16-token tiles
  * and the launched waves (as many as the device holds at once) take equal runs
- * of consecutive tiles, whatever the length mix.  A pair cut by a run boundary
- * is finished by a second kernel on the same stream, which merges the pieces'
- * running maxima, sums and accumulators with the same rule.
+ * of consecutive tiles, whatever the length mix; the last eighth of every run is
+ * handed to whichever wave is free first.  A pair cut by a run boundary is
+ * finished by a second kernel on the same stream, which merges the pieces'
+ * running maxima, sums and accumulators with the same rule.  The boundaries
+ * depend only on the lengths, so which wave did which part never changes the
+ * result.
  *
  *   q            [num_seqs][num_heads][head_dim]            dtype
  *   k_cache      [num_blocks][block_size][num_kv_heads][head_dim]  dtype
@@ -104,8 +108,11 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, i
  *   seq_lens     [num_seqs] int32, 0 <= L <= max_seq_len
  *   out          [num_seqs][num_heads][head_dim] dtype; must not alias inputs
  *   workspace    device scratch of at least pa_decode_workspace_size(...)
- *                bytes, 256-byte aligned; its contents on entry do not
- *                matter and are clobbered
+ *                bytes, 256-byte aligned, zero-filled before its first use.
+ *                A call leaves it ready for the next one (the counter it
+ *                uses to hand out work is back at 0), so it is zeroed once,
+ *                not per call.  Calls that share a workspace must not run
+ *                concurrently (put them on one stream).
  *   max_seq_len  caller's upper bound on every seq_lens[s]; must be
  *                <= max_blocks_per_seq * block_size and <= 2^24.  Lengths
  *                above it are clamped to it, negative lengths to 0.

@@ -100,12 +100,13 @@ def pa_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, max_se
 
 
 def decode_workspace(q, num_kv_heads, max_seq_len):
-    """A workspace tensor sized for ``pa_decode`` with these arguments (None if the
-    arguments are invalid; pa_decode then reports why)."""
+    """A zero-filled workspace tensor sized for ``pa_decode`` with these arguments (None if
+    the arguments are invalid; pa_decode then reports why).  Reuse it across calls on one
+    stream: each call leaves it ready for the next."""
     n = pa_decode_workspace_size(q.shape[0], q.shape[1], num_kv_heads, q.shape[2], max_seq_len)
     if n == 0:
         return None
-    return torch.empty(n, dtype=torch.uint8, device=q.device)
+    return torch.zeros(n, dtype=torch.uint8, device=q.device)
 
 
 def pa_decode(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, scale, out, *,

@@ -55,6 +55,19 @@ int requested_waves() {
   return v;
 }
 
+// The last 1/8 of every wave's share goes to whichever wave is free first;
+// PA_DECODE_TAIL = d overrides the divisor (0 = no tails), for tuning sweeps.
+int tail_divisor() {
+  static const int v = [] {
+    const char* s = getenv("PA_DECODE_TAIL");
+    if (!s || !*s) return 8;
+    char* end = nullptr;
+    const long x = strtol(s, &end, 10);
+    return (end && *end == 0 && x >= 0 && x <= 1024) ? (int)x : 8;
+  }();
+  return v;
+}
+
 bool valid_block_size(int bs) { return bs == 8 || bs == 16 || bs == 32; }
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
@@ -63,12 +76,16 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 constexpr int kMaxSeqLen = 1 << 24;
 
-// Workspace of one pa_decode call: per launched wave a 16-byte record saying which
-// split pair it owns, and two partial-result slots (running max and sum, and the
-// unnormalised accumulator, for each query head of the group).  It is sized for
-// the most waves the call could launch, a bound that depends only on the shapes
-// (one wave per kMinTilesPerWave tiles of the longest possible batch, at most
-// kMaxWaves); the launch never uses more waves than that.
+// Workspace of one pa_decode call.  Each launched wave's share of the step is
+// cut into two chunks (head and tail); each chunk has a 16-byte record (the pair
+// it owns, if split, and whether it left a first piece) and two partial-result
+// slots (running max and sum, and the unnormalised accumulator, for each query
+// head of the group).  A 256-byte header holds the chunk count and the counter
+// that hands out tail chunks; the merge kernel leaves that counter at 0, so the
+// workspace must be zero-filled before its first use only.  The size is the
+// bound for the most waves the call could launch, which depends only on the
+// shapes (one wave per kMinTilesPerWave tiles of the longest possible batch, at
+// most kMaxWaves); the launch never uses more waves than that.
 struct WorkspaceLayout {
   int waves;
   size_t ml_offset;
@@ -83,16 +100,22 @@ WorkspaceLayout plan_workspace(int num_seqs, int num_heads, int num_kv_heads, in
   long long waves = waves_used(t_max, kMaxWaves);
   if (waves < 1) waves = 1;
   const size_t g = (size_t)(num_heads / num_kv_heads);
+  const size_t chunks = 2 * (size_t)waves;
+  const size_t slots = 2 * chunks;
   w.waves = (int)waves;
-  w.ml_offset = align_up((size_t)waves * 16, 256);
-  w.acc_offset = w.ml_offset + align_up(2 * (size_t)waves * g * 2 * sizeof(float), 256);
-  w.total = w.acc_offset + 2 * (size_t)waves * g * head_dim * sizeof(float);
+  w.ml_offset = align_up(256 + chunks * 16, 256);
+  w.acc_offset = w.ml_offset + align_up(slots * g * 2 * sizeof(float), 256);
+  w.total = w.acc_offset + slots * g * head_dim * sizeof(float);
   return w;
 }
 
-// Waves of `kernel` the current device holds at once (one 64-lane wave per
-// workgroup), cached per device and kernel.
-hipError_t resident_waves(const void* kernel, int* out) {
+// Decode waves to launch on the current device: one per SIMD (4 per CU), or
+// fewer if the kernel's occupancy does not allow that many at once; cached per
+// device and kernel.  One wave per SIMD is deliberate: the SIMD issues its
+// oldest wave first, so a second or third wave on it mostly waits for the
+// first and then runs alone at the end; a single wave with two tiles in flight
+// keeps HBM as busy and leaves no such tail.
+hipError_t decode_waves(const void* kernel, int* out) {
   static std::mutex mu;
   static std::map<std::pair<int, const void*>, int> cache;
   int dev = 0;
@@ -109,7 +132,7 @@ hipError_t resident_waves(const void* kernel, int* out) {
   if (e != hipSuccess) return e;
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64, 0);
   if (e != hipSuccess) return e;
-  const int n = std::max(1, cus * per_cu);
+  const int n = std::max(1, cus * std::min(per_cu, 4));
   cache[{dev, kernel}] = n;
   *out = n;
   return hipSuccess;
@@ -219,7 +242,7 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
   }
 
   int waves = 0;
-  hipError_t e = resident_waves(dec, &waves);
+  hipError_t e = decode_waves(dec, &waves);
   if (e != hipSuccess) return hip_fail(e, "pa_decode occupancy query");
   waves = std::min(waves, ws.waves);
   if (requested_waves() > 0) waves = std::min(waves, requested_waves());
@@ -243,15 +266,16 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
   p.num_blocks = num_blocks;
   p.max_blocks_per_seq = max_blocks_per_seq;
   p.max_seq_len = max_seq_len;
+  p.num_waves = waves;
+  p.tail_div = tail_divisor();
   p.scale_log2e = (float)((double)scale * 1.4426950408889634074);
 
   void* kargs[] = {&p};
   e = hipLaunchKernel(dec, dim3(waves), dim3(64), kargs, 0, st);
   if (e != hipSuccess) return hip_fail(e, "pa_decode launch");
-  if (waves > 1) {  // with one wave no pair can be split
-    e = hipLaunchKernel(red, dim3(waves, group), dim3(256), kargs, 0, st);
-    if (e != hipSuccess) return hip_fail(e, "pa_decode merge launch");
-  }
+  // always: it also resets the tail counter for the next call
+  e = hipLaunchKernel(red, dim3((2 * waves + 3) / 4), dim3(256), kargs, 0, st);
+  if (e != hipSuccess) return hip_fail(e, "pa_decode merge launch");
   return PA_OK;
 }
 

@@ -20,9 +20,10 @@ struct DecodeParams {
   const int32_t* block_tables;
   const int32_t* seq_lens;
   void* out;
-  int* ws_meta;        // [waves][4]: pair a wave owns and how many waves share it
-  float* ws_ml;        // [2 * waves][group][2]: running max and sum of each piece
-  float* ws_acc;       // [2 * waves][group][head_dim]: unnormalised accumulator
+  int* ws_meta;        // 64-int header, then [2 * waves][4]: per chunk, the pair it
+                       // owns, how many chunks share it, whether it left a first piece
+  float* ws_ml;        // [4 * waves][group][2]: running max and sum of each piece
+  float* ws_acc;       // [4 * waves][group][head_dim]: unnormalised accumulator
   int num_seqs;
   int num_heads;
   int num_kv_heads;
@@ -32,6 +33,9 @@ struct DecodeParams {
   int num_blocks;
   int max_blocks_per_seq;
   int max_seq_len;
+  int num_waves;       // decode waves launched
+  int tail_div;        // the last 1/tail_div of each wave's share is handed out on
+                       // demand; 0 = none
   float scale_log2e;   // scale * log2(e): logits are taken in base 2
 };
 

@@ -42,9 +42,10 @@
 //     accumulates acc[h][.] for every head h of the group.  The weight p of
 //     (head h, token 4*grp + j) sits in lane (grp, h); DPP row_newbcast:h
 //     broadcasts it to the 16 lanes of the row -- no LDS, no barrier.
-//   Block ids: a segment is walked in windows of up to 64 blocks; lane i holds
-//     the id of the window's block i (v_readlane picks it per tile), and the next
-//     window's ids are fetched while the current one is processed.
+//   Block ids: lane i holds the id of the segment's block 64 w + i for the
+//     current window w (v_readlane picks it per tile) and the next 64 ids are
+//     fetched a window ahead, so the two-tile pipeline runs through a whole
+//     segment without draining at window boundaries.
 //
 // Logits are taken in base 2 (scale * log2 e folded in), so every exponential is
 // one v_exp_f32.  Running maxima start at a finite -1e30 so that a stream with
@@ -91,20 +92,22 @@ __device__ __forceinline__ float row_bcast(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ int wave_sum(int x) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d);
+// Inclusive prefix sum over the 64 lanes, in registers: shifts by 1, 2, 4, 8
+// inside each 16-lane row (lanes shifted in from outside the row read 0), then
+// lane 15 of each row is added to the next row and lane 31 to rows 2 and 3.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false); // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false); // row_bcast:31 -> rows 2, 3
   return x;
 }
 
-__device__ __forceinline__ int wave_inclusive_scan(int x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int y = __shfl_up(x, d);
-    if (lane >= d) x += y;
-  }
-  return x;
+// Sum over the 64 lanes, the same in every lane.
+__device__ __forceinline__ int wave_sum(int x) {
+  return __builtin_amdgcn_readlane(wave_inclusive_scan(x), 63);
 }
 
 // Length of sequence s as the kernels use it: clamped to [0, max_seq_len].
@@ -160,14 +163,16 @@ __device__ __forceinline__ void store_row(void* dst, const float (&v)[N]) {
       }
       w[i] = (uint32_t)lo | ((uint32_t)hi << 16);
     }
-    if constexpr (N == 8) {
-      *reinterpret_cast<u32x4*>(dst) = u32x4{w[0], w[1], w[2], w[3]};
+    if constexpr (N % 8 == 0) {
+#pragma unroll
+      for (int i = 0; i < N / 8; ++i)
+        reinterpret_cast<u32x4*>(dst)[i] = u32x4{w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]};
     } else if constexpr (N == 4) {
       *reinterpret_cast<u32x2*>(dst) = u32x2{w[0], w[1]};
     } else if constexpr (N == 2) {
       *reinterpret_cast<uint32_t*>(dst) = w[0];
     } else {
-      static_assert(N == 1, "row piece of 1, 2, 4 or 8 elements");
+      static_assert(N == 1, "row piece of 1, 2, 4 or a multiple of 8 elements");
       if constexpr (DT == kBF16) *reinterpret_cast<__bf16*>(dst) = (__bf16)v[0];
       else *reinterpret_cast<_Float16*>(dst) = (_Float16)v[0];
     }
@@ -224,16 +229,40 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
   long long seq_tiles = 0;
   for (int c = 0; c < N; c += 64) {
     const int s = c + lane;
-    seq_tiles += __builtin_amdgcn_readfirstlane(wave_sum(s < N ? tiles_of(seq_len_at(p, s)) : 0));
+    seq_tiles += wave_sum(s < N ? tiles_of(seq_len_at(p, s)) : 0);
   }
   const long long T = seq_tiles * Hkv;
   const long long nw = waves_used(T, launched);
 
-  int meta_s = 0, meta_kv = 0, meta_parts = 0;
+  // Workspace header: [0] = chunks of this call (for the merge kernel), [32] =
+  // counter of tail chunks handed out (the merge kernel sets it back to 0).
+  int* const hdr = p.ws_meta;
+  int* const chunk_meta = p.ws_meta + 64;
+  if (w == 0 && lane == 0) hdr[0] = (int)(2 * nw);
 
-  if (w < nw) {
-    const long long t0 = wave_begin(w, T, nw);
-    const long long t1 = wave_begin(w + 1, T, nw);
+  // Next tail chunk for this wave, or -1 when all are taken.
+  auto next_tail = [&]() -> long long {
+    int ticket = 0;
+    if (lane == 0) ticket = atomicAdd(hdr + 32, 1);
+    ticket = __builtin_amdgcn_readfirstlane(ticket);
+    return ticket < nw ? 2 * (long long)ticket + 1 : -1;
+  };
+
+  const size_t tok_stride = (size_t)Hkv * ROWB;
+  const size_t blk_bytes = (size_t)BS * tok_stride;
+  const float sl2 = p.scale_log2e;
+
+  // The wave's own head chunk first, then tails while any are left.  Without
+  // tails each wave records its own (empty) tail chunk instead.
+  const int tail_div = p.tail_div;
+  if (tail_div == 0 && w < nw && lane == 0)
+    *reinterpret_cast<u32x4*>(chunk_meta + 4 * (2 * (size_t)w + 1)) = u32x4{0u, 0u, 0u, 0u};
+  auto next_chunk = [&]() -> long long { return tail_div > 0 ? next_tail() : -1; };
+  for (long long ck = w < nw ? 2 * (long long)w : next_chunk(); ck >= 0; ck = next_chunk()) {
+    const long long t0 = chunk_begin(ck, T, nw, tail_div);
+    const long long t1 = chunk_begin(ck + 1, T, nw, tail_div);
+    int meta_s = 0, meta_kv = 0, meta_parts = 0, meta_first = 0;
+    if (t0 < t1) {
     // Find the pair and tile of t0: the first sequence whose tiles end past t0.
     int s0 = -1;
     long long pair_base = 0;
@@ -242,7 +271,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
       const int s = c + lane;
       const int n = s < N ? tiles_of(seq_len_at(p, s)) : 0;
       const int incl = wave_inclusive_scan(n);
-      const unsigned long long hit = __ballot(base + (long long)incl * Hkv > t0);
+      const unsigned long long hit = __ballot(s < N && base + (long long)incl * Hkv > t0);
       if (hit) {
         const int ln = __ffsll(hit) - 1;
         s0 = c + ln;
@@ -251,15 +280,13 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
       }
       base += (long long)__builtin_amdgcn_readlane(incl, 63) * Hkv;
     }
-    // s0 >= 0 always (t0 < T); the test only guards against reading past the lengths
-    const int n0 = s0 >= 0 ? tiles_of(seq_len_at(p, s0)) : 0;
+    // s0 >= 0 and 0 <= off < Hkv * n0 always (t0 < T); the tests only guard
+    // against reading past the lengths or the pool
+    int n0 = s0 >= 0 ? tiles_of(seq_len_at(p, s0)) : 0;
     const long long off = t0 - pair_base;
+    if (off < 0 || off >= (long long)Hkv * n0) n0 = 0;
     const int kv0 = n0 > 0 ? (int)(off / n0) : 0;
     const int j0 = n0 > 0 ? (int)(off % n0) : 0;
-
-    const size_t tok_stride = (size_t)Hkv * ROWB;
-    const size_t blk_bytes = (size_t)BS * tok_stride;
-    const float sl2 = p.scale_log2e;
 
     long long t_seg = t0;  // global index of the current segment's first tile
     auto segment = [&](int s, int kv, int jb, int je, int L) __attribute__((always_inline)) {
@@ -281,15 +308,20 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
           qf[c] = col < g ? *reinterpret_cast<const u32x4*>(qrow + (4 * c + grp) * 16) : u32x4{0, 0, 0, 0};
       }
 
-      // Block ids of the window starting at block wb, one per lane.  An id outside
-      // the pool is a contract violation; it becomes 0 so no access leaves the pool.
-      auto load_ids = [&](int wb) __attribute__((always_inline)) {
-        int id = 0;
-        if (wb + lane < b_end) {
-          id = trow[wb + lane];
-          id = (unsigned)id < (unsigned)p.num_blocks ? id : 0;
-        }
-        return id;
+      // Block ids, 64 at a time, one per lane: `ids` holds those of blocks
+      // b_first + 64 win + lane and `ids_next` the next 64, fetched a whole window
+      // ahead.  Ids are range-checked only where a tile uses them, so the prefetch
+      // never stalls on its data; an id outside the pool is a contract violation
+      // and becomes 0, so no access leaves the pool.
+      auto fetch_ids = [&](int wi) __attribute__((always_inline)) {
+        const int b = b_first + 64 * wi + lane;
+        return b < b_end ? trow[b] : 0;
+      };
+      int win = 0;
+      int ids = fetch_ids(0);
+      int ids_next = b_end - b_first > 64 ? fetch_ids(1) : 0;
+      auto valid_id = [&](int id) __attribute__((always_inline)) {
+        return (unsigned)id < (unsigned)p.num_blocks ? id : 0;
       };
 
       float m = kNegBig;
@@ -305,120 +337,126 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
         uint32_t v[4][VW];
       };
 
-      int idw = load_ids(b_first);
-      for (int wb = b_first; wb < b_end; wb += 64) {
-        int idn = 0;
-        if (wb + 64 < b_end) idn = load_ids(wb + 64);
-        const int w0 = max(tok0, wb * BS);                      // a multiple of 16
-        const int wn = min(tok_end, (wb + 64) * BS) - w0;      // tokens in the window
-        const int last = wn - 1;
+      const int n_tok = tok_end - tok0;
+      const int last = n_tok - 1;
 
-        // Tile tt covers window tokens [16 tt, 16 tt + 16).  A token index past the
-        // window's last token is clamped to it, so every load reads a real row of
-        // this sequence; such tokens get weight exactly 0 from the score mask.
-        auto load_tile = [&](Tile& Tl, int tt) __attribute__((always_inline)) {
-          const int a = w0 + kTileTokens * tt;                  // first token of the tile
-          const int tk = w0 + min(kTileTokens * tt + col, last);
-          int tv[4];
+      // Tile tt covers the segment's tokens [16 tt, 16 tt + 16).  A token index
+      // past the segment's last token is clamped to it, so every load reads a real
+      // row of this sequence; such tokens get weight exactly 0 from the score mask.
+      // The window `win` is that of the older of the two tiles being loaded; a
+      // window holds at least 32 tiles, so the younger one is in `win` or the next.
+      auto load_tile = [&](Tile& Tl, int tt) __attribute__((always_inline)) {
+        const int a = kTileTokens * tt;
+        const int blk = (tok0 + a) / BS - b_first;        // first block of the tile
+        const int idsrc = (blk >> 6) != win ? ids_next : ids;
+        const int tk = tok0 + min(a + col, last);
+        int tv[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) tv[j] = w0 + min(kTileTokens * tt + 4 * grp + j, last);
-          int pk, pv[4];
-          if constexpr (BS == 8) {
-            const int bi = a / BS - wb;
-            const int ida = __builtin_amdgcn_readlane(idw, bi);
-            const int idb = __builtin_amdgcn_readlane(idw, bi + 1);
-            pk = (tk & 8) ? idb : ida;
+        for (int j = 0; j < 4; ++j) tv[j] = tok0 + min(a + 4 * grp + j, last);
+        int pk, pv[4];
+        if constexpr (BS == 8) {
+          // a tile spans two blocks; the tile starts on a multiple of 16 tokens
+          const int ida = valid_id(__builtin_amdgcn_readlane(idsrc, blk & 63));
+          const int idb = valid_id(__builtin_amdgcn_readlane(idsrc, (blk & 63) + 1));
+          pk = (tk & 8) ? idb : ida;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) pv[j] = (tv[j] & 8) ? idb : ida;
-          } else {
-            const int id = __builtin_amdgcn_readlane(idw, a / BS - wb);
-            pk = id;
+          for (int j = 0; j < 4; ++j) pv[j] = (tv[j] & 8) ? idb : ida;
+        } else {
+          const int id = valid_id(__builtin_amdgcn_readlane(idsrc, blk & 63));
+          pk = id;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) pv[j] = id;
-          }
-          const char* kp = kbase + (size_t)pk * blk_bytes + (size_t)(tk % BS) * tok_stride;
-#pragma unroll
-          for (int c = 0; c < NKC; ++c) Tl.k[c] = *reinterpret_cast<const u32x4*>(kp + (4 * c + grp) * 16);
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            load_dwords<VW>(vbase + (size_t)pv[j] * blk_bytes + (size_t)(tv[j] % BS) * tok_stride, Tl.v[j]);
-        };
-
-        auto compute = [&](const Tile& Tl, int tt) __attribute__((always_inline)) {
-          // S = K q^T on the matrix cores
-          f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int c = 0; c < NKC; ++c) {
-            if constexpr (DT == kBF16) {
-              sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, Tl.k[c]),
-                                                           __builtin_bit_cast(bf16x8, qf[c]), sc, 0, 0, 0);
-            } else if constexpr (DT == kF16) {
-              sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, Tl.k[c]),
-                                                          __builtin_bit_cast(f16x8, qf[c]), sc, 0, 0, 0);
-            } else {
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                sc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(Tl.k[c][e]),
-                                                          __uint_as_float(qf[c][e]), sc, 0, 0, 0);
-            }
-          }
-          // online softmax, stream (grp, head col); tokens past the end get -inf
-          const int lim = wn - kTileTokens * tt - 4 * grp;
-          float sv[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sv[r] = r < lim ? sc[r] * sl2 : -__builtin_inff();
-          const float mn = fmaxf(m, fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
-          const float alpha = fast_exp2(m - mn);
-          float pr[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(sv[r] - mn);
-          l = l * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-          m = mn;
-          // rescale the accumulators only when some running max moved
-          if (__any(col < GP && alpha != 1.0f)) {
-            static_for<GP>([&](auto hc) {
-              constexpr int h = decltype(hc)::value;
-              const float a = row_bcast<h>(alpha);
-#pragma unroll
-              for (int e = 0; e < VE; ++e) acc[h][e] *= a;
-            });
-          }
-          // P V on the vector ALU
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            float vf[VE];
-            unpack<DT, VW>(Tl.v[j], vf);
-            static_for<GP>([&](auto hc) {
-              constexpr int h = decltype(hc)::value;
-              const float pj = row_bcast<h>(pr[j]);
-#pragma unroll
-              for (int e = 0; e < VE; ++e) acc[h][e] = fmaf(pj, vf[e], acc[h][e]);
-            });
-          }
-        };
-
-        // Two tiles in flight: while one is reduced the next two are being fetched.
-        // Loads are unconditional (clamped tile index) so no tile register is ever
-        // copied, and the scheduling barriers keep a refill after the last use of
-        // the registers it overwrites.
-        const int n_tiles = (wn + kTileTokens - 1) / kTileTokens;
-        const int lt = n_tiles - 1;
-        Tile A, B;
-        load_tile(A, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        load_tile(B, min(1, lt));
-        __builtin_amdgcn_sched_barrier(0);
-        for (int tt = 0; tt < n_tiles; tt += 2) {
-          compute(A, tt);
-          __builtin_amdgcn_sched_barrier(0);
-          load_tile(A, min(tt + 2, lt));
-          __builtin_amdgcn_sched_barrier(0);
-          if (tt + 1 < n_tiles) compute(B, tt + 1);
-          __builtin_amdgcn_sched_barrier(0);
-          load_tile(B, min(tt + 3, lt));
-          __builtin_amdgcn_sched_barrier(0);
+          for (int j = 0; j < 4; ++j) pv[j] = id;
         }
-        idw = idn;
+        const char* kp = kbase + (size_t)pk * blk_bytes + (size_t)(tk % BS) * tok_stride;
+#pragma unroll
+        for (int c = 0; c < NKC; ++c) Tl.k[c] = *reinterpret_cast<const u32x4*>(kp + (4 * c + grp) * 16);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          load_dwords<VW>(vbase + (size_t)pv[j] * blk_bytes + (size_t)(tv[j] % BS) * tok_stride, Tl.v[j]);
+      };
+
+      auto compute = [&](const Tile& Tl, int tt) __attribute__((always_inline)) {
+        // S = K q^T on the matrix cores
+        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NKC; ++c) {
+          if constexpr (DT == kBF16) {
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, Tl.k[c]),
+                                                         __builtin_bit_cast(bf16x8, qf[c]), sc, 0, 0, 0);
+          } else if constexpr (DT == kF16) {
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, Tl.k[c]),
+                                                        __builtin_bit_cast(f16x8, qf[c]), sc, 0, 0, 0);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              sc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(Tl.k[c][e]),
+                                                        __uint_as_float(qf[c][e]), sc, 0, 0, 0);
+          }
+        }
+        // online softmax, stream (grp, head col); tokens past the end get -inf
+        const int lim = n_tok - kTileTokens * tt - 4 * grp;
+        float sv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sv[r] = r < lim ? sc[r] * sl2 : -__builtin_inff();
+        const float mn = fmaxf(m, fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+        const float alpha = fast_exp2(m - mn);
+        float pr[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(sv[r] - mn);
+        l = l * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+        m = mn;
+        // rescale the accumulators only when some running max moved
+        if (__any(col < GP && alpha != 1.0f)) {
+          static_for<GP>([&](auto hc) {
+            constexpr int h = decltype(hc)::value;
+            const float a = row_bcast<h>(alpha);
+#pragma unroll
+            for (int e = 0; e < VE; ++e) acc[h][e] *= a;
+          });
+        }
+        // P V on the vector ALU
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float vf[VE];
+          unpack<DT, VW>(Tl.v[j], vf);
+          static_for<GP>([&](auto hc) {
+            constexpr int h = decltype(hc)::value;
+            const float pj = row_bcast<h>(pr[j]);
+#pragma unroll
+            for (int e = 0; e < VE; ++e) acc[h][e] = fmaf(pj, vf[e], acc[h][e]);
+          });
+        }
+      };
+
+      // Two tiles in flight across the whole segment: while one is reduced the
+      // next two are being fetched.  Loads are unconditional (clamped tile index)
+      // so no tile register is ever copied, and the scheduling barriers keep a
+      // refill after the last use of the registers it overwrites.
+      const int n_tiles = je - jb;
+      const int lt = n_tiles - 1;
+      Tile A, B;
+      load_tile(A, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      load_tile(B, min(1, lt));
+      __builtin_amdgcn_sched_barrier(0);
+      for (int tt = 0; tt < n_tiles; tt += 2) {
+        {
+          // move the block window forward before loading tiles tt + 2 and tt + 3
+          const int blk = (tok0 + kTileTokens * min(tt + 2, lt)) / BS - b_first;
+          if ((blk >> 6) != win) {
+            ++win;
+            ids = ids_next;
+            ids_next = b_first + 64 * (win + 1) < b_end ? fetch_ids(win + 1) : 0;
+          }
+        }
+        compute(A, tt);
+        __builtin_amdgcn_sched_barrier(0);
+        load_tile(A, min(tt + 2, lt));
+        __builtin_amdgcn_sched_barrier(0);
+        if (tt + 1 < n_tiles) compute(B, tt + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        load_tile(B, min(tt + 3, lt));
+        __builtin_amdgcn_sched_barrier(0);
       }
 
       // Merge the four per-group streams of every head.
@@ -455,10 +493,10 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
           }
         });
       } else {
-        // one piece of a pair split over waves: the owner (first tile) writes to
-        // slot 2w + 1, every other piece is its wave's first segment, slot 2w
+        // one piece of a pair split over chunks: the owner (first tile) writes to
+        // slot 2c + 1, every other piece is its chunk's first segment, slot 2c
         const bool owner = jb == 0;
-        const size_t slot = 2 * (size_t)w + (owner ? 1 : 0);
+        const size_t slot = 2 * (size_t)ck + (owner ? 1 : 0);
         static_for<GP>([&](auto hc) {
           constexpr int h = decltype(hc)::value;
           if (h < g && (h & 3) == grp) {
@@ -476,7 +514,9 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
         if (owner) {
           meta_s = s;
           meta_kv = kv;
-          meta_parts = (int)(wave_of(t_seg + n_pair - 1, T, nw) - w + 1);
+          meta_parts = (int)(chunk_of(t_seg + n_pair - 1, T, nw, tail_div) - ck + 1);
+        } else {
+          meta_first = 1;
         }
       }
       t_seg += je - jb;
@@ -484,88 +524,94 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
 
     if (n0 > 0)
       walk_tiles(t0, t1, s0, kv0, j0, N, Hkv, [&](int s) { return seq_len_at(p, s); }, segment);
-  }
-
-  // Every launched wave states whether it owns a split pair (parts >= 2).
-  if (lane == 0) {
-    int* meta = p.ws_meta + 4 * (size_t)w;
-    *reinterpret_cast<u32x4*>(meta) = u32x4{(uint32_t)meta_s, (uint32_t)meta_kv, (uint32_t)meta_parts, 0u};
+    }
+    // Every chunk states whether it owns a split pair (parts >= 2) and whether it
+    // left a first piece of one in slot 2c.
+    if (lane == 0)
+      *reinterpret_cast<u32x4*>(chunk_meta + 4 * ck) =
+          u32x4{(uint32_t)meta_s, (uint32_t)meta_kv, (uint32_t)meta_parts, (uint32_t)meta_first};
   }
 }
 
-// Merge the pieces of every pair split over waves.  Workgroup (w, h) handles query
-// head h of the group of the pair wave w owns, if any: with the pieces' running
-// maxima m_i, sums l_i and accumulators a_i, M = max_i m_i and
-//     out = sum_i 2^(m_i - M) a_i / sum_i 2^(m_i - M) l_i.
-// Wave k of the workgroup sums the pieces i = k (mod 4); the four sums are then
-// added in a fixed order, so the result does not depend on timing.
-template <int DT, int D>
+// Merge the pieces of every pair split over chunks, and hand the workspace back
+// ready for the next call (tail counter at 0).  Wave k of workgroup b handles the
+// pair owned by chunk c = 4 b + k, if any, all query heads of the group at once
+// (64 / GP lanes per head).  The pieces are the owner's (slot 2c + 1) and the
+// first piece of every later chunk up to the pair's last one that left one (slot
+// 2c'); empty tail chunks leave none.  They are folded in chunk order with the
+// same running-max rule as the blocks of one piece:
+//     m' = max(m, m_i),  l' = 2^(m - m') l + 2^(m_i - m') l_i,
+//     acc' = 2^(m - m') acc + 2^(m_i - m') a_i,      out = acc / l,
+// so the result does not depend on timing.
+template <int DT, int D, int GP>
 __global__ __launch_bounds__(256) void reduce_kernel(DecodeParams p) {
-  constexpr int EPT = D / 64;
+  constexpr int LPH = 64 / GP;   // lanes per head
+  constexpr int EPL = D / LPH;   // accumulator elements per lane
   constexpr int EB = Elem<DT>::bytes;
-  const int w = blockIdx.x;
-  const int h = blockIdx.y;
-  const int* meta = p.ws_meta + 4 * (size_t)w;
+  int* const hdr = p.ws_meta;
+  const int* const chunk_meta = p.ws_meta + 64;
+  if (blockIdx.x == 0 && threadIdx.x == 0) hdr[32] = 0;
+  const int lane = threadIdx.x & 63;
+  const int c = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (c >= hdr[0]) return;
+  const int* meta = chunk_meta + 4 * (size_t)c;
   const int parts = meta[2];
   if (parts < 2) return;
   const int s = meta[0];
   const int kv = meta[1];
   const int g = p.group;
-  const int tid = threadIdx.x;
-  const int wid = tid >> 6;
-  const int lane = tid & 63;
-  auto slot = [&](int i) -> size_t { return i == 0 ? 2 * (size_t)w + 1 : 2 * ((size_t)w + i); };
+  const int h = lane / LPH;
+  const int sub = lane % LPH;
+  const int hr = h < g ? h : 0;  // lanes of padding heads read head 0 and store nothing
 
-  __shared__ float red_max[4];
-  __shared__ float red_l[4];
-  __shared__ float red_acc[4][D];
-
-  float mx = kNegBig;
-  for (int i = tid; i < parts; i += 256) mx = fmaxf(mx, p.ws_ml[(slot(i) * g + h) * 2]);
+  float m = kNegBig, l = 0.f;
+  float acc[EPL];
 #pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d));
-  if (lane == 0) red_max[wid] = mx;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(red_max[0], red_max[1]), fmaxf(red_max[2], red_max[3]));
-
-  float acc[EPT];
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) acc[e] = 0.f;
-  float ls = 0.f;
-  for (int i = wid; i < parts; i += 4) {
-    const size_t r = slot(i) * g + h;
-    const float wt = fast_exp2(p.ws_ml[r * 2] - M);
-    ls = fmaf(wt, p.ws_ml[r * 2 + 1], ls);
-    const float* a = p.ws_acc + r * D + lane * EPT;
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) acc[e] = fmaf(wt, a[e], acc[e]);
-  }
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) red_acc[wid][lane * EPT + e] = acc[e];
-  if (lane == 0) red_l[wid] = ls;
-  __syncthreads();
-  if (wid == 0) {
-    const float lsum = (red_l[0] + red_l[1]) + (red_l[2] + red_l[3]);
-    float o[EPT];
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      const int i = lane * EPT + e;
-      o[e] = ((red_acc[0][i] + red_acc[1][i]) + (red_acc[2][i] + red_acc[3][i])) / lsum;
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  for (int i = 0; i < parts; ++i) {
+    size_t sl;
+    if (i == 0) {
+      sl = 2 * (size_t)c + 1;
+    } else {
+      if (!chunk_meta[4 * ((size_t)c + i) + 3]) continue;
+      sl = 2 * ((size_t)c + i);
     }
-    store_row<DT, EPT>((char*)p.out + ((size_t)s * p.num_heads + kv * g + h) * (D * EB) + lane * (EPT * EB), o);
+    const size_t r = sl * g + hr;
+    const float mi = p.ws_ml[2 * r];
+    const float li = p.ws_ml[2 * r + 1];
+    const float* a = p.ws_acc + r * D + sub * EPL;
+    const float mn = fmaxf(m, mi);
+    const float fa = fast_exp2(m - mn);
+    const float fb = fast_exp2(mi - mn);
+    l = fmaf(li, fb, l * fa);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = fmaf(a[e], fb, acc[e] * fa);
+    m = mn;
+  }
+  if (h < g) {
+    float o[EPL];
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[e] = acc[e] / l;
+    store_row<DT, EPL>((char*)p.out + ((size_t)s * p.num_heads + kv * g + h) * (D * EB) + sub * (EPL * EB), o);
   }
 }
 
 // The decode and merge kernels of one shape (nullptr if not compiled).
+template <int DT, int D, int BS, int GP>
+bool pick(const void** dec, const void** red) {
+  *dec = reinterpret_cast<const void*>(&decode_kernel<DT, D, BS, GP>);
+  *red = reinterpret_cast<const void*>(&reduce_kernel<DT, D, GP>);
+  return true;
+}
+
 template <int DT, int D, int BS>
 bool pick_group(int gp, const void** dec, const void** red) {
-  *red = reinterpret_cast<const void*>(&reduce_kernel<DT, D>);
   switch (gp) {
-    case 1: *dec = reinterpret_cast<const void*>(&decode_kernel<DT, D, BS, 1>); return true;
-    case 2: *dec = reinterpret_cast<const void*>(&decode_kernel<DT, D, BS, 2>); return true;
-    case 4: *dec = reinterpret_cast<const void*>(&decode_kernel<DT, D, BS, 4>); return true;
-    case 8: *dec = reinterpret_cast<const void*>(&decode_kernel<DT, D, BS, 8>); return true;
-    case 16: *dec = reinterpret_cast<const void*>(&decode_kernel<DT, D, BS, 16>); return true;
+    case 1: return pick<DT, D, BS, 1>(dec, red);
+    case 2: return pick<DT, D, BS, 2>(dec, red);
+    case 4: return pick<DT, D, BS, 4>(dec, red);
+    case 8: return pick<DT, D, BS, 8>(dec, red);
+    case 16: return pick<DT, D, BS, 16>(dec, red);
     default: return false;
   }
 }

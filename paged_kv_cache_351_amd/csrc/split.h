@@ -17,6 +17,15 @@
 //     The wave that holds the pair's first tile "owns" the pair; its piece is
 //     its last segment.  Every other piece is the first segment of its wave.
 //
+// Waves do not all run at the same speed (the oldest wave on a SIMD is issued
+// first, and some XCDs are slower than others), so each share can be cut into
+// two chunks: its head (all but the last 1/tail_div of it), which wave k
+// processes first, and its tail, which goes to whichever wave asks first once
+// its own head is done (tail_div = 0: no tails, every share is one chunk).
+// Chunk 2k is the head of share k and chunk 2k+1 its tail; chunk boundaries are
+// fixed by the lengths alone, so the result does not depend on which wave took
+// which tail.  Pieces and owners are defined per chunk exactly as above.
+//
 // Everything here is plain integer arithmetic shared by the kernels and by the
 // host code that sizes the workspace.
 #pragma once
@@ -49,7 +58,24 @@ __host__ __device__ inline long long wave_of(long long t, long long T, long long
   return ((t + 1) * nw + T - 1) / T - 1;
 }
 
-// Walk the tiles [t0, t1) of one wave, starting in pair (s, kv) at tile j of
+// First tile of chunk c (c = 2 nw gives T).  Chunk 2k is the head of share k,
+// chunk 2k+1 its last (length / tail_div) tiles, which may be none.
+__host__ __device__ inline long long chunk_begin(long long c, long long T, long long nw, int tail_div) {
+  const long long k = c >> 1;
+  const long long b = wave_begin(k, T, nw);
+  if ((c & 1) == 0) return b;
+  const long long e = wave_begin(k + 1, T, nw);
+  return tail_div > 0 ? e - (e - b) / tail_div : e;
+}
+
+// The chunk holding tile t (0 <= t < T): the largest c with chunk_begin(c) <= t,
+// so an empty chunk is never returned.
+__host__ __device__ inline long long chunk_of(long long t, long long T, long long nw, int tail_div) {
+  const long long k = wave_of(t, T, nw);
+  return 2 * k + (t >= chunk_begin(2 * k + 1, T, nw, tail_div) ? 1 : 0);
+}
+
+// Walk the tiles [t0, t1) of one chunk, starting in pair (s, kv) at tile j of
 // that pair.  len(s) gives the length of sequence s (already clamped); seg(s,
 // kv, jb, je, L) is called for each segment, tiles [jb, je) of pair (s, kv).
 // The caller guarantees that tile t0 is tile j of pair (s, kv) and t1 <= T,

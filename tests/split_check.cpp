@@ -1,16 +1,17 @@
 // Host check of the even tile split used by the decode kernel (split.h).
 //
 // For seeded random batches (empty sequences, partial tiles, long sequences, more
-// waves than tiles) it replays what every wave does -- locate its first tile,
-// walk its segments -- and checks that:
+// waves than tiles) it replays what the kernel does for every chunk (the head and
+// the tail of each wave's share) -- locate its first tile, walk its segments --
+// and checks that:
 //   * every tile of every (sequence, KV head) pair is visited exactly once, and
-//     the waves' ranges cover [0, T) in order;
+//     the chunks' ranges cover [0, T) in order (tail chunks may be empty);
 //   * a segment never leaves its pair, and segments follow the pair order;
 //   * a split pair has exactly one owner (the piece holding its first tile), which
-//     is its wave's last segment; every other piece is its wave's first segment;
-//   * the pieces the merge step reads for an owned pair (slot 2w+1 of the owner,
-//     then slot 2v of waves v = w+1 .. w+parts-1) are exactly that pair's pieces
-//     and together cover its tiles.
+//     is its chunk's last segment; every other piece is its chunk's first segment;
+//   * the pieces the merge step reads for an owned pair (slot 2c+1 of the owner
+//     chunk c, then slot 2c' of every chunk c' = c+1 .. c+parts-1 that wrote a
+//     first piece) are exactly that pair's pieces and together cover its tiles.
 // Prints "split ok: <cases>" and exits 0, or prints the first failure and exits 1.
 #include <stdio.h>
 #include <stdlib.h>
@@ -31,7 +32,7 @@ static int fail(const char* what, int c) {
   return 1;
 }
 
-int check(const std::vector<int>& lens, int Hkv, long long launched, int c) {
+int check(const std::vector<int>& lens, int Hkv, long long launched, int c, int td) {
   const int N = (int)lens.size();
   std::vector<long long> C(N + 1, 0);  // C[s] = tiles of sequences before s
   for (int s = 0; s < N; ++s) C[s + 1] = C[s] + tiles_of(lens[s]);
@@ -41,12 +42,17 @@ int check(const std::vector<int>& lens, int Hkv, long long launched, int c) {
   if (T == 0 && nw != 0) return fail("waves for an empty batch", c);
 
   std::vector<int> seen(T, 0);  // visits of each tile, by its global index
-  std::vector<Piece> first(launched, Piece{-1, -1, -1, -1}), owned(launched, Piece{-1, -1, -1, -1});
-  std::vector<int> parts(launched, 0);
+  const long long nc = 2 * nw;  // chunks
+  std::vector<Piece> first(nc, Piece{-1, -1, -1, -1}), owned(nc, Piece{-1, -1, -1, -1});
+  std::vector<int> parts(nc, 0);
   long long covered = 0;
-  for (long long w = 0; w < nw; ++w) {
-    const long long t0 = wave_begin(w, T, nw), t1 = wave_begin(w + 1, T, nw);
-    if (t0 != covered || t1 <= t0) return fail("wave ranges do not tile [0, T)", c);
+  for (long long w = 0; w < nc; ++w) {
+    const long long t0 = chunk_begin(w, T, nw, td), t1 = chunk_begin(w + 1, T, nw, td);
+    if (t0 != covered || t1 < t0) return fail("chunk ranges do not tile [0, T)", c);
+    if (t1 == t0 && (w & 1) == 0) return fail("empty head chunk", c);
+    if (td == 0 && (w & 1) == 1 && t1 != t0) return fail("tail chunk without tails", c);
+    if (t1 == t0) continue;
+    if (chunk_of(t0, T, nw, td) != w || chunk_of(t1 - 1, T, nw, td) != w) return fail("chunk_of mismatch", c);
     // locate tile t0 as the kernel does: the first sequence whose tiles end past t0
     int s0 = 0;
     while (C[s0 + 1] * Hkv <= t0) ++s0;
@@ -68,7 +74,7 @@ int check(const std::vector<int>& lens, int Hkv, long long launched, int c) {
                  if (nseg == 0 && jb == 0 && je < n) first[w] = Piece{-1, -1, -1, -1};
                  if (jb == 0 && je < n) {
                    owned[w] = Piece{s, kv, jb, je};
-                   parts[w] = (int)(wave_of(t_seg + n - 1, T, nw) - w + 1);
+                   parts[w] = (int)(chunk_of(t_seg + n - 1, T, nw, td) - w + 1);
                  }
                  last_jb = jb;
                  last_je = je;
@@ -90,9 +96,9 @@ int check(const std::vector<int>& lens, int Hkv, long long launched, int c) {
   // pair's own index range, so a count of one everywhere means exact coverage)
   for (long long t = 0; t < T; ++t)
     if (seen[t] != 1) return fail("tile not visited exactly once", c);
-  // the merge step's reads
+  // the merge step's reads: chunks that wrote no first piece (empty tails) are skipped
   int owners = 0;
-  for (long long w = 0; w < nw; ++w) {
+  for (long long w = 0; w < nc; ++w) {
     if (owned[w].s < 0) continue;
     ++owners;
     const Piece o = owned[w];
@@ -100,8 +106,13 @@ int check(const std::vector<int>& lens, int Hkv, long long launched, int c) {
     int next = o.je;
     for (int i = 1; i < parts[w]; ++i) {
       const long long v = w + i;
-      if (v >= nw) return fail("merge reads a wave that got no tiles", c);
+      if (v >= nc) return fail("merge reads past the last chunk", c);
       const Piece f = first[v];
+      if (f.s < 0) {
+        if (chunk_begin(v, T, nw, td) != chunk_begin(v + 1, T, nw, td))
+          return fail("merge skips a non-empty chunk", c);
+        continue;
+      }
       if (f.s != o.s || f.kv != o.kv || f.jb != next) return fail("merge piece mismatch", c);
       next = f.je;
     }
@@ -114,7 +125,7 @@ int check(const std::vector<int>& lens, int Hkv, long long launched, int c) {
       const int n = tiles_of(lens[s]);
       if (n == 0) continue;
       const long long a = C[s] * Hkv + (long long)kv * n;
-      if (wave_of(a, T, nw) != wave_of(a + n - 1, T, nw)) ++split_pairs;
+      if (chunk_of(a, T, nw, td) != chunk_of(a + n - 1, T, nw, td)) ++split_pairs;
     }
   if (split_pairs != owners) return fail("split pairs and owners differ", c);
   return 0;
@@ -137,16 +148,19 @@ int main() {
       else L = (r % 3 == 0) ? (int)(r % 17) : 8192 + (int)(r % 24577);
     }
     for (int Hkv : hkv_set)
-      for (long long launched : launched_set) {
-        if (check(lens, Hkv, launched, cases)) return 1;
-        ++cases;
-      }
+      for (long long launched : launched_set)
+        for (int td : {0, 4, 8}) {
+          if (check(lens, Hkv, launched, cases, td)) return 1;
+          ++cases;
+        }
   }
   // all empty, single token, one huge sequence
-  if (check(std::vector<int>(5, 0), 2, 3072, cases++)) return 1;
-  if (check(std::vector<int>{1}, 1, 3072, cases++)) return 1;
-  if (check(std::vector<int>{0, 0, 1, 0}, 8, 3072, cases++)) return 1;
-  if (check(std::vector<int>{32768}, 8, 3072, cases++)) return 1;
+  for (int td : {0, 8}) {
+    if (check(std::vector<int>(5, 0), 2, 3072, cases++, td)) return 1;
+    if (check(std::vector<int>{1}, 1, 3072, cases++, td)) return 1;
+    if (check(std::vector<int>{0, 0, 1, 0}, 8, 3072, cases++, td)) return 1;
+    if (check(std::vector<int>{32768}, 8, 3072, cases++, td)) return 1;
+  }
   printf("split ok: %d cases\n", cases);
   return 0;
 }

@@ -62,13 +62,14 @@ def test_version(pk):
                                          (1, 8, 8, 128, 1)])
 def test_workspace_size_formula(pk, N, H, HKV, D, L):
     # waves: one per 8 tiles of the longest possible batch, at least 1, at most 8192;
-    # 16 bytes of bookkeeping per wave, then two partial slots of (D + 2) floats per
-    # query head of the group, each region 256-byte aligned
+    # two chunks per wave; a 256-byte header and 16 bytes per chunk, then two partial
+    # slots of (D + 2) floats per query head of the group per chunk, each region
+    # 256-byte aligned
     up = lambda x: -(-x // 256) * 256
     waves = min(8192, max(1, -(-(N * HKV * math.ceil(L / 16)) // 8)))
-    g = H // HKV
+    chunks, g = 2 * waves, H // HKV
     got = pk.pa_decode_workspace_size(N, H, HKV, D, L)
-    assert got == up(waves * 16) + up(2 * waves * g * 2 * 4) + 2 * waves * g * D * 4
+    assert got == up(256 + chunks * 16) + up(2 * chunks * g * 2 * 4) + 2 * chunks * g * D * 4
 
 
 def test_workspace_size_rejects_bad_arguments(pk):
