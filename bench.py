@@ -35,7 +35,7 @@ import workloads  # noqa: E402
 METRIC = "paged-decode KV GB/s read (% of HBM peak) and seqs/s, Llama-3-8B-shaped, 1 GPU"
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, vendor figure
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_llama3_8b_traffic.json")
-KERNEL_SOURCES = ["decode_kernel.h", "decode_bf16.hip", "common.h", "api.hip"]
+KERNEL_SOURCES = ["decode_kernel.h", "split.h", "decode_bf16.hip", "common.h", "api.hip"]
 DECODE_KERNELS = ["decode_kernel", "reduce_kernel"]   # kernels one pa_decode call launches
 
 
