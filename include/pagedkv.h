@@ -73,7 +73,7 @@ const char* pa_last_error(void);
 /* Bytes of workspace pa_decode needs for these arguments (0 for invalid
  * arguments).  It depends only on the shapes: the number of waves a call may
  * launch is bounded by num_seqs * num_kv_heads * ceil(max_seq_len / 16) / 8
- * and by 8192; each wave's work is cut into two chunks, and each chunk needs
+ * and by 4096; each wave's work is cut into two chunks, and each chunk needs
  * 16 bytes of bookkeeping plus two partial results of (head_dim + 2) floats per
  * query head of its group, after a 256-byte header. */
 size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, int head_dim,

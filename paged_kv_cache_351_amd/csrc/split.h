@@ -36,7 +36,7 @@ namespace pagedkv {
 
 constexpr int kTileTokens = 16;       // tokens per tile (the MFMA row count)
 constexpr int kMinTilesPerWave = 8;   // fewer tiles per wave would only add partials
-constexpr int kMaxWaves = 8192;       // 256 CUs x 4 SIMDs x 8 waves: the whole chip
+constexpr int kMaxWaves = 4096;       // 4 per SIMD of a 256-CU chip; the launch uses 1 per SIMD
 
 __host__ __device__ inline int tiles_of(int len) { return (len + kTileTokens - 1) / kTileTokens; }
 
