@@ -1,17 +1,19 @@
 """Benchmark: paged decode attention on one MI355X, Llama-3-8B-shaped GQA layer.
 
 One step = pa_write_kv of 256 new tokens (one per sequence) followed by pa_decode
-over all 256 sequences (decode kernel + split-K reduce kernel), on one stream, with
-every input already resident in HBM.  Workload: 256 sequences, 32 query / 8 KV
-heads, head_dim 128, bf16 KV and q, fp32 accumulation, block size 16, lengths
-uniform in [512, 4096] (seed 0), 70,000-block pool with random block placement.
+over all 256 sequences (decode kernel + merge kernel), on one stream, with every
+input already resident in HBM.  Workload: 256 sequences, 32 query / 8 KV heads,
+head_dim 128, bf16 KV and q, fp32 accumulation, block size 16, lengths uniform in
+[512, 4096] (seed 0), 70,000-block pool with random block placement.
+--workload picks one of the other workloads instead (its step also runs its block
+copies, if any, before the write).
 
 Prints ONE JSON line.  ``value`` is the K/V bytes the decode step must read
 (each (token, KV head) row of K and V once) divided by the measured step time;
 ``roofline`` reports the decode call alone, timed with HIP events on the stream it
 runs on; ``cpu_baseline`` times the float64 CPU oracle on the host.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME [--block-size B]]
     python bench.py --copy-calibration   # a block copy of known size, for counter scaling
     python bench.py --record-traffic DEC_FETCH.csv DEC_WRITE.csv COPY_FETCH.csv COPY_WRITE.csv
 """
@@ -130,9 +132,9 @@ def copy_calibration(steps):
 
 
 def cpu_baseline(b, gpu_out, time_cap=25.0):
-    """The float64 oracle on the host: the step's write, then decode over the workload's
-    sequences in order until all are done or the time cap is reached.  Also reports its
-    max abs difference from the GPU output on those sequences."""
+    """The float64 oracle on the host: the step's block copies and write, then decode over the
+    workload's sequences in order until all are done or the time cap is reached.  Also reports
+    its max abs difference from the GPU output on those sequences."""
     import oracle
     from workloads import as_numpy
     try:
@@ -143,22 +145,65 @@ def cpu_baseline(b, gpu_out, time_cap=25.0):
     q, bt, lens = as_numpy(b.q), as_numpy(b.block_tables), as_numpy(b.seq_lens)
     done, err = 0, 0.0
     t0, c0 = time.time(), time.process_time()
-    # the step's write of the new tokens, then decode sequence by sequence
-    kc, vc = oracle.write_kv(as_numpy(b.new_k), as_numpy(b.new_v), as_numpy(b.slot_mapping),
-                             as_numpy(b.k_cache), as_numpy(b.v_cache))
+    kc, vc = as_numpy(b.k_cache), as_numpy(b.v_cache)
+    if b.cow_pairs is not None:
+        kc, vc = oracle.copy_blocks(kc, vc, as_numpy(b.cow_pairs))
+    if b.slot_mapping is not None:
+        kc, vc = oracle.write_kv(as_numpy(b.new_k), as_numpy(b.new_v), as_numpy(b.slot_mapping), kc, vc)
     while done < b.num_seqs and time.time() - t0 < time_cap:
         ref = oracle.paged_decode(q, kc, vc, bt, lens, b.scale, b.dtype, seqs=[done])
         err = max(err, float(np.abs(gpu_out[done] - ref[0]).max()))
         done += 1
     wall, cpu = time.time() - t0, time.process_time() - c0
-    kv = int(lens[:done].astype(np.int64).sum()) * b.num_kv_heads * b.head_dim * 2 * 2
+    esize = 4 if b.dtype == "f32" else 2
+    kv = int(lens[:done].astype(np.int64).sum()) * b.num_kv_heads * b.head_dim * 2 * esize
+    steps = ("block copies, " if b.cow_pairs is not None else "") + \
+            (f"write of all {len(b.slot_mapping)} new tokens, " if b.slot_mapping is not None else "")
     return {"value": kv / wall / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"write of all {b.num_seqs} new tokens, then decode of the first {done} of "
-                      f"{b.num_seqs} sequences of the same workload (numpy float64, "
-                      f"{kv / 1e9:.3f} GB of K/V)",
+            "sample": f"{steps}then decode of the first {done} of {b.num_seqs} sequences of the "
+                      f"same workload (numpy float64, {kv / 1e9:.3f} GB of K/V)",
             "seqs_per_s": done / wall, "wall_s": wall, "cpu_s": cpu,
             "host_cpus": len(os.sched_getaffinity(0)),
             "max_abs_err_gpu_vs_oracle": err}
+
+
+def unique_kv_bytes(b):
+    """K/V bytes of the distinct pool slots the step's sequences read (shared blocks once)."""
+    B = b.block_size
+    seen = set()
+    for s, L in enumerate(b.seq_lens.tolist()):
+        row = b.block_tables[s].tolist()
+        for j in range(-(-L // B)):
+            seen.add((row[j], min(B, L - j * B)))
+    slots = {}
+    for blk, fill in seen:
+        slots[blk] = max(slots.get(blk, 0), fill)
+    esize = 4 if b.dtype == "f32" else 2
+    return sum(slots.values()) * b.num_kv_heads * b.head_dim * 2 * esize
+
+
+WORKLOADS = {
+    # name: (builder, shape description)
+    "llama3_8b": (lambda a: workloads.llama3_8b(seed=0),
+                  {"num_heads": 32, "num_kv_heads": 8, "head_dim": 128, "block_size": 16,
+                   "seq_len_range": [512, 4096], "num_blocks": 70000}),
+    "llama7b": (lambda a: workloads.llama7b(seed=0),
+                {"num_heads": 32, "num_kv_heads": 32, "head_dim": 128, "block_size": 16,
+                 "seq_len_range": [1, 2048]}),
+    "opt13b_shared": (lambda a: workloads.opt13b_shared(seed=0),
+                      {"num_heads": 40, "num_kv_heads": 40, "head_dim": 128, "block_size": 16,
+                       "prompts": 32, "samples": 8, "prompt_len": 1024, "tail_range": [0, 256]}),
+    "opt13b_cow": (lambda a: workloads.opt13b_cow(seed=0),
+                   {"num_heads": 40, "num_kv_heads": 40, "head_dim": 128, "block_size": 16,
+                    "prompts": 32, "samples": 8, "prompt_len": 1000, "cow_pairs": 224}),
+    "llama2_70b": (lambda a: workloads.llama2_70b(seed=0, block_size=a.block_size),
+                   {"num_heads": 64, "num_kv_heads": 8, "head_dim": 128,
+                    "seq_len_range": [8192, 32768], "key_outliers": 0.01}),
+}
+WORKLOAD_NAMES = {"llama3_8b": "llama3_8b_gqa_decode", "llama7b": "llama7b_mha_decode",
+                  "opt13b_shared": "opt13b_shared_prefix_decode", "opt13b_cow": "opt13b_cow_decode",
+                  "llama2_70b": "llama2_70b_long_context_decode"}
+DTYPE_NAME = {"f32": "f32", "f16": "fp16", "bf16": "bf16"}
 
 
 def main():
@@ -168,6 +213,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--workload", default="llama3_8b", choices=sorted(WORKLOADS),
+                    help="the benchmark line is llama3_8b; the others are the remaining workloads "
+                         "of the same study, measured the same way")
+    ap.add_argument("--block-size", type=int, default=16, choices=[8, 16, 32],
+                    help="block size of the llama2_70b workload")
     ap.add_argument("--record-traffic", nargs=4, metavar="CSV",
                     help="decode FETCH_SIZE, decode WRITE_SIZE, copy FETCH_SIZE, copy WRITE_SIZE "
                          "counter files from rocprofv3 --pmc -f csv")
@@ -185,11 +235,15 @@ def main():
         return
 
     dev = torch.device("cuda:0")
-    log("building the llama3_8b workload (seed 0)")
-    b = workloads.llama3_8b(seed=0)
+    build, shape = WORKLOADS[args.workload]
+    log(f"building the {args.workload} workload (seed 0)")
+    b = build(args)
     q, kc, vc = b.q.to(dev), b.k_cache.to(dev), b.v_cache.to(dev)
     bt, lens = b.block_tables.to(dev), b.seq_lens.to(dev)
-    nk, nv, slots = b.new_k.to(dev), b.new_v.to(dev), b.slot_mapping.to(dev)
+    has_write = b.slot_mapping is not None
+    if has_write:
+        nk, nv, slots = b.new_k.to(dev), b.new_v.to(dev), b.slot_mapping.to(dev)
+    pairs = b.cow_pairs.to(dev) if b.cow_pairs is not None else None
     out = torch.empty_like(q)
     max_len = b.max_seq_len
     ws = pk.decode_workspace(q, b.num_kv_heads, max_len)
@@ -197,7 +251,11 @@ def main():
     stream = torch.cuda.current_stream()
 
     def step(ev0=None, ev1=None):
-        pk.pa_write_kv(nk, nv, slots, kc, vc)
+        # copies and writes are idempotent, so every step repeats the same state change
+        if pairs is not None:
+            pk.pa_copy_blocks(kc, vc, pairs)
+        if has_write:
+            pk.pa_write_kv(nk, nv, slots, kc, vc)
         if ev0 is not None:
             ev0.record(stream)
         pk.pa_decode(q, kc, vc, bt, lens, b.num_kv_heads, b.scale, out, max_seq_len=max_len,
@@ -230,10 +288,10 @@ def main():
     res = {
         "metric": METRIC, "value": value, "unit": "GB/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "llama3_8b_gqa_decode", "num_seqs": b.num_seqs, "num_heads": 32,
-                   "num_kv_heads": 8, "head_dim": 128, "block_size": 16,
-                   "seq_len_range": [512, 4096], "num_blocks": b.num_blocks, "write_tokens": 256,
+        "scaling": "weak", "vs_baseline": None, "dtype": DTYPE_NAME[b.dtype], "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES[args.workload], "num_seqs": b.num_seqs, **shape,
+                   "block_size": b.block_size, "num_blocks": b.num_blocks,
+                   "write_tokens": len(b.slot_mapping) if has_write else 0,
                    "seed": 0, "kv_bytes_per_step": kv_bytes},
         "pct_of_hbm_peak": 100.0 * value / HBM_PEAK_GBS,
         "seqs_per_s": b.num_seqs / (total / K),
@@ -245,6 +303,14 @@ def main():
                      "p90_us": float(np.percentile(dec_ms, 90)) * 1e3},
         "cpu_baseline": None,
     }
+    if args.workload != "llama3_8b":
+        # counters are recorded for the benchmark line's kernel only
+        res["roofline"]["traffic"] = None
+    if args.workload.startswith("opt13b"):
+        # samples share their prompt's blocks: logical bytes count them once per sample
+        ub = unique_kv_bytes(b)
+        res["config"]["unique_kv_bytes_per_step"] = ub
+        res["roofline"]["achieved_unique"] = ub / (dec_avg * 1e-3) / 1e9
     if not args.no_cpu_baseline:
         log("cpu baseline: float64 oracle on the host")
         torch.cuda.synchronize()
