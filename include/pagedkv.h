@@ -73,9 +73,9 @@ const char* pa_last_error(void);
 /* Bytes of workspace pa_decode needs for these arguments (0 for invalid
  * arguments).  It depends only on the shapes: the number of waves a call may
  * launch is bounded by num_seqs * num_kv_heads * ceil(max_seq_len / 16) / 8
- * and by 4096; each wave's work is cut into two chunks, and each chunk needs
- * 16 bytes of bookkeeping plus two partial results of (head_dim + 2) floats per
- * query head of its group, after a 256-byte header. */
+ * and by 2048; each wave's work is cut into at most five chunks, and each chunk
+ * needs 16 bytes of bookkeeping plus two partial results of (head_dim + 2)
+ * floats per query head of its group, after a 256-byte header. */
 size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
                                 int max_seq_len);
 
@@ -93,8 +93,8 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, i
  *
  * Work split: the step's (sequence, KV head) pairs are cut into 16-token tiles
  * and the launched waves (as many as the device holds at once) take equal runs
- * of consecutive tiles, whatever the length mix; the last eighth of every run is
- * handed to whichever wave is free first.  A pair cut by a run boundary is
+ * of consecutive tiles, whatever the length mix; the last eighth of every run,
+ * cut into parts of halving size, is handed to whichever wave is free first.  A pair cut by a run boundary is
  * finished by a second kernel on the same stream, which merges the pieces'
  * running maxima, sums and accumulators with the same rule.  The boundaries
  * depend only on the lengths, so which wave did which part never changes the

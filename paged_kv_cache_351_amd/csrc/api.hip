@@ -55,15 +55,23 @@ int requested_waves() {
   return v;
 }
 
-// The last 1/8 of every wave's share goes to whichever wave is free first;
-// PA_DECODE_TAIL = d overrides the divisor (0 = no tails), for tuning sweeps.
+// The last 1/12 of every wave's share goes to whichever wave is free first, in
+// one part (smaller tails leave a longer finish, larger ones cost more chunk
+// starts and partial results); PA_DECODE_TAIL = d overrides the divisor (0 = no tails) and
+// PA_DECODE_TAIL_PIECES the number of parts (halving sizes), for tuning sweeps.
+constexpr int kDefaultTailDiv = 12;
+int tail_pieces() {
+  static const int v = std::min(env_int("PA_DECODE_TAIL_PIECES", 1), kMaxTailPieces);
+  return v;
+}
+
 int tail_divisor() {
   static const int v = [] {
     const char* s = getenv("PA_DECODE_TAIL");
-    if (!s || !*s) return 8;
+    if (!s || !*s) return kDefaultTailDiv;
     char* end = nullptr;
     const long x = strtol(s, &end, 10);
-    return (end && *end == 0 && x >= 0 && x <= 1024) ? (int)x : 8;
+    return (end && *end == 0 && x >= 0 && x <= 1024) ? (int)x : kDefaultTailDiv;
   }();
   return v;
 }
@@ -77,10 +85,10 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 constexpr int kMaxSeqLen = 1 << 24;
 
 // Workspace of one pa_decode call.  Each launched wave's share of the step is
-// cut into two chunks (head and tail); each chunk has a 16-byte record (the pair
-// it owns, if split, and whether it left a first piece) and two partial-result
-// slots (running max and sum, and the unnormalised accumulator, for each query
-// head of the group).  A 256-byte header holds the chunk count and the counter
+// cut into chunks (a head and up to kMaxTailPieces tail parts); each chunk has
+// a 16-byte record (the pair it owns, if split, and whether it left a first
+// piece) and two partial-result slots (running max and sum, and the
+// unnormalised accumulator, for each query head of the group).  A 256-byte header holds the chunk count and the counter
 // that hands out tail chunks; the merge kernel leaves that counter at 0, so the
 // workspace must be zero-filled before its first use only.  The size is the
 // bound for the most waves the call could launch, which depends only on the
@@ -100,7 +108,7 @@ WorkspaceLayout plan_workspace(int num_seqs, int num_heads, int num_kv_heads, in
   long long waves = waves_used(t_max, kMaxWaves);
   if (waves < 1) waves = 1;
   const size_t g = (size_t)(num_heads / num_kv_heads);
-  const size_t chunks = 2 * (size_t)waves;
+  const size_t chunks = (size_t)waves * (kMaxTailPieces + 1);
   const size_t slots = 2 * chunks;
   w.waves = (int)waves;
   w.ml_offset = align_up(256 + chunks * 16, 256);
@@ -130,9 +138,9 @@ hipError_t decode_waves(const void* kernel, int* out) {
   int cus = 0, per_cu = 0;
   e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
-  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64, 0);
+  e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0);
   if (e != hipSuccess) return e;
-  const int n = std::max(1, cus * std::min(per_cu, 4));
+  const int n = std::max(1, cus * std::min(per_cu, 1) * 4);
   cache[{dev, kernel}] = n;
   *out = n;
   return hipSuccess;
@@ -268,13 +276,15 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
   p.max_seq_len = max_seq_len;
   p.num_waves = waves;
   p.tail_div = tail_divisor();
+  p.tail_pieces = tail_pieces();
   p.scale_log2e = (float)((double)scale * 1.4426950408889634074);
 
   void* kargs[] = {&p};
-  e = hipLaunchKernel(dec, dim3(waves), dim3(64), kargs, 0, st);
+  // four waves per workgroup: one workgroup per CU, one wave per SIMD
+  e = hipLaunchKernel(dec, dim3((waves + 3) / 4), dim3(256), kargs, 0, st);
   if (e != hipSuccess) return hip_fail(e, "pa_decode launch");
   // always: it also resets the tail counter for the next call
-  e = hipLaunchKernel(red, dim3((2 * waves + 3) / 4), dim3(256), kargs, 0, st);
+  e = hipLaunchKernel(red, dim3((waves * (p.tail_pieces + 1) + 3) / 4), dim3(256), kargs, 0, st);
   if (e != hipSuccess) return hip_fail(e, "pa_decode merge launch");
   return PA_OK;
 }

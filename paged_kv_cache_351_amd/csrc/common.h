@@ -20,10 +20,10 @@ struct DecodeParams {
   const int32_t* block_tables;
   const int32_t* seq_lens;
   void* out;
-  int* ws_meta;        // 64-int header, then [2 * waves][4]: per chunk, the pair it
+  int* ws_meta;        // 64-int header, then [chunks][4]: per chunk, the pair it
                        // owns, how many chunks share it, whether it left a first piece
-  float* ws_ml;        // [4 * waves][group][2]: running max and sum of each piece
-  float* ws_acc;       // [4 * waves][group][head_dim]: unnormalised accumulator
+  float* ws_ml;        // [2 * chunks][group][2]: running max and sum of each piece
+  float* ws_acc;       // [2 * chunks][group][head_dim]: unnormalised accumulator
   int num_seqs;
   int num_heads;
   int num_kv_heads;
@@ -36,6 +36,7 @@ struct DecodeParams {
   int num_waves;       // decode waves launched
   int tail_div;        // the last 1/tail_div of each wave's share is handed out on
                        // demand; 0 = none
+  int tail_pieces;     // parts the tail is cut into (halving sizes), 1..kMaxTailPieces
   float scale_log2e;   // scale * log2(e): logits are taken in base 2
 };
 

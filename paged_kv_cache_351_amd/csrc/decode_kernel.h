@@ -11,10 +11,9 @@
 //
 // Work decomposition (split.h)
 //   The step's work is cut into 16-token tiles of (sequence, KV head) pairs and
-//   every one of the launched waves (one 64-lane wave per workgroup, as many as
-//   the chip holds at once) takes the same number of consecutive tiles.  Each
-//   wave therefore reads the same number of K/V bytes whatever the length mix,
-//   and no wave waits for a second round of dispatch.  A pair that falls entirely
+//   every launched wave takes the same number of consecutive tiles, so each reads
+//   the same number of K/V bytes whatever the length mix.  There is one wave per
+//   SIMD: four independent 64-lane waves per workgroup, one workgroup per CU.  A pair that falls entirely
 //   inside one wave is finished there; a pair cut by a wave boundary leaves one
 //   partial result per piece, and reduce_kernel merges them.  Every query head of
 //   a KV head's group (g = num_heads / num_kv_heads <= GP) is handled by the same
@@ -199,7 +198,7 @@ __device__ __forceinline__ void load_dwords(const char* src, uint32_t (&w)[NW]) 
 }
 
 template <int DT, int D, int BS, int GP>
-__global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   constexpr int EB = Elem<DT>::bytes;
   constexpr int ROWB = D * EB;       // bytes of one (token, KV head) row
   constexpr int NKC = ROWB / 64;     // 16-byte K chunks per lane per tile
@@ -207,11 +206,12 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
   constexpr int VW = VE * EB / 4;    // V dwords per lane per token
   static_assert(ROWB % 64 == 0 && (BS == 8 || BS == 16 || BS == 32), "shape");
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int grp = lane >> 4;
   const int col = lane & 15;
-  const int w = blockIdx.x;
-  const int launched = gridDim.x;
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);  // waves never talk to each other
+  const int launched = p.num_waves;
+  if (w >= launched) return;
   const int N = p.num_seqs;
   const int Hkv = p.num_kv_heads;
   const int g = p.group;
@@ -225,104 +225,152 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
     }
   }
 
-  // Total tiles of the step.
+  // Tiles of sequence s as seen by this lane (0 past the batch).
+  auto lane_tiles = [&](int s) { return s < N ? tiles_of(seq_len_at(p, s)) : 0; };
+
+  // Total tiles of the step; the lengths of the next 64 sequences are loaded
+  // while the current 64 are summed.
   long long seq_tiles = 0;
-  for (int c = 0; c < N; c += 64) {
-    const int s = c + lane;
-    seq_tiles += wave_sum(s < N ? tiles_of(seq_len_at(p, s)) : 0);
+  {
+    int n_cur = lane_tiles(lane);
+    for (int c = 0; c < N; c += 64) {
+      const int n_nxt = lane_tiles(c + 64 + lane);
+      seq_tiles += wave_sum(n_cur);
+      n_cur = n_nxt;
+    }
   }
   const long long T = seq_tiles * Hkv;
   const long long nw = waves_used(T, launched);
+  const ChunkPlan plan{T, nw, p.tail_div, p.tail_pieces};
 
   // Workspace header: [0] = chunks of this call (for the merge kernel), [32] =
-  // counter of tail chunks handed out (the merge kernel sets it back to 0).
+  // counter of tail parts handed out (the merge kernel sets it back to 0).
   int* const hdr = p.ws_meta;
   int* const chunk_meta = p.ws_meta + 64;
-  if (w == 0 && lane == 0) hdr[0] = (int)(2 * nw);
+  if (w == 0 && lane == 0) hdr[0] = (int)plan.chunks();
 
-  // Next tail chunk for this wave, or -1 when all are taken.
+  // Next tail part for this wave, or -1 when all are taken.
   auto next_tail = [&]() -> long long {
     int ticket = 0;
     if (lane == 0) ticket = atomicAdd(hdr + 32, 1);
     ticket = __builtin_amdgcn_readfirstlane(ticket);
-    return ticket < nw ? 2 * (long long)ticket + 1 : -1;
+    return ticket < (long long)plan.pieces * nw ? plan.ticket_chunk(ticket) : -1;
   };
 
   const size_t tok_stride = (size_t)Hkv * ROWB;
   const size_t blk_bytes = (size_t)BS * tok_stride;
   const float sl2 = p.scale_log2e;
+  auto lenf = [&](int s) { return seq_len_at(p, s); };
+  auto valid_id = [&](int id) __attribute__((always_inline)) {
+    return (unsigned)id < (unsigned)p.num_blocks ? id : 0;
+  };
+  // Raw ids of blocks 64 wi + lane of sequence s, which has nblk blocks.  They
+  // are range-checked only where a tile uses them, so a prefetch never stalls on
+  // its data; an id outside the pool is a contract violation and becomes 0, so no
+  // access leaves the pool.
+  auto fetch_ids = [&](int s, int nblk, int wi) __attribute__((always_inline)) {
+    const int b = 64 * wi + lane;
+    return b < nblk ? p.block_tables[(size_t)s * p.max_blocks_per_seq + b] : 0;
+  };
+  auto blocks_of = [&](int L) { return (L + BS - 1) / BS; };
+  auto next_seq = [&](int s) {  // next non-empty sequence after s (N if none)
+    int t = s + 1;
+    while (t < N && seq_len_at(p, t) == 0) ++t;
+    return t;
+  };
+  // Query fragments (MFMA B operand) of pair (s, kv): head kv g + col, chunks 4c + grp.
+  auto load_q = [&](u32x4 (&qf)[NKC], int s, int kv) __attribute__((always_inline)) {
+    const char* qrow = (const char*)p.q + ((size_t)s * p.num_heads + kv * g + col) * ROWB;
+#pragma unroll
+    for (int c = 0; c < NKC; ++c)
+      qf[c] = col < g ? *reinterpret_cast<const u32x4*>(qrow + (4 * c + grp) * 16) : u32x4{0, 0, 0, 0};
+  };
 
-  // The wave's own head chunk first, then tails while any are left.  Without
-  // tails each wave records its own (empty) tail chunk instead.
-  const int tail_div = p.tail_div;
-  if (tail_div == 0 && w < nw && lane == 0)
-    *reinterpret_cast<u32x4*>(chunk_meta + 4 * (2 * (size_t)w + 1)) = u32x4{0u, 0u, 0u, 0u};
-  auto next_chunk = [&]() -> long long { return tail_div > 0 ? next_tail() : -1; };
-  for (long long ck = w < nw ? 2 * (long long)w : next_chunk(); ck >= 0; ck = next_chunk()) {
-    const long long t0 = chunk_begin(ck, T, nw, tail_div);
-    const long long t1 = chunk_begin(ck + 1, T, nw, tail_div);
+  struct Tile {
+    u32x4 k[NKC];
+    uint32_t v[4][VW];
+  };
+
+  // The wave's own head chunk first, then tail parts while any are left.
+  // Without tails each wave records its own (empty) tail parts instead.
+  const long long head = (long long)w * (plan.pieces + 1);
+  if (plan.tail_div == 0 && w < nw && lane == 0)
+    for (int r = 1; r <= plan.pieces; ++r)
+      *reinterpret_cast<u32x4*>(chunk_meta + 4 * (head + r)) = u32x4{0u, 0u, 0u, 0u};
+  auto next_chunk = [&]() -> long long { return plan.tail_div > 0 ? next_tail() : -1; };
+  int scan_c = 0;            // block of 64 sequences where the last located chunk began
+  long long scan_base = 0;   // tiles before that block
+  for (long long ck = w < nw ? head : next_chunk(); ck >= 0; ck = next_chunk()) {
+    const long long t0 = plan.begin(ck);
+    const long long t1 = plan.begin(ck + 1);
     int meta_s = 0, meta_kv = 0, meta_parts = 0, meta_first = 0;
-    if (t0 < t1) {
     // Find the pair and tile of t0: the first sequence whose tiles end past t0.
+    // The scan goes 64 sequences at a time (the next 64 lengths load while the
+    // current ones are scanned) and resumes from the block of 64 where this
+    // wave's previous chunk began when t0 lies past it.
     int s0 = -1;
     long long pair_base = 0;
-    long long base = 0;
-    for (int c = 0; c < N; c += 64) {
-      const int s = c + lane;
-      const int n = s < N ? tiles_of(seq_len_at(p, s)) : 0;
-      const int incl = wave_inclusive_scan(n);
-      const unsigned long long hit = __ballot(s < N && base + (long long)incl * Hkv > t0);
-      if (hit) {
-        const int ln = __ffsll(hit) - 1;
-        s0 = c + ln;
-        pair_base = base + (long long)__builtin_amdgcn_readlane(incl - n, ln) * Hkv;
-        break;
+    if (t0 < t1) {
+      if (t0 < scan_base) {
+        scan_c = 0;
+        scan_base = 0;
       }
-      base += (long long)__builtin_amdgcn_readlane(incl, 63) * Hkv;
+      long long base = scan_base;
+      int n_cur = lane_tiles(scan_c + lane);
+      for (int c = scan_c; c < N; c += 64) {
+        const int n_nxt = lane_tiles(c + 64 + lane);
+        const int incl = wave_inclusive_scan(n_cur);
+        const unsigned long long hit = __ballot(c + lane < N && base + (long long)incl * Hkv > t0);
+        if (hit) {
+          const int ln = __ffsll(hit) - 1;
+          s0 = c + ln;
+          pair_base = base + (long long)__builtin_amdgcn_readlane(incl - n_cur, ln) * Hkv;
+          scan_c = c;
+          scan_base = base;
+          break;
+        }
+        base += (long long)__builtin_amdgcn_readlane(incl, 63) * Hkv;
+        n_cur = n_nxt;
+      }
     }
-    // s0 >= 0 and 0 <= off < Hkv * n0 always (t0 < T); the tests only guard
-    // against reading past the lengths or the pool
-    int n0 = s0 >= 0 ? tiles_of(seq_len_at(p, s0)) : 0;
+    // s0 >= 0 and 0 <= off < Hkv * n0 always for a non-empty chunk (t0 < T); the
+    // tests only guard against reading past the lengths or the pool
+    const int L0 = s0 >= 0 ? seq_len_at(p, s0) : 0;
+    int n0 = tiles_of(L0);
     const long long off = t0 - pair_base;
-    if (off < 0 || off >= (long long)Hkv * n0) n0 = 0;
-    const int kv0 = n0 > 0 ? (int)(off / n0) : 0;
-    const int j0 = n0 > 0 ? (int)(off % n0) : 0;
+    if (t0 >= t1 || off < 0 || off >= (long long)Hkv * n0) n0 = 0;
+    if (n0 > 0) {
+      const int nt = (int)(t1 - t0);
+      // Two cursors walk the chunk's tiles in pair order: `lc` two tiles ahead,
+      // issuing loads, and `cc` behind it, computing.  Loads never stop at the end
+      // of a pair, so the pipeline stays full across segments; the softmax state
+      // is flushed when `cc` finishes a segment.
+      TileCursor lc{s0, (int)(off / n0), (int)(off % n0), n0, L0};
+      TileCursor cc = lc;
 
-    long long t_seg = t0;  // global index of the current segment's first tile
-    auto segment = [&](int s, int kv, int jb, int je, int L) __attribute__((always_inline)) {
-      const int tok0 = jb * kTileTokens;
-      const int tok_end = min(je * kTileTokens, L);
-      const int head0 = kv * g;
-      const char* kbase = (const char*)p.k_cache + (size_t)kv * ROWB;
-      const char* vbase = (const char*)p.v_cache + (size_t)kv * ROWB + col * (VE * EB);
-      const int* trow = p.block_tables + (size_t)s * p.max_blocks_per_seq;
-      const int b_first = tok0 / BS;
-      const int b_end = (tok_end + BS - 1) / BS;
+      // load side: ids of lc's current window (`ids_cur`) and the next one, the
+      // first two windows of lc's sequence (for its next KV head) and of the next
+      // non-empty sequence (prefetched a sequence ahead)
+      int l_seq = s0, l_nblk = blocks_of(L0);
+      int lw = (kTileTokens * lc.j / BS) >> 6;
+      int ids_cur = fetch_ids(l_seq, l_nblk, lw);
+      int ids_nxt = fetch_ids(l_seq, l_nblk, lw + 1);
+      int ids_row0 = fetch_ids(l_seq, l_nblk, 0);
+      int ids_row1 = fetch_ids(l_seq, l_nblk, 1);
+      int pf_seq = next_seq(l_seq);
+      int pf_nblk = pf_seq < N ? blocks_of(seq_len_at(p, pf_seq)) : 0;
+      int ids_pf0 = pf_seq < N ? fetch_ids(pf_seq, pf_nblk, 0) : 0;
+      int ids_pf1 = pf_seq < N ? fetch_ids(pf_seq, pf_nblk, 1) : 0;
+      int l_pair = 0, l_count = 0;
 
-      // Query fragments (MFMA B operand): head head0 + col, chunks 4c + grp.
-      u32x4 qf[NKC];
-      {
-        const char* qrow = (const char*)p.q + ((size_t)s * p.num_heads + head0 + col) * ROWB;
+      // compute side: q of cc's pair, q of the next pair when lc has fetched it
+      int c_pair = 0, c_count = 0, seg_jb = cc.j;
+      long long seg_t = t0;
+      u32x4 qf[NKC], qf_nxt[NKC];
+      int qn_pair = -1;
+      load_q(qf, cc.s, cc.kv);
 #pragma unroll
-        for (int c = 0; c < NKC; ++c)
-          qf[c] = col < g ? *reinterpret_cast<const u32x4*>(qrow + (4 * c + grp) * 16) : u32x4{0, 0, 0, 0};
-      }
-
-      // Block ids, 64 at a time, one per lane: `ids` holds those of blocks
-      // b_first + 64 win + lane and `ids_next` the next 64, fetched a whole window
-      // ahead.  Ids are range-checked only where a tile uses them, so the prefetch
-      // never stalls on its data; an id outside the pool is a contract violation
-      // and becomes 0, so no access leaves the pool.
-      auto fetch_ids = [&](int wi) __attribute__((always_inline)) {
-        const int b = b_first + 64 * wi + lane;
-        return b < b_end ? trow[b] : 0;
-      };
-      int win = 0;
-      int ids = fetch_ids(0);
-      int ids_next = b_end - b_first > 64 ? fetch_ids(1) : 0;
-      auto valid_id = [&](int id) __attribute__((always_inline)) {
-        return (unsigned)id < (unsigned)p.num_blocks ? id : 0;
-      };
+      for (int c = 0; c < NKC; ++c) qf_nxt[c] = u32x4{0, 0, 0, 0};
 
       float m = kNegBig;
       float l = 0.f;
@@ -332,50 +380,152 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
 #pragma unroll
         for (int e = 0; e < VE; ++e) acc[h][e] = 0.f;
 
-      struct Tile {
-        u32x4 k[NKC];
-        uint32_t v[4][VW];
-      };
-
-      const int n_tok = tok_end - tok0;
-      const int last = n_tok - 1;
-
-      // Tile tt covers the segment's tokens [16 tt, 16 tt + 16).  A token index
-      // past the segment's last token is clamped to it, so every load reads a real
-      // row of this sequence; such tokens get weight exactly 0 from the score mask.
-      // The window `win` is that of the older of the two tiles being loaded; a
-      // window holds at least 32 tiles, so the younger one is in `win` or the next.
-      auto load_tile = [&](Tile& Tl, int tt) __attribute__((always_inline)) {
-        const int a = kTileTokens * tt;
-        const int blk = (tok0 + a) / BS - b_first;        // first block of the tile
-        const int idsrc = (blk >> 6) != win ? ids_next : ids;
-        const int tk = tok0 + min(a + col, last);
+      // Issue the loads of lc's tile, then step lc (the chunk's last tile is
+      // loaded again rather than stepping past it).  A token index past the pair's
+      // last token is clamped to it, so every load reads a real row of the
+      // sequence; such tokens get weight exactly 0 from the score mask.
+      auto load_next = [&](Tile& Tl) __attribute__((always_inline)) {
+        const int blk = kTileTokens * lc.j / BS;  // first block of the tile
+        if ((blk >> 6) != lw) {                    // a window holds >= 32 tiles
+          ++lw;
+          ids_cur = ids_nxt;
+          ids_nxt = fetch_ids(l_seq, l_nblk, lw + 1);
+        }
+        const int a = kTileTokens * lc.j;
+        const int last = lc.L - 1;
+        const int tk = min(a + col, last);
         int tv[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) tv[j] = tok0 + min(a + 4 * grp + j, last);
+        for (int j = 0; j < 4; ++j) tv[j] = min(a + 4 * grp + j, last);
         int pk, pv[4];
         if constexpr (BS == 8) {
-          // a tile spans two blocks; the tile starts on a multiple of 16 tokens
-          const int ida = valid_id(__builtin_amdgcn_readlane(idsrc, blk & 63));
-          const int idb = valid_id(__builtin_amdgcn_readlane(idsrc, (blk & 63) + 1));
+          // a tile spans two blocks; it starts on a multiple of 16 tokens
+          const int ida = valid_id(__builtin_amdgcn_readlane(ids_cur, blk & 63));
+          const int idb = valid_id(__builtin_amdgcn_readlane(ids_cur, (blk & 63) + 1));
           pk = (tk & 8) ? idb : ida;
 #pragma unroll
           for (int j = 0; j < 4; ++j) pv[j] = (tv[j] & 8) ? idb : ida;
         } else {
-          const int id = valid_id(__builtin_amdgcn_readlane(idsrc, blk & 63));
+          const int id = valid_id(__builtin_amdgcn_readlane(ids_cur, blk & 63));
           pk = id;
 #pragma unroll
           for (int j = 0; j < 4; ++j) pv[j] = id;
         }
-        const char* kp = kbase + (size_t)pk * blk_bytes + (size_t)(tk % BS) * tok_stride;
+        const char* kp = (const char*)p.k_cache + (size_t)lc.kv * ROWB + (size_t)pk * blk_bytes +
+                         (size_t)(tk % BS) * tok_stride;
+        const char* vb = (const char*)p.v_cache + (size_t)lc.kv * ROWB + col * (VE * EB);
 #pragma unroll
         for (int c = 0; c < NKC; ++c) Tl.k[c] = *reinterpret_cast<const u32x4*>(kp + (4 * c + grp) * 16);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          load_dwords<VW>(vbase + (size_t)pv[j] * blk_bytes + (size_t)(tv[j] % BS) * tok_stride, Tl.v[j]);
+          load_dwords<VW>(vb + (size_t)pv[j] * blk_bytes + (size_t)(tv[j] % BS) * tok_stride, Tl.v[j]);
+
+        TileCursor nx = lc;  // a chunk never ends past the batch, so the step succeeds
+        if (l_count + 1 < nt && nx.next(N, Hkv, lenf)) {
+          ++l_count;
+          const int old_s = lc.s, old_kv = lc.kv;
+          lc = nx;
+          if (lc.s != old_s || lc.kv != old_kv) {  // lc entered the next pair
+            ++l_pair;
+            if (lc.s != old_s) {
+              l_seq = lc.s;
+              l_nblk = blocks_of(lc.L);
+              if (pf_seq == l_seq) {
+                ids_row0 = ids_pf0;
+                ids_row1 = ids_pf1;
+              } else {
+                ids_row0 = fetch_ids(l_seq, l_nblk, 0);
+                ids_row1 = fetch_ids(l_seq, l_nblk, 1);
+              }
+              pf_seq = next_seq(l_seq);
+              pf_nblk = pf_seq < N ? blocks_of(seq_len_at(p, pf_seq)) : 0;
+              ids_pf0 = pf_seq < N ? fetch_ids(pf_seq, pf_nblk, 0) : 0;
+              ids_pf1 = pf_seq < N ? fetch_ids(pf_seq, pf_nblk, 1) : 0;
+            }
+            lw = 0;
+            ids_cur = ids_row0;
+            ids_nxt = ids_row1;
+            if (l_pair == c_pair + 1) {
+              load_q(qf_nxt, lc.s, lc.kv);
+              qn_pair = l_pair;
+            }
+          }
+        }
       };
 
-      auto compute = [&](const Tile& Tl, int tt) __attribute__((always_inline)) {
+      // Normalise or store the finished segment [jb, je) of pair (s, kv).
+      auto flush = [&](int s, int kv, int jb, int je, int L, long long tseg) __attribute__((always_inline)) {
+        // Merge the four per-group streams of every head.
+        float M = fmaxf(m, __shfl_xor(m, 16));
+        M = fmaxf(M, __shfl_xor(M, 32));
+        const float f = fast_exp2(m - M);
+        float ls = l * f;
+        ls += __shfl_xor(ls, 16);
+        ls += __shfl_xor(ls, 32);
+        static_for<GP>([&](auto hc) {
+          constexpr int h = decltype(hc)::value;
+          const float fh = row_bcast<h>(f);
+#pragma unroll
+          for (int e = 0; e < VE; ++e) {
+            float x = acc[h][e] * fh;
+            x += __shfl_xor(x, 16);
+            x += __shfl_xor(x, 32);
+            acc[h][e] = x;
+          }
+        });
+        const int head0 = kv * g;
+        const int n_pair = tiles_of(L);
+        if (jb == 0 && je == n_pair) {
+          // whole pair in this chunk: every row now holds the full sums; row grp
+          // stores heads h = grp (mod 4)
+          static_for<GP>([&](auto hc) {
+            constexpr int h = decltype(hc)::value;
+            const float lh = row_bcast<h>(ls);
+            if (h < g && (h & 3) == grp) {
+              float o[VE];
+#pragma unroll
+              for (int e = 0; e < VE; ++e) o[e] = acc[h][e] / lh;
+              store_row<DT, VE>((char*)p.out + ((size_t)s * p.num_heads + head0 + h) * ROWB + col * (VE * EB), o);
+            }
+          });
+        } else {
+          // one piece of a pair split over chunks: the owner (first tile) writes to
+          // slot 2c + 1, every other piece is its chunk's first segment, slot 2c
+          const bool owner = jb == 0;
+          const size_t slot = 2 * (size_t)ck + (owner ? 1 : 0);
+          static_for<GP>([&](auto hc) {
+            constexpr int h = decltype(hc)::value;
+            if (h < g && (h & 3) == grp) {
+              float* dst = p.ws_acc + (slot * g + h) * D + col * VE;
+#pragma unroll
+              for (int e = 0; e < VE; e += 4)
+                *reinterpret_cast<f32x4*>(dst + e) = f32x4{acc[h][e], acc[h][e + 1], acc[h][e + 2], acc[h][e + 3]};
+            }
+          });
+          if (grp == 0 && col < g) {
+            float* ml = p.ws_ml + (slot * g + col) * 2;
+            ml[0] = M;
+            ml[1] = ls;
+          }
+          if (owner) {
+            meta_s = s;
+            meta_kv = kv;
+            meta_parts = (int)(plan.chunk_of(tseg + n_pair - 1) - ck + 1);
+          } else {
+            meta_first = 1;
+          }
+        }
+        m = kNegBig;
+        l = 0.f;
+#pragma unroll
+        for (int h = 0; h < GP; ++h)
+#pragma unroll
+          for (int e = 0; e < VE; ++e) acc[h][e] = 0.f;
+      };
+
+      // Fold cc's tile into the running softmax, flush at the end of a segment,
+      // then step cc.
+      auto compute_next = [&](const Tile& Tl) __attribute__((always_inline)) {
         // S = K q^T on the matrix cores
         f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -394,7 +544,7 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
           }
         }
         // online softmax, stream (grp, head col); tokens past the end get -inf
-        const int lim = n_tok - kTileTokens * tt - 4 * grp;
+        const int lim = cc.L - kTileTokens * cc.j - 4 * grp;
         float sv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) sv[r] = r < lim ? sc[r] * sl2 : -__builtin_inff();
@@ -426,104 +576,49 @@ __global__ __launch_bounds__(64) void decode_kernel(DecodeParams p) {
             for (int e = 0; e < VE; ++e) acc[h][e] = fmaf(pj, vf[e], acc[h][e]);
           });
         }
+
+        TileCursor nx = cc;  // as for lc, the step succeeds whenever a tile is left
+        const bool last_tile = c_count + 1 == nt || !nx.next(N, Hkv, lenf);
+        if (last_tile || cc.j + 1 == cc.n) {
+          flush(cc.s, cc.kv, seg_jb, cc.j + 1, cc.L, seg_t);
+          if (!last_tile) {  // on to the next pair
+            cc = nx;
+            ++c_count;
+            ++c_pair;
+            seg_jb = 0;
+            seg_t = t0 + c_count;
+            if (qn_pair == c_pair) {
+#pragma unroll
+              for (int c = 0; c < NKC; ++c) qf[c] = qf_nxt[c];
+            } else {
+              load_q(qf, cc.s, cc.kv);
+            }
+          }
+        } else {
+          cc = nx;
+          ++c_count;
+        }
       };
 
-      // Two tiles in flight across the whole segment: while one is reduced the
-      // next two are being fetched.  Loads are unconditional (clamped tile index)
-      // so no tile register is ever copied, and the scheduling barriers keep a
-      // refill after the last use of the registers it overwrites.
-      const int n_tiles = je - jb;
-      const int lt = n_tiles - 1;
+      // Two tiles in flight: while one is reduced the next two are being fetched.
+      // Loads are unconditional so no tile register is ever copied, and the
+      // scheduling barriers keep a refill after the last use of the registers it
+      // overwrites.
       Tile A, B;
-      load_tile(A, 0);
+      load_next(A);
       __builtin_amdgcn_sched_barrier(0);
-      load_tile(B, min(1, lt));
+      load_next(B);
       __builtin_amdgcn_sched_barrier(0);
-      for (int tt = 0; tt < n_tiles; tt += 2) {
-        {
-          // move the block window forward before loading tiles tt + 2 and tt + 3
-          const int blk = (tok0 + kTileTokens * min(tt + 2, lt)) / BS - b_first;
-          if ((blk >> 6) != win) {
-            ++win;
-            ids = ids_next;
-            ids_next = b_first + 64 * (win + 1) < b_end ? fetch_ids(win + 1) : 0;
-          }
-        }
-        compute(A, tt);
+      for (int tt = 0; tt < nt; tt += 2) {
+        compute_next(A);
         __builtin_amdgcn_sched_barrier(0);
-        load_tile(A, min(tt + 2, lt));
+        load_next(A);
         __builtin_amdgcn_sched_barrier(0);
-        if (tt + 1 < n_tiles) compute(B, tt + 1);
+        if (tt + 1 < nt) compute_next(B);
         __builtin_amdgcn_sched_barrier(0);
-        load_tile(B, min(tt + 3, lt));
+        load_next(B);
         __builtin_amdgcn_sched_barrier(0);
       }
-
-      // Merge the four per-group streams of every head.
-      float M = fmaxf(m, __shfl_xor(m, 16));
-      M = fmaxf(M, __shfl_xor(M, 32));
-      const float f = fast_exp2(m - M);
-      float ls = l * f;
-      ls += __shfl_xor(ls, 16);
-      ls += __shfl_xor(ls, 32);
-      static_for<GP>([&](auto hc) {
-        constexpr int h = decltype(hc)::value;
-        const float fh = row_bcast<h>(f);
-#pragma unroll
-        for (int e = 0; e < VE; ++e) {
-          float x = acc[h][e] * fh;
-          x += __shfl_xor(x, 16);
-          x += __shfl_xor(x, 32);
-          acc[h][e] = x;
-        }
-      });
-
-      const int n_pair = tiles_of(L);
-      if (jb == 0 && je == n_pair) {
-        // whole pair in this wave: every row now holds the full sums; row grp
-        // stores heads h = grp (mod 4)
-        static_for<GP>([&](auto hc) {
-          constexpr int h = decltype(hc)::value;
-          const float lh = row_bcast<h>(ls);
-          if (h < g && (h & 3) == grp) {
-            float o[VE];
-#pragma unroll
-            for (int e = 0; e < VE; ++e) o[e] = acc[h][e] / lh;
-            store_row<DT, VE>((char*)p.out + ((size_t)s * p.num_heads + head0 + h) * ROWB + col * (VE * EB), o);
-          }
-        });
-      } else {
-        // one piece of a pair split over chunks: the owner (first tile) writes to
-        // slot 2c + 1, every other piece is its chunk's first segment, slot 2c
-        const bool owner = jb == 0;
-        const size_t slot = 2 * (size_t)ck + (owner ? 1 : 0);
-        static_for<GP>([&](auto hc) {
-          constexpr int h = decltype(hc)::value;
-          if (h < g && (h & 3) == grp) {
-            float* dst = p.ws_acc + (slot * g + h) * D + col * VE;
-#pragma unroll
-            for (int e = 0; e < VE; e += 4)
-              *reinterpret_cast<f32x4*>(dst + e) = f32x4{acc[h][e], acc[h][e + 1], acc[h][e + 2], acc[h][e + 3]};
-          }
-        });
-        if (grp == 0 && col < g) {
-          float* ml = p.ws_ml + (slot * g + col) * 2;
-          ml[0] = M;
-          ml[1] = ls;
-        }
-        if (owner) {
-          meta_s = s;
-          meta_kv = kv;
-          meta_parts = (int)(chunk_of(t_seg + n_pair - 1, T, nw, tail_div) - ck + 1);
-        } else {
-          meta_first = 1;
-        }
-      }
-      t_seg += je - jb;
-    };
-
-    if (n0 > 0)
-      walk_tiles(t0, t1, s0, kv0, j0, N, Hkv, [&](int s) { return seq_len_at(p, s); }, segment);
     }
     // Every chunk states whether it owns a split pair (parts >= 2) and whether it
     // left a first piece of one in slot 2c.

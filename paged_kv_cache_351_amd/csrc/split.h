@@ -18,13 +18,17 @@
 //     its last segment.  Every other piece is the first segment of its wave.
 //
 // Waves do not all run at the same speed (the oldest wave on a SIMD is issued
-// first, and some XCDs are slower than others), so each share can be cut into
-// two chunks: its head (all but the last 1/tail_div of it), which wave k
-// processes first, and its tail, which goes to whichever wave asks first once
-// its own head is done (tail_div = 0: no tails, every share is one chunk).
-// Chunk 2k is the head of share k and chunk 2k+1 its tail; chunk boundaries are
-// fixed by the lengths alone, so the result does not depend on which wave took
-// which tail.  Pieces and owners are defined per chunk exactly as above.
+// first, and some XCDs are slower than others), so each share is cut into
+// chunks: its head (all but the last 1/tail_div of it), which wave k processes
+// first, and its tail, cut into `pieces` parts of halving size (1/2, 1/4, ...,
+// the last one taking the rest).  Tail parts go to whichever wave asks first
+// once its head is done, all shares' first parts before any second part, so the
+// work handed out last is the smallest and the waves finish close together.
+// With tail_div = 0 there are no tails.  Chunk c = k (pieces + 1) + r is the
+// head (r = 0) or tail part r - 1 of share k, so chunks follow the tile order.
+// Chunk boundaries are fixed by the lengths alone, so the result does not
+// depend on which wave took which part.  Pieces and owners are defined per
+// chunk exactly as above.
 //
 // Everything here is plain integer arithmetic shared by the kernels and by the
 // host code that sizes the workspace.
@@ -36,7 +40,8 @@ namespace pagedkv {
 
 constexpr int kTileTokens = 16;       // tokens per tile (the MFMA row count)
 constexpr int kMinTilesPerWave = 8;   // fewer tiles per wave would only add partials
-constexpr int kMaxWaves = 4096;       // 4 per SIMD of a 256-CU chip; the launch uses 1 per SIMD
+constexpr int kMaxWaves = 2048;       // 2 per SIMD of a 256-CU chip; the launch uses 1 per SIMD
+constexpr int kMaxTailPieces = 4;     // tail parts per share, at most
 
 __host__ __device__ inline int tiles_of(int len) { return (len + kTileTokens - 1) / kTileTokens; }
 
@@ -58,22 +63,70 @@ __host__ __device__ inline long long wave_of(long long t, long long T, long long
   return ((t + 1) * nw + T - 1) / T - 1;
 }
 
-// First tile of chunk c (c = 2 nw gives T).  Chunk 2k is the head of share k,
-// chunk 2k+1 its last (length / tail_div) tiles, which may be none.
-__host__ __device__ inline long long chunk_begin(long long c, long long T, long long nw, int tail_div) {
-  const long long k = c >> 1;
-  const long long b = wave_begin(k, T, nw);
-  if ((c & 1) == 0) return b;
-  const long long e = wave_begin(k + 1, T, nw);
-  return tail_div > 0 ? e - (e - b) / tail_div : e;
-}
+// Chunk layout of one call: nw shares, each a head and `pieces` tail parts.
+struct ChunkPlan {
+  long long T;    // tiles of the step
+  long long nw;   // shares (waves that get a head)
+  int tail_div;   // 0 = no tails
+  int pieces;     // tail parts per share, >= 1
 
-// The chunk holding tile t (0 <= t < T): the largest c with chunk_begin(c) <= t,
-// so an empty chunk is never returned.
-__host__ __device__ inline long long chunk_of(long long t, long long T, long long nw, int tail_div) {
-  const long long k = wave_of(t, T, nw);
-  return 2 * k + (t >= chunk_begin(2 * k + 1, T, nw, tail_div) ? 1 : 0);
-}
+  __host__ __device__ long long chunks() const { return nw * (pieces + 1); }
+
+  // First tile of chunk c (c = chunks() gives T).
+  __host__ __device__ long long begin(long long c) const {
+    const long long k = c / (pieces + 1);
+    const int r = (int)(c - k * (pieces + 1));
+    const long long b = wave_begin(k, T, nw);
+    if (r == 0) return b;
+    const long long e = wave_begin(k + 1, T, nw);
+    const long long tail = tail_div > 0 ? (e - b) / tail_div : 0;
+    return e - tail + (tail - (tail >> (r - 1)));  // part r-1 starts after 1 - 2^-(r-1) of the tail
+  }
+
+  // The chunk holding tile t (0 <= t < T): the largest c with begin(c) <= t, so
+  // an empty chunk is never returned.
+  __host__ __device__ long long chunk_of(long long t) const {
+    const long long k = wave_of(t, T, nw);
+    const long long c0 = k * (pieces + 1);
+    for (int r = pieces; r > 0; --r)
+      if (begin(c0 + r) <= t) return c0 + r;
+    return c0;
+  }
+
+  // Chunk of tail ticket t (0 <= t < pieces * nw): the first parts of all shares,
+  // then the second parts, and so on.
+  __host__ __device__ long long ticket_chunk(long long t) const {
+    const long long part = t / nw;
+    const long long k = t - part * nw;
+    return k * (pieces + 1) + 1 + part;
+  }
+};
+
+// Position of one tile in pair order: sequence s (length L, n tiles), KV head
+// kv, tile j of the pair.
+struct TileCursor {
+  int s, kv, j, n, L;
+
+  // Step to the next tile of the batch (the next tile of the pair, else the
+  // first tile of the next KV head, else of the next non-empty sequence).
+  // Returns false, leaving n = 0, when there is none; num_seqs bounds every read.
+  template <class LenFn>
+  __host__ __device__ bool next(int num_seqs, int num_kv_heads, LenFn len) {
+    if (++j < n) return true;
+    j = 0;
+    if (++kv < num_kv_heads) return true;
+    kv = 0;
+    do {
+      if (++s >= num_seqs) {
+        n = 0;
+        return false;
+      }
+      L = len(s);
+    } while (L == 0);
+    n = tiles_of(L);
+    return true;
+  }
+};
 
 // Walk the tiles [t0, t1) of one chunk, starting in pair (s, kv) at tile j of
 // that pair.  len(s) gives the length of sequence s (already clamped); seg(s,

@@ -61,13 +61,13 @@ def test_version(pk):
                                          (4, 4, 4, 64, 41), (64, 32, 32, 128, 2048), (3, 8, 2, 64, 0),
                                          (1, 8, 8, 128, 1)])
 def test_workspace_size_formula(pk, N, H, HKV, D, L):
-    # waves: one per 8 tiles of the longest possible batch, at least 1, at most 4096;
-    # two chunks per wave; a 256-byte header and 16 bytes per chunk, then two partial
-    # slots of (D + 2) floats per query head of the group per chunk, each region
-    # 256-byte aligned
+    # waves: one per 8 tiles of the longest possible batch, at least 1, at most 2048;
+    # up to five chunks per wave (a head and four tail parts); a 256-byte header and
+    # 16 bytes per chunk, then two partial slots of (D + 2) floats per query head of
+    # the group per chunk, each region 256-byte aligned
     up = lambda x: -(-x // 256) * 256
-    waves = min(4096, max(1, -(-(N * HKV * math.ceil(L / 16)) // 8)))
-    chunks, g = 2 * waves, H // HKV
+    waves = min(2048, max(1, -(-(N * HKV * math.ceil(L / 16)) // 8)))
+    chunks, g = 5 * waves, H // HKV
     got = pk.pa_decode_workspace_size(N, H, HKV, D, L)
     assert got == up(256 + chunks * 16) + up(2 * chunks * g * 2 * 4) + 2 * chunks * g * D * 4
 
