@@ -60,7 +60,8 @@ typedef enum {
   PA_ERR_INVALID = 1,     /* bad argument or (debug mode) bad index data */
   PA_ERR_UNSUPPORTED = 2, /* valid request outside the compiled kernel set */
   PA_ERR_WORKSPACE = 3,   /* workspace missing or too small */
-  PA_ERR_HIP = 4          /* the HIP runtime reported an error */
+  PA_ERR_HIP = 4,         /* the HIP runtime reported an error */
+  PA_ERR_NO_BLOCKS = 5    /* block manager: the pool has no free block left */
 } pa_status;
 
 /* Library ABI version (incremented on any signature change). */
@@ -168,6 +169,78 @@ pa_status pa_write_kv(const void* k, const void* v, const int32_t* slot_mapping,
 pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst_pairs,
                          int num_pairs, int block_size, int num_kv_heads,
                          int head_dim, int num_blocks, pa_dtype dtype, void* stream);
+
+/*
+ * Block manager -- host bookkeeping of the block pool ([PA-notes] §3 block
+ * table; §5 ①② pool and on-demand allocation; §6.1, §6.2 and §12 题4 sharing,
+ * reference counts and copy-on-write).
+ *
+ * It owns no device memory: it decides which physical block every token of
+ * every sequence lives in and hands the kernels their index inputs -- block
+ * tables and lengths (pa_bm_batch -> pa_decode), one slot per new token
+ * (pa_bm_append_slot -> pa_write_kv) and copy-on-write pairs (-> pa_copy_blocks).
+ * Every array here is HOST memory.  A manager is not thread-safe: use it from
+ * one thread at a time.  On any non-PA_OK status the manager is unchanged.
+ *
+ * Rules: free blocks form a queue (taken from the front, released to the back;
+ * the initial order is free_order, or 0..num_blocks-1).  A prompt of n tokens
+ * takes ceil(n / block_size) blocks.  A new token goes to the next slot after
+ * the filled ones of the sequence's last block, and a new block is taken only
+ * when that block is full.  A fork shares every block of the parent (each
+ * block's count goes up by one).  Writing into a block whose count is above one
+ * first takes a fresh block, points only the writer's table at it, moves one
+ * count from the old block to it and reports the (old, fresh) pair, whose
+ * contents the caller copies with pa_copy_blocks before writing.  Freeing a
+ * sequence decrements its blocks; a block whose count reaches zero returns to
+ * the queue.  Sequences are named by any int64 id.
+ */
+typedef struct pa_block_manager pa_block_manager;
+
+/* New manager of num_blocks blocks of block_size tokens.  free_order: NULL or
+ * a host array holding a permutation of 0..num_blocks-1. */
+pa_status pa_bm_create(int num_blocks, int block_size, const int32_t* free_order,
+                       pa_block_manager** out);
+void pa_bm_destroy(pa_block_manager* bm);
+
+/* Prefill: give a new sequence ceil(num_tokens / block_size) blocks holding
+ * num_tokens tokens.  PA_ERR_NO_BLOCKS if the pool is too small. */
+pa_status pa_bm_allocate(pa_block_manager* bm, int64_t seq, int64_t num_tokens);
+
+/* Reserve the slot of the sequence's next token: *slot = block * block_size +
+ * offset.  If the write needs a private copy of a shared block, *cow_src and
+ * *cow_dst name it (else both are -1). */
+pa_status pa_bm_append_slot(pa_block_manager* bm, int64_t seq, int64_t* slot,
+                            int32_t* cow_src, int32_t* cow_dst);
+
+/* One decode step: reserve the next slot of each of the num_seqs distinct
+ * sequences seqs[i], in that order, as pa_bm_append_slot does.  Writes
+ * slot_mapping[i] (the pa_write_kv input) and the step's copy-on-write pairs to
+ * pairs[2 * *num_pairs] as (src, dst) rows (the pa_copy_blocks input; at most
+ * num_seqs rows, none of whose dst is a src).  Run pa_copy_blocks on the pairs
+ * before pa_write_kv.  All or nothing: if the pool cannot supply every block
+ * the step takes, returns PA_ERR_NO_BLOCKS and changes nothing.
+ * PA_ERR_UNSUPPORTED if num_blocks * block_size does not fit int32 slots. */
+pa_status pa_bm_append_step(pa_block_manager* bm, const int64_t* seqs, int num_seqs,
+                            int32_t* slot_mapping, int32_t* pairs, int* num_pairs);
+
+/* Parallel sampling / beam fork: `child` shares every block of `parent`. */
+pa_status pa_bm_fork(pa_block_manager* bm, int64_t parent, int64_t child);
+
+/* Drop a sequence (finished, or pruned from a beam). */
+pa_status pa_bm_free(pa_block_manager* bm, int64_t seq);
+
+int pa_bm_num_free(const pa_block_manager* bm);               /* -1 if bm is NULL */
+int64_t pa_bm_seq_len(const pa_block_manager* bm, int64_t seq); /* -1 if unknown */
+/* Copies up to cap entries of the sequence's table to out; returns its length
+ * in blocks (-1 if unknown). */
+int pa_bm_table(const pa_block_manager* bm, int64_t seq, int32_t* out, int cap);
+int pa_bm_ref_count(const pa_block_manager* bm, int32_t block); /* -1 out of range */
+
+/* Decode inputs for a batch: row i of block_tables[num_seqs][max_blocks_per_seq]
+ * gets the table of seqs[i] padded with -1, seq_lens[i] its length.  Host
+ * arrays; the caller copies them to the device. */
+pa_status pa_bm_batch(const pa_block_manager* bm, const int64_t* seqs, int num_seqs,
+                      int32_t* block_tables, int max_blocks_per_seq, int32_t* seq_lens);
 
 #ifdef __cplusplus
 }

@@ -18,6 +18,7 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
 
 PA_OK = 0
+PA_ERR_NO_BLOCKS = 5
 _DTYPE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 
 _lib = None
@@ -54,6 +55,24 @@ def lib():
     L.pa_write_kv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
     L.pa_copy_blocks.restype = i32
     L.pa_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+    i64 = ctypes.c_int64
+    pi32, pi64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
+    for name, res, args in (
+            ("pa_bm_create", i32, [i32, i32, pi32, ctypes.POINTER(vp)]),
+            ("pa_bm_destroy", None, [vp]),
+            ("pa_bm_allocate", i32, [vp, i64, i64]),
+            ("pa_bm_append_slot", i32, [vp, i64, pi64, pi32, pi32]),
+            ("pa_bm_append_step", i32, [vp, pi64, i32, pi32, pi32, ctypes.POINTER(i32)]),
+            ("pa_bm_fork", i32, [vp, i64, i64]),
+            ("pa_bm_free", i32, [vp, i64]),
+            ("pa_bm_num_free", i32, [vp]),
+            ("pa_bm_seq_len", i64, [vp, i64]),
+            ("pa_bm_table", i32, [vp, i64, pi32, i32]),
+            ("pa_bm_ref_count", i32, [vp, ctypes.c_int32]),
+            ("pa_bm_batch", i32, [vp, pi64, i32, pi32, i32, pi32])):
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
     _lib = L
     return L
 
@@ -185,6 +204,102 @@ def pa_copy_blocks(k_cache, v_cache, src_dst_pairs, *, stream=None):
                                 _DTYPE[k_cache.dtype], _stream(stream)))
 
 
+class BlockManager:
+    """Host block manager of the library (the ``pa_bm_*`` entry points): a pool of
+    ``num_blocks`` blocks of ``block_size`` tokens, one block table per sequence,
+    reference counts and copy-on-write.  Sequences are named by Python ints.
+
+    Pure host bookkeeping: it yields the index inputs of the kernels -- block
+    tables and lengths (``batch`` -> ``pa_decode``), write slots (``append_slot``
+    -> ``pa_write_kv``) and copy-on-write pairs (-> ``pa_copy_blocks``).  Failed
+    calls raise ``PagedKVError`` (status 5 when the pool is out of blocks) and
+    leave the manager unchanged.
+    """
+
+    def __init__(self, num_blocks, block_size, free_order=None):
+        self._h = None
+        self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+        order = None
+        if free_order is not None:
+            order = (ctypes.c_int32 * len(free_order))(*[int(b) for b in free_order])
+            if len(free_order) != self.num_blocks:
+                raise ValueError("free_order must list every block once")
+        h = ctypes.c_void_p()
+        _check(lib().pa_bm_create(self.num_blocks, self.block_size, order, ctypes.byref(h)))
+        self._h = h
+
+    def __del__(self):
+        if getattr(self, "_h", None) is not None and _lib is not None:
+            _lib.pa_bm_destroy(self._h)
+            self._h = None
+
+    def allocate(self, seq, num_tokens):
+        """Prefill: ``seq`` gets ceil(num_tokens / block_size) fresh blocks; returns its table."""
+        _check(lib().pa_bm_allocate(self._h, int(seq), int(num_tokens)))
+        return self.table(seq)
+
+    def append_slot(self, seq):
+        """Slot of ``seq``'s next token and the (src, dst) copy-on-write pair, or None."""
+        slot, src, dst = ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int32()
+        _check(lib().pa_bm_append_slot(self._h, int(seq), ctypes.byref(slot), ctypes.byref(src),
+                                       ctypes.byref(dst)))
+        return slot.value, ((src.value, dst.value) if src.value >= 0 else None)
+
+    def append_step(self, seqs):
+        """One decode step for the distinct ``seqs``: (slot_mapping int32 [n], copy-on-write
+        pairs int32 [p, 2]) as CPU tensors, the inputs of ``pa_write_kv`` and
+        ``pa_copy_blocks`` (copy first).  All or nothing when blocks run out."""
+        n = len(seqs)
+        ids = (ctypes.c_int64 * max(n, 1))(*[int(s) for s in seqs])
+        slots = torch.empty(n, dtype=torch.int32)
+        pairs = torch.empty((max(n, 1), 2), dtype=torch.int32)
+        np_ = ctypes.c_int()
+        as_p = lambda t: ctypes.cast(t.data_ptr(), ctypes.POINTER(ctypes.c_int32))
+        _check(lib().pa_bm_append_step(self._h, ids, n, as_p(slots), as_p(pairs), ctypes.byref(np_)))
+        return slots, pairs[:np_.value].clone()
+
+    def fork(self, parent, child):
+        _check(lib().pa_bm_fork(self._h, int(parent), int(child)))
+
+    def free_seq(self, seq):
+        _check(lib().pa_bm_free(self._h, int(seq)))
+
+    def num_free(self):
+        return lib().pa_bm_num_free(self._h)
+
+    def seq_len(self, seq):
+        n = lib().pa_bm_seq_len(self._h, int(seq))
+        if n < 0:
+            raise KeyError(seq)
+        return n
+
+    def table(self, seq):
+        n = lib().pa_bm_table(self._h, int(seq), None, 0)
+        if n < 0:
+            raise KeyError(seq)
+        buf = (ctypes.c_int32 * max(n, 1))()
+        lib().pa_bm_table(self._h, int(seq), buf, n)
+        return list(buf[:n])
+
+    def ref_count(self, block):
+        r = lib().pa_bm_ref_count(self._h, int(block))
+        if r < 0:
+            raise IndexError(block)
+        return r
+
+    def batch(self, seqs, max_blocks_per_seq):
+        """(block_tables [n, max_blocks_per_seq], seq_lens [n]) as int32 CPU tensors, tables
+        padded with -1; move them to the device for ``pa_decode``."""
+        n = len(seqs)
+        ids = (ctypes.c_int64 * max(n, 1))(*[int(s) for s in seqs])
+        tables = torch.empty((n, int(max_blocks_per_seq)), dtype=torch.int32)
+        lens = torch.empty(n, dtype=torch.int32)
+        _check(lib().pa_bm_batch(
+            self._h, ids, n, ctypes.cast(tables.data_ptr(), ctypes.POINTER(ctypes.c_int32)),
+            int(max_blocks_per_seq), ctypes.cast(lens.data_ptr(), ctypes.POINTER(ctypes.c_int32))))
+        return tables, lens
+
+
 __all__ = ["pa_decode", "pa_write_kv", "pa_copy_blocks", "pa_decode_workspace_size",
            "decode_workspace", "pa_last_error", "pa_version",
-           "PagedKVError", "lib", "LIB_PATH"]
+           "PagedKVError", "BlockManager", "lib", "LIB_PATH"]

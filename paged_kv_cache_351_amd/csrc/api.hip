@@ -32,6 +32,12 @@ pa_status fail(pa_status st, const char* fmt, ...) {
   return st;
 }
 
+}  // namespace
+
+void pagedkv::set_last_error(const char* msg) { g_err = msg; }
+
+namespace {
+
 pa_status hip_fail(hipError_t e, const char* what) {
   return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
@@ -163,7 +169,7 @@ bool to_host(std::vector<T>& dst, const void* src, size_t n, hipStream_t stream,
 
 extern "C" {
 
-int pa_version(void) { return 2; }
+int pa_version(void) { return 3; }
 
 const char* pa_last_error(void) { return g_err.c_str(); }
 

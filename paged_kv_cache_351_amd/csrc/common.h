@@ -54,6 +54,9 @@ hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs
                               int num_pairs, long long block_bytes, int num_blocks,
                               hipStream_t stream);
 
+// Message returned by pa_last_error() on the calling thread.
+void set_last_error(const char* msg);
+
 // Smallest group size of the compiled decode variants that can hold `group`
 // query heads (1, 2, 4, 8, 16), or 0 if none can.
 inline int padded_group(int group) {
