@@ -16,6 +16,12 @@ tables, write slots, copy-on-write pairs).  It follows the pages:
   a block whose count reaches zero returns to the pool ([PA-notes] §6.1, §6.2,
   §12 题4).
 
+* Preemption: a suspended request's blocks move to CPU RAM and come back
+  later through its block table ([PA-notes] §5 ③).  ``swap_out(seqs)`` moves
+  every block the listed sequences reference into a second pool of
+  ``num_cpu_blocks`` host blocks and ``swap_in(seqs)`` brings them back into
+  fresh GPU blocks; both return the (src, dst) block pairs to copy.
+
 Readings: the free list is a queue whose initial order the caller gives (the
 workloads pass a seeded permutation, so placement is random); [PA-explainer]'s
 LRU eviction on an empty pool is not modelled -- allocation from an empty pool
@@ -23,9 +29,20 @@ raises and leaves every table and count unchanged.  Copy-on-write fires iff the
 target block's count is above one at write time, so with k sharers the first
 k-1 writers copy and the last writes in place.
 
-Pins (tests/test_oracle_blockmgr.py): the 40-token and 1000-token examples
-([PA-notes] §9.2, §12 题1), the four-sharer copy-on-write trace ([PA-notes]
-§12 题4), waste < B for every sequence, and no leaked blocks after all frees.
+Swap readings: the sequences named in one call move together, and a block
+they share is moved once, its count carried over (so a sample group swaps as
+a group).  A block also held by a sequence outside the call keeps its GPU copy
+for that sequence and only loses the leaving sharers.  A swapped-out sequence
+can only be swapped in or freed.  Either call raises, changing nothing, when the
+target pool has too few free blocks.  The host pool's free list is a queue in
+id order.  Blocks freed by a swap-out may be handed out again at once, so the
+caller copies the returned pairs before any later write (one stream in order).
+
+Pins (tests/test_oracle_blockmgr.py, tests/test_oracle_swap.py): the 40-token
+and 1000-token examples ([PA-notes] §9.2, §12 题1), the four-sharer copy-on-write trace ([PA-notes]
+§12 题4), waste < B for every sequence, and no leaked blocks after all frees;
+with swaps, every sequence reads back its own token history through its table
+from the pool it lives in, after every step of random traces.
 """
 
 from collections import deque
@@ -36,8 +53,12 @@ class OutOfBlocks(RuntimeError):
 
 
 class BlockManager:
-    def __init__(self, num_blocks, block_size, free_order=None):
+    def __init__(self, num_blocks, block_size, free_order=None, num_cpu_blocks=0):
         self.num_blocks = int(num_blocks)
+        self.num_cpu_blocks = int(num_cpu_blocks)
+        self.cpu_free = deque(range(self.num_cpu_blocks))
+        self.cpu_ref = [0] * self.num_cpu_blocks
+        self.swapped = set()
         self.block_size = int(block_size)
         order = range(self.num_blocks) if free_order is None else [int(b) for b in free_order]
         if sorted(order) != list(range(self.num_blocks)):
@@ -68,12 +89,17 @@ class BlockManager:
         self.lens[seq] = int(num_tokens)
         return list(self.tables[seq])
 
+    def _resident(self, seq):
+        if seq in self.swapped:
+            raise ValueError(f"sequence {seq!r} is swapped out")
+
     def append_slot(self, seq):
         """Reserve the slot of ``seq``'s next token.
 
         Returns ``(slot, cow)`` with ``cow = (src, dst)`` when the write needed a
         private copy of a shared block, else ``None``.
         """
+        self._resident(seq)
         B = self.block_size
         table = self.tables[seq]
         pos = self.lens[seq]
@@ -96,18 +122,66 @@ class BlockManager:
         """``child`` shares every block of ``parent`` (parallel sampling / beam fork)."""
         if child in self.tables:
             raise ValueError(f"sequence {child!r} already exists")
+        self._resident(parent)
         self.tables[child] = list(self.tables[parent])
         self.lens[child] = self.lens[parent]
         for b in self.tables[child]:
             self.ref[b] += 1
 
     def free_seq(self, seq):
-        """Drop ``seq``: every block loses one sharer; blocks at zero return to the pool."""
+        """Drop ``seq``: every block loses one sharer; blocks at zero return to the pool
+        (the host pool for a swapped-out sequence)."""
+        ref, free = (self.cpu_ref, self.cpu_free) if seq in self.swapped else (self.ref, self.free)
         for b in self.tables.pop(seq):
-            self.ref[b] -= 1
-            if self.ref[b] == 0:
-                self.free.append(b)
+            ref[b] -= 1
+            if ref[b] == 0:
+                free.append(b)
         del self.lens[seq]
+        self.swapped.discard(seq)
+
+    def _move(self, seqs, to_cpu):
+        """Move the listed sequences' blocks to the other pool; returns the (src, dst) pairs."""
+        seqs = list(seqs)
+        if len(set(seqs)) != len(seqs):
+            raise ValueError("a sequence is listed twice")
+        for s in seqs:
+            if s not in self.tables:
+                raise KeyError(s)
+            if (s in self.swapped) == to_cpu:
+                raise ValueError(f"sequence {s!r} is already {'out' if to_cpu else 'in'}")
+        src_ref, src_free = (self.ref, self.free) if to_cpu else (self.cpu_ref, self.cpu_free)
+        dst_ref, dst_free = (self.cpu_ref, self.cpu_free) if to_cpu else (self.ref, self.free)
+        moving = {}                                # src block -> sharers leaving with it
+        for s in seqs:
+            for b in self.tables[s]:
+                moving[b] = moving.get(b, 0) + 1
+        if len(dst_free) < len(moving):
+            raise OutOfBlocks(f"need {len(moving)} blocks in the target pool, {len(dst_free)} free")
+        new_id, pairs = {}, []
+        for b, n in moving.items():                # first-reference order
+            d = dst_free.popleft()
+            dst_ref[d] = n
+            new_id[b] = d
+            pairs.append((b, d))
+        for b, n in moving.items():
+            src_ref[b] -= n
+            if src_ref[b] == 0:
+                src_free.append(b)
+        for s in seqs:
+            self.tables[s] = [new_id[b] for b in self.tables[s]]
+            if to_cpu:
+                self.swapped.add(s)
+            else:
+                self.swapped.discard(s)
+        return pairs
+
+    def swap_out(self, seqs):
+        """Preempt ``seqs``: (gpu_block, cpu_block) pairs to copy GPU -> host."""
+        return self._move(seqs, True)
+
+    def swap_in(self, seqs):
+        """Restore ``seqs``: (cpu_block, gpu_block) pairs to copy host -> GPU."""
+        return self._move(seqs, False)
 
     # -- queries -----------------------------------------------------------
     def slot(self, seq, pos):

@@ -18,10 +18,22 @@ copy_blocks
     simultaneous (every read happens before any write); a pair with src == dst,
     a repeated dst, or a dst that is also some pair's src is invalid.
 
-Both operations move bits and compute nothing, so the GPU must match them bit
+swap_blocks
+    Preemption: when memory runs short a request is suspended, its blocks are
+    released or moved to CPU RAM, and it is later restored through its block
+    table ([PA-notes] §5 ③, likened there to OS paging).  The move is a block
+    copy between two different pools (HBM and pinned host memory, either way):
+    block ``dst`` of the destination pool := block ``src`` of the source pool,
+    whole blocks, K and V.  A repeated dst is invalid; since the pools are
+    distinct, a src may equal a dst id.
+
+All three operations move bits and compute nothing, so the GPU must match them bit
 for bit.  Pins (tests/test_oracle_cache_ops.py): the worked mapping of
 [PA-notes] §9.2 (table [5, 2, 9]: token 40 goes to slot 152), targets equal
-sources bit for bit, every other pool byte unchanged, invalid inputs rejected.
+sources bit for bit, every other pool byte unchanged, invalid inputs rejected;
+swap_blocks also through the block manager's swap traces
+(tests/test_oracle_swap.py), where every sequence must read back its own tokens
+after any mix of appends, forks, copies, swap-outs and swap-ins.
 """
 
 import numpy as np
@@ -83,4 +95,25 @@ def copy_blocks(k_cache, v_cache, pairs):
         vs = v_cache[p[:, 0]].copy()
         kc[p[:, 1]] = ks                            # ... then all writes
         vc[p[:, 1]] = vs
+    return kc, vc
+
+
+def swap_blocks(src_k, src_v, dst_k, dst_v, pairs):
+    """Return copies of (dst_k, dst_v) with block dst := source block src for every
+    (src, dst) pair; the source pools are not changed."""
+    p = np.asarray(pairs, dtype=np.int64).reshape(-1, 2)
+    if src_k.shape[1:] != dst_k.shape[1:] or src_k.dtype != dst_k.dtype:
+        raise ValueError("pools differ in block shape or storage type")
+    kc = dst_k.copy()
+    vc = dst_v.copy()
+    if p.size == 0:
+        return kc, vc
+    if p[:, 0].min() < 0 or p[:, 0].max() >= src_k.shape[0]:
+        raise ValueError("src block out of range")
+    if p[:, 1].min() < 0 or p[:, 1].max() >= dst_k.shape[0]:
+        raise ValueError("dst block out of range")
+    if np.unique(p[:, 1]).size != len(p):
+        raise ValueError("repeated dst")
+    kc[p[:, 1]] = src_k[p[:, 0]]
+    vc[p[:, 1]] = src_v[p[:, 0]]
     return kc, vc

@@ -13,8 +13,10 @@ import pytest
 import oracle
 import oracle.attention as att
 import oracle.cache_ops as cops
+import oracle.blockmgr as bmod
 import test_oracle_attention as TA
 import test_oracle_cache_ops as TC
+import test_oracle_swap as TS
 
 
 def attend_factory(kind):
@@ -81,6 +83,46 @@ def write_factory(kind):
     return write_kv
 
 
+def swap_factory(kind):
+    orig = cops.swap_blocks
+
+    def swap_blocks(src_k, src_v, dst_k, dst_v, pairs):
+        p = [tuple(x) for x in pairs]
+        if kind == "v_from_k":
+            return orig(src_k, src_v, dst_k, dst_v, p)[0], orig(src_k, src_k, dst_k, dst_v, p)[1]
+        if kind == "first_pair_only":
+            p = p[:1]
+        if kind == "reversed_pair":
+            p = [(d, s) for s, d in p if d < src_k.shape[0] and s < dst_k.shape[0]]
+        return orig(src_k, src_v, dst_k, dst_v, p)
+    return swap_blocks
+
+
+def move_factory(kind):
+    orig = bmod.BlockManager._move
+
+    def _move(self, seqs, to_cpu):
+        src_ref = self.ref if to_cpu else self.cpu_ref
+        before = list(src_ref)
+        pairs = orig(self, seqs, to_cpu)
+        dst_ref = self.cpu_ref if to_cpu else self.ref
+        if kind == "count_one":                    # a shared block arrives with count 1
+            for _, d in pairs:
+                dst_ref[d] = 1
+        elif kind == "no_release":                 # leaving sharers keep their source count
+            src_free = self.free if to_cpu else self.cpu_free
+            for b, _ in pairs:
+                if before[b] and not src_ref[b]:
+                    src_free.remove(b)
+                src_ref[b] = before[b]
+        elif kind == "table_not_repointed" and pairs:
+            back = {d: b for b, d in pairs}
+            for s in seqs:
+                self.tables[s] = [back[d] for d in self.tables[s]]
+        return pairs
+    return _move
+
+
 ATTN_PINS = [
     lambda: TA.test_single_token_returns_v_exactly("f32"),
     lambda: TA.test_single_token_returns_v_exactly("bf16"),
@@ -95,6 +137,11 @@ CACHE_PINS = [
     TC.test_worked_mapping_slots_and_next_write,
     TC.test_write_is_a_bit_copy_and_skips_negative_slots,
 ]
+
+
+SWAP_PINS = [TS.test_swap_blocks_small_example] + \
+    [(lambda seed=seed: TS.test_swap_traces_read_back_every_sequence(seed)) for seed in range(3)] + \
+    [TS.test_group_swap_moves_a_shared_block_once_and_keeps_outside_sharers]
 
 
 def caught(pins):
@@ -126,5 +173,17 @@ def test_write_mutants_are_caught(monkeypatch, kind):
     assert caught(CACHE_PINS), kind
 
 
+@pytest.mark.parametrize("kind", ["v_from_k", "first_pair_only", "reversed_pair"])
+def test_swap_mutants_are_caught(monkeypatch, kind):
+    monkeypatch.setattr(oracle, "swap_blocks", swap_factory(kind))
+    assert caught(SWAP_PINS), kind
+
+
+@pytest.mark.parametrize("kind", ["count_one", "no_release", "table_not_repointed"])
+def test_swap_bookkeeping_mutants_are_caught(monkeypatch, kind):
+    monkeypatch.setattr(bmod.BlockManager, "_move", move_factory(kind))
+    assert caught(SWAP_PINS), kind
+
+
 def test_unmutated_oracle_passes_every_pin():
-    assert not caught(ATTN_PINS) and not caught(CACHE_PINS)
+    assert not caught(ATTN_PINS) and not caught(CACHE_PINS) and not caught(SWAP_PINS)
