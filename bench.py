@@ -14,6 +14,7 @@ Prints ONE JSON line.  ``value`` is the K/V bytes the decode step must read
 runs on; ``cpu_baseline`` times the float64 CPU oracle on the host.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME [--block-size B]]
+    python bench.py --swap               # pa_swap_blocks HBM <-> pinned host throughput
     python bench.py --copy-calibration   # a block copy of known size, for counter scaling
     python bench.py --record-traffic DEC_FETCH.csv DEC_WRITE.csv COPY_FETCH.csv COPY_WRITE.csv
 """
@@ -131,6 +132,76 @@ def copy_calibration(steps):
                       "write_bytes_per_launch": per}))
 
 
+PCIE_PEAK_GBS = 64.0             # PCIe 5.0 x16 host link, per direction, vendor figure
+
+
+def swap_bench(steps, warmup, with_cpu):
+    """pa_swap_blocks of 4096 Llama-3-8B blocks (16 tokens x 8 KV heads x 128, bf16; K and V,
+    64 KiB a block, 256 MiB a call) from the HBM pool to a pinned host pool and back, random
+    block ids on both sides.  A plain contiguous copy of the same byte count (the runtime's
+    DMA engines) is timed beside it as the host link's practical ceiling."""
+    dev = torch.device("cuda:0")
+    B, H, D, NG, NC, N = 16, 8, 128, 16384, 8192, 4096
+    g = torch.Generator(device=dev).manual_seed(0)
+    gk = torch.randn((NG, B, H, D), device=dev, generator=g).to(torch.bfloat16)
+    gv = torch.randn((NG, B, H, D), device=dev, generator=g).to(torch.bfloat16)
+    hk = torch.zeros((NC, B, H, D), dtype=torch.bfloat16).pin_memory()
+    hv = torch.zeros((NC, B, H, D), dtype=torch.bfloat16).pin_memory()
+    rng = np.random.default_rng(0)
+    out_pairs = np.stack([rng.choice(NG, N, replace=False), rng.choice(NC, N, replace=False)], 1)
+    po = torch.from_numpy(out_pairs.astype(np.int32)).to(dev)
+    pi = torch.from_numpy(out_pairs[:, ::-1].astype(np.int32).copy()).to(dev)
+    nbytes = N * B * H * D * 2 * 2
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for a, z in ev:
+            a.record(stream)
+            fn()
+            z.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(z) for a, z in ev])) * 1e-3
+
+    log(f"swap out / in: {N} blocks, {nbytes / 2**20:.0f} MiB per call, {steps} calls each")
+    t_out = timed(lambda: pk.pa_swap_blocks(gk, gv, hk, hv, po))
+    t_in = timed(lambda: pk.pa_swap_blocks(hk, hv, gk, gv, pi))
+    flat_g, flat_h = gk[:2 * N].reshape(-1), hk[:2 * N].reshape(-1)
+    t_d2h = timed(lambda: flat_h.copy_(flat_g, non_blocking=True))
+    t_h2d = timed(lambda: flat_g.copy_(flat_h, non_blocking=True))
+    res = {"metric": "pa_swap_blocks host-link GB/s (swap-out and swap-in of 4096 scattered blocks)",
+           "value": 2 * nbytes / (t_out + t_in) / 1e9, "unit": "GB/s", "n_gpus": 1,
+           "steps": steps, "warmup": warmup, "higher_is_better": True, "dtype": "bf16",
+           "data": "synthetic",
+           "config": {"workload": "Llama-3-8B blocks, HBM <-> pinned host", "blocks_per_call": N,
+                      "block_bytes_kv": B * H * D * 2 * 2, "gpu_pool_blocks": NG, "host_pool_blocks": NC},
+           "swap_out_gbs": nbytes / t_out / 1e9, "swap_in_gbs": nbytes / t_in / 1e9,
+           "swap_out_us": t_out * 1e6, "swap_in_us": t_in * 1e6,
+           "contiguous_copy_gbs": {"d2h": nbytes / t_d2h / 1e9, "h2d": nbytes / t_h2d / 1e9},
+           "roofline": {"kernel": "copy_blocks_kernel (two pools)", "bound": "host link",
+                        "achieved": 2 * nbytes / (t_out + t_in) / 1e9, "peak": PCIE_PEAK_GBS,
+                        "unit": "GB/s", "frac": 2 * nbytes / (t_out + t_in) / 1e9 / PCIE_PEAK_GBS,
+                        "traffic": None},
+           "cpu_baseline": None}
+    if with_cpu:
+        import oracle
+        n = 512                                   # a bounded sample of the same copy
+        hk_np = hk.view(torch.int16).numpy().view(np.uint16)
+        src = gk[:n].cpu().view(torch.int16).numpy().view(np.uint16)
+        pairs = np.stack([np.arange(n), out_pairs[:n, 1]], 1)
+        t0 = time.perf_counter()
+        oracle.swap_blocks(src, src, hk_np, hk_np, pairs)
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": n * B * H * D * 2 * 2 / dt / 1e9, "unit": "GB/s", "cores": 1,
+                               "kind": "oracle", "sample": f"{n} blocks of oracle.swap_blocks "
+                               "between host arrays (includes its copy of the 8192-block target pool)"}
+    print(json.dumps(res))
+
+
 def cpu_baseline(b, gpu_out, time_cap=25.0):
     """The float64 oracle on the host: the step's block copies and write, then decode over the
     workload's sequences in order until all are done or the time cap is reached.  Also reports
@@ -213,6 +284,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--swap", action="store_true",
+                    help="measure pa_swap_blocks (HBM <-> pinned host) instead of the decode step")
     ap.add_argument("--workload", default="llama3_8b", choices=sorted(WORKLOADS),
                     help="the benchmark line is llama3_8b; the others are the remaining workloads "
                          "of the same study, measured the same way")
@@ -232,6 +305,9 @@ def main():
     pk.lib()
     if args.copy_calibration:
         copy_calibration(max(1, args.steps))
+        return
+    if args.swap:
+        swap_bench(max(1, min(args.steps, 20)), max(1, min(args.warmup, 3)), not args.no_cpu_baseline)
         return
 
     dev = torch.device("cuda:0")

@@ -171,8 +171,33 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst_pa
                          int head_dim, int num_blocks, pa_dtype dtype, void* stream);
 
 /*
+ * Swap blocks between two pools -- preemption ([PA-notes] §5 ③: when memory
+ * runs short a request is suspended, its blocks freed or moved to CPU RAM, and
+ * it is restored later through its block table).  For every (src, dst) row of
+ * src_dst_pairs[num_pairs][2], block dst of the destination pool becomes a bit
+ * copy of block src of the source pool, K and V, every slot and KV head.
+ * Swap-out: source = the HBM pool, destination = a host pool; swap-in: the
+ * reverse.  Both pools have the layout above with the same block_size,
+ * num_kv_heads, head_dim and dtype, and src_num_blocks / dst_num_blocks blocks.
+ *
+ * Memory.  Unlike the other entry points, the pools and the pair array may be
+ * device memory or pinned host memory allocated with hipHostMalloc (torch:
+ * pin_memory=True); the kernel reads and writes host memory directly over the
+ * host link, in one launch for all pairs.  Any other pointer (pageable host
+ * memory) is refused with PA_ERR_INVALID before launching.  The two pools must
+ * not overlap (identical base pointers are refused; use pa_copy_blocks within
+ * one pool).  Repeated dst ids are invalid; pairs outside either pool are
+ * skipped (PA_DEBUG_CHECK=1 rejects both).  The host must not touch a host
+ * pool while a swap that uses it is in flight: synchronise the stream first.
+ */
+pa_status pa_swap_blocks(const void* src_k, const void* src_v, int src_num_blocks, void* dst_k,
+                         void* dst_v, int dst_num_blocks, const int32_t* src_dst_pairs,
+                         int num_pairs, int block_size, int num_kv_heads, int head_dim,
+                         pa_dtype dtype, void* stream);
+
+/*
  * Block manager -- host bookkeeping of the block pool ([PA-notes] §3 block
- * table; §5 ①② pool and on-demand allocation; §6.1, §6.2 and §12 题4 sharing,
+ * table; §5 ①② pool and on-demand allocation; §5 ③ swapping; §6.1, §6.2 and §12 题4 sharing,
  * reference counts and copy-on-write).
  *
  * It owns no device memory: it decides which physical block every token of
@@ -196,10 +221,12 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst_pa
  */
 typedef struct pa_block_manager pa_block_manager;
 
-/* New manager of num_blocks blocks of block_size tokens.  free_order: NULL or
- * a host array holding a permutation of 0..num_blocks-1. */
+/* New manager of num_blocks GPU blocks of block_size tokens, plus a host pool
+ * of num_cpu_blocks blocks for swapped-out sequences (0 = no swapping).
+ * free_order: NULL or a host array holding a permutation of 0..num_blocks-1
+ * (the host pool is handed out in id order). */
 pa_status pa_bm_create(int num_blocks, int block_size, const int32_t* free_order,
-                       pa_block_manager** out);
+                       int num_cpu_blocks, pa_block_manager** out);
 void pa_bm_destroy(pa_block_manager* bm);
 
 /* Prefill: give a new sequence ceil(num_tokens / block_size) blocks holding
@@ -229,7 +256,27 @@ pa_status pa_bm_fork(pa_block_manager* bm, int64_t parent, int64_t child);
 /* Drop a sequence (finished, or pruned from a beam). */
 pa_status pa_bm_free(pa_block_manager* bm, int64_t seq);
 
+/* Preemption ([PA-notes] §5 ③).  pa_bm_swap_out moves the listed sequences
+ * (distinct, resident) to the host pool; pa_bm_swap_in brings the listed
+ * (swapped-out) ones back into fresh GPU blocks.  The sequences of one call
+ * move together: each distinct block they reference moves once, in order of
+ * first reference, to the next free block of the target pool, and keeps its
+ * count of listed sharers; a block also held by an unlisted sequence stays
+ * where it is for that sequence.  The (src, dst) block pairs to copy with
+ * pa_swap_blocks go to pairs[2 * *num_pairs] (pairs_cap rows available; the
+ * sum of the listed tables' lengths always suffices).  Blocks released by the
+ * move can be handed out again at once, so enqueue the copy before any later
+ * write.  A swapped-out sequence can only be swapped in or freed.
+ * PA_ERR_NO_BLOCKS if the target pool is short; nothing changes on error. */
+pa_status pa_bm_swap_out(pa_block_manager* bm, const int64_t* seqs, int num_seqs, int32_t* pairs,
+                         int pairs_cap, int* num_pairs);
+pa_status pa_bm_swap_in(pa_block_manager* bm, const int64_t* seqs, int num_seqs, int32_t* pairs,
+                        int pairs_cap, int* num_pairs);
+
 int pa_bm_num_free(const pa_block_manager* bm);               /* -1 if bm is NULL */
+int pa_bm_num_free_cpu(const pa_block_manager* bm);           /* host pool; -1 if bm is NULL */
+int pa_bm_is_swapped(const pa_block_manager* bm, int64_t seq); /* 1, 0, or -1 if unknown */
+int pa_bm_cpu_ref_count(const pa_block_manager* bm, int32_t block); /* -1 out of range */
 int64_t pa_bm_seq_len(const pa_block_manager* bm, int64_t seq); /* -1 if unknown */
 /* Copies up to cap entries of the sequence's table to out; returns its length
  * in blocks (-1 if unknown). */

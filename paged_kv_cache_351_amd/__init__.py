@@ -55,10 +55,17 @@ def lib():
     L.pa_write_kv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
     L.pa_copy_blocks.restype = i32
     L.pa_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+    L.pa_swap_blocks.restype = i32
+    L.pa_swap_blocks.argtypes = [vp, vp, i32, vp, vp, i32, vp, i32, i32, i32, i32, i32, vp]
     i64 = ctypes.c_int64
     pi32, pi64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
     for name, res, args in (
-            ("pa_bm_create", i32, [i32, i32, pi32, ctypes.POINTER(vp)]),
+            ("pa_bm_create", i32, [i32, i32, pi32, i32, ctypes.POINTER(vp)]),
+            ("pa_bm_swap_out", i32, [vp, pi64, i32, pi32, i32, ctypes.POINTER(i32)]),
+            ("pa_bm_swap_in", i32, [vp, pi64, i32, pi32, i32, ctypes.POINTER(i32)]),
+            ("pa_bm_num_free_cpu", i32, [vp]),
+            ("pa_bm_is_swapped", i32, [vp, i64]),
+            ("pa_bm_cpu_ref_count", i32, [vp, ctypes.c_int32]),
             ("pa_bm_destroy", None, [vp]),
             ("pa_bm_allocate", i32, [vp, i64, i64]),
             ("pa_bm_append_slot", i32, [vp, i64, pi64, pi32, pi32]),
@@ -204,6 +211,44 @@ def pa_copy_blocks(k_cache, v_cache, src_dst_pairs, *, stream=None):
                                 _DTYPE[k_cache.dtype], _stream(stream)))
 
 
+def _acc(name, t, dtype=None, ndim=None):
+    """Like _dev, but pinned host tensors are accepted too (pa_swap_blocks reads and
+    writes them directly)."""
+    if isinstance(t, torch.Tensor) and t.device.type == "cpu":
+        if not t.is_pinned():
+            raise ValueError(f"{name} must be on the GPU or in pinned host memory "
+                             "(pin_memory=True)")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if dtype is not None and t.dtype != dtype:
+            raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+        if ndim is not None and t.dim() != ndim:
+            raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+        return
+    _dev(name, t, dtype, ndim)
+
+
+def pa_swap_blocks(src_k, src_v, dst_k, dst_v, src_dst_pairs, *, stream=None):
+    """dst_k[dst] = src_k[src] and dst_v[dst] = src_v[src] for every (src, dst) pair, between
+    two pools of the same block shape: a GPU pool and a pinned host pool (either way), or two
+    GPU pools.  The pairs may be a GPU tensor or a pinned host tensor.  Enqueued on the
+    stream; synchronise before the host reads a host pool that was written."""
+    _acc("src_k", src_k, ndim=4)
+    if src_k.dtype not in _DTYPE:
+        raise TypeError(f"unsupported dtype {src_k.dtype}")
+    _acc("src_v", src_v, src_k.dtype, 4)
+    _acc("dst_k", dst_k, src_k.dtype, 4)
+    _acc("dst_v", dst_v, src_k.dtype, 4)
+    _acc("src_dst_pairs", src_dst_pairs, torch.int32, 2)
+    if src_v.shape != src_k.shape or dst_v.shape != dst_k.shape or \
+            src_k.shape[1:] != dst_k.shape[1:] or src_dst_pairs.shape[1] != 2:
+        raise ValueError("pool shapes disagree or pairs are not [n, 2]")
+    _, block_size, nkv, hd = src_k.shape
+    _check(lib().pa_swap_blocks(_ptr(src_k), _ptr(src_v), src_k.shape[0], _ptr(dst_k), _ptr(dst_v),
+                                dst_k.shape[0], _ptr(src_dst_pairs), src_dst_pairs.shape[0],
+                                block_size, nkv, hd, _DTYPE[src_k.dtype], _stream(stream)))
+
+
 class BlockManager:
     """Host block manager of the library (the ``pa_bm_*`` entry points): a pool of
     ``num_blocks`` blocks of ``block_size`` tokens, one block table per sequence,
@@ -216,16 +261,18 @@ class BlockManager:
     leave the manager unchanged.
     """
 
-    def __init__(self, num_blocks, block_size, free_order=None):
+    def __init__(self, num_blocks, block_size, free_order=None, num_cpu_blocks=0):
         self._h = None
         self.num_blocks, self.block_size = int(num_blocks), int(block_size)
+        self.num_cpu_blocks = int(num_cpu_blocks)
         order = None
         if free_order is not None:
             order = (ctypes.c_int32 * len(free_order))(*[int(b) for b in free_order])
             if len(free_order) != self.num_blocks:
                 raise ValueError("free_order must list every block once")
         h = ctypes.c_void_p()
-        _check(lib().pa_bm_create(self.num_blocks, self.block_size, order, ctypes.byref(h)))
+        _check(lib().pa_bm_create(self.num_blocks, self.block_size, order, self.num_cpu_blocks,
+                                  ctypes.byref(h)))
         self._h = h
 
     def __del__(self):
@@ -257,6 +304,41 @@ class BlockManager:
         as_p = lambda t: ctypes.cast(t.data_ptr(), ctypes.POINTER(ctypes.c_int32))
         _check(lib().pa_bm_append_step(self._h, ids, n, as_p(slots), as_p(pairs), ctypes.byref(np_)))
         return slots, pairs[:np_.value].clone()
+
+    def _move(self, fn, seqs):
+        n = len(seqs)
+        ids = (ctypes.c_int64 * max(n, 1))(*[int(s) for s in seqs])
+        cap = sum(len(self.table(s)) for s in seqs)
+        pairs = torch.empty((max(cap, 1), 2), dtype=torch.int32)
+        np_ = ctypes.c_int()
+        _check(fn(self._h, ids, n, ctypes.cast(pairs.data_ptr(), ctypes.POINTER(ctypes.c_int32)),
+                  cap, ctypes.byref(np_)))
+        return pairs[:np_.value].clone()
+
+    def swap_out(self, seqs):
+        """Preempt ``seqs`` together: (gpu_block, cpu_block) pairs, int32 CPU tensor [p, 2], to
+        copy with ``pa_swap_blocks`` from the GPU pool to the host pool."""
+        return self._move(lib().pa_bm_swap_out, seqs)
+
+    def swap_in(self, seqs):
+        """Restore ``seqs`` together: (cpu_block, gpu_block) pairs, int32 CPU tensor [p, 2], to
+        copy with ``pa_swap_blocks`` from the host pool to the GPU pool."""
+        return self._move(lib().pa_bm_swap_in, seqs)
+
+    def num_free_cpu(self):
+        return lib().pa_bm_num_free_cpu(self._h)
+
+    def is_swapped(self, seq):
+        r = lib().pa_bm_is_swapped(self._h, int(seq))
+        if r < 0:
+            raise KeyError(seq)
+        return bool(r)
+
+    def cpu_ref_count(self, block):
+        r = lib().pa_bm_cpu_ref_count(self._h, int(block))
+        if r < 0:
+            raise IndexError(block)
+        return r
 
     def fork(self, parent, child):
         _check(lib().pa_bm_fork(self._h, int(parent), int(child)))
@@ -300,6 +382,6 @@ class BlockManager:
         return tables, lens
 
 
-__all__ = ["pa_decode", "pa_write_kv", "pa_copy_blocks", "pa_decode_workspace_size",
+__all__ = ["pa_decode", "pa_write_kv", "pa_copy_blocks", "pa_swap_blocks", "pa_decode_workspace_size",
            "decode_workspace", "pa_last_error", "pa_version",
            "PagedKVError", "BlockManager", "lib", "LIB_PATH"]

@@ -86,6 +86,28 @@ bool valid_block_size(int bs) { return bs == 8 || bs == 16 || bs == 32; }
 
 bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
+// Device address of ptr if the GPU may access it: device memory (returned as
+// is) or pinned host memory mapped for the device.  Pageable host memory and
+// unknown pointers give false; the query's error is cleared so that it does
+// not surface in a later call.
+bool device_address(const void* ptr, void** dev) {
+  hipPointerAttribute_t a;
+  const hipError_t e = hipPointerGetAttributes(&a, ptr);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  if (a.type == hipMemoryTypeDevice || a.type == hipMemoryTypeManaged) {
+    *dev = const_cast<void*>(ptr);
+    return true;
+  }
+  if (a.type == hipMemoryTypeHost && a.devicePointer != nullptr) {
+    *dev = a.devicePointer;
+    return true;
+  }
+  return false;
+}
+
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 constexpr int kMaxSeqLen = 1 << 24;
@@ -169,7 +191,7 @@ bool to_host(std::vector<T>& dst, const void* src, size_t n, hipStream_t stream,
 
 extern "C" {
 
-int pa_version(void) { return 3; }
+int pa_version(void) { return 4; }
 
 const char* pa_last_error(void) { return g_err.c_str(); }
 
@@ -371,9 +393,64 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst_pa
       if (std::binary_search(srcs.begin(), srcs.end(), d))
         return fail(PA_ERR_INVALID, "pa_copy_blocks: block %d is both a src and a dst", d);
   }
-  hipError_t e = launch_copy_blocks(k_cache, v_cache, src_dst_pairs, num_pairs, block_bytes,
-                                    num_blocks, st);
+  hipError_t e = launch_copy_blocks(k_cache, v_cache, k_cache, v_cache, src_dst_pairs, num_pairs,
+                                    block_bytes, num_blocks, num_blocks, st);
   if (e != hipSuccess) return hip_fail(e, "pa_copy_blocks launch");
+  return PA_OK;
+}
+
+pa_status pa_swap_blocks(const void* src_k, const void* src_v, int src_num_blocks, void* dst_k,
+                         void* dst_v, int dst_num_blocks, const int32_t* src_dst_pairs,
+                         int num_pairs, int block_size, int num_kv_heads, int head_dim,
+                         pa_dtype dtype, void* stream) {
+  if (dtype != PA_F32 && dtype != PA_F16 && dtype != PA_BF16)
+    return fail(PA_ERR_INVALID, "pa_swap_blocks: unknown dtype %d", (int)dtype);
+  if (num_pairs < 0 || block_size <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      src_num_blocks <= 0 || dst_num_blocks <= 0)
+    return fail(PA_ERR_INVALID, "pa_swap_blocks: need num_pairs >= 0 and positive sizes");
+  const long long block_bytes = (long long)block_size * num_kv_heads * head_dim * elem_bytes(dtype);
+  if (block_bytes % 16 != 0 || block_bytes / 16 > 65535LL * 1024)
+    return fail(PA_ERR_UNSUPPORTED, "pa_swap_blocks: a block of %lld bytes is not a multiple of 16 "
+                "bytes or exceeds 1 GiB", block_bytes);
+  if (num_pairs == 0) return PA_OK;
+  if (!src_k || !src_v || !dst_k || !dst_v || !src_dst_pairs)
+    return fail(PA_ERR_INVALID, "pa_swap_blocks: null pointer argument");
+  if (src_k == dst_k || src_v == dst_v)
+    return fail(PA_ERR_INVALID, "pa_swap_blocks: source and destination are the same pool "
+                "(use pa_copy_blocks)");
+  if (!aligned16(src_k) || !aligned16(src_v) || !aligned16(dst_k) || !aligned16(dst_v))
+    return fail(PA_ERR_INVALID, "pa_swap_blocks: pools must be 16-byte aligned");
+  // Every array the kernel touches must be device memory or pinned host memory
+  // mapped for the device; a pageable host pointer is refused here rather than
+  // faulting in the kernel.
+  const void* in[5] = {src_k, src_v, dst_k, dst_v, src_dst_pairs};
+  const char* name[5] = {"src_k", "src_v", "dst_k", "dst_v", "src_dst_pairs"};
+  void* dev[5];
+  for (int i = 0; i < 5; ++i) {
+    if (!device_address(in[i], &dev[i]))
+      return fail(PA_ERR_INVALID, "pa_swap_blocks: %s is neither device memory nor pinned host "
+                  "memory mapped for the device", name[i]);
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (debug_checks()) {
+    pa_status bad = PA_OK;
+    std::vector<int32_t> pr;
+    if (!to_host(pr, src_dst_pairs, (size_t)num_pairs * 2, st, &bad)) return bad;
+    std::vector<int32_t> dsts;
+    for (int i = 0; i < num_pairs; ++i) {
+      const int s = pr[2 * i], d = pr[2 * i + 1];
+      if (s < 0 || s >= src_num_blocks || d < 0 || d >= dst_num_blocks)
+        return fail(PA_ERR_INVALID, "pa_swap_blocks: pair %d (%d, %d) outside the pools", i, s, d);
+      dsts.push_back(d);
+    }
+    std::sort(dsts.begin(), dsts.end());
+    for (size_t i = 1; i < dsts.size(); ++i)
+      if (dsts[i] == dsts[i - 1]) return fail(PA_ERR_INVALID, "pa_swap_blocks: dst %d repeated", dsts[i]);
+  }
+  hipError_t e = launch_copy_blocks(dev[0], dev[1], dev[2], dev[3],
+                                    static_cast<const int32_t*>(dev[4]), num_pairs, block_bytes,
+                                    src_num_blocks, dst_num_blocks, st);
+  if (e != hipSuccess) return hip_fail(e, "pa_swap_blocks launch");
   return PA_OK;
 }
 

@@ -2,17 +2,19 @@
 // sequence, reference counts, and the slot and copy-on-write decisions a decode
 // step needs ("LLM 注意力与计算内核精读笔记 · 05 PagedAttention 与 KV 显存管理",
 // §3 and §5 ①②: blocks taken on demand, a new block only when the last one is
-// full; §6.1, §6.2 and §12 题4: shared blocks, reference counts, copy before
-// writing into a shared block, release when the count reaches zero).
+// full; §5 ③: a preempted request's blocks move to CPU RAM and come back through
+// its block table; §6.1, §6.2 and §12 题4: shared blocks, reference counts, copy
+// before writing into a shared block, release when the count reaches zero).
 //
 // This file holds host code only.  It produces the index inputs of the kernels:
 // block tables and lengths for pa_decode, one slot per new token for
-// pa_write_kv, and (src, dst) pairs for pa_copy_blocks.
+// pa_write_kv, and (src, dst) pairs for pa_copy_blocks and pa_swap_blocks.
 #include <stdint.h>
 
 #include <deque>
 #include <string>
 #include <unordered_map>
+#include <utility>
 #include <vector>
 
 #include "common.h"
@@ -23,9 +25,13 @@ struct pa_block_manager {
   int block_size = 0;
   std::deque<int32_t> free_list;     // taken from the front, released to the back
   std::vector<int32_t> ref;          // sharers of each physical block
+  int num_cpu_blocks = 0;            // host pool of swapped-out blocks
+  std::deque<int32_t> cpu_free;
+  std::vector<int32_t> cpu_ref;
   struct Seq {
-    std::vector<int32_t> table;      // logical block -> physical block
+    std::vector<int32_t> table;      // logical block -> block of the pool it lives in
     int64_t len = 0;                 // tokens written
+    bool swapped = false;            // table names host blocks
   };
   std::unordered_map<int64_t, Seq> seqs;
 
@@ -49,15 +55,19 @@ pa_status bm_fail(pa_status st, const char* what) {
 extern "C" {
 
 pa_status pa_bm_create(int num_blocks, int block_size, const int32_t* free_order,
-                       pa_block_manager** out) {
+                       int num_cpu_blocks, pa_block_manager** out) {
   if (!out) return bm_fail(PA_ERR_INVALID, "pa_bm_create: null output pointer");
   *out = nullptr;
-  if (num_blocks <= 0 || block_size <= 0)
-    return bm_fail(PA_ERR_INVALID, "pa_bm_create: num_blocks and block_size must be positive");
+  if (num_blocks <= 0 || block_size <= 0 || num_cpu_blocks < 0)
+    return bm_fail(PA_ERR_INVALID, "pa_bm_create: num_blocks and block_size must be positive, "
+                   "num_cpu_blocks not negative");
   auto* bm = new pa_block_manager;
   bm->num_blocks = num_blocks;
   bm->block_size = block_size;
   bm->ref.assign(num_blocks, 0);
+  bm->num_cpu_blocks = num_cpu_blocks;
+  bm->cpu_ref.assign(num_cpu_blocks, 0);
+  for (int32_t b = 0; b < num_cpu_blocks; ++b) bm->cpu_free.push_back(b);
   if (free_order) {
     std::vector<char> seen(num_blocks, 0);
     for (int i = 0; i < num_blocks; ++i) {
@@ -99,6 +109,7 @@ pa_status pa_bm_append_slot(pa_block_manager* bm, int64_t seq, int64_t* slot, in
     return bm_fail(PA_ERR_INVALID, "pa_bm_append_slot: null argument");
   auto it = bm->seqs.find(seq);
   if (it == bm->seqs.end()) return bm_fail(PA_ERR_INVALID, "pa_bm_append_slot: unknown sequence");
+  if (it->second.swapped) return bm_fail(PA_ERR_INVALID, "pa_bm_append_slot: sequence is swapped out");
   auto& s = it->second;
   const int B = bm->block_size;
   const int64_t pos = s.len;
@@ -142,6 +153,7 @@ pa_status pa_bm_append_step(pa_block_manager* bm, const int64_t* seqs, int num_s
     if (it == bm->seqs.end()) return bm_fail(PA_ERR_INVALID, "pa_bm_append_step: unknown sequence");
     if (!once.emplace(seqs[i], 1).second)
       return bm_fail(PA_ERR_INVALID, "pa_bm_append_step: a sequence is listed twice");
+    if (it->second.swapped) return bm_fail(PA_ERR_INVALID, "pa_bm_append_step: a sequence is swapped out");
     const auto& sq = it->second;
     const size_t lb = (size_t)(sq.len / bm->block_size);
     if (lb == sq.table.size()) {
@@ -177,6 +189,7 @@ pa_status pa_bm_fork(pa_block_manager* bm, int64_t parent, int64_t child) {
   if (!bm) return bm_fail(PA_ERR_INVALID, "pa_bm_fork: null manager");
   auto it = bm->seqs.find(parent);
   if (it == bm->seqs.end()) return bm_fail(PA_ERR_INVALID, "pa_bm_fork: unknown parent");
+  if (it->second.swapped) return bm_fail(PA_ERR_INVALID, "pa_bm_fork: parent is swapped out");
   if (bm->seqs.count(child)) return bm_fail(PA_ERR_INVALID, "pa_bm_fork: child already exists");
   pa_block_manager::Seq c = it->second;
   for (int32_t b : c.table) bm->ref[b] += 1;
@@ -188,10 +201,99 @@ pa_status pa_bm_free(pa_block_manager* bm, int64_t seq) {
   if (!bm) return bm_fail(PA_ERR_INVALID, "pa_bm_free: null manager");
   auto it = bm->seqs.find(seq);
   if (it == bm->seqs.end()) return bm_fail(PA_ERR_INVALID, "pa_bm_free: unknown sequence");
+  auto& ref = it->second.swapped ? bm->cpu_ref : bm->ref;
+  auto& free_list = it->second.swapped ? bm->cpu_free : bm->free_list;
   for (int32_t b : it->second.table)
-    if (--bm->ref[b] == 0) bm->free_list.push_back(b);
+    if (--ref[b] == 0) free_list.push_back(b);
   bm->seqs.erase(it);
   return PA_OK;
+}
+
+namespace {
+
+// Move the listed sequences' blocks to the other pool.  Each distinct block
+// they reference moves once, in first-reference order, to the next free block
+// of the target pool, carrying the number of listed sharers as its count; the
+// source block loses those sharers and is released at zero.  All or nothing.
+pa_status bm_move(pa_block_manager* bm, const int64_t* seqs, int num_seqs, int32_t* pairs,
+                  int pairs_cap, int* num_pairs, bool to_cpu, const char* who) {
+  static thread_local std::string msg;
+  auto failf = [&](pa_status st, const char* what) {
+    msg = std::string(who) + ": " + what;
+    return bm_fail(st, msg.c_str());
+  };
+  if (!bm || num_seqs < 0 || !num_pairs || pairs_cap < 0) return failf(PA_ERR_INVALID, "bad arguments");
+  if (num_seqs > 0 && !seqs) return failf(PA_ERR_INVALID, "null array");
+  std::unordered_map<int64_t, char> once;
+  std::vector<std::pair<int32_t, int32_t>> moving;  // (source block, leaving sharers)
+  std::unordered_map<int32_t, size_t> where;
+  for (int i = 0; i < num_seqs; ++i) {
+    auto it = bm->seqs.find(seqs[i]);
+    if (it == bm->seqs.end()) return failf(PA_ERR_INVALID, "unknown sequence");
+    if (!once.emplace(seqs[i], 1).second) return failf(PA_ERR_INVALID, "a sequence is listed twice");
+    if (it->second.swapped == to_cpu)
+      return failf(PA_ERR_INVALID, to_cpu ? "sequence already swapped out" : "sequence is not swapped out");
+    for (int32_t b : it->second.table) {
+      auto w = where.find(b);
+      if (w == where.end()) {
+        where.emplace(b, moving.size());
+        moving.emplace_back(b, 1);
+      } else {
+        moving[w->second].second += 1;
+      }
+    }
+  }
+  auto& src_ref = to_cpu ? bm->ref : bm->cpu_ref;
+  auto& src_free = to_cpu ? bm->free_list : bm->cpu_free;
+  auto& dst_ref = to_cpu ? bm->cpu_ref : bm->ref;
+  auto& dst_free = to_cpu ? bm->cpu_free : bm->free_list;
+  if (moving.size() > dst_free.size())
+    return failf(PA_ERR_NO_BLOCKS, to_cpu ? "not enough free host blocks" : "not enough free blocks");
+  if ((int64_t)moving.size() > pairs_cap) return failf(PA_ERR_INVALID, "pairs array too small");
+  if (!moving.empty() && !pairs) return failf(PA_ERR_INVALID, "null pairs array");
+  std::unordered_map<int32_t, int32_t> new_id;
+  for (size_t i = 0; i < moving.size(); ++i) {
+    const int32_t d = dst_free.front();
+    dst_free.pop_front();
+    dst_ref[d] = moving[i].second;
+    new_id.emplace(moving[i].first, d);
+    pairs[2 * i] = moving[i].first;
+    pairs[2 * i + 1] = d;
+  }
+  for (const auto& m : moving)
+    if ((src_ref[m.first] -= m.second) == 0) src_free.push_back(m.first);
+  for (int i = 0; i < num_seqs; ++i) {
+    auto& sq = bm->seqs[seqs[i]];
+    for (int32_t& b : sq.table) b = new_id[b];
+    sq.swapped = to_cpu;
+  }
+  *num_pairs = (int)moving.size();
+  return PA_OK;
+}
+
+}  // namespace
+
+pa_status pa_bm_swap_out(pa_block_manager* bm, const int64_t* seqs, int num_seqs, int32_t* pairs,
+                         int pairs_cap, int* num_pairs) {
+  return bm_move(bm, seqs, num_seqs, pairs, pairs_cap, num_pairs, true, "pa_bm_swap_out");
+}
+
+pa_status pa_bm_swap_in(pa_block_manager* bm, const int64_t* seqs, int num_seqs, int32_t* pairs,
+                        int pairs_cap, int* num_pairs) {
+  return bm_move(bm, seqs, num_seqs, pairs, pairs_cap, num_pairs, false, "pa_bm_swap_in");
+}
+
+int pa_bm_num_free_cpu(const pa_block_manager* bm) { return bm ? (int)bm->cpu_free.size() : -1; }
+
+int pa_bm_cpu_ref_count(const pa_block_manager* bm, int32_t block) {
+  if (!bm || block < 0 || block >= bm->num_cpu_blocks) return -1;
+  return bm->cpu_ref[block];
+}
+
+int pa_bm_is_swapped(const pa_block_manager* bm, int64_t seq) {
+  if (!bm) return -1;
+  auto it = bm->seqs.find(seq);
+  return it == bm->seqs.end() ? -1 : (it->second.swapped ? 1 : 0);
 }
 
 int pa_bm_num_free(const pa_block_manager* bm) { return bm ? (int)bm->free_list.size() : -1; }
@@ -226,6 +328,7 @@ pa_status pa_bm_batch(const pa_block_manager* bm, const int64_t* seqs, int num_s
   for (int i = 0; i < num_seqs; ++i) {
     auto it = bm->seqs.find(seqs[i]);
     if (it == bm->seqs.end()) return bm_fail(PA_ERR_INVALID, "pa_bm_batch: unknown sequence");
+    if (it->second.swapped) return bm_fail(PA_ERR_INVALID, "pa_bm_batch: a sequence is swapped out");
     const auto& t = it->second.table;
     if ((int)t.size() > max_blocks_per_seq)
       return bm_fail(PA_ERR_INVALID, "pa_bm_batch: a table is longer than max_blocks_per_seq");

@@ -7,6 +7,8 @@
 // ("LLM 注意力与计算内核精读笔记 · 05 PagedAttention 与 KV 显存管理", §5 ②).
 // Copy: before writing into a block other sequences still share, the writer's
 // block is duplicated (same page, §6.1 and §12 题4).
+// Swap: a preempted request's blocks move to CPU RAM and back (same page, §5 ③);
+// the same block copy, between two pools.
 #include "common.h"
 
 namespace pagedkv {
@@ -35,18 +37,22 @@ __global__ __launch_bounds__(256) void write_kv_kernel(const u32x4* __restrict__
 }
 
 // grid.x = pair, grid.y = 1024-piece chunk of the block; each lane moves four
-// 16-byte pieces of K and four of V, loads first.
-__global__ __launch_bounds__(256) void copy_blocks_kernel(u32x4* k_cache, u32x4* v_cache,
+// 16-byte pieces of K and four of V, loads first.  Source and destination pools
+// may be the same (copy-on-write) or two different pools (swap between HBM and
+// pinned host memory, which the GPU reads and writes over the host link).
+__global__ __launch_bounds__(256) void copy_blocks_kernel(const u32x4* ksrc, const u32x4* vsrc,
+                                                           u32x4* kdst, u32x4* vdst,
                                                            const int32_t* __restrict__ pairs,
-                                                           int num_blocks, long long blk_vec) {
+                                                           int src_blocks, int dst_blocks,
+                                                           long long blk_vec) {
   const int src = pairs[2 * blockIdx.x];
   const int dst = pairs[2 * blockIdx.x + 1];
-  if ((unsigned)src >= (unsigned)num_blocks || (unsigned)dst >= (unsigned)num_blocks) return;
+  if ((unsigned)src >= (unsigned)src_blocks || (unsigned)dst >= (unsigned)dst_blocks) return;
   const long long base = (long long)blockIdx.y * 1024 + threadIdx.x;
-  const u32x4* ks = k_cache + (size_t)src * blk_vec;
-  const u32x4* vs = v_cache + (size_t)src * blk_vec;
-  u32x4* kd = k_cache + (size_t)dst * blk_vec;
-  u32x4* vd = v_cache + (size_t)dst * blk_vec;
+  const u32x4* ks = ksrc + (size_t)src * blk_vec;
+  const u32x4* vs = vsrc + (size_t)src * blk_vec;
+  u32x4* kd = kdst + (size_t)dst * blk_vec;
+  u32x4* vd = vdst + (size_t)dst * blk_vec;
   u32x4 a[4], b[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -81,14 +87,17 @@ hipError_t launch_write_kv(const void* k, const void* v, const int32_t* slots, v
                          dim3(256), args, 0, stream);
 }
 
-hipError_t launch_copy_blocks(void* k_cache, void* v_cache, const int32_t* pairs, int num_pairs,
-                              long long block_bytes, int num_blocks, hipStream_t stream) {
+hipError_t launch_copy_blocks(const void* k_src, const void* v_src, void* k_dst, void* v_dst,
+                              const int32_t* pairs, int num_pairs, long long block_bytes,
+                              int src_blocks, int dst_blocks, hipStream_t stream) {
   if (num_pairs == 0) return hipSuccess;
   long long blk_vec = block_bytes / 16;
   const long long chunks = (blk_vec + 1023) / 1024;
-  u32x4* kc = static_cast<u32x4*>(k_cache);
-  u32x4* vc = static_cast<u32x4*>(v_cache);
-  void* args[] = {&kc, &vc, &pairs, &num_blocks, &blk_vec};
+  const u32x4* ks = static_cast<const u32x4*>(k_src);
+  const u32x4* vs = static_cast<const u32x4*>(v_src);
+  u32x4* kd = static_cast<u32x4*>(k_dst);
+  u32x4* vd = static_cast<u32x4*>(v_dst);
+  void* args[] = {&ks, &vs, &kd, &vd, &pairs, &src_blocks, &dst_blocks, &blk_vec};
   return hipLaunchKernel(reinterpret_cast<const void*>(&copy_blocks_kernel),
                          dim3(num_pairs, (unsigned)chunks), dim3(256), args, 0, stream);
 }

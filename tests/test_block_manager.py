@@ -245,3 +245,97 @@ def test_append_step_rejects_duplicates_and_unknown(pk):
     assert bm.seq_len(1) == 3
     slots, pairs = bm.append_step([])
     assert slots.numel() == 0 and pairs.shape == (0, 2)
+
+
+def same_state_swap(nat, ref):
+    same_state_tables = {s: t for s, t in ref.tables.items()}
+    assert nat.num_free() == ref.num_free() and nat.num_free_cpu() == len(ref.cpu_free)
+    for s, t in same_state_tables.items():
+        assert nat.table(s) == t and nat.seq_len(s) == ref.lens[s], s
+        assert nat.is_swapped(s) == (s in ref.swapped), s
+    for b in range(ref.num_blocks):
+        assert nat.ref_count(b) == ref.ref[b], b
+    for b in range(ref.num_cpu_blocks):
+        assert nat.cpu_ref_count(b) == ref.cpu_ref[b], b
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_swap_traces_match_the_oracle(pk, seed):
+    rng = random.Random(1000 + seed)
+    NB, B, NC = rng.choice([(24, 4), (40, 16), (16, 2)]) + (rng.randrange(4, 24),)
+    order = list(range(NB))
+    rng.shuffle(order)
+    nat = pk.BlockManager(NB, B, free_order=order, num_cpu_blocks=NC)
+    ref = oracle.BlockManager(NB, B, free_order=order, num_cpu_blocks=NC)
+    ids, seen = 0, {"out": 0, "in": 0, "refused": 0}
+    for step in range(500):
+        live = [s for s in ref.tables if s not in ref.swapped]
+        away = [s for s in ref.tables if s in ref.swapped]
+        op = rng.randrange(7)
+        try:
+            if op == 0 or not ref.tables:
+                n = rng.randrange(0, 3 * B)
+                try:
+                    expect = ref.allocate(ids, n)
+                except OutOfBlocks:
+                    with pytest.raises(pk.PagedKVError):
+                        nat.allocate(ids, n)
+                    raise
+                assert nat.allocate(ids, n) == expect
+                ids += 1
+            elif op in (1, 2) and live:
+                s = rng.choice(live)
+                try:
+                    expect = ref.append_slot(s)
+                except OutOfBlocks:
+                    with pytest.raises(pk.PagedKVError):
+                        nat.append_slot(s)
+                    raise
+                assert nat.append_slot(s) == expect
+            elif op == 3 and live:
+                p = rng.choice(live)
+                ref.fork(p, ids)
+                nat.fork(p, ids)
+                ids += 1
+            elif op == 4:
+                s = rng.choice(list(ref.tables))
+                ref.free_seq(s)
+                nat.free_seq(s)
+            elif op == 5 and live:
+                group = rng.sample(live, rng.randrange(1, min(3, len(live)) + 1))
+                try:
+                    expect = ref.swap_out(group)
+                except OutOfBlocks:
+                    with pytest.raises(pk.PagedKVError) as e:
+                        nat.swap_out(group)
+                    assert e.value.status == pk.PA_ERR_NO_BLOCKS
+                    raise
+                assert nat.swap_out(group).tolist() == [list(p) for p in expect]
+                seen["out"] += 1
+            elif op == 6 and away:
+                group = rng.sample(away, rng.randrange(1, len(away) + 1))
+                try:
+                    expect = ref.swap_in(group)
+                except OutOfBlocks:
+                    with pytest.raises(pk.PagedKVError) as e:
+                        nat.swap_in(group)
+                    assert e.value.status == pk.PA_ERR_NO_BLOCKS
+                    raise
+                assert nat.swap_in(group).tolist() == [list(p) for p in expect]
+                seen["in"] += 1
+        except OutOfBlocks:
+            seen["refused"] += 1
+        same_state_swap(nat, ref)
+    assert seen["out"] and seen["in"] and seen["refused"]
+
+
+def test_swapped_sequences_refuse_other_operations(pk):
+    bm = pk.BlockManager(8, 4, num_cpu_blocks=4)
+    bm.allocate(1, 6)
+    bm.swap_out([1])
+    for call in (lambda: bm.append_slot(1), lambda: bm.fork(1, 2), lambda: bm.batch([1], 4),
+                 lambda: bm.append_step([1]), lambda: bm.swap_out([1])):
+        with pytest.raises(pk.PagedKVError):
+            call()
+    bm.free_seq(1)
+    assert bm.num_free() == 8 and bm.num_free_cpu() == 4
