@@ -24,14 +24,14 @@ invariants or a library routine.
 """
 
 from .dtypes import DTYPES, to_f64, from_f32_bits
-from .attention import gather, attend, paged_decode, paged_decode_blockwise
+from .attention import gather, attend, paged_decode, paged_decode_blockwise, paged_multi_query
 from .cache_ops import write_kv, copy_blocks, swap_blocks
 from .blockmgr import BlockManager, OutOfBlocks
 from .kv_bytes import kv_bytes_per_token, kv_bytes, blocks_needed, last_block_fill
 
 __all__ = [
     "DTYPES", "to_f64", "from_f32_bits",
-    "gather", "attend", "paged_decode", "paged_decode_blockwise",
+    "gather", "attend", "paged_decode", "paged_decode_blockwise", "paged_multi_query",
     "write_kv", "copy_blocks", "swap_blocks",
     "BlockManager", "OutOfBlocks",
     "kv_bytes_per_token", "kv_bytes", "blocks_needed", "last_block_fill",

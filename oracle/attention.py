@@ -27,6 +27,10 @@ Readings where the pages are silent (each also listed in the design doc)
 * Table entries past ceil(L/B), and pool slots past a sequence's length, are
   never read.
 
+``paged_multi_query`` extends the decode step to several query tokens per
+sequence (chunked prefill, speculative verification): each query sees the
+sequence's tokens up to and including its own position.
+
 ``attend`` is the two-pass stable softmax of the definition.  It deliberately is
 *not* the blockwise online merge that the GPU uses, so the GPU's merge is
 checked against a different algorithm.  ``paged_decode_blockwise`` is the
@@ -39,7 +43,12 @@ the mean of the valid V rows; a constructed one-hot attention returns the
 selected row; a two-token case matches the logistic closed form; agreement
 with torch's scaled_dot_product_attention in float64 on unpaged tensors (GQA by
 repeating KV heads); bit-identical results under any relabelling of physical
-block ids; blockwise == two-pass within 1e-12.
+block ids; blockwise == two-pass within 1e-12.  Multi-query
+(tests/test_oracle_multi_query.py): one query per sequence equals the decode
+oracle; agreement with torch's scaled_dot_product_attention in float64 under an
+explicit causal mask offset by the cached prefix; the first query of a fresh
+prompt returns V[0] exactly; changing K/V after a query's position leaves it
+bit-identical while changing one at or before it does not.
 """
 
 import numpy as np
@@ -101,6 +110,46 @@ def paged_decode(q, k_cache, v_cache, block_tables, seq_lens, scale, dtype, seqs
         V = to_f64(gather(v_cache, block_tables[s], L, block_size), dtype)
         res.append(attend(to_f64(q[s], dtype), K, V, scale))
     return np.stack(res) if res else np.zeros((0,) + q.shape[1:])
+
+
+def paged_multi_query(q, k_cache, v_cache, block_tables, seq_lens, q_start, scale, dtype):
+    """Oracle for several query tokens per sequence over the paged cache, causal.
+
+    The pages pair PagedAttention with chunked prefill (long prompts processed
+    in pieces: [PA-explainer] "2026年最新进展"; the per-batch token cap for long
+    prompts in [vLLM-what] "5）关键参数旋钮") and with speculative decoding
+    ([PA-explainer] "2026年最新进展"), where a sequence brings several new
+    tokens at once.  Sequence s owns the
+    query rows ``q_start[s] .. q_start[s+1]-1``; they are its *last* n_s tokens
+    (already written to the cache), so query i sits at position p = L_s - n_s + i
+    and attends to the tokens 0..p of the sequence -- the dense causal definition,
+    softmax(scale * q K[0..p]^T) V[0..p], with GQA as in ``attend``.
+
+    q: [total_q, num_heads, head_dim]; seq_lens: [N] tokens in the cache
+    including the queries' own; q_start: [N+1] non-decreasing offsets into q.
+    Rows of q owned by no sequence stay zero.  Requires n_s <= L_s.
+    Returns float64 [total_q, num_heads, head_dim].
+    """
+    block_size = k_cache.shape[1]
+    q_start = [int(x) for x in q_start]
+    total_q = q.shape[0]
+    out = np.zeros(q.shape, dtype=np.float64)
+    for s in range(len(seq_lens)):
+        L = int(seq_lens[s])
+        a, b = q_start[s], q_start[s + 1]
+        n = b - a
+        if n < 0 or b > total_q or a < 0:
+            raise ValueError(f"sequence {s}: bad query range [{a}, {b})")
+        if n > L:
+            raise ValueError(f"sequence {s}: {n} queries but only {L} tokens")
+        if n == 0:
+            continue
+        K = to_f64(gather(k_cache, block_tables[s], L, block_size), dtype)
+        V = to_f64(gather(v_cache, block_tables[s], L, block_size), dtype)
+        for i in range(n):
+            pos = L - n + i
+            out[a + i] = attend(to_f64(q[a + i], dtype), K[:pos + 1], V[:pos + 1], scale)
+    return out
 
 
 def paged_decode_blockwise(q, k_cache, v_cache, table_row, seq_len, scale, dtype):

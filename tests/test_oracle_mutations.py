@@ -17,6 +17,7 @@ import oracle.blockmgr as bmod
 import test_oracle_attention as TA
 import test_oracle_cache_ops as TC
 import test_oracle_swap as TS
+import test_oracle_multi_query as TM
 
 
 def attend_factory(kind):
@@ -123,6 +124,33 @@ def move_factory(kind):
     return _move
 
 
+def multi_query_factory(kind):
+    from oracle.dtypes import to_f64
+
+    def paged_multi_query(q, k_cache, v_cache, block_tables, seq_lens, q_start, scale, dtype):
+        B = k_cache.shape[1]
+        out = np.zeros(q.shape)
+        for s in range(len(seq_lens)):
+            L = int(seq_lens[s])
+            a, b = int(q_start[s]), int(q_start[s + 1])
+            n = b - a
+            if n > L or n < 0 or b > q.shape[0]:
+                raise ValueError("bad range")
+            K = to_f64(att.gather(k_cache, block_tables[s], L, B), dtype)
+            V = to_f64(att.gather(v_cache, block_tables[s], L, B), dtype)
+            for i in range(n):
+                pos = {"from_start": i, "strict": L - n + i - 1, "no_mask": L - 1}.get(kind, L - n + i)
+                if kind == "next_row":
+                    pos = L - n + i
+                    i_out = (i + 1) % n
+                else:
+                    i_out = i
+                out[a + i_out] = att.attend(to_f64(q[a + i], dtype), K[:max(pos, 0) + 1],
+                                            V[:max(pos, 0) + 1], scale)
+        return out
+    return paged_multi_query
+
+
 ATTN_PINS = [
     lambda: TA.test_single_token_returns_v_exactly("f32"),
     lambda: TA.test_single_token_returns_v_exactly("bf16"),
@@ -138,6 +166,10 @@ CACHE_PINS = [
     TC.test_write_is_a_bit_copy_and_skips_negative_slots,
 ]
 
+
+MQ_PINS = [lambda: TM.test_matches_torch_sdpa_with_offset_causal_mask(8, 2),
+           TM.test_first_token_of_a_fresh_prompt_sees_only_itself,
+           TM.test_causality_by_perturbing_single_rows]
 
 SWAP_PINS = [TS.test_swap_blocks_small_example] + \
     [(lambda seed=seed: TS.test_swap_traces_read_back_every_sequence(seed)) for seed in range(3)] + \
@@ -185,5 +217,12 @@ def test_swap_bookkeeping_mutants_are_caught(monkeypatch, kind):
     assert caught(SWAP_PINS), kind
 
 
+@pytest.mark.parametrize("kind", ["from_start", "strict", "no_mask", "next_row"])
+def test_multi_query_mutants_are_caught(monkeypatch, kind):
+    monkeypatch.setattr(oracle, "paged_multi_query", multi_query_factory(kind))
+    assert caught(MQ_PINS), kind
+
+
 def test_unmutated_oracle_passes_every_pin():
-    assert not caught(ATTN_PINS) and not caught(CACHE_PINS) and not caught(SWAP_PINS)
+    assert not caught(ATTN_PINS) and not caught(CACHE_PINS) and not caught(SWAP_PINS) \
+        and not caught(MQ_PINS)

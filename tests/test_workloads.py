@@ -43,6 +43,9 @@ def check_tables(b, bm):
     lambda: workloads.llama3_8b(num_seqs=12, num_blocks=3000),
     lambda: workloads.llama7b(num_seqs=6, max_len=300),
     lambda: workloads.llama2_70b(block_size=8, num_seqs=3, min_len=100, max_len=400),
+    lambda: workloads.multi_query_small(),
+    lambda: workloads.llama3_8b_spec(num_seqs=10, num_blocks=3000),
+    lambda: workloads.llama3_8b_chunk(num_seqs=3, chunk=40, max_prior=100),
 ])
 def test_independent_sequences_match_block_manager(make):
     b = make()
@@ -125,3 +128,12 @@ def test_outliers_scale_key_rows_by_eight():
     same = np.all(rows0 == rows1, axis=-1)
     eight = np.all(rows1 == 8 * rows0, axis=-1)
     assert np.all(same | eight) and 0 < (~same).sum() < 0.05 * same.size
+
+
+def test_multi_query_batches_have_one_query_row_per_written_token():
+    for b in (workloads.multi_query_small(), workloads.llama3_8b_chunk(num_seqs=3, chunk=40,
+                                                                       max_prior=100)):
+        n = (b.q_start[1:] - b.q_start[:-1]).tolist()
+        assert b.q.shape[0] == sum(n) == len(b.slot_mapping)
+        assert ((b.seq_lens - b.seq_lens_before).tolist()) == n
+        assert all(k <= L for k, L in zip(n, b.seq_lens.tolist()))

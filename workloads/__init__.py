@@ -34,6 +34,9 @@ Workloads (shapes of the pages' examples; see the design doc for the full recipe):
                   token of 7 of the 8 samples forces a block copy
   llama2_70b      GQA 64/8, D=128, bf16, 32 seqs, L ~ U{8192..32768},
                   B in {8,16,32}, 1% of key rows x8
+  llama3_8b_spec  multi-query: the llama3_8b shape with 4 new tokens per sequence
+  llama3_8b_chunk multi-query: 16 sequences x 512-token prompt chunks after cached
+                  prefixes of U{0..3584} tokens
 Every size parameter can be shrunk for oracle-sized parity cases.
 """
 
@@ -66,11 +69,28 @@ class PagedBatch:
     new_v: Optional[torch.Tensor] = None
     slot_mapping: Optional[torch.Tensor] = None   # int32 [T]
     cow_pairs: Optional[torch.Tensor] = None      # int32 [P, 2] (src, dst) before the write
+    q_start: Optional[torch.Tensor] = None        # int32 [N+1]: multi-query batches only
     info: dict = field(default_factory=dict)
 
     @property
     def num_seqs(self):
-        return int(self.q.shape[0])
+        return int(self.seq_lens.shape[0])
+
+    @property
+    def max_q_len(self):
+        if self.q_start is None:
+            return 1
+        d = self.q_start[1:] - self.q_start[:-1]
+        return int(d.max()) if d.numel() else 0
+
+    def causal_pairs(self):
+        """Multi-query batches: sum over query rows of the tokens each attends to."""
+        qs, lens = self.q_start.tolist(), self.seq_lens.tolist()
+        tot = 0
+        for s, L in enumerate(lens):
+            n = qs[s + 1] - qs[s]
+            tot += n * (L - n) + n * (n + 1) // 2
+        return tot
 
     @property
     def max_seq_len(self):
@@ -136,12 +156,22 @@ def _pool(num_blocks, B, Hkv, D, dtype, fill):
 
 
 def _paged(*, name, dtype, lens, Hq, Hkv, D, B, num_blocks=None, slack=0.10, gen,
-           write_last=False, outlier_frac=0.0, fill="nan"):
-    """Independent sequences: prompts of L-1 (write_last) or L tokens, random placement."""
+           write_last=False, outlier_frac=0.0, fill="nan", queries=None):
+    """Independent sequences: prompts of L-1 (write_last) or L tokens, random placement.
+
+    With ``queries`` (tokens per sequence), the last queries[s] tokens of every
+    sequence arrive through the write step and each of them has a query row
+    (several queries per sequence, causal); q is then [sum(queries), Hq, D]."""
     lens = [int(x) for x in lens]
     N = len(lens)
-    prompt = [L - 1 if write_last else L for L in lens]
-    appended = [1 if write_last else 0 for _ in lens]
+    if queries is not None:
+        queries = [int(x) for x in queries]
+        if any(n > L for n, L in zip(queries, lens)):
+            raise ValueError(f"{name}: more queries than tokens")
+        appended = queries
+    else:
+        appended = [1 if write_last else 0 for _ in lens]
+    prompt = [L - a for L, a in zip(lens, appended)]
     need = sum(-(-L // B) for L in lens)
     if num_blocks is None:
         num_blocks = max(1, int(np.ceil(need * (1.0 + slack))))
@@ -149,7 +179,7 @@ def _paged(*, name, dtype, lens, Hq, Hkv, D, B, num_blocks=None, slack=0.10, gen
         raise ValueError(f"{name}: pool of {num_blocks} blocks cannot hold {need}")
     perm = torch.randperm(num_blocks, generator=gen).tolist()
     tables, _ = _tables(prompt, appended, B, perm)
-    q = torch.randn(N, Hq, D, generator=gen)
+    q = torch.randn(N if queries is None else sum(queries), Hq, D, generator=gen)
     total = sum(lens)
     K = torch.randn(total, Hkv, D, generator=gen)
     if outlier_frac > 0:
@@ -167,9 +197,9 @@ def _paged(*, name, dtype, lens, Hq, Hkv, D, B, num_blocks=None, slack=0.10, gen
         sl = _slots(tables[s], 0, stored, B)
         kflat[sl] = K[off:off + stored]
         vflat[sl] = V[off:off + stored]
-        if write_last:
-            new_rows.append(off + L - 1)
-            new_slots.append(int(_slots(tables[s], L - 1, L, B)[0]))
+        if appended[s]:
+            new_rows.extend(range(off + stored, off + L))
+            new_slots.extend(int(x) for x in _slots(tables[s], stored, L, B))
         off += L
     b = PagedBatch(
         name=name, dtype=dtype, num_heads=Hq, num_kv_heads=Hkv, head_dim=D, block_size=B,
@@ -177,10 +207,12 @@ def _paged(*, name, dtype, lens, Hq, Hkv, D, B, num_blocks=None, slack=0.10, gen
         block_tables=_table_tensor(tables), seq_lens=torch.tensor(lens, dtype=torch.int32),
         seq_lens_before=torch.tensor(prompt, dtype=torch.int32),
         info={"blocks_needed": need, "free_list": perm})
-    if write_last:
+    if new_rows:
         idx = torch.tensor(new_rows, dtype=torch.int64)
         b.new_k, b.new_v = K[idx].clone(), V[idx].clone()
         b.slot_mapping = torch.tensor(new_slots, dtype=torch.int32)
+    if queries is not None:
+        b.q_start = torch.tensor(np.concatenate([[0], np.cumsum(queries)]), dtype=torch.int32)
     return b
 
 
@@ -244,6 +276,35 @@ def llama2_70b(seed=0, block_size=16, num_seqs=32, min_len=8192, max_len=32768,
     lens = torch.randint(min_len, max_len + 1, (num_seqs,), generator=g).tolist()
     return _paged(name=f"llama2_70b_b{block_size}", dtype="bf16", lens=lens, Hq=64, Hkv=8,
                   D=128, B=block_size, gen=g, outlier_frac=outlier_frac, fill=fill)
+
+
+def llama3_8b_spec(seed=0, num_seqs=256, queries=4, min_len=512, max_len=4096,
+                   num_blocks=70_000, fill="nan"):
+    """Speculative verification on the Llama-3-8B shape: every sequence brings ``queries``
+    new tokens (written by the write step), each scored against the whole cached context
+    causally; lengths, including the new tokens, uniform in [min_len, max_len]."""
+    g = torch.Generator().manual_seed(seed)
+    lens = torch.randint(min_len, max_len + 1, (num_seqs,), generator=g).tolist()
+    return _paged(name="llama3_8b_spec", dtype="bf16", lens=lens, Hq=32, Hkv=8, D=128, B=16,
+                  num_blocks=num_blocks, gen=g, queries=[queries] * num_seqs, fill=fill)
+
+
+def llama3_8b_chunk(seed=0, num_seqs=16, chunk=512, max_prior=3584, fill="nan"):
+    """Chunked prefill on the Llama-3-8B shape: every sequence brings a ``chunk``-token
+    piece of its prompt after a cached prefix of U{0..max_prior} tokens."""
+    g = torch.Generator().manual_seed(seed)
+    prior = torch.randint(0, max_prior + 1, (num_seqs,), generator=g).tolist()
+    lens = [p + chunk for p in prior]
+    return _paged(name="llama3_8b_chunk", dtype="bf16", lens=lens, Hq=32, Hkv=8, D=128, B=16,
+                  gen=g, queries=[chunk] * num_seqs, fill=fill)
+
+
+def multi_query_small(seed=0, dtype="f32", lens=(1, 7, 16, 40, 64, 33), queries=(1, 3, 16, 5, 64, 33),
+                      Hq=8, Hkv=2, D=64, B=16, fill="nan"):
+    """Oracle-sized multi-query batch: single queries, short and whole-prompt chunks."""
+    g = torch.Generator().manual_seed(seed)
+    return _paged(name=f"multi_query_small_{dtype}", dtype=dtype, lens=list(lens), Hq=Hq,
+                  Hkv=Hkv, D=D, B=B, gen=g, queries=list(queries), fill=fill)
 
 
 def _shared(*, name, seed, num_prompts, samples, prompt_len, tail_max, cow, Hq, D, B, fill):
@@ -355,4 +416,6 @@ WORKLOADS = {
     "opt13b_shared": opt13b_shared,
     "opt13b_cow": opt13b_cow,
     "llama2_70b": llama2_70b,
+    "llama3_8b_spec": llama3_8b_spec,
+    "llama3_8b_chunk": llama3_8b_chunk,
 }
