@@ -171,6 +171,46 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst_pa
                          int head_dim, int num_blocks, pa_dtype dtype, void* stream);
 
 /*
+ * Multi-query paged attention -- several query tokens per sequence, causal:
+ * the attention of chunked prefill (a long prompt processed in pieces) and of
+ * speculative verification (several drafted tokens scored at once), which
+ * [PA-explainer] "2026年最新进展" pairs with PagedAttention.
+ *
+ * Sequence s owns query rows q_start[s] .. q_start[s+1]-1 of q: its last
+ * n_s = q_start[s+1] - q_start[s] tokens, whose K/V are already in the cache
+ * (pa_write_kv).  seq_lens[s] = L_s counts every cached token including those.
+ * Query i of the sequence sits at position p = L_s - n_s + i and attends to
+ * tokens 0..p ([PA-notes] §4 blockwise softmax over the sequence's blocks):
+ *     out[q_start[s] + i, h] = softmax_{t <= p}(scale * q[.., h] . K_s[t]) V_s[t]
+ * with GQA as in pa_decode.  One query per sequence is exactly pa_decode.
+ *
+ *   q, out         [total_q][num_heads][head_dim], dtype
+ *   k_cache, ...   as for pa_decode (block_size any positive value here)
+ *   q_start        device int32 [num_seqs + 1], non-decreasing, q_start[0] = 0,
+ *                  q_start[num_seqs] = total_q
+ *   seq_lens       device int32 [num_seqs], n_s <= L_s <= max_seq_len
+ *   max_q_len      host bound on every n_s (no device sync is made)
+ *   workspace      pa_multi_query_workspace_size(...) bytes (0 when the launch
+ *                  needs no partition merge); no zero-fill needed
+ *
+ * Work is cut into (sequence, KV head, block of 64 query rows, context
+ * partition) items; with few items the context is split into partitions that
+ * a second kernel merges, in a fixed order.  Head_dim 64 or 128; any group size
+ * up to 64.  Errors as for pa_decode; index data violating the contract above
+ * is clamped so that no access leaves the arrays, with unspecified results
+ * (PA_DEBUG_CHECK=1 rejects it).  Results are deterministic.
+ */
+size_t pa_multi_query_workspace_size(int num_seqs, int total_q, int num_heads, int num_kv_heads,
+                                     int head_dim, int max_q_len, int max_seq_len);
+pa_status pa_multi_query(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* seq_lens,
+                         const int32_t* q_start, int num_seqs, int total_q, int num_heads,
+                         int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                         int max_blocks_per_seq, int max_q_len, int max_seq_len, float scale,
+                         pa_dtype dtype, void* out, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
  * Swap blocks between two pools -- preemption ([PA-notes] §5 ③: when memory
  * runs short a request is suspended, its blocks freed or moved to CPU RAM, and
  * it is restored later through its block table).  For every (src, dst) row of

@@ -55,6 +55,11 @@ def lib():
     L.pa_write_kv.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
     L.pa_copy_blocks.restype = i32
     L.pa_copy_blocks.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, vp]
+    L.pa_multi_query_workspace_size.restype = sz
+    L.pa_multi_query_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    L.pa_multi_query.restype = i32
+    L.pa_multi_query.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                 i32, f32, i32, vp, vp, sz, vp]
     L.pa_swap_blocks.restype = i32
     L.pa_swap_blocks.argtypes = [vp, vp, i32, vp, vp, i32, vp, i32, i32, i32, i32, i32, vp]
     i64 = ctypes.c_int64
@@ -174,6 +179,57 @@ def pa_decode(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, scale, 
         num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
         block_tables.shape[1], int(max_seq_len), float(scale), _DTYPE[q.dtype], _ptr(out),
         _ptr(workspace), ws_bytes, _stream(stream)))
+    return out
+
+
+def pa_multi_query_workspace_size(num_seqs, total_q, num_heads, num_kv_heads, head_dim, max_q_len,
+                                  max_seq_len):
+    return int(lib().pa_multi_query_workspace_size(int(num_seqs), int(total_q), int(num_heads),
+                                                   int(num_kv_heads), int(head_dim), int(max_q_len),
+                                                   int(max_seq_len)))
+
+
+def pa_multi_query(q, k_cache, v_cache, block_tables, seq_lens, q_start, num_kv_heads, scale, out, *,
+                   max_q_len, max_seq_len, workspace=None, stream=None):
+    """Several causal queries per sequence (chunked prefill, speculative verification):
+    rows q_start[s] .. q_start[s+1]-1 of q are the last n_s of sequence s's seq_lens[s]
+    cached tokens; query i attends to tokens 0 .. seq_lens[s] - n_s + i (include/pagedkv.h).
+
+    q, out: [total_q, num_heads, head_dim]; q_start: int32 [num_seqs + 1] from 0 to total_q;
+    max_q_len / max_seq_len: host bounds (no device sync); workspace: uint8 tensor of at least
+    pa_multi_query_workspace_size(...) bytes, allocated here if needed and omitted.
+    """
+    _dev("q", q, ndim=3)
+    if q.dtype not in _DTYPE:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev(name, t, q.dtype, 4)
+    if k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+    _dev("block_tables", block_tables, torch.int32, 2)
+    _dev("seq_lens", seq_lens, torch.int32, 1)
+    _dev("q_start", q_start, torch.int32, 1)
+    _dev("out", out, q.dtype)
+    total_q, num_heads, head_dim = q.shape
+    num_blocks, block_size, nkv, hd = k_cache.shape
+    num_seqs = seq_lens.shape[0]
+    if nkv != num_kv_heads or hd != head_dim:
+        raise ValueError(f"cache shape {tuple(k_cache.shape)} does not match num_kv_heads="
+                         f"{num_kv_heads}, head_dim={head_dim}")
+    if out.shape != q.shape or block_tables.shape[0] != num_seqs or q_start.shape[0] != num_seqs + 1:
+        raise ValueError("q, out, block_tables, seq_lens and q_start disagree")
+    need = pa_multi_query_workspace_size(num_seqs, total_q, num_heads, num_kv_heads, head_dim,
+                                         max_q_len, max_seq_len)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _dev("workspace", workspace)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().pa_multi_query(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens), _ptr(q_start),
+        num_seqs, total_q, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+        block_tables.shape[1], int(max_q_len), int(max_seq_len), float(scale), _DTYPE[q.dtype],
+        _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
     return out
 
 
@@ -382,6 +438,7 @@ class BlockManager:
         return tables, lens
 
 
-__all__ = ["pa_decode", "pa_write_kv", "pa_copy_blocks", "pa_swap_blocks", "pa_decode_workspace_size",
+__all__ = ["pa_decode", "pa_multi_query", "pa_multi_query_workspace_size", "pa_write_kv",
+           "pa_copy_blocks", "pa_swap_blocks", "pa_decode_workspace_size",
            "decode_workspace", "pa_last_error", "pa_version",
            "PagedKVError", "BlockManager", "lib", "LIB_PATH"]

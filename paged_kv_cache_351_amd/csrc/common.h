@@ -54,6 +54,39 @@ hipError_t launch_copy_blocks(const void* k_src, const void* v_src, void* k_dst,
                               const int32_t* pairs, int num_pairs, long long block_bytes,
                               int src_blocks, int dst_blocks, hipStream_t stream);
 
+// Everything one pa_multi_query launch needs, already validated by the host code.
+struct MultiQueryParams {
+  const void* q;               // [total_q][num_heads][head_dim]
+  const void* k_cache;
+  const void* v_cache;
+  const int32_t* block_tables;
+  const int32_t* seq_lens;     // tokens in the cache, including the queries' own
+  const int32_t* q_start;      // [num_seqs + 1] query row offsets
+  void* out;                   // [total_q][num_heads][head_dim]
+  float* ws_ml;                // [total_q * num_heads][parts][2] running max and sum
+  float* ws_acc;               // [total_q * num_heads][parts][head_dim]
+  int num_seqs;
+  int total_q;
+  int num_heads;
+  int num_kv_heads;
+  int group;
+  int head_dim;
+  int block_size;
+  int num_blocks;
+  int max_blocks_per_seq;
+  int max_q_len;
+  int max_seq_len;
+  int tq;                      // query tokens per workgroup (64 rows / group)
+  int qblocks;                 // query blocks per (sequence, KV head): ceil(max_q_len / tq)
+  int parts;                   // context partitions; 1 = no merge step
+  int part_len;                // tokens per partition, a multiple of the 32-token tile
+  long long items;             // num_seqs * num_kv_heads * qblocks
+  float scale_log2e;
+};
+
+// The multi-query and partition-merge kernels for one element type and head_dim.
+bool multi_query_kernels(int dtype, int head_dim, const void** main, const void** merge);
+
 // Message returned by pa_last_error() on the calling thread.
 void set_last_error(const char* msg);
 

@@ -1,0 +1,435 @@
+// Multi-query paged attention for gfx950 (CDNA4): several query tokens per
+// sequence, each attending causally to the sequence's cached tokens -- the
+// attention of chunked prefill (a long prompt processed in pieces) and of
+// speculative verification (several drafted tokens scored at once), both of
+// which the pages pair with PagedAttention ("PagedAttention：分页注意力——推理引擎的显存革命",
+// section "2026年最新进展").  Sequence s owns query rows q_start[s] ..
+// q_start[s+1]-1, its last n_s tokens (already in the cache); query i sits at
+// position p = L_s - n_s + i and attends to tokens 0..p:
+//     out[row, h] = softmax_t<=p(scale * q[row, h] . K_s[t]) V_s[t],
+// K/V fetched through the block table ("LLM 注意力与计算内核精读笔记 · 05
+// PagedAttention 与 KV 显存管理", §3, §4), the softmax merged tile by tile with a
+// running maximum and sum (same page, §4).
+//
+// Work decomposition
+//   A workgroup (4 waves) owns one (sequence, KV head, query block, context
+//   partition).  A query block is 64 rows: up to floor(64 / g) consecutive query
+//   tokens times the g query heads of the KV head's group, row = token * g +
+//   head; wave w computes rows 16w .. 16w+15.  Its partition of the context
+//   [part * part_len, ...) is cut at the block's last query position.  With one
+//   partition the workgroup writes the output; otherwise it leaves (m, l, acc)
+//   per row and a second kernel merges the partitions in order.  Workgroups are
+//   numbered so that every query block and partition of one (sequence, KV head)
+//   runs on the same XCD (workgroup id mod 8), where they share its L2.
+//
+// Per tile of 32 tokens
+//   All 256 lanes load the tile's K and V rows (16 bytes per load, token ->
+//   block through the table) one tile ahead in registers and store them to LDS:
+//   K as [token][head_dim] rows, V transposed as [head_dim][slot] rows, where
+//   token t = 16 h + 4 grp + i (h in 0..1, grp and i in 0..3) sits in slot
+//   8 grp + 4 h + i (slot_of).  Then each wave, on the matrix cores:
+//     S^T = K Q^T   v_mfma_f32_16x16x32_{bf16,f16} (16x16x4_f32 for fp32): A = K
+//                   rows of one 16-token half, B = the wave's 16 query rows, both
+//                   cut into the same head_dim chunks; lane (grp, col) gets the
+//                   scores of tokens 16 h + 4 grp + i, i = 0..3, for row col.
+//     online softmax per row: the row's maximum over the four lanes (grp 0..3)
+//                   that hold it, exponentials in base 2, the running sum kept
+//                   per lane (the four partial sums are added at the end).
+//     O^T += V^T P^T with A = V^T (16 head_dim rows x 32 slots) and B = P^T:
+//                   lane (grp, col) holds P for slots 8 grp .. 8 grp + 7, which
+//                   are exactly the tokens whose scores it computed, so the
+//                   scores never move between lanes.
+//   P is rounded to the storage type for the matrix cores: fp16 keeps 11
+//   significant bits, bf16 is split into two bf16 terms (about 16 bits) fed to
+//   two products, fp32 stays fp32.  The running sum adds the rounded values, so
+//   the output is a weighted mean with exactly the weights used.  Masked tokens
+//   get -inf, i.e. weight 0; running maxima start at -1e30 so no row ever forms
+//   inf - inf.
+#include <type_traits>
+
+#include "common.h"
+
+namespace pagedkv {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kTile = 32;   // tokens per K/V tile
+constexpr float kNegBig = -1.0e30f;
+
+template <int DT, int D>
+struct Shape {
+  static constexpr int EB = DT == kF32 ? 4 : 2;   // bytes per element
+  static constexpr int ROWB = D * EB;             // bytes per K/V row
+  static constexpr int CR = ROWB / 16;            // 16-byte chunks per row
+  static constexpr int NKC = CR / 4;              // chunks per lane of one row (4 lane groups)
+  static constexpr int KSTRIDE = ROWB + 16;       // LDS bytes per K row, padded
+  static constexpr int VSTRIDE = kTile * EB + 16; // LDS bytes per transposed V row, padded
+  static constexpr int KBYTES = kTile * KSTRIDE;
+  static constexpr int LDS = KBYTES + D * VSTRIDE;
+  static constexpr int KLOADS = kTile * CR / 256;         // K chunks per thread per tile
+  static constexpr int VLOADS = (16 * CR + 255) / 256;    // V token-pair chunks per thread
+  static constexpr int NJ = D / 16;                       // 16-row head_dim blocks of O^T
+  static_assert(KLOADS >= 1 && kTile * CR % 256 == 0, "tile does not split over 256 lanes");
+};
+
+// Chunk (16 bytes) of a row that lane group grp feeds to the matrix cores in step c.
+template <int DT, int D>
+__device__ __forceinline__ int chunk_of(int c, int grp) {
+  if constexpr (DT == kF32) return grp * Shape<DT, D>::NKC + c;  // 4 floats, one per MFMA
+  else return 4 * c + grp;                                        // 8 halves, one MFMA
+}
+
+// Slot of tile token t in the transposed V rows (see the file comment).
+__device__ __forceinline__ int slot_of(int t) {
+  const int h = t >> 4, r = t & 15;
+  return 8 * (r >> 2) + 4 * h + (r & 3);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int DT>
+__device__ __forceinline__ uint16_t to_store(float x) {
+  if constexpr (DT == kBF16) return __builtin_bit_cast(uint16_t, (__bf16)x);
+  else return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+template <int DT>
+__device__ __forceinline__ float from_store(uint16_t x) {
+  if constexpr (DT == kBF16) return __uint_as_float((uint32_t)x << 16);
+  else return (float)__builtin_bit_cast(_Float16, x);
+}
+
+// Store 4 consecutive output elements.
+template <int DT>
+__device__ __forceinline__ void store4(void* dst, f32x4 v) {
+  if constexpr (DT == kF32) {
+    *reinterpret_cast<f32x4*>(dst) = v;
+  } else {
+    const uint32_t a = (uint32_t)to_store<DT>(v[0]) | ((uint32_t)to_store<DT>(v[1]) << 16);
+    const uint32_t b = (uint32_t)to_store<DT>(v[2]) | ((uint32_t)to_store<DT>(v[3]) << 16);
+    *reinterpret_cast<u32x2*>(dst) = u32x2{a, b};
+  }
+}
+
+// Decode the workgroup's item: XCD-major numbering, then (s, kv, qb, part).
+struct Item {
+  int s, kv, qb, part;
+};
+
+__device__ __forceinline__ bool item_of(const MultiQueryParams& p, Item& it) {
+  const long long per = (long long)gridDim.x / 8;  // the grid is a multiple of 8
+  const long long b = blockIdx.x;
+  const long long logical = (b % 8) * per + b / 8;
+  if (logical >= (long long)p.items * p.parts) return false;
+  it.part = (int)(logical % p.parts);
+  long long r = logical / p.parts;
+  it.qb = (int)(r % p.qblocks);
+  r /= p.qblocks;
+  it.kv = (int)(r % p.num_kv_heads);
+  it.s = (int)(r / p.num_kv_heads);
+  return it.s < p.num_seqs;
+}
+
+template <int DT, int D>
+__global__ __launch_bounds__(256) void multi_query_kernel(MultiQueryParams p) {
+  using S = Shape<DT, D>;
+  constexpr int EB = S::EB, CR = S::CR, NKC = S::NKC, NJ = S::NJ;
+  __shared__ __attribute__((aligned(16))) char lds[S::LDS];
+  char* ldsK = lds;
+  char* ldsV = lds + S::KBYTES;
+
+  Item it;
+  if (!item_of(p, it)) return;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int g = p.group, Hq = p.num_heads, Hkv = p.num_kv_heads;
+
+  // the sequence's query range and length, clamped so that no access leaves the arrays
+  int L = p.seq_lens[it.s];
+  L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
+  const int qa = p.q_start[it.s];
+  int n = p.q_start[it.s + 1] - qa;
+  n = n < 0 ? 0 : (n > p.max_q_len ? p.max_q_len : n);
+  if (qa < 0 || qa + n > p.total_q) n = 0;
+  const int tok0 = it.qb * p.tq;                   // first query token of the block
+  if (tok0 >= n) return;
+  const int tok1 = min(n, tok0 + p.tq);            // one past the last
+  const int pos_hi = L - n + tok1 - 1;             // last query position of the block
+  const int kv_end = min(L, pos_hi + 1);
+  const int t_begin = it.part * p.part_len;
+  const int t_end = min(kv_end, t_begin + p.part_len);
+
+  // this lane's query row (row col of the wave)
+  const int rloc = wave * 16 + col;
+  const int qtok = tok0 + rloc / g;
+  const int qh = rloc % g;
+  const bool row_ok = rloc < p.tq * g && qtok < tok1;
+  const int pos = L - n + qtok;                    // the row's causal limit (inclusive)
+  const size_t out_row = (size_t)(qa + qtok) * Hq + (size_t)it.kv * g + qh;
+
+  // query fragments: the same chunks of the row as the K fragments
+  u32x4 qf[NKC];
+#pragma unroll
+  for (int c = 0; c < NKC; ++c) {
+    qf[c] = u32x4{0u, 0u, 0u, 0u};
+    if (row_ok)
+      qf[c] = *reinterpret_cast<const u32x4*>((const char*)p.q + out_row * S::ROWB +
+                                              chunk_of<DT, D>(c, grp) * 16);
+  }
+
+  f32x4 acc[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = kNegBig, l = 0.f;
+
+  const int32_t* table = p.block_tables + (size_t)it.s * p.max_blocks_per_seq;
+  const int B = p.block_size;
+  const size_t kv_off = (size_t)it.kv * S::ROWB;
+  const size_t slot_bytes = (size_t)Hkv * S::ROWB;
+  // byte offset of token t's row of this KV head in the pool; t is clamped to the
+  // partition's last token so that nothing outside the sequence is read
+  auto row_addr = [&](int t) -> size_t {
+    t = min(t, t_end - 1);
+    int b = table[t / B];
+    b = b < 0 ? 0 : (b >= p.num_blocks ? p.num_blocks - 1 : b);
+    return ((size_t)b * B + t % B) * slot_bytes + kv_off;
+  };
+
+  u32x4 kr[S::KLOADS];
+  u32x4 va[S::VLOADS], vb[S::VLOADS];
+  auto load_tile = [&](int t0) {
+#pragma unroll
+    for (int k = 0; k < S::KLOADS; ++k) {
+      const int idx = tid + 256 * k;
+      const int tk = idx / CR, ch = idx % CR;
+      kr[k] = *reinterpret_cast<const u32x4*>((const char*)p.k_cache + row_addr(t0 + tk) + ch * 16);
+    }
+#pragma unroll
+    for (int k = 0; k < S::VLOADS; ++k) {
+      const int idx = tid + 256 * k;
+      if (idx < 16 * CR) {
+        const int ch = idx / 16, pr = idx % 16;   // pairs fastest: conflict-free transposes
+        va[k] = *reinterpret_cast<const u32x4*>((const char*)p.v_cache + row_addr(t0 + 2 * pr) + ch * 16);
+        vb[k] = *reinterpret_cast<const u32x4*>((const char*)p.v_cache + row_addr(t0 + 2 * pr + 1) + ch * 16);
+      }
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int k = 0; k < S::KLOADS; ++k) {
+      const int idx = tid + 256 * k;
+      const int tk = idx / CR, ch = idx % CR;
+      *reinterpret_cast<u32x4*>(ldsK + tk * S::KSTRIDE + ch * 16) = kr[k];
+    }
+#pragma unroll
+    for (int k = 0; k < S::VLOADS; ++k) {
+      const int idx = tid + 256 * k;
+      if (idx < 16 * CR) {
+        const int ch = idx / 16, pr = idx % 16;
+        const int sl = slot_of(2 * pr);           // even; token 2 pr + 1 is the next slot
+        if constexpr (DT == kF32) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            *reinterpret_cast<u32x2*>(ldsV + (ch * 4 + e) * S::VSTRIDE + sl * 4) = u32x2{va[k][e], vb[k][e]};
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t lo = (va[k][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+            const uint32_t hi = (vb[k][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+            *reinterpret_cast<uint32_t*>(ldsV + (ch * 8 + e) * S::VSTRIDE + sl * 2) = lo | (hi << 16);
+          }
+        }
+      }
+    }
+  };
+
+  const float sl2 = p.scale_log2e;
+  const int ntiles = t_end > t_begin ? (t_end - t_begin + kTile - 1) / kTile : 0;
+  if (ntiles > 0) load_tile(t_begin);
+  for (int k = 0; k < ntiles; ++k) {
+    const int t0 = t_begin + k * kTile;
+    __syncthreads();  // the previous tile is no longer read
+    store_tile();
+    __syncthreads();
+    if (k + 1 < ntiles) load_tile(t0 + kTile);
+
+    // S^T = K Q^T for the two 16-token halves
+    f32x4 sc[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      sc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const char* krow = ldsK + (16 * h + col) * S::KSTRIDE;
+#pragma unroll
+      for (int c = 0; c < NKC; ++c) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(krow + chunk_of<DT, D>(c, grp) * 16);
+        if constexpr (DT == kBF16) {
+          sc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                          __builtin_bit_cast(bf16x8, qf[c]), sc[h], 0, 0, 0);
+        } else if constexpr (DT == kF16) {
+          sc[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                         __builtin_bit_cast(f16x8, qf[c]), sc[h], 0, 0, 0);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            sc[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[e]), __uint_as_float(qf[c][e]),
+                                                         sc[h], 0, 0, 0);
+        }
+      }
+    }
+    // online softmax: token t0 + 16 h + 4 grp + i of row col
+    float sv[8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + 16 * h + 4 * grp + i;
+        sv[4 * h + i] = (t <= pos && t < t_end) ? sc[h][i] * sl2 : -__builtin_inff();
+      }
+    float mx = sv[0];
+#pragma unroll
+    for (int u = 1; u < 8; ++u) mx = fmaxf(mx, sv[u]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mn = fmaxf(m, mx);
+    const float alpha = fast_exp2(m - mn);
+    m = mn;
+    float pr[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) pr[u] = fast_exp2(sv[u] - mn);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[j] *= alpha;
+
+    if constexpr (DT == kF32) {
+      l = l * alpha + (((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7])));
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const char* vrow = ldsV + (16 * j + col) * S::VSTRIDE + grp * 32;
+        const u32x4 a0 = *reinterpret_cast<const u32x4*>(vrow);
+        const u32x4 a1 = *reinterpret_cast<const u32x4*>(vrow + 16);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a0[u]), pr[u], acc[j], 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a1[u]), pr[4 + u], acc[j], 0, 0, 0);
+      }
+    } else {
+      // P in the storage type; for bf16 (8 significant bits) as a sum of two bf16
+      // values, the second the rounding error of the first, which carries about 16
+      // significant bits through two products with the same V fragment
+      uint32_t pw[4], pw_lo[4];
+      float ps = 0.f;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint16_t a = to_store<DT>(pr[2 * u]), b = to_store<DT>(pr[2 * u + 1]);
+        const float fa = from_store<DT>(a), fb = from_store<DT>(b);
+        pw[u] = (uint32_t)a | ((uint32_t)b << 16);
+        if constexpr (DT == kBF16) {
+          const uint16_t a2 = to_store<DT>(pr[2 * u] - fa), b2 = to_store<DT>(pr[2 * u + 1] - fb);
+          pw_lo[u] = (uint32_t)a2 | ((uint32_t)b2 << 16);
+          ps += (fa + from_store<DT>(a2)) + (fb + from_store<DT>(b2));
+        } else {
+          ps += fa + fb;
+        }
+      }
+      l = l * alpha + ps;
+      const u32x4 pb = u32x4{pw[0], pw[1], pw[2], pw[3]};
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(ldsV + (16 * j + col) * S::VSTRIDE + grp * 16);
+        if constexpr (DT == kBF16) {
+          const u32x4 pb_lo = u32x4{pw_lo[0], pw_lo[1], pw_lo[2], pw_lo[3]};
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                           __builtin_bit_cast(bf16x8, pb), acc[j], 0, 0, 0);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                           __builtin_bit_cast(bf16x8, pb_lo), acc[j], 0, 0, 0);
+        } else {
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                          __builtin_bit_cast(f16x8, pb), acc[j], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // the row's sum over its four lanes; lane (grp, col) holds head_dim 16 j + 4 grp + i
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  if (!row_ok) return;
+  if (p.parts == 1) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      store4<DT>((char*)p.out + out_row * S::ROWB + (16 * j + 4 * grp) * EB, acc[j] * inv);
+  } else {
+    const size_t slot = out_row * p.parts + it.part;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      *reinterpret_cast<f32x4*>(p.ws_acc + slot * D + 16 * j + 4 * grp) = acc[j];
+    if (grp == 0) *reinterpret_cast<u32x2*>(p.ws_ml + slot * 2) = u32x2{__float_as_uint(m), __float_as_uint(l)};
+  }
+}
+
+// Merge the partitions of every (query row, head), in partition order:
+//   M = max_p m_p,  out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
+// One wave per (row, head); lane i handles head_dim elements i, i + 64.
+template <int DT, int D>
+__global__ __launch_bounds__(256) void multi_query_merge_kernel(MultiQueryParams p) {
+  const long long rh = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (rh >= (long long)p.total_q * p.num_heads) return;
+  const int lane = threadIdx.x & 63;
+  const float* ml = p.ws_ml + (size_t)rh * p.parts * 2;
+  float M = kNegBig;
+  for (int q = 0; q < p.parts; ++q) M = fmaxf(M, ml[2 * q]);
+  constexpr int PER = D / 64;
+  float o[PER] = {};
+  float lsum = 0.f;
+  for (int q = 0; q < p.parts; ++q) {
+    const float w = fast_exp2(ml[2 * q] - M);
+    lsum += w * ml[2 * q + 1];
+    const float* a = p.ws_acc + ((size_t)rh * p.parts + q) * D;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) o[e] += w * a[lane + 64 * e];
+  }
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  constexpr int EB = DT == kF32 ? 4 : 2;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    char* dst = (char*)p.out + (size_t)rh * D * EB + (size_t)(lane + 64 * e) * EB;
+    if constexpr (DT == kF32) *reinterpret_cast<float*>(dst) = o[e] * inv;
+    else *reinterpret_cast<uint16_t*>(dst) = to_store<DT>(o[e] * inv);
+  }
+}
+
+template <int DT>
+bool pick_dt(int head_dim, const void** main, const void** merge) {
+  if (head_dim == 64) {
+    *main = reinterpret_cast<const void*>(&multi_query_kernel<DT, 64>);
+    *merge = reinterpret_cast<const void*>(&multi_query_merge_kernel<DT, 64>);
+    return true;
+  }
+  if (head_dim == 128) {
+    *main = reinterpret_cast<const void*>(&multi_query_kernel<DT, 128>);
+    *merge = reinterpret_cast<const void*>(&multi_query_merge_kernel<DT, 128>);
+    return true;
+  }
+  return false;
+}
+
+}  // namespace
+
+bool multi_query_kernels(int dtype, int head_dim, const void** main, const void** merge) {
+  switch (dtype) {
+    case kF32: return pick_dt<kF32>(head_dim, main, merge);
+    case kF16: return pick_dt<kF16>(head_dim, main, merge);
+    case kBF16: return pick_dt<kBF16>(head_dim, main, merge);
+    default: return false;
+  }
+}
+
+}  // namespace pagedkv

@@ -54,7 +54,7 @@ def test_binding_names_match_the_abi(pk):
 
 
 def test_version(pk):
-    assert pk.pa_version() == 4
+    assert pk.pa_version() == 5
 
 
 @pytest.mark.parametrize("N,H,HKV,D,L", [(256, 32, 8, 128, 4096), (32, 64, 8, 128, 32768),
@@ -136,3 +136,52 @@ def test_binding_rejects_cpu_tensors(pk):
         pk.pa_decode(q, torch.zeros(2, 16, 4, 64), torch.zeros(2, 16, 4, 64),
                      torch.zeros(1, 1, dtype=torch.int32), torch.ones(1, dtype=torch.int32), 4,
                      0.125, q, max_seq_len=1)
+
+
+@pytest.mark.parametrize("N,TQ,H,HKV,D,MQ,L", [(256, 1024, 32, 8, 128, 4, 4096), (16, 8192, 32, 8, 128, 512, 4096),
+                                              (1, 4, 64, 8, 128, 4, 32768), (3, 20, 8, 2, 64, 9, 300),
+                                              (2, 2, 4, 4, 64, 1, 0)])
+def test_multi_query_workspace_formula(pk, N, TQ, H, HKV, D, MQ, L):
+    # 64 query rows per workgroup (64 // group query tokens); about 1024 workgroups wanted,
+    # partitions of >= 256 tokens, at most 64; with one partition nothing is needed,
+    # else (m, l) and head_dim floats per row, head and partition
+    g = H // HKV
+    tq = max(1, 64 // g)
+    items = N * HKV * (-(-MQ // tq))
+    parts = max(1, min(-(-1024 // items), -(-L // 256), 64)) if items and L else 1
+    up = lambda x: -(-x // 256) * 256
+    want = 0 if parts == 1 else up(TQ * H * parts * 2 * 4) + TQ * H * parts * D * 4
+    assert pk.pa_multi_query_workspace_size(N, TQ, H, HKV, D, MQ, L) == want
+
+
+def call_mq(pk, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, lens=FAKE, qs=FAKE, N=1, TQ=4, H=64, HKV=8, D=128,
+             BS=16, NB=4000, MB=2048, MQ=4, L=32768, scale=0.088, dt=2, out=FAKE, ws=FAKE, wsb=0,
+             stream=None)
+    a.update(over)
+    return pk.lib().pa_multi_query(a["q"], a["k"], a["v"], a["bt"], a["lens"], a["qs"], a["N"], a["TQ"],
+                                   a["H"], a["HKV"], a["D"], a["BS"], a["NB"], a["MB"], a["MQ"], a["L"],
+                                   a["scale"], a["dt"], a["out"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status,words", [
+    (dict(D=96), 2, "head_dim"),
+    (dict(H=9), 1, "multiple"),
+    (dict(dt=7), 1, "dtype"),
+    (dict(L=32769), 1, "max_seq_len"),
+    (dict(MQ=8, L=6, MB=1), 1, "max_q_len"),
+    (dict(qs=None), 1, "null"),
+    (dict(out=FAKE + 4), 1, "aligned"),
+    (dict(scale=float("inf")), 1, "finite"),
+    (dict(wsb=16), 3, "workspace"),
+    (dict(ws=None, wsb=1 << 30), 3, "workspace"),
+    (dict(BS=0), 1, "block_size"),
+])
+def test_multi_query_rejects_host_visible_errors(pk, over, status, words):
+    assert call_mq(pk, **over) == status
+    assert words in pk.pa_last_error()
+
+
+def test_multi_query_with_no_queries_is_a_no_op(pk):
+    assert call_mq(pk, N=0, q=None, out=None) == 0
+    assert call_mq(pk, TQ=0, MQ=0, q=None, out=None) == 0

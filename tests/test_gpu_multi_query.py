@@ -1,0 +1,163 @@
+"""GPU parity of pa_multi_query (several causal queries per sequence) against the oracle.
+
+Every batch's query tokens first reach the cache through pa_write_kv, as in a
+serving step; the oracle applies the same write and computes each query row's
+attention over the sequence's tokens up to its own position, in float64.
+Tolerances are those of pa_decode (max-abs 1e-5 fp32, 4e-3 fp16, 8e-3 bf16).
+Pools are NaN wherever no token lives, so any read past a row's causal limit,
+a sequence end or a table's used entries poisons the output.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from workloads import as_numpy
+from _gpu import TOL, assert_close, bits, log, pk, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    pk()
+
+
+def run_gpu(b, d=None, max_q_len=None):
+    m = pk()
+    d = d or to_dev(b)
+    if d.slots is not None:
+        m.pa_write_kv(d.new_k, d.new_v, d.slots, d.kc, d.vc)
+    qs = b.q_start.cuda()
+    out = torch.empty_like(d.q)
+    m.pa_multi_query(d.q, d.kc, d.vc, d.bt, d.lens, qs, b.num_kv_heads, b.scale, out,
+                     max_q_len=b.max_q_len if max_q_len is None else max_q_len,
+                     max_seq_len=b.max_seq_len)
+    torch.cuda.synchronize()
+    return out, d
+
+
+def written(b):
+    if b.slot_mapping is None:
+        return as_numpy(b.k_cache), as_numpy(b.v_cache)
+    return oracle.write_kv(as_numpy(b.new_k), as_numpy(b.new_v), as_numpy(b.slot_mapping),
+                           as_numpy(b.k_cache), as_numpy(b.v_cache))
+
+
+def run_oracle(b):
+    kc, vc = written(b)
+    return oracle.paged_multi_query(as_numpy(b.q), kc, vc, as_numpy(b.block_tables),
+                                    as_numpy(b.seq_lens), as_numpy(b.q_start), b.scale, b.dtype)
+
+
+def batch(seed, dtype, lens, queries, Hq, Hkv, D, B, extra=4):
+    g = torch.Generator().manual_seed(seed)
+    return workloads._paged(name=f"mq{seed}", dtype=dtype, lens=lens, Hq=Hq, Hkv=Hkv, D=D, B=B,
+                            num_blocks=sum(-(-L // B) for L in lens) + extra, gen=g, queries=queries)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_small_batch(dtype):
+    b = workloads.multi_query_small(dtype=dtype)
+    log(f"multi_query_small {dtype}")
+    out, _ = run_gpu(b)
+    assert_close(out.float().cpu().double().numpy(), run_oracle(b), dtype, "small")
+
+
+SWEEP = [  # dtype, D, B, Hq, Hkv, lens, queries
+    ("bf16", 128, 16, 32, 8, [1, 40, 97, 300, 64], [1, 40, 5, 130, 64]),
+    ("f16", 128, 8, 8, 8, [33, 100, 17], [33, 7, 16]),
+    ("bf16", 64, 32, 16, 1, [250, 3, 64], [70, 3, 1]),
+    ("f16", 64, 16, 12, 3, [129, 31], [65, 31]),
+    ("bf16", 128, 5, 64, 8, [77, 200], [9, 8]),
+    ("f32", 128, 16, 8, 2, [45, 90], [20, 90]),
+    ("bf16", 128, 16, 40, 40, [18, 260], [18, 33]),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SWEEP)))
+def test_shape_sweep(case):
+    dt, D, B, Hq, Hkv, lens, qn = SWEEP[case]
+    b = batch(100 + case, dt, lens, qn, Hq, Hkv, D, B)
+    log(f"sweep {SWEEP[case]}")
+    out, _ = run_gpu(b)
+    assert_close(out.float().cpu().double().numpy(), run_oracle(b), dt, f"sweep {case}")
+
+
+def test_long_context_few_queries_uses_partitions():
+    # one sequence, 3 queries, 5000 tokens: few work items, so the context is split
+    # into partitions and merged by the second kernel
+    b = batch(7, "bf16", [5000], [3], 8, 8, 128, 16)
+    m = pk()
+    assert m.pa_multi_query_workspace_size(1, 3, 8, 8, 128, 3, 5000) > 0
+    log("partitioned long context")
+    out, _ = run_gpu(b)
+    assert_close(out.float().cpu().double().numpy(), run_oracle(b), "bf16", "partitions")
+
+
+def test_one_query_per_sequence_matches_decode():
+    b = batch(9, "bf16", [1, 17, 300, 1000, 64, 2], [1] * 6, 32, 8, 128, 16)
+    m = pk()
+    log("one query per sequence vs pa_decode")
+    out, d = run_gpu(b)
+    dec = torch.empty_like(d.q)
+    m.pa_decode(d.q, d.kc, d.vc, d.bt, d.lens, b.num_kv_heads, b.scale, dec, max_seq_len=b.max_seq_len)
+    torch.cuda.synchronize()
+    ref = run_oracle(b)
+    assert_close(out.float().cpu().double().numpy(), ref, "bf16", "mq")
+    assert_close(dec.float().cpu().double().numpy(), ref, "bf16", "decode")
+
+
+def test_max_q_len_larger_than_needed_and_deterministic():
+    b = batch(11, "f16", [50, 120, 7], [10, 120, 7], 16, 4, 128, 16)
+    log("max_q_len slack, determinism")
+    out1, d = run_gpu(b, max_q_len=120)
+    out2, _ = run_gpu(b, d=d, max_q_len=120)
+    assert torch.equal(bits(out1.cpu()), bits(out2.cpu()))
+    assert_close(out1.float().cpu().double().numpy(), run_oracle(b), "f16", "slack")
+
+
+@pytest.mark.parametrize("name,make", [
+    ("spec", lambda: workloads.llama3_8b_spec(num_seqs=12, num_blocks=5000)),
+    ("chunk", lambda: workloads.llama3_8b_chunk(num_seqs=2, chunk=96, max_prior=500)),
+])
+def test_workloads_reduced(name, make):
+    b = make()
+    log(f"{name} reduced")
+    out, _ = run_gpu(b)
+    assert_close(out.float().cpu().double().numpy(), run_oracle(b), "bf16", name)
+
+
+def sampled_rows(b, rows):
+    """Oracle output for sampled query rows only (full-size batches)."""
+    kc, vc = written(b)
+    qs = b.q_start.tolist()
+    lens = b.seq_lens.tolist()
+    bt = as_numpy(b.block_tables)
+    res = []
+    for r in rows:
+        s = int(np.searchsorted(qs, r, side="right") - 1)
+        n, L = qs[s + 1] - qs[s], lens[s]
+        pos = L - n + (r - qs[s])
+        K = oracle.to_f64(oracle.gather(kc, bt[s], pos + 1, b.block_size), b.dtype)
+        V = oracle.to_f64(oracle.gather(vc, bt[s], pos + 1, b.block_size), b.dtype)
+        res.append(oracle.attend(oracle.to_f64(as_numpy(b.q[r]), b.dtype), K, V, b.scale))
+    return np.stack(res)
+
+
+@pytest.mark.parametrize("name", ["llama3_8b_spec", "llama3_8b_chunk"])
+def test_full_size_workloads_on_sampled_rows(name):
+    b = workloads.WORKLOADS[name]()
+    log(f"{name} full size")
+    out, _ = run_gpu(b)
+    got = out.float().cpu().double().numpy()
+    assert np.isfinite(got).all()
+    rng = np.random.default_rng(0)
+    qs = b.q_start.tolist()
+    rows = sorted(set(rng.choice(b.q.shape[0], 48, replace=False).tolist()
+                      + [0, b.q.shape[0] - 1] + [qs[s] for s in range(0, b.num_seqs, 7)]))
+    assert_close(got[rows], sampled_rows(b, rows), "bf16", name)
