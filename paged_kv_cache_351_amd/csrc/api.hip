@@ -325,6 +325,7 @@ namespace {
 // 256 tokens, at most 64 of them.
 struct MQPlan {
   int tq = 1, qblocks = 0, parts = 1, part_len = 32;
+  bool split = false;          // every block has at most 16 rows: the waves split the context
   long long items = 0;
   size_t ml_bytes = 0, total = 0;
 };
@@ -333,10 +334,12 @@ constexpr int kMQMaxParts = 64;
 constexpr long long kMQTargetItems = 1024;
 
 MQPlan mq_plan(int num_seqs, int total_q, int num_heads, int num_kv_heads, int head_dim,
-               int max_q_len, int max_seq_len) {
+               int max_q_len, int max_seq_len, int dtype) {
   MQPlan pl;
   const int group = num_heads / num_kv_heads;
   pl.tq = group >= 64 ? 1 : 64 / group;
+  pl.split = dtype != PA_F32 && max_q_len >= 1 && (long long)max_q_len * group <= 16;
+  if (pl.split) pl.tq = 16 / group;
   pl.qblocks = max_q_len > 0 ? (max_q_len + pl.tq - 1) / pl.tq : 0;
   pl.items = (long long)num_seqs * num_kv_heads * pl.qblocks;
   if (pl.items > 0 && max_seq_len > 0) {
@@ -369,7 +372,9 @@ size_t pa_multi_query_workspace_size(int num_seqs, int total_q, int num_heads, i
                                      int head_dim, int max_q_len, int max_seq_len) {
   if (!mq_shapes_ok(num_seqs, total_q, num_heads, num_kv_heads, head_dim, max_q_len, max_seq_len))
     return 0;
-  return mq_plan(num_seqs, total_q, num_heads, num_kv_heads, head_dim, max_q_len, max_seq_len).total;
+  // the workspace does not depend on the element type (the split variant has one
+  // query block whenever it applies, like the other)
+  return mq_plan(num_seqs, total_q, num_heads, num_kv_heads, head_dim, max_q_len, max_seq_len, PA_BF16).total;
 }
 
 pa_status pa_multi_query(const void* q, const void* k_cache, const void* v_cache,
@@ -407,7 +412,8 @@ pa_status pa_multi_query(const void* q, const void* k_cache, const void* v_cache
     return fail(PA_ERR_INVALID, "pa_multi_query: null pointer argument");
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
     return fail(PA_ERR_INVALID, "pa_multi_query: q, caches and out must be 16-byte aligned");
-  const MQPlan pl = mq_plan(num_seqs, total_q, num_heads, num_kv_heads, head_dim, max_q_len, max_seq_len);
+  const MQPlan pl = mq_plan(num_seqs, total_q, num_heads, num_kv_heads, head_dim, max_q_len, max_seq_len,
+                            (int)dtype);
   if (pl.items * pl.parts + 8 >= (1LL << 31))
     return fail(PA_ERR_UNSUPPORTED, "pa_multi_query: more than 2^31 workgroups");
   if (pl.total > 0 && (!workspace || workspace_bytes < pl.total))
@@ -440,7 +446,7 @@ pa_status pa_multi_query(const void* q, const void* k_cache, const void* v_cache
   }
   const void* kmain = nullptr;
   const void* kmerge = nullptr;
-  if (!multi_query_kernels((int)dtype, head_dim, &kmain, &kmerge))
+  if (!multi_query_kernels((int)dtype, head_dim, pl.split, &kmain, &kmerge))
     return fail(PA_ERR_UNSUPPORTED, "pa_multi_query: no kernel for this dtype and head_dim");
   MultiQueryParams mp;
   mp.q = q;

@@ -76,7 +76,8 @@ struct MultiQueryParams {
   int max_blocks_per_seq;
   int max_q_len;
   int max_seq_len;
-  int tq;                      // query tokens per workgroup (64 rows / group)
+  int tq;                      // query tokens per workgroup: 64 rows / group, or
+                               // 16 / group when all four waves share 16 rows
   int qblocks;                 // query blocks per (sequence, KV head): ceil(max_q_len / tq)
   int parts;                   // context partitions; 1 = no merge step
   int part_len;                // tokens per partition, a multiple of the 32-token tile
@@ -84,8 +85,9 @@ struct MultiQueryParams {
   float scale_log2e;
 };
 
-// The multi-query and partition-merge kernels for one element type and head_dim.
-bool multi_query_kernels(int dtype, int head_dim, const void** main, const void** merge);
+// The multi-query and partition-merge kernels for one element type and head_dim;
+// `split` picks the variant for blocks of at most 16 query rows (16-bit types).
+bool multi_query_kernels(int dtype, int head_dim, bool split, const void** main, const void** merge);
 
 // Message returned by pa_last_error() on the calling thread.
 void set_last_error(const char* msg);

@@ -135,13 +135,21 @@ __device__ __forceinline__ bool item_of(const MultiQueryParams& p, Item& it) {
   return it.s < p.num_seqs;
 }
 
-template <int DT, int D>
+// SPLIT = false: the four waves own 16 rows each of a 64-row query block and
+// share every K/V tile through LDS (prefill-sized blocks).
+// SPLIT = true (16-bit types, at most 16 rows per block): the four waves work on
+// the same 16 rows and take every fourth tile of the partition each, K straight
+// from HBM into registers in the matrix-core layout and V through a
+// wave-private LDS region, with no workgroup barrier in the loop; their four
+// partial results are merged through LDS at the end.
+template <int DT, int D, bool SPLIT>
 __global__ __launch_bounds__(256) void multi_query_kernel(MultiQueryParams p) {
   using S = Shape<DT, D>;
   constexpr int EB = S::EB, CR = S::CR, NKC = S::NKC, NJ = S::NJ;
-  __shared__ __attribute__((aligned(16))) char lds[S::LDS];
-  char* ldsK = lds;
-  char* ldsV = lds + S::KBYTES;
+  constexpr int VREG = D * S::VSTRIDE;                     // one transposed V tile
+  constexpr int LDS_BYTES = SPLIT ? 4 * VREG : S::LDS;
+  static_assert(!SPLIT || (DT != kF32 && 4 * 16 * (D + 2) * 4 <= LDS_BYTES), "split merge space");
+  __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
 
   Item it;
   if (!item_of(p, it)) return;
@@ -149,6 +157,8 @@ __global__ __launch_bounds__(256) void multi_query_kernel(MultiQueryParams p) {
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int g = p.group, Hq = p.num_heads, Hkv = p.num_kv_heads;
+  char* ldsK = lds;
+  char* ldsV = SPLIT ? lds + wave * VREG : lds + S::KBYTES;
 
   // the sequence's query range and length, clamped so that no access leaves the arrays
   int L = p.seq_lens[it.s];
@@ -161,12 +171,13 @@ __global__ __launch_bounds__(256) void multi_query_kernel(MultiQueryParams p) {
   if (tok0 >= n) return;
   const int tok1 = min(n, tok0 + p.tq);            // one past the last
   const int pos_hi = L - n + tok1 - 1;             // last query position of the block
+  const int pos_lo = L - n + tok0;                 // first query position of the block
   const int kv_end = min(L, pos_hi + 1);
   const int t_begin = it.part * p.part_len;
   const int t_end = min(kv_end, t_begin + p.part_len);
 
-  // this lane's query row (row col of the wave)
-  const int rloc = wave * 16 + col;
+  // this lane's query row (row col of the wave's 16)
+  const int rloc = SPLIT ? col : wave * 16 + col;
   const int qtok = tok0 + rloc / g;
   const int qh = rloc % g;
   const bool row_ok = rloc < p.tq * g && qtok < tok1;
@@ -201,18 +212,15 @@ __global__ __launch_bounds__(256) void multi_query_kernel(MultiQueryParams p) {
     return ((size_t)b * B + t % B) * slot_bytes + kv_off;
   };
 
-  u32x4 kr[S::KLOADS];
-  u32x4 va[S::VLOADS], vb[S::VLOADS];
-  auto load_tile = [&](int t0) {
+  // V rows of a tile as token pairs: `lanes` lanes take pair-chunks idx = me + lanes k
+  constexpr int VLANES = SPLIT ? 64 : 256;
+  constexpr int VL = (16 * CR + VLANES - 1) / VLANES;
+  const int vme = SPLIT ? lane : tid;
+  u32x4 va[VL], vb[VL];
+  auto load_v = [&](int t0) {
 #pragma unroll
-    for (int k = 0; k < S::KLOADS; ++k) {
-      const int idx = tid + 256 * k;
-      const int tk = idx / CR, ch = idx % CR;
-      kr[k] = *reinterpret_cast<const u32x4*>((const char*)p.k_cache + row_addr(t0 + tk) + ch * 16);
-    }
-#pragma unroll
-    for (int k = 0; k < S::VLOADS; ++k) {
-      const int idx = tid + 256 * k;
+    for (int k = 0; k < VL; ++k) {
+      const int idx = vme + VLANES * k;
       if (idx < 16 * CR) {
         const int ch = idx / 16, pr = idx % 16;   // pairs fastest: conflict-free transposes
         va[k] = *reinterpret_cast<const u32x4*>((const char*)p.v_cache + row_addr(t0 + 2 * pr) + ch * 16);
@@ -220,16 +228,10 @@ __global__ __launch_bounds__(256) void multi_query_kernel(MultiQueryParams p) {
       }
     }
   };
-  auto store_tile = [&]() {
+  auto store_v = [&]() {
 #pragma unroll
-    for (int k = 0; k < S::KLOADS; ++k) {
-      const int idx = tid + 256 * k;
-      const int tk = idx / CR, ch = idx % CR;
-      *reinterpret_cast<u32x4*>(ldsK + tk * S::KSTRIDE + ch * 16) = kr[k];
-    }
-#pragma unroll
-    for (int k = 0; k < S::VLOADS; ++k) {
-      const int idx = tid + 256 * k;
+    for (int k = 0; k < VL; ++k) {
+      const int idx = vme + VLANES * k;
       if (idx < 16 * CR) {
         const int ch = idx / 16, pr = idx % 16;
         const int sl = slot_of(2 * pr);           // even; token 2 pr + 1 is the next slot
@@ -248,49 +250,110 @@ __global__ __launch_bounds__(256) void multi_query_kernel(MultiQueryParams p) {
       }
     }
   };
+  // K: through LDS (shared tiles) or straight into the matrix-core layout (split)
+  constexpr int KL = SPLIT ? 2 * NKC : S::KLOADS;
+  u32x4 kr[KL];
+  auto load_k = [&](int t0) {
+    if constexpr (SPLIT) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const char* row = (const char*)p.k_cache + row_addr(t0 + 16 * h + col);
+#pragma unroll
+        for (int c = 0; c < NKC; ++c)
+          kr[h * NKC + c] = *reinterpret_cast<const u32x4*>(row + chunk_of<DT, D>(c, grp) * 16);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < KL; ++k) {
+        const int idx = tid + 256 * k;
+        const int tk = idx / CR, ch = idx % CR;
+        kr[k] = *reinterpret_cast<const u32x4*>((const char*)p.k_cache + row_addr(t0 + tk) + ch * 16);
+      }
+    }
+  };
+  auto store_k = [&]() {
+    if constexpr (!SPLIT) {
+#pragma unroll
+      for (int k = 0; k < KL; ++k) {
+        const int idx = tid + 256 * k;
+        const int tk = idx / CR, ch = idx % CR;
+        *reinterpret_cast<u32x4*>(ldsK + tk * S::KSTRIDE + ch * 16) = kr[k];
+      }
+    }
+  };
 
   const float sl2 = p.scale_log2e;
   const int ntiles = t_end > t_begin ? (t_end - t_begin + kTile - 1) / kTile : 0;
-  if (ntiles > 0) load_tile(t_begin);
-  for (int k = 0; k < ntiles; ++k) {
+  const int k0 = SPLIT ? wave : 0, kstep = SPLIT ? 4 : 1;
+  if (k0 < ntiles) {
+    load_k(t_begin + k0 * kTile);
+    load_v(t_begin + k0 * kTile);
+  }
+  for (int k = k0; k < ntiles; k += kstep) {
     const int t0 = t_begin + k * kTile;
-    __syncthreads();  // the previous tile is no longer read
-    store_tile();
-    __syncthreads();
-    if (k + 1 < ntiles) load_tile(t0 + kTile);
-
     // S^T = K Q^T for the two 16-token halves
     f32x4 sc[2];
+    auto qk = [&](int h, int c, u32x4 a) {
+      if constexpr (DT == kBF16) {
+        sc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                        __builtin_bit_cast(bf16x8, qf[c]), sc[h], 0, 0, 0);
+      } else if constexpr (DT == kF16) {
+        sc[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                       __builtin_bit_cast(f16x8, qf[c]), sc[h], 0, 0, 0);
+      } else {
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      sc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const char* krow = ldsK + (16 * h + col) * S::KSTRIDE;
+        for (int e = 0; e < 4; ++e)
+          sc[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[e]), __uint_as_float(qf[c][e]),
+                                                       sc[h], 0, 0, 0);
+      }
+    };
+    sc[0] = sc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (SPLIT) {
+      // this tile's K is in registers: stage its V and fetch the wave's next V,
+      // multiply, then fetch the next K (no second copy of the K registers)
+      store_v();
+      const bool more = k + kstep < ntiles;
+      if (more) load_v(t0 + kstep * kTile);
 #pragma unroll
-      for (int c = 0; c < NKC; ++c) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(krow + chunk_of<DT, D>(c, grp) * 16);
-        if constexpr (DT == kBF16) {
-          sc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                          __builtin_bit_cast(bf16x8, qf[c]), sc[h], 0, 0, 0);
-        } else if constexpr (DT == kF16) {
-          sc[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
-                                                         __builtin_bit_cast(f16x8, qf[c]), sc[h], 0, 0, 0);
-        } else {
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            sc[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[e]), __uint_as_float(qf[c][e]),
-                                                         sc[h], 0, 0, 0);
-        }
+        for (int c = 0; c < NKC; ++c) qk(h, c, kr[h * NKC + c]);
+      if (more) load_k(t0 + kstep * kTile);
+      __builtin_amdgcn_wave_barrier();   // V stores above are read by other lanes below
+    } else {
+      __syncthreads();  // the previous tile is no longer read
+      store_k();
+      store_v();
+      __syncthreads();
+      if (k + 1 < ntiles) {
+        load_k(t0 + kTile);
+        load_v(t0 + kTile);
+      }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const char* krow = ldsK + (16 * h + col) * S::KSTRIDE;
+#pragma unroll
+        for (int c = 0; c < NKC; ++c)
+          qk(h, c, *reinterpret_cast<const u32x4*>(krow + chunk_of<DT, D>(c, grp) * 16));
       }
     }
-    // online softmax: token t0 + 16 h + 4 grp + i of row col
+    // online softmax: token t0 + 16 h + 4 grp + i of row col; tiles that end before
+    // the block's first query position and the partition's end need no mask
     float sv[8];
+    if (t0 + kTile - 1 <= pos_lo && t0 + kTile <= t_end) {
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = t0 + 16 * h + 4 * grp + i;
-        sv[4 * h + i] = (t <= pos && t < t_end) ? sc[h][i] * sl2 : -__builtin_inff();
-      }
+        for (int i = 0; i < 4; ++i) sv[4 * h + i] = sc[h][i] * sl2;
+    } else {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = t0 + 16 * h + 4 * grp + i;
+          sv[4 * h + i] = (t <= pos && t < t_end) ? sc[h][i] * sl2 : -__builtin_inff();
+        }
+    }
     float mx = sv[0];
 #pragma unroll
     for (int u = 1; u < 8; ++u) mx = fmaxf(mx, sv[u]);
@@ -302,8 +365,10 @@ __global__ __launch_bounds__(256) void multi_query_kernel(MultiQueryParams p) {
     float pr[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) pr[u] = fast_exp2(sv[u] - mn);
+    if (__any(alpha != 1.0f)) {  // rescale only when some row's maximum moved
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) acc[j] *= alpha;
+      for (int j = 0; j < NJ; ++j) acc[j] *= alpha;
+    }
 
     if constexpr (DT == kF32) {
       l = l * alpha + (((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7])));
@@ -355,23 +420,67 @@ __global__ __launch_bounds__(256) void multi_query_kernel(MultiQueryParams p) {
         }
       }
     }
+    if constexpr (SPLIT) __builtin_amdgcn_wave_barrier();  // V reads above before the next stores
   }
 
   // the row's sum over its four lanes; lane (grp, col) holds head_dim 16 j + 4 grp + i
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
-  if (!row_ok) return;
-  if (p.parts == 1) {
-    const float inv = l > 0.f ? 1.f / l : 0.f;
+  if constexpr (SPLIT) {
+    // merge the four waves' results for the same 16 rows: wave w's (m, l) and
+    // accumulator go to LDS region w; then wave w combines head_dim blocks j = w (mod 4)
+    __syncthreads();   // every wave is done with its V region
+    float* mine = reinterpret_cast<float*>(lds) + wave * 16 * (D + 2);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      store4<DT>((char*)p.out + out_row * S::ROWB + (16 * j + 4 * grp) * EB, acc[j] * inv);
+    for (int j = 0; j < NJ; ++j) *reinterpret_cast<f32x4*>(mine + col * D + 16 * j + 4 * grp) = acc[j];
+    if (grp == 0) {
+      mine[16 * D + 2 * col] = m;
+      mine[16 * D + 2 * col + 1] = l;
+    }
+    __syncthreads();
+    if (!row_ok) return;
+    const float* part = reinterpret_cast<const float*>(lds);
+    float M = kNegBig;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, part[w * 16 * (D + 2) + 16 * D + 2 * col]);
+    float wt[4], Lsum = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float* src = part + w * 16 * (D + 2) + 16 * D + 2 * col;
+      wt[w] = fast_exp2(src[0] - M);
+      Lsum += wt[w] * src[1];
+    }
+    const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
+    for (int j = wave; j < NJ; j += 4) {
+      f32x4 o = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        o += wt[w] * *reinterpret_cast<const f32x4*>(part + w * 16 * (D + 2) + col * D + 16 * j + 4 * grp);
+      if (p.parts == 1) {
+        store4<DT>((char*)p.out + out_row * S::ROWB + (16 * j + 4 * grp) * EB, o * inv);
+      } else {
+        const size_t slot = out_row * p.parts + it.part;
+        *reinterpret_cast<f32x4*>(p.ws_acc + slot * D + 16 * j + 4 * grp) = o;
+      }
+    }
+    if (p.parts > 1 && wave == 0 && grp == 0) {
+      const size_t slot = out_row * p.parts + it.part;
+      *reinterpret_cast<u32x2*>(p.ws_ml + slot * 2) = u32x2{__float_as_uint(M), __float_as_uint(Lsum)};
+    }
   } else {
-    const size_t slot = out_row * p.parts + it.part;
+    if (!row_ok) return;
+    if (p.parts == 1) {
+      const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      *reinterpret_cast<f32x4*>(p.ws_acc + slot * D + 16 * j + 4 * grp) = acc[j];
-    if (grp == 0) *reinterpret_cast<u32x2*>(p.ws_ml + slot * 2) = u32x2{__float_as_uint(m), __float_as_uint(l)};
+      for (int j = 0; j < NJ; ++j)
+        store4<DT>((char*)p.out + out_row * S::ROWB + (16 * j + 4 * grp) * EB, acc[j] * inv);
+    } else {
+      const size_t slot = out_row * p.parts + it.part;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        *reinterpret_cast<f32x4*>(p.ws_acc + slot * D + 16 * j + 4 * grp) = acc[j];
+      if (grp == 0) *reinterpret_cast<u32x2*>(p.ws_ml + slot * 2) = u32x2{__float_as_uint(m), __float_as_uint(l)};
+    }
   }
 }
 
@@ -406,16 +515,28 @@ __global__ __launch_bounds__(256) void multi_query_merge_kernel(MultiQueryParams
   }
 }
 
+template <int DT, int D>
+void pick_d(bool split, const void** main, const void** merge) {
+  if constexpr (DT != kF32) {
+    if (split) {
+      *main = reinterpret_cast<const void*>(&multi_query_kernel<DT, D, true>);
+      *merge = reinterpret_cast<const void*>(&multi_query_merge_kernel<DT, D>);
+      return;
+    }
+  }
+  *main = reinterpret_cast<const void*>(&multi_query_kernel<DT, D, false>);
+  *merge = reinterpret_cast<const void*>(&multi_query_merge_kernel<DT, D>);
+}
+
 template <int DT>
-bool pick_dt(int head_dim, const void** main, const void** merge) {
+bool pick_dt(int head_dim, bool split, const void** main, const void** merge) {
+  if (split && DT == kF32) return false;
   if (head_dim == 64) {
-    *main = reinterpret_cast<const void*>(&multi_query_kernel<DT, 64>);
-    *merge = reinterpret_cast<const void*>(&multi_query_merge_kernel<DT, 64>);
+    pick_d<DT, 64>(split, main, merge);
     return true;
   }
   if (head_dim == 128) {
-    *main = reinterpret_cast<const void*>(&multi_query_kernel<DT, 128>);
-    *merge = reinterpret_cast<const void*>(&multi_query_merge_kernel<DT, 128>);
+    pick_d<DT, 128>(split, main, merge);
     return true;
   }
   return false;
@@ -423,11 +544,11 @@ bool pick_dt(int head_dim, const void** main, const void** merge) {
 
 }  // namespace
 
-bool multi_query_kernels(int dtype, int head_dim, const void** main, const void** merge) {
+bool multi_query_kernels(int dtype, int head_dim, bool split, const void** main, const void** merge) {
   switch (dtype) {
-    case kF32: return pick_dt<kF32>(head_dim, main, merge);
-    case kF16: return pick_dt<kF16>(head_dim, main, merge);
-    case kBF16: return pick_dt<kBF16>(head_dim, main, merge);
+    case kF32: return pick_dt<kF32>(head_dim, split, main, merge);
+    case kF16: return pick_dt<kF16>(head_dim, split, main, merge);
+    case kBF16: return pick_dt<kBF16>(head_dim, split, main, merge);
     default: return false;
   }
 }

@@ -76,6 +76,11 @@ SWEEP = [  # dtype, D, B, Hq, Hkv, lens, queries
     ("bf16", 128, 5, 64, 8, [77, 200], [9, 8]),
     ("f32", 128, 16, 8, 2, [45, 90], [20, 90]),
     ("bf16", 128, 16, 40, 40, [18, 260], [18, 33]),
+    # at most 16 rows per (sequence, KV head): the four waves split the context
+    ("f16", 64, 16, 16, 8, [5, 300, 33], [5, 8, 1]),
+    ("bf16", 128, 8, 16, 1, [40, 1, 77], [1, 1, 1]),
+    ("bf16", 64, 32, 4, 4, [700, 16, 90], [16, 16, 2]),
+    ("bf16", 128, 16, 32, 8, [31, 64, 65, 200], [4, 4, 3, 4]),
 ]
 
 
