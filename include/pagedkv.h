@@ -211,6 +211,46 @@ pa_status pa_multi_query(const void* q, const void* k_cache, const void* v_cache
                          void* stream);
 
 /*
+ * Shared-prefix decode -- pa_decode's result, reading each shared prefix once.
+ * Parallel samples of one prompt (and beam candidates) point at the same
+ * physical blocks for the prompt ([PA-notes] §6.1, §6.2; [vLLM-what] "3）Prefix
+ * Caching"); pa_decode reads those blocks once per sample, this call once per
+ * group.  Sequences are listed group by group: group j is sequences
+ * group_start[j] .. group_start[j+1]-1, and the first prefix_lens[j] tokens of
+ * every member sit in the same physical blocks (the first
+ * ceil(prefix_lens[j] / block_size) table entries of all members are equal).
+ * Every member's remaining tokens are its own.  The output equals pa_decode's
+ * for the same q, tables and lengths (to rounding), per sequence:
+ *     out[s, h] = softmax_t(scale * q[s, h] . K_s[t]) V_s[t] over its L_s tokens.
+ *
+ *   group_start    device int32 [num_groups + 1]: 0 = group_start[0] <= ... <=
+ *                  group_start[num_groups] = num_seqs
+ *   prefix_lens    device int32 [num_groups], 0 <= prefix_lens[j] <= every
+ *                  member's length
+ *   max_group_size host bound on every group's size
+ *   other arguments as for pa_decode (block_size any positive value here)
+ *   workspace      pa_decode_shared_prefix_workspace_size(...) bytes (0 when no
+ *                  partition merge is needed); no zero-fill needed
+ *
+ * A group is processed in blocks of 16 / (num_heads / num_kv_heads) members
+ * (at most 16 query heads per KV head); each block reads the prefix once.
+ * float16 and bfloat16 only (PA_ERR_UNSUPPORTED for float32).  Index data that
+ * breaks the contract is clamped so that no access leaves the arrays, with
+ * unspecified results; PA_DEBUG_CHECK=1 rejects it, including tables that do
+ * not share the stated prefix.  Results are deterministic.
+ */
+size_t pa_decode_shared_prefix_workspace_size(int num_seqs, int num_groups, int num_heads,
+                                              int num_kv_heads, int head_dim, int max_group_size,
+                                              int max_seq_len);
+pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_tables, const int32_t* seq_lens,
+                                  const int32_t* group_start, const int32_t* prefix_lens,
+                                  int num_seqs, int num_groups, int num_heads, int num_kv_heads,
+                                  int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+                                  int max_group_size, int max_seq_len, float scale, pa_dtype dtype,
+                                  void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Swap blocks between two pools -- preemption ([PA-notes] §5 ③: when memory
  * runs short a request is suspended, its blocks freed or moved to CPU RAM, and
  * it is restored later through its block table).  For every (src, dst) row of

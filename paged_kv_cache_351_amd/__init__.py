@@ -60,6 +60,11 @@ def lib():
     L.pa_multi_query.restype = i32
     L.pa_multi_query.argtypes = [vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, i32,
                                  i32, f32, i32, vp, vp, sz, vp]
+    L.pa_decode_shared_prefix_workspace_size.restype = sz
+    L.pa_decode_shared_prefix_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    L.pa_decode_shared_prefix.restype = i32
+    L.pa_decode_shared_prefix.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32,
+                                          i32, i32, i32, i32, f32, i32, vp, vp, sz, vp]
     L.pa_swap_blocks.restype = i32
     L.pa_swap_blocks.argtypes = [vp, vp, i32, vp, vp, i32, vp, i32, i32, i32, i32, i32, vp]
     i64 = ctypes.c_int64
@@ -230,6 +235,56 @@ def pa_multi_query(q, k_cache, v_cache, block_tables, seq_lens, q_start, num_kv_
         num_seqs, total_q, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
         block_tables.shape[1], int(max_q_len), int(max_seq_len), float(scale), _DTYPE[q.dtype],
         _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
+    return out
+
+
+def pa_decode_shared_prefix_workspace_size(num_seqs, num_groups, num_heads, num_kv_heads, head_dim,
+                                           max_group_size, max_seq_len):
+    return int(lib().pa_decode_shared_prefix_workspace_size(
+        int(num_seqs), int(num_groups), int(num_heads), int(num_kv_heads), int(head_dim),
+        int(max_group_size), int(max_seq_len)))
+
+
+def pa_decode_shared_prefix(q, k_cache, v_cache, block_tables, seq_lens, group_start, prefix_lens,
+                            num_kv_heads, scale, out, *, max_group_size, max_seq_len, workspace=None,
+                            stream=None):
+    """pa_decode's result, reading every group's shared prefix once (include/pagedkv.h):
+    sequences group_start[j] .. group_start[j+1]-1 share the blocks of their first
+    prefix_lens[j] tokens.  group_start: int32 [G + 1] from 0 to num_seqs; prefix_lens:
+    int32 [G]; max_group_size / max_seq_len: host bounds (no device sync)."""
+    _dev("q", q, ndim=3)
+    if q.dtype not in _DTYPE:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev(name, t, q.dtype, 4)
+    if k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+    _dev("block_tables", block_tables, torch.int32, 2)
+    _dev("seq_lens", seq_lens, torch.int32, 1)
+    _dev("group_start", group_start, torch.int32, 1)
+    _dev("prefix_lens", prefix_lens, torch.int32, 1)
+    _dev("out", out, q.dtype)
+    num_seqs, num_heads, head_dim = q.shape
+    num_blocks, block_size, nkv, hd = k_cache.shape
+    num_groups = prefix_lens.shape[0]
+    if nkv != num_kv_heads or hd != head_dim:
+        raise ValueError(f"cache shape {tuple(k_cache.shape)} does not match num_kv_heads="
+                         f"{num_kv_heads}, head_dim={head_dim}")
+    if out.shape != q.shape or block_tables.shape[0] != num_seqs or seq_lens.shape[0] != num_seqs \
+            or group_start.shape[0] != num_groups + 1:
+        raise ValueError("q, out, block_tables, seq_lens, group_start and prefix_lens disagree")
+    need = pa_decode_shared_prefix_workspace_size(num_seqs, num_groups, num_heads, num_kv_heads,
+                                                  head_dim, max_group_size, max_seq_len)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _dev("workspace", workspace)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().pa_decode_shared_prefix(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens), _ptr(group_start),
+        _ptr(prefix_lens), num_seqs, num_groups, num_heads, num_kv_heads, head_dim, block_size,
+        num_blocks, block_tables.shape[1], int(max_group_size), int(max_seq_len), float(scale),
+        _DTYPE[q.dtype], _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
     return out
 
 
@@ -438,7 +493,8 @@ class BlockManager:
         return tables, lens
 
 
-__all__ = ["pa_decode", "pa_multi_query", "pa_multi_query_workspace_size", "pa_write_kv",
+__all__ = ["pa_decode", "pa_multi_query", "pa_multi_query_workspace_size", "pa_decode_shared_prefix",
+           "pa_decode_shared_prefix_workspace_size", "pa_write_kv",
            "pa_copy_blocks", "pa_swap_blocks", "pa_decode_workspace_size",
            "decode_workspace", "pa_last_error", "pa_version",
            "PagedKVError", "BlockManager", "lib", "LIB_PATH"]

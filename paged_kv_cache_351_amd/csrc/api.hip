@@ -191,7 +191,7 @@ bool to_host(std::vector<T>& dst, const void* src, size_t n, hipStream_t stream,
 
 extern "C" {
 
-int pa_version(void) { return 5; }
+int pa_version(void) { return 6; }
 
 const char* pa_last_error(void) { return g_err.c_str(); }
 
@@ -324,7 +324,7 @@ namespace {
 // query block, partition) items for about 1024 workgroups; partitions of at least
 // 256 tokens, at most 64 of them.
 struct MQPlan {
-  int tq = 1, qblocks = 0, parts = 1, part_len = 32;
+  int tq = 1, qblocks = 0, parts = 1;
   bool split = false;          // every block has at most 16 rows: the waves split the context
   long long items = 0;
   size_t ml_bytes = 0, total = 0;
@@ -349,8 +349,6 @@ MQPlan mq_plan(int num_seqs, int total_q, int num_heads, int num_kv_heads, int h
     if (parts > kMQMaxParts) parts = kMQMaxParts;
     pl.parts = parts < 1 ? 1 : (int)parts;
   }
-  const long long per = ((long long)max_seq_len + pl.parts - 1) / pl.parts;
-  pl.part_len = (int)(per < 32 ? 32 : (per + 31) / 32 * 32);
   if (pl.parts > 1) {
     const size_t slots = (size_t)total_q * num_heads * pl.parts;
     pl.ml_bytes = (slots * 2 * sizeof(float) + 255) / 256 * 256;
@@ -446,7 +444,7 @@ pa_status pa_multi_query(const void* q, const void* k_cache, const void* v_cache
   }
   const void* kmain = nullptr;
   const void* kmerge = nullptr;
-  if (!multi_query_kernels((int)dtype, head_dim, pl.split, &kmain, &kmerge))
+  if (!multi_query_kernels((int)dtype, head_dim, pl.split, false, &kmain, &kmerge))
     return fail(PA_ERR_UNSUPPORTED, "pa_multi_query: no kernel for this dtype and head_dim");
   MultiQueryParams mp;
   mp.q = q;
@@ -455,6 +453,7 @@ pa_status pa_multi_query(const void* q, const void* k_cache, const void* v_cache
   mp.block_tables = block_tables;
   mp.seq_lens = seq_lens;
   mp.q_start = q_start;
+  mp.prefix_lens = nullptr;
   mp.out = out;
   mp.ws_ml = pl.total > 0 ? reinterpret_cast<float*>(workspace) : nullptr;
   mp.ws_acc = pl.total > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.ml_bytes) : nullptr;
@@ -472,7 +471,6 @@ pa_status pa_multi_query(const void* q, const void* k_cache, const void* v_cache
   mp.tq = pl.tq;
   mp.qblocks = pl.qblocks;
   mp.parts = pl.parts;
-  mp.part_len = pl.part_len;
   mp.items = pl.items;
   mp.scale_log2e = (float)((double)scale * 1.4426950408889634074);
   const long long wgs = (pl.items * pl.parts + 7) / 8 * 8;
@@ -483,6 +481,173 @@ pa_status pa_multi_query(const void* q, const void* k_cache, const void* v_cache
     const long long rows = (long long)total_q * num_heads;
     e = hipLaunchKernel(kmerge, dim3((unsigned)((rows + 3) / 4)), dim3(256), args, 0, st);
     if (e != hipSuccess) return hip_fail(e, "pa_multi_query merge launch");
+  }
+  return PA_OK;
+}
+
+namespace {
+
+// Launch plan of pa_decode_shared_prefix: items are (group, KV head, block of
+// 16 / group members); otherwise as for pa_multi_query.
+MQPlan sp_plan(int num_seqs, int num_groups, int num_heads, int num_kv_heads, int head_dim,
+               int max_group_size, int max_seq_len) {
+  MQPlan pl;
+  const int group = num_heads / num_kv_heads;
+  pl.split = true;
+  pl.tq = 16 / group;
+  pl.qblocks = max_group_size > 0 ? (max_group_size + pl.tq - 1) / pl.tq : 0;
+  pl.items = (long long)num_groups * num_kv_heads * pl.qblocks;
+  if (pl.items > 0 && max_seq_len > 0) {
+    const long long want = (kMQTargetItems + pl.items - 1) / pl.items;
+    const long long by_len = ((long long)max_seq_len + 255) / 256;
+    long long parts = want < by_len ? want : by_len;
+    if (parts > kMQMaxParts) parts = kMQMaxParts;
+    pl.parts = parts < 1 ? 1 : (int)parts;
+  }
+  if (pl.parts > 1) {
+    const size_t slots = (size_t)num_seqs * num_heads * pl.parts;
+    pl.ml_bytes = (slots * 2 * sizeof(float) + 255) / 256 * 256;
+    pl.total = pl.ml_bytes + slots * head_dim * sizeof(float);
+  }
+  return pl;
+}
+
+}  // namespace
+
+size_t pa_decode_shared_prefix_workspace_size(int num_seqs, int num_groups, int num_heads,
+                                              int num_kv_heads, int head_dim, int max_group_size,
+                                              int max_seq_len) {
+  if (num_seqs < 0 || num_groups < 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 ||
+      num_heads % num_kv_heads != 0 || num_heads / num_kv_heads > 16 || max_group_size < 0 ||
+      max_seq_len < 0 || max_seq_len > kMaxSeqLen)
+    return 0;
+  return sp_plan(num_seqs, num_groups, num_heads, num_kv_heads, head_dim, max_group_size, max_seq_len).total;
+}
+
+pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_tables, const int32_t* seq_lens,
+                                  const int32_t* group_start, const int32_t* prefix_lens,
+                                  int num_seqs, int num_groups, int num_heads, int num_kv_heads,
+                                  int head_dim, int block_size, int num_blocks, int max_blocks_per_seq,
+                                  int max_group_size, int max_seq_len, float scale, pa_dtype dtype,
+                                  void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* who = "pa_decode_shared_prefix";
+  if (dtype != PA_F32 && dtype != PA_F16 && dtype != PA_BF16)
+    return fail(PA_ERR_INVALID, "%s: unknown dtype %d", who, (int)dtype);
+  if (num_seqs < 0 || num_groups < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
+      max_blocks_per_seq <= 0 || max_group_size < 0 || max_seq_len < 0 || block_size <= 0)
+    return fail(PA_ERR_INVALID,
+                "%s: need num_seqs, num_groups, max_group_size, max_seq_len >= 0 and num_heads, "
+                "num_kv_heads, block_size, num_blocks, max_blocks_per_seq > 0", who);
+  if (num_heads % num_kv_heads != 0)
+    return fail(PA_ERR_INVALID, "%s: num_heads (%d) is not a multiple of num_kv_heads (%d)", who,
+                num_heads, num_kv_heads);
+  if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f)
+    return fail(PA_ERR_INVALID, "%s: scale must be finite", who);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d not in {64, 128}", who, head_dim);
+  if (dtype == PA_F32)
+    return fail(PA_ERR_UNSUPPORTED, "%s: float32 caches are not supported (use pa_decode)", who);
+  if (num_heads / num_kv_heads > 16)
+    return fail(PA_ERR_UNSUPPORTED, "%s: %d query heads per KV head (at most 16)", who,
+                num_heads / num_kv_heads);
+  if ((long long)max_seq_len > (long long)max_blocks_per_seq * block_size)
+    return fail(PA_ERR_INVALID, "%s: max_seq_len %d exceeds max_blocks_per_seq * block_size (%lld)", who,
+                max_seq_len, (long long)max_blocks_per_seq * block_size);
+  if (max_seq_len > kMaxSeqLen)
+    return fail(PA_ERR_UNSUPPORTED, "%s: max_seq_len %d above %d", who, max_seq_len, kMaxSeqLen);
+  if (max_group_size > num_seqs)
+    return fail(PA_ERR_INVALID, "%s: max_group_size %d above num_seqs %d", who, max_group_size, num_seqs);
+  if ((long long)num_seqs * num_heads >= (1LL << 31))
+    return fail(PA_ERR_UNSUPPORTED, "%s: num_seqs * num_heads above 2^31", who);
+  if (num_seqs == 0 || num_groups == 0 || max_group_size == 0) return PA_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !group_start || !prefix_lens || !out)
+    return fail(PA_ERR_INVALID, "%s: null pointer argument", who);
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+    return fail(PA_ERR_INVALID, "%s: q, caches and out must be 16-byte aligned", who);
+  const MQPlan pl = sp_plan(num_seqs, num_groups, num_heads, num_kv_heads, head_dim, max_group_size,
+                            max_seq_len);
+  if (pl.items * pl.parts + 8 >= (1LL << 31))
+    return fail(PA_ERR_UNSUPPORTED, "%s: more than 2^31 workgroups", who);
+  if (pl.total > 0 && (!workspace || workspace_bytes < pl.total))
+    return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", who, workspace_bytes, pl.total);
+  if (pl.total > 0 && !aligned16(workspace))
+    return fail(PA_ERR_INVALID, "%s: workspace must be 16-byte aligned", who);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (debug_checks()) {
+    pa_status bad = PA_OK;
+    std::vector<int32_t> lens, gs, pre, tab;
+    if (!to_host(lens, seq_lens, num_seqs, st, &bad)) return bad;
+    if (!to_host(gs, group_start, (size_t)num_groups + 1, st, &bad)) return bad;
+    if (!to_host(pre, prefix_lens, num_groups, st, &bad)) return bad;
+    if (!to_host(tab, block_tables, (size_t)num_seqs * max_blocks_per_seq, st, &bad)) return bad;
+    if (gs[0] != 0 || gs[num_groups] != num_seqs)
+      return fail(PA_ERR_INVALID, "%s: group_start must run from 0 to num_seqs", who);
+    for (int s = 0; s < num_seqs; ++s) {
+      if (lens[s] < 0 || lens[s] > max_seq_len)
+        return fail(PA_ERR_INVALID, "%s: seq_lens[%d] = %d outside [0, %d]", who, s, lens[s], max_seq_len);
+      for (int j = 0; j < (lens[s] + block_size - 1) / block_size; ++j) {
+        const int b = tab[(size_t)s * max_blocks_per_seq + j];
+        if (b < 0 || b >= num_blocks)
+          return fail(PA_ERR_INVALID, "%s: block_tables[%d][%d] = %d outside [0, %d)", who, s, j, b, num_blocks);
+      }
+    }
+    for (int gi = 0; gi < num_groups; ++gi) {
+      const int a = gs[gi], b = gs[gi + 1];
+      if (b < a || b - a > max_group_size)
+        return fail(PA_ERR_INVALID, "%s: group %d has %d members (max_group_size %d)", who, gi, b - a,
+                    max_group_size);
+      const int P = pre[gi];
+      for (int s = a; s < b; ++s) {
+        if (P < 0 || P > lens[s])
+          return fail(PA_ERR_INVALID, "%s: prefix_lens[%d] = %d not within sequence %d's %d tokens", who,
+                      gi, P, s, lens[s]);
+        for (int j = 0; j < (P + block_size - 1) / block_size; ++j)
+          if (tab[(size_t)s * max_blocks_per_seq + j] != tab[(size_t)a * max_blocks_per_seq + j])
+            return fail(PA_ERR_INVALID, "%s: sequence %d does not share block %d of group %d's prefix", who,
+                        s, j, gi);
+      }
+    }
+  }
+  const void* kmain = nullptr;
+  const void* kmerge = nullptr;
+  if (!multi_query_kernels((int)dtype, head_dim, true, true, &kmain, &kmerge))
+    return fail(PA_ERR_UNSUPPORTED, "%s: no kernel for this dtype and head_dim", who);
+  MultiQueryParams mp;
+  mp.q = q;
+  mp.k_cache = k_cache;
+  mp.v_cache = v_cache;
+  mp.block_tables = block_tables;
+  mp.seq_lens = seq_lens;
+  mp.q_start = group_start;
+  mp.prefix_lens = prefix_lens;
+  mp.out = out;
+  mp.ws_ml = pl.total > 0 ? reinterpret_cast<float*>(workspace) : nullptr;
+  mp.ws_acc = pl.total > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.ml_bytes) : nullptr;
+  mp.num_seqs = num_groups;          // items run over groups
+  mp.total_q = num_seqs;             // rows are member sequences
+  mp.num_heads = num_heads;
+  mp.num_kv_heads = num_kv_heads;
+  mp.group = num_heads / num_kv_heads;
+  mp.head_dim = head_dim;
+  mp.block_size = block_size;
+  mp.num_blocks = num_blocks;
+  mp.max_blocks_per_seq = max_blocks_per_seq;
+  mp.max_q_len = max_group_size;
+  mp.max_seq_len = max_seq_len;
+  mp.tq = pl.tq;
+  mp.qblocks = pl.qblocks;
+  mp.parts = pl.parts;
+  mp.items = pl.items;
+  mp.scale_log2e = (float)((double)scale * 1.4426950408889634074);
+  const long long wgs = (pl.items * pl.parts + 7) / 8 * 8;
+  void* args[] = {&mp};
+  hipError_t e = hipLaunchKernel(kmain, dim3((unsigned)wgs), dim3(256), args, 0, st);
+  if (e != hipSuccess) return hip_fail(e, "pa_decode_shared_prefix launch");
+  if (pl.parts > 1) {
+    const long long rows = (long long)num_seqs * num_heads;
+    e = hipLaunchKernel(kmerge, dim3((unsigned)((rows + 3) / 4)), dim3(256), args, 0, st);
+    if (e != hipSuccess) return hip_fail(e, "pa_decode_shared_prefix merge launch");
   }
   return PA_OK;
 }

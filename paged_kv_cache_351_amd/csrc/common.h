@@ -61,7 +61,9 @@ struct MultiQueryParams {
   const void* v_cache;
   const int32_t* block_tables;
   const int32_t* seq_lens;     // tokens in the cache, including the queries' own
-  const int32_t* q_start;      // [num_seqs + 1] query row offsets
+  const int32_t* q_start;      // [num_seqs + 1] query row offsets; shared-prefix decode:
+                               // [num_groups + 1] first member sequence of each group
+  const int32_t* prefix_lens;  // shared-prefix decode: [num_groups] shared tokens
   void* out;                   // [total_q][num_heads][head_dim]
   float* ws_ml;                // [total_q * num_heads][parts][2] running max and sum
   float* ws_acc;               // [total_q * num_heads][parts][head_dim]
@@ -80,14 +82,15 @@ struct MultiQueryParams {
                                // 16 / group when all four waves share 16 rows
   int qblocks;                 // query blocks per (sequence, KV head): ceil(max_q_len / tq)
   int parts;                   // context partitions; 1 = no merge step
-  int part_len;                // tokens per partition, a multiple of the 32-token tile
   long long items;             // num_seqs * num_kv_heads * qblocks
   float scale_log2e;
 };
 
 // The multi-query and partition-merge kernels for one element type and head_dim;
-// `split` picks the variant for blocks of at most 16 query rows (16-bit types).
-bool multi_query_kernels(int dtype, int head_dim, bool split, const void** main, const void** merge);
+// `split` picks the variant for blocks of at most 16 query rows, `shared` the
+// shared-prefix decode (both 16-bit types only).
+bool multi_query_kernels(int dtype, int head_dim, bool split, bool shared, const void** main,
+                         const void** merge);
 
 // Message returned by pa_last_error() on the calling thread.
 void set_last_error(const char* msg);

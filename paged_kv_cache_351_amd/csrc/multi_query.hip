@@ -15,8 +15,8 @@
 //   A workgroup (4 waves) owns one (sequence, KV head, query block, context
 //   partition).  A query block is 64 rows: up to floor(64 / g) consecutive query
 //   tokens times the g query heads of the KV head's group, row = token * g +
-//   head; wave w computes rows 16w .. 16w+15.  Its partition of the context
-//   [part * part_len, ...) is cut at the block's last query position.  With one
+//   head; wave w computes rows 16w .. 16w+15.  The context up to the block's
+//   last query position is cut into `parts` equal partitions of whole tiles.  With one
 //   partition the workgroup writes the output; otherwise it leaves (m, l, acc)
 //   per row and a second kernel merges the partitions in order.  Workgroups are
 //   numbered so that every query block and partition of one (sequence, KV head)
@@ -135,6 +135,15 @@ __device__ __forceinline__ bool item_of(const MultiQueryParams& p, Item& it) {
   return it.s < p.num_seqs;
 }
 
+// Where the 32 tokens of one tile come from: tokens base .. base + count - 1 of
+// the sequence whose block table is `table`; slots past `count` are masked (and
+// read as a copy of the last valid token).  owner >= 0: only the rows of that
+// member may see the tile (a member's private tail in a shared-prefix group).
+struct TileMap {
+  const int32_t* table;
+  int base, count, owner;
+};
+
 // SPLIT = false: the four waves own 16 rows each of a 64-row query block and
 // share every K/V tile through LDS (prefill-sized blocks).
 // SPLIT = true (16-bit types, at most 16 rows per block): the four waves work on
@@ -142,13 +151,18 @@ __device__ __forceinline__ bool item_of(const MultiQueryParams& p, Item& it) {
 // from HBM into registers in the matrix-core layout and V through a
 // wave-private LDS region, with no workgroup barrier in the loop; their four
 // partial results are merged through LDS at the end.
-template <int DT, int D, bool SPLIT>
+// SHARED (split only): the item is a group of sequences whose first tokens sit in
+// the same blocks; rows are (member, head), and the tiles are the shared prefix
+// (read once, seen by every member) followed by each member's own tail (seen by
+// that member only), each padded to whole tiles.
+template <int DT, int D, bool SPLIT, bool SHARED>
 __global__ __launch_bounds__(256) void multi_query_kernel(MultiQueryParams p) {
   using S = Shape<DT, D>;
   constexpr int EB = S::EB, CR = S::CR, NKC = S::NKC, NJ = S::NJ;
   constexpr int VREG = D * S::VSTRIDE;                     // one transposed V tile
   constexpr int LDS_BYTES = SPLIT ? 4 * VREG : S::LDS;
   static_assert(!SPLIT || (DT != kF32 && 4 * 16 * (D + 2) * 4 <= LDS_BYTES), "split merge space");
+  static_assert(SPLIT || !SHARED, "shared-prefix groups use the split variant");
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
 
   Item it;
@@ -160,29 +174,86 @@ __global__ __launch_bounds__(256) void multi_query_kernel(MultiQueryParams p) {
   char* ldsK = lds;
   char* ldsV = SPLIT ? lds + wave * VREG : lds + S::KBYTES;
 
-  // the sequence's query range and length, clamped so that no access leaves the arrays
-  int L = p.seq_lens[it.s];
-  L = L < 0 ? 0 : (L > p.max_seq_len ? p.max_seq_len : L);
+  // The item's rows: query tokens qa + tok0 .. qa + tok1 - 1 of one sequence (multi-query),
+  // or member sequences qa + tok0 .. qa + tok1 - 1 of one group (shared prefix), g heads
+  // each.  Everything read from the index arrays is clamped so no access leaves them.
   const int qa = p.q_start[it.s];
   int n = p.q_start[it.s + 1] - qa;
   n = n < 0 ? 0 : (n > p.max_q_len ? p.max_q_len : n);
   if (qa < 0 || qa + n > p.total_q) n = 0;
-  const int tok0 = it.qb * p.tq;                   // first query token of the block
+  const int tok0 = it.qb * p.tq;
   if (tok0 >= n) return;
-  const int tok1 = min(n, tok0 + p.tq);            // one past the last
-  const int pos_hi = L - n + tok1 - 1;             // last query position of the block
-  const int pos_lo = L - n + tok0;                 // first query position of the block
-  const int kv_end = min(L, pos_hi + 1);
-  const int t_begin = it.part * p.part_len;
-  const int t_end = min(kv_end, t_begin + p.part_len);
+  const int tok1 = min(n, tok0 + p.tq);
+  auto clamp_len = [&](int x) { return x < 0 ? 0 : (x > p.max_seq_len ? p.max_seq_len : x); };
 
-  // this lane's query row (row col of the wave's 16)
+  // this lane's row (row col of the wave's 16)
   const int rloc = SPLIT ? col : wave * 16 + col;
   const int qtok = tok0 + rloc / g;
   const int qh = rloc % g;
   const bool row_ok = rloc < p.tq * g && qtok < tok1;
-  const int pos = L - n + qtok;                    // the row's causal limit (inclusive)
   const size_t out_row = (size_t)(qa + qtok) * Hq + (size_t)it.kv * g + qh;
+
+  int L = 0, pos = 0, pos_lo = 0, t_end = 0;       // multi-query
+  int P = 0, VP = 0, m_off = 0, m_tail = 0;        // shared prefix: lane i < tok1 - tok0 = member i
+  const int32_t* tables = p.block_tables;
+  const int32_t* seq_table = nullptr;
+  if constexpr (!SHARED) {
+    L = clamp_len(p.seq_lens[it.s]);
+    const int pos_hi = L - n + tok1 - 1;           // last query position of the block
+    pos_lo = L - n + tok0;                         // first query position of the block
+    pos = L - n + qtok;                            // the row's causal limit (inclusive)
+    t_end = min(L, pos_hi + 1);
+    seq_table = tables + (size_t)it.s * p.max_blocks_per_seq;
+  } else {
+    const int cnt = tok1 - tok0;
+    const int mine = lane < cnt ? clamp_len(p.seq_lens[qa + tok0 + lane]) : 0x7fffffff;
+    // member data lives in lanes 0..15; reductions run inside that 16-lane row and
+    // their results are broadcast from it, so every lane agrees on P and t_end
+    int lmin = mine;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) lmin = min(lmin, __shfl_xor(lmin, o));
+    lmin = __shfl(lmin, 0);
+    P = min(clamp_len(p.prefix_lens[it.s]), lmin);  // a prefix longer than a member is cut
+    VP = (P + kTile - 1) / kTile * kTile;
+    m_tail = lane < cnt ? mine - P : 0;
+    const int padded = (m_tail + kTile - 1) / kTile * kTile;
+    int incl = padded;                             // prefix sum over lanes 0..15
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      const int v = __shfl_up(incl, o, 16);
+      if ((lane & 15) >= o) incl += v;
+    }
+    m_off = incl - padded;
+    t_end = VP + __shfl(incl, 15);
+    seq_table = tables + (size_t)(qa + tok0) * p.max_blocks_per_seq;  // the group's first member
+  }
+  // with several partitions, the item's own range is cut into equal whole tiles
+  int t_begin = 0;
+  if (p.parts > 1) {
+    const int plen = ((t_end + p.parts - 1) / p.parts + kTile - 1) / kTile * kTile;
+    t_begin = it.part * plen;
+    t_end = min(t_end, t_begin + plen);
+  }
+
+  // Source of the tile starting at t0 (uniform over the workgroup).
+  auto tile_map = [&](int t0) -> TileMap {
+    TileMap mp;
+    if constexpr (!SHARED) {
+      mp = TileMap{seq_table, t0, min(kTile, t_end - t0), -1};
+    } else {
+      if (t0 < VP) {
+        mp = TileMap{seq_table, t0, min(kTile, P - t0), -1};
+      } else {
+        const int rel = t0 - VP;
+        const unsigned long long below = __ballot(lane < tok1 - tok0 && m_off <= rel);
+        const int owner = __popcll(below & 0xffffull) - 1;
+        const int off = __shfl(m_off, owner), tail = __shfl(m_tail, owner);
+        mp = TileMap{tables + (size_t)(qa + tok0 + owner) * p.max_blocks_per_seq, P + rel - off,
+                     min(kTile, tail - (rel - off)), owner};
+      }
+    }
+    return mp;
+  };
 
   // query fragments: the same chunks of the row as the K fragments
   u32x4 qf[NKC];
@@ -199,15 +270,14 @@ __global__ __launch_bounds__(256) void multi_query_kernel(MultiQueryParams p) {
   for (int j = 0; j < NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = kNegBig, l = 0.f;
 
-  const int32_t* table = p.block_tables + (size_t)it.s * p.max_blocks_per_seq;
   const int B = p.block_size;
   const size_t kv_off = (size_t)it.kv * S::ROWB;
   const size_t slot_bytes = (size_t)Hkv * S::ROWB;
-  // byte offset of token t's row of this KV head in the pool; t is clamped to the
-  // partition's last token so that nothing outside the sequence is read
-  auto row_addr = [&](int t) -> size_t {
-    t = min(t, t_end - 1);
-    int b = table[t / B];
+  // byte offset of token i (0..31) of a mapped tile in the pool: tokens past the
+  // tile's count read its last valid token, so nothing outside a sequence is read
+  auto row_addr = [&](const TileMap& mp, int i) -> size_t {
+    const int t = mp.base + min(i, mp.count - 1);
+    int b = mp.table[t / B];
     b = b < 0 ? 0 : (b >= p.num_blocks ? p.num_blocks - 1 : b);
     return ((size_t)b * B + t % B) * slot_bytes + kv_off;
   };
@@ -217,14 +287,14 @@ __global__ __launch_bounds__(256) void multi_query_kernel(MultiQueryParams p) {
   constexpr int VL = (16 * CR + VLANES - 1) / VLANES;
   const int vme = SPLIT ? lane : tid;
   u32x4 va[VL], vb[VL];
-  auto load_v = [&](int t0) {
+  auto load_v = [&](const TileMap& mp) {
 #pragma unroll
     for (int k = 0; k < VL; ++k) {
       const int idx = vme + VLANES * k;
       if (idx < 16 * CR) {
         const int ch = idx / 16, pr = idx % 16;   // pairs fastest: conflict-free transposes
-        va[k] = *reinterpret_cast<const u32x4*>((const char*)p.v_cache + row_addr(t0 + 2 * pr) + ch * 16);
-        vb[k] = *reinterpret_cast<const u32x4*>((const char*)p.v_cache + row_addr(t0 + 2 * pr + 1) + ch * 16);
+        va[k] = *reinterpret_cast<const u32x4*>((const char*)p.v_cache + row_addr(mp, 2 * pr) + ch * 16);
+        vb[k] = *reinterpret_cast<const u32x4*>((const char*)p.v_cache + row_addr(mp, 2 * pr + 1) + ch * 16);
       }
     }
   };
@@ -253,11 +323,11 @@ __global__ __launch_bounds__(256) void multi_query_kernel(MultiQueryParams p) {
   // K: through LDS (shared tiles) or straight into the matrix-core layout (split)
   constexpr int KL = SPLIT ? 2 * NKC : S::KLOADS;
   u32x4 kr[KL];
-  auto load_k = [&](int t0) {
+  auto load_k = [&](const TileMap& mp) {
     if constexpr (SPLIT) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const char* row = (const char*)p.k_cache + row_addr(t0 + 16 * h + col);
+        const char* row = (const char*)p.k_cache + row_addr(mp, 16 * h + col);
 #pragma unroll
         for (int c = 0; c < NKC; ++c)
           kr[h * NKC + c] = *reinterpret_cast<const u32x4*>(row + chunk_of<DT, D>(c, grp) * 16);
@@ -267,7 +337,7 @@ __global__ __launch_bounds__(256) void multi_query_kernel(MultiQueryParams p) {
       for (int k = 0; k < KL; ++k) {
         const int idx = tid + 256 * k;
         const int tk = idx / CR, ch = idx % CR;
-        kr[k] = *reinterpret_cast<const u32x4*>((const char*)p.k_cache + row_addr(t0 + tk) + ch * 16);
+        kr[k] = *reinterpret_cast<const u32x4*>((const char*)p.k_cache + row_addr(mp, tk) + ch * 16);
       }
     }
   };
@@ -285,12 +355,15 @@ __global__ __launch_bounds__(256) void multi_query_kernel(MultiQueryParams p) {
   const float sl2 = p.scale_log2e;
   const int ntiles = t_end > t_begin ? (t_end - t_begin + kTile - 1) / kTile : 0;
   const int k0 = SPLIT ? wave : 0, kstep = SPLIT ? 4 : 1;
+  TileMap cur = tile_map(t_begin + k0 * kTile);
   if (k0 < ntiles) {
-    load_k(t_begin + k0 * kTile);
-    load_v(t_begin + k0 * kTile);
+    load_k(cur);
+    load_v(cur);
   }
   for (int k = k0; k < ntiles; k += kstep) {
     const int t0 = t_begin + k * kTile;
+    const bool more = k + kstep < ntiles;
+    const TileMap nxt = more ? tile_map(t0 + kstep * kTile) : cur;
     // S^T = K Q^T for the two 16-token halves
     f32x4 sc[2];
     auto qk = [&](int h, int c, u32x4 a) {
@@ -312,22 +385,21 @@ __global__ __launch_bounds__(256) void multi_query_kernel(MultiQueryParams p) {
       // this tile's K is in registers: stage its V and fetch the wave's next V,
       // multiply, then fetch the next K (no second copy of the K registers)
       store_v();
-      const bool more = k + kstep < ntiles;
-      if (more) load_v(t0 + kstep * kTile);
+      if (more) load_v(nxt);
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int c = 0; c < NKC; ++c) qk(h, c, kr[h * NKC + c]);
-      if (more) load_k(t0 + kstep * kTile);
+      if (more) load_k(nxt);
       __builtin_amdgcn_wave_barrier();   // V stores above are read by other lanes below
     } else {
       __syncthreads();  // the previous tile is no longer read
       store_k();
       store_v();
       __syncthreads();
-      if (k + 1 < ntiles) {
-        load_k(t0 + kTile);
-        load_v(t0 + kTile);
+      if (more) {
+        load_k(nxt);
+        load_v(nxt);
       }
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
@@ -337,23 +409,27 @@ __global__ __launch_bounds__(256) void multi_query_kernel(MultiQueryParams p) {
           qk(h, c, *reinterpret_cast<const u32x4*>(krow + chunk_of<DT, D>(c, grp) * 16));
       }
     }
-    // online softmax: token t0 + 16 h + 4 grp + i of row col; tiles that end before
-    // the block's first query position and the partition's end need no mask
+    // online softmax: tile token 16 h + 4 grp + i of row col; full tiles that every
+    // row may see in full need no mask
     float sv[8];
-    if (t0 + kTile - 1 <= pos_lo && t0 + kTile <= t_end) {
+    const bool whole = cur.count == kTile && (SHARED ? cur.owner < 0 : t0 + kTile - 1 <= pos_lo);
+    if (whole) {
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int i = 0; i < 4; ++i) sv[4 * h + i] = sc[h][i] * sl2;
     } else {
+      const bool row_sees = !SHARED || cur.owner < 0 || cur.owner == qtok - tok0;
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int t = t0 + 16 * h + 4 * grp + i;
-          sv[4 * h + i] = (t <= pos && t < t_end) ? sc[h][i] * sl2 : -__builtin_inff();
+          const int u = 16 * h + 4 * grp + i;
+          const bool ok = SHARED ? (row_sees && u < cur.count) : (u < cur.count && t0 + u <= pos);
+          sv[4 * h + i] = ok ? sc[h][i] * sl2 : -__builtin_inff();
         }
     }
+    cur = nxt;
     float mx = sv[0];
 #pragma unroll
     for (int u = 1; u < 8; ++u) mx = fmaxf(mx, sv[u]);
@@ -516,27 +592,30 @@ __global__ __launch_bounds__(256) void multi_query_merge_kernel(MultiQueryParams
 }
 
 template <int DT, int D>
-void pick_d(bool split, const void** main, const void** merge) {
+void pick_d(bool split, bool shared, const void** main, const void** merge) {
+  *merge = reinterpret_cast<const void*>(&multi_query_merge_kernel<DT, D>);
   if constexpr (DT != kF32) {
+    if (shared) {
+      *main = reinterpret_cast<const void*>(&multi_query_kernel<DT, D, true, true>);
+      return;
+    }
     if (split) {
-      *main = reinterpret_cast<const void*>(&multi_query_kernel<DT, D, true>);
-      *merge = reinterpret_cast<const void*>(&multi_query_merge_kernel<DT, D>);
+      *main = reinterpret_cast<const void*>(&multi_query_kernel<DT, D, true, false>);
       return;
     }
   }
-  *main = reinterpret_cast<const void*>(&multi_query_kernel<DT, D, false>);
-  *merge = reinterpret_cast<const void*>(&multi_query_merge_kernel<DT, D>);
+  *main = reinterpret_cast<const void*>(&multi_query_kernel<DT, D, false, false>);
 }
 
 template <int DT>
-bool pick_dt(int head_dim, bool split, const void** main, const void** merge) {
-  if (split && DT == kF32) return false;
+bool pick_dt(int head_dim, bool split, bool shared, const void** main, const void** merge) {
+  if ((split || shared) && DT == kF32) return false;
   if (head_dim == 64) {
-    pick_d<DT, 64>(split, main, merge);
+    pick_d<DT, 64>(split, shared, main, merge);
     return true;
   }
   if (head_dim == 128) {
-    pick_d<DT, 128>(split, main, merge);
+    pick_d<DT, 128>(split, shared, main, merge);
     return true;
   }
   return false;
@@ -544,11 +623,12 @@ bool pick_dt(int head_dim, bool split, const void** main, const void** merge) {
 
 }  // namespace
 
-bool multi_query_kernels(int dtype, int head_dim, bool split, const void** main, const void** merge) {
+bool multi_query_kernels(int dtype, int head_dim, bool split, bool shared, const void** main,
+                         const void** merge) {
   switch (dtype) {
-    case kF32: return pick_dt<kF32>(head_dim, split, main, merge);
-    case kF16: return pick_dt<kF16>(head_dim, split, main, merge);
-    case kBF16: return pick_dt<kBF16>(head_dim, split, main, merge);
+    case kF32: return pick_dt<kF32>(head_dim, split, shared, main, merge);
+    case kF16: return pick_dt<kF16>(head_dim, split, shared, main, merge);
+    case kBF16: return pick_dt<kBF16>(head_dim, split, shared, main, merge);
     default: return false;
   }
 }

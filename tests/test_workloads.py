@@ -137,3 +137,20 @@ def test_multi_query_batches_have_one_query_row_per_written_token():
         assert b.q.shape[0] == sum(n) == len(b.slot_mapping)
         assert ((b.seq_lens - b.seq_lens_before).tolist()) == n
         assert all(k <= L for k, L in zip(n, b.seq_lens.tolist()))
+
+
+@pytest.mark.parametrize("make", [lambda: workloads.opt13b_shared(num_prompts=3, samples=4, prompt_len=48,
+                                                                  tail_max=30),
+                                  lambda: workloads.opt13b_cow(num_prompts=3, samples=4, prompt_len=37)])
+def test_shared_groups_really_share_their_prefix_blocks(make):
+    b = make()
+    B = b.block_size
+    gs, P = b.group_start.tolist(), b.prefix_lens.tolist()
+    assert gs[0] == 0 and gs[-1] == b.num_seqs and len(P) == len(gs) - 1
+    tables, lens = b.block_tables.tolist(), b.seq_lens.tolist()
+    for g in range(len(P)):
+        nb = -(-P[g] // B)
+        assert nb > 0
+        for s in range(gs[g], gs[g + 1]):
+            assert P[g] <= lens[s]
+            assert tables[s][:nb] == tables[gs[g]][:nb]

@@ -70,6 +70,8 @@ class PagedBatch:
     slot_mapping: Optional[torch.Tensor] = None   # int32 [T]
     cow_pairs: Optional[torch.Tensor] = None      # int32 [P, 2] (src, dst) before the write
     q_start: Optional[torch.Tensor] = None        # int32 [N+1]: multi-query batches only
+    group_start: Optional[torch.Tensor] = None    # int32 [G+1]: sequences sharing a prefix
+    prefix_lens: Optional[torch.Tensor] = None    # int32 [G]: tokens in shared blocks
     info: dict = field(default_factory=dict)
 
     @property
@@ -390,6 +392,11 @@ def _shared(*, name, seed, num_prompts, samples, prompt_len, tail_max, cow, Hq, 
         b.new_k, b.new_v = Kt, Vt
         b.slot_mapping = torch.tensor(new_slots, dtype=torch.int32)
         b.cow_pairs = torch.tensor(cow_pairs, dtype=torch.int32).reshape(-1, 2)
+    # the samples of a prompt are contiguous and share the prompt's blocks: all of
+    # them, or (after copy-on-write of a partly filled last block) its full blocks
+    shared = prompt_len if not (cow and partial) else (prompt_len // B) * B
+    b.group_start = torch.arange(0, N + 1, samples, dtype=torch.int32)
+    b.prefix_lens = torch.full((num_prompts,), shared, dtype=torch.int32)
     return b
 
 
