@@ -14,6 +14,8 @@ Prints ONE JSON line.  ``value`` is the K/V bytes the decode step must read
 runs on; ``cpu_baseline`` times the float64 CPU oracle on the host.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME [--block-size B]]
+    python bench.py --workload opt13b_shared --shared-prefix   # shared-prefix decode
+    python bench.py --workload llama3_8b_spec                  # multi-query (also llama3_8b_chunk)
     python bench.py --swap               # pa_swap_blocks HBM <-> pinned host throughput
     python bench.py --copy-calibration   # a block copy of known size, for counter scaling
     python bench.py --record-traffic DEC_FETCH.csv DEC_WRITE.csv COPY_FETCH.csv COPY_WRITE.csv
@@ -230,12 +232,42 @@ def cpu_baseline(b, gpu_out, time_cap=25.0):
     kv = int(lens[:done].astype(np.int64).sum()) * b.num_kv_heads * b.head_dim * 2 * esize
     steps = ("block copies, " if b.cow_pairs is not None else "") + \
             (f"write of all {len(b.slot_mapping)} new tokens, " if b.slot_mapping is not None else "")
+    steps = steps + "then decode" if steps else "decode"
     return {"value": kv / wall / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{steps}then decode of the first {done} of {b.num_seqs} sequences of the "
+            "sample": f"{steps} of the first {done} of {b.num_seqs} sequences of the "
                       f"same workload (numpy float64, {kv / 1e9:.3f} GB of K/V)",
             "seqs_per_s": done / wall, "wall_s": wall, "cpu_s": cpu,
             "host_cpus": len(os.sched_getaffinity(0)),
             "max_abs_err_gpu_vs_oracle": err}
+
+
+def cpu_baseline_multi_query(b, gpu_out, time_cap=25.0):
+    """The float64 oracle on the host for a multi-query step: the write of the new tokens, then
+    attention for the workload's sequences in order until done or the time cap is reached."""
+    import oracle
+    from workloads import as_numpy
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads = 1
+    q, bt, lens, qs = as_numpy(b.q), as_numpy(b.block_tables), as_numpy(b.seq_lens), b.q_start.tolist()
+    t0 = time.time()
+    kc, vc = oracle.write_kv(as_numpy(b.new_k), as_numpy(b.new_v), as_numpy(b.slot_mapping),
+                             as_numpy(b.k_cache), as_numpy(b.v_cache))
+    done, err, kv = 0, 0.0, 0
+    while done < b.num_seqs and time.time() - t0 < time_cap:
+        a, z = qs[done], qs[done + 1]
+        ref = oracle.paged_multi_query(q[a:z], kc, vc, bt[done:done + 1], lens[done:done + 1],
+                                       np.array([0, z - a]), b.scale, b.dtype)
+        err = max(err, float(np.abs(gpu_out[a:z] - ref).max()))
+        kv += int(lens[done]) * b.num_kv_heads * b.head_dim * 2 * 2
+        done += 1
+    wall = time.time() - t0
+    return {"value": kv / wall / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"write of all {len(b.slot_mapping)} new tokens, then the queries of the first "
+                      f"{done} of {b.num_seqs} sequences of the same workload (numpy float64)",
+            "seqs_per_s": done / wall, "wall_s": wall, "max_abs_err_gpu_vs_oracle": err}
 
 
 def unique_kv_bytes(b):
@@ -270,10 +302,19 @@ WORKLOADS = {
     "llama2_70b": (lambda a: workloads.llama2_70b(seed=0, block_size=a.block_size),
                    {"num_heads": 64, "num_kv_heads": 8, "head_dim": 128,
                     "seq_len_range": [8192, 32768], "key_outliers": 0.01}),
+    "llama3_8b_spec": (lambda a: workloads.llama3_8b_spec(seed=0),
+                       {"num_heads": 32, "num_kv_heads": 8, "head_dim": 128, "block_size": 16,
+                        "seq_len_range": [512, 4096], "queries_per_seq": 4, "num_blocks": 70000}),
+    "llama3_8b_chunk": (lambda a: workloads.llama3_8b_chunk(seed=0),
+                        {"num_heads": 32, "num_kv_heads": 8, "head_dim": 128, "block_size": 16,
+                         "prior_range": [0, 3584], "chunk": 512}),
 }
 WORKLOAD_NAMES = {"llama3_8b": "llama3_8b_gqa_decode", "llama7b": "llama7b_mha_decode",
                   "opt13b_shared": "opt13b_shared_prefix_decode", "opt13b_cow": "opt13b_cow_decode",
-                  "llama2_70b": "llama2_70b_long_context_decode"}
+                  "llama2_70b": "llama2_70b_long_context_decode",
+                  "llama3_8b_spec": "llama3_8b_speculative_verify_4_tokens",
+                  "llama3_8b_chunk": "llama3_8b_chunked_prefill_512"}
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak, vendor figure
 DTYPE_NAME = {"f32": "f32", "f16": "fp16", "bf16": "bf16"}
 
 
@@ -286,6 +327,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--swap", action="store_true",
                     help="measure pa_swap_blocks (HBM <-> pinned host) instead of the decode step")
+    ap.add_argument("--shared-prefix", action="store_true",
+                    help="opt13b_* workloads: decode with pa_decode_shared_prefix (each group's "
+                         "shared prompt blocks read once) instead of pa_decode")
     ap.add_argument("--workload", default="llama3_8b", choices=sorted(WORKLOADS),
                     help="the benchmark line is llama3_8b; the others are the remaining workloads "
                          "of the same study, measured the same way")
@@ -322,9 +366,37 @@ def main():
     pairs = b.cow_pairs.to(dev) if b.cow_pairs is not None else None
     out = torch.empty_like(q)
     max_len = b.max_seq_len
-    ws = pk.decode_workspace(q, b.num_kv_heads, max_len)
     kv_bytes = b.kv_bytes()
     stream = torch.cuda.current_stream()
+    multi = b.q_start is not None
+    shared = args.shared_prefix
+    if shared and b.group_start is None:
+        raise SystemExit("--shared-prefix needs a workload with shared-prefix groups (opt13b_*)")
+    if multi:
+        qs = b.q_start.to(dev)
+        need = pk.pa_multi_query_workspace_size(b.num_seqs, q.shape[0], b.num_heads, b.num_kv_heads,
+                                                b.head_dim, b.max_q_len, max_len)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+
+        def attend():
+            pk.pa_multi_query(q, kc, vc, bt, lens, qs, b.num_kv_heads, b.scale, out,
+                              max_q_len=b.max_q_len, max_seq_len=max_len, workspace=ws)
+    elif shared:
+        gs, pre = b.group_start.to(dev), b.prefix_lens.to(dev)
+        max_group = int((b.group_start[1:] - b.group_start[:-1]).max())
+        need = pk.pa_decode_shared_prefix_workspace_size(b.num_seqs, len(b.prefix_lens), b.num_heads,
+                                                         b.num_kv_heads, b.head_dim, max_group, max_len)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+
+        def attend():
+            pk.pa_decode_shared_prefix(q, kc, vc, bt, lens, gs, pre, b.num_kv_heads, b.scale, out,
+                                       max_group_size=max_group, max_seq_len=max_len, workspace=ws)
+    else:
+        ws = pk.decode_workspace(q, b.num_kv_heads, max_len)
+
+        def attend():
+            pk.pa_decode(q, kc, vc, bt, lens, b.num_kv_heads, b.scale, out, max_seq_len=max_len,
+                         workspace=ws)
 
     def step(ev0=None, ev1=None):
         # copies and writes are idempotent, so every step repeats the same state change
@@ -334,8 +406,7 @@ def main():
             pk.pa_write_kv(nk, nv, slots, kc, vc)
         if ev0 is not None:
             ev0.record(stream)
-        pk.pa_decode(q, kc, vc, bt, lens, b.num_kv_heads, b.scale, out, max_seq_len=max_len,
-                     workspace=ws)
+        attend()
         if ev1 is not None:
             ev1.record(stream)
 
@@ -387,10 +458,41 @@ def main():
         ub = unique_kv_bytes(b)
         res["config"]["unique_kv_bytes_per_step"] = ub
         res["roofline"]["achieved_unique"] = ub / (dec_avg * 1e-3) / 1e9
+        res["metric"] = "paged-decode KV GB/s read (logical, each sample's prompt counted), OPT-13B-shaped, 1 GPU"
+        if shared:
+            # the shared-prefix call reads each distinct block once: its algorithmic bytes
+            # are the unique bytes, and so is the step's rate
+            res["metric"] = "shared-prefix paged-decode KV GB/s read (distinct blocks), OPT-13B-shaped, 1 GPU"
+            res["config"]["workload"] = WORKLOAD_NAMES[args.workload] + "_grouped"
+            res["value"] = ub / (total / K) / 1e9
+            res["pct_of_hbm_peak"] = 100.0 * res["value"] / HBM_PEAK_GBS
+            res["logical_kv_gbs"] = kv_bytes / (total / K) / 1e9
+            res["roofline"].update({"kernel": "pa_decode_shared_prefix (multi_query_kernel, shared layout)",
+                                    "achieved": res["roofline"]["achieved_unique"],
+                                    "frac": res["roofline"]["achieved_unique"] / HBM_PEAK_GBS,
+                                    "algorithmic_bytes_per_launch": ub})
+    if args.workload in ("llama7b", "llama2_70b"):
+        res["metric"] = f"paged-decode KV GB/s read (% of HBM peak), {WORKLOAD_NAMES[args.workload]}, 1 GPU"
+    if multi:
+        res["metric"] = ("paged multi-query attention, Llama-3-8B-shaped, 1 GPU: KV GB/s read"
+                         if args.workload.endswith("spec") else
+                         "paged multi-query attention, Llama-3-8B-shaped, 1 GPU: causal TFLOP/s")
+        flops = 4.0 * b.causal_pairs() * b.num_heads * b.head_dim
+        res["config"]["query_rows"] = int(q.shape[0])
+        res["config"]["causal_flops_per_step"] = flops
+        res["roofline"]["kernel"] = "pa_multi_query (multi_query_kernel)"
+        if args.workload.endswith("chunk"):
+            tf = flops / (dec_avg * 1e-3) / 1e12
+            res.update({"value": flops / (total / K) / 1e12, "unit": "TFLOP/s"})
+            res["roofline"].update({"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS,
+                                    "unit": "TFLOP/s", "frac": tf / MFMA_BF16_PEAK_TFLOPS,
+                                    "algorithmic_flops_per_launch": flops})
+            res.pop("pct_of_hbm_peak", None)
     if not args.no_cpu_baseline:
         log("cpu baseline: float64 oracle on the host")
         torch.cuda.synchronize()
-        res["cpu_baseline"] = cpu_baseline(b, out.float().cpu().double().numpy())
+        gpu_out = out.float().cpu().double().numpy()
+        res["cpu_baseline"] = (cpu_baseline_multi_query(b, gpu_out) if multi else cpu_baseline(b, gpu_out))
     print(json.dumps(res))
 
 
