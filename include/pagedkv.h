@@ -190,13 +190,15 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst_pa
  *                  q_start[num_seqs] = total_q
  *   seq_lens       device int32 [num_seqs], n_s <= L_s <= max_seq_len
  *   max_q_len      host bound on every n_s (no device sync is made)
- *   workspace      pa_multi_query_workspace_size(...) bytes (0 when the launch
- *                  needs no partition merge); no zero-fill needed
+ *   workspace      pa_multi_query_workspace_size(...) bytes (may be 0): a
+ *                  longest-first order of the sequences when every sequence has
+ *                  at most 16 / group queries, and partial results when the
+ *                  context is partitioned; no zero-fill needed
  *
- * Work is cut into (sequence, KV head, block of 64 query rows, context
+ * Work is cut into (sequence, KV head, block of query rows, context
  * partition) items; with few items the context is split into partitions that
- * a second kernel merges, in a fixed order.  Head_dim 64 or 128; any group size
- * up to 64.  Errors as for pa_decode; index data violating the contract above
+ * a second kernel merges, in a fixed order.  Head_dim 64 or 128; at most 64
+ * query heads per KV head (PA_ERR_UNSUPPORTED above).  Errors as for pa_decode; index data violating the contract above
  * is clamped so that no access leaves the arrays, with unspecified results
  * (PA_DEBUG_CHECK=1 rejects it).  Results are deterministic.
  */
@@ -229,8 +231,9 @@ pa_status pa_multi_query(const void* q, const void* k_cache, const void* v_cache
  *                  member's length
  *   max_group_size host bound on every group's size
  *   other arguments as for pa_decode (block_size any positive value here)
- *   workspace      pa_decode_shared_prefix_workspace_size(...) bytes (0 when no
- *                  partition merge is needed); no zero-fill needed
+ *   workspace      pa_decode_shared_prefix_workspace_size(...) bytes: a
+ *                  longest-first order of the groups and, when the context is
+ *                  partitioned, partial results; no zero-fill needed
  *
  * A group is processed in blocks of 16 / (num_heads / num_kv_heads) members
  * (at most 16 query heads per KV head); each block reads the prefix once.

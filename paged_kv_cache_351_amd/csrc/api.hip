@@ -325,7 +325,9 @@ namespace {
 // 256 tokens, at most 64 of them.
 struct MQPlan {
   int tq = 1, qblocks = 0, parts = 1;
-  bool split = false;          // every block has at most 16 rows: the waves split the context
+  int rows = 64;               // query rows per workgroup (16: the waves split the context)
+  bool split = false;
+  size_t order_bytes = 0;      // longest-first item order at the head of the workspace
   long long items = 0;
   size_t ml_bytes = 0, total = 0;
 };
@@ -337,9 +339,9 @@ MQPlan mq_plan(int num_seqs, int total_q, int num_heads, int num_kv_heads, int h
                int max_q_len, int max_seq_len, int dtype) {
   MQPlan pl;
   const int group = num_heads / num_kv_heads;
-  pl.tq = group >= 64 ? 1 : 64 / group;
   pl.split = dtype != PA_F32 && max_q_len >= 1 && (long long)max_q_len * group <= 16;
-  if (pl.split) pl.tq = 16 / group;
+  pl.rows = pl.split ? 16 : ((long long)max_q_len * group > 64 ? 128 : 64);
+  pl.tq = pl.rows / group;
   pl.qblocks = max_q_len > 0 ? (max_q_len + pl.tq - 1) / pl.tq : 0;
   pl.items = (long long)num_seqs * num_kv_heads * pl.qblocks;
   if (pl.items > 0 && max_seq_len > 0) {
@@ -349,18 +351,23 @@ MQPlan mq_plan(int num_seqs, int total_q, int num_heads, int num_kv_heads, int h
     if (parts > kMQMaxParts) parts = kMQMaxParts;
     pl.parts = parts < 1 ? 1 : (int)parts;
   }
+  // one query block per item (at most 16 rows): lengths alone set each item's work,
+  // so the items are taken longest first
+  if ((long long)max_q_len * group <= 16 && num_seqs > 0)
+    pl.order_bytes = ((size_t)num_seqs * sizeof(int32_t) + 255) / 256 * 256;
   if (pl.parts > 1) {
     const size_t slots = (size_t)total_q * num_heads * pl.parts;
     pl.ml_bytes = (slots * 2 * sizeof(float) + 255) / 256 * 256;
     pl.total = pl.ml_bytes + slots * head_dim * sizeof(float);
   }
+  pl.total += pl.order_bytes;
   return pl;
 }
 
 bool mq_shapes_ok(int num_seqs, int total_q, int num_heads, int num_kv_heads, int head_dim,
                   int max_q_len, int max_seq_len) {
   return num_seqs >= 0 && total_q >= 0 && num_heads > 0 && num_kv_heads > 0 && head_dim > 0 &&
-         num_heads % num_kv_heads == 0 && max_q_len >= 0 && max_seq_len >= 0 &&
+         num_heads % num_kv_heads == 0 && num_heads / num_kv_heads <= 64 && max_q_len >= 0 && max_seq_len >= 0 &&
          max_seq_len <= kMaxSeqLen && max_q_len <= kMaxSeqLen;
 }
 
@@ -396,6 +403,9 @@ pa_status pa_multi_query(const void* q, const void* k_cache, const void* v_cache
     return fail(PA_ERR_INVALID, "pa_multi_query: scale must be finite");
   if (head_dim != 64 && head_dim != 128)
     return fail(PA_ERR_UNSUPPORTED, "pa_multi_query: head_dim %d not in {64, 128}", head_dim);
+  if (num_heads / num_kv_heads > 64)
+    return fail(PA_ERR_UNSUPPORTED, "pa_multi_query: %d query heads per KV head (at most 64)",
+                num_heads / num_kv_heads);
   if ((long long)max_seq_len > (long long)max_blocks_per_seq * block_size)
     return fail(PA_ERR_INVALID, "pa_multi_query: max_seq_len %d exceeds max_blocks_per_seq * block_size (%lld)",
                 max_seq_len, (long long)max_blocks_per_seq * block_size);
@@ -444,7 +454,7 @@ pa_status pa_multi_query(const void* q, const void* k_cache, const void* v_cache
   }
   const void* kmain = nullptr;
   const void* kmerge = nullptr;
-  if (!multi_query_kernels((int)dtype, head_dim, pl.split, false, &kmain, &kmerge))
+  if (!multi_query_kernels((int)dtype, head_dim, pl.rows, false, &kmain, &kmerge))
     return fail(PA_ERR_UNSUPPORTED, "pa_multi_query: no kernel for this dtype and head_dim");
   MultiQueryParams mp;
   mp.q = q;
@@ -455,8 +465,11 @@ pa_status pa_multi_query(const void* q, const void* k_cache, const void* v_cache
   mp.q_start = q_start;
   mp.prefix_lens = nullptr;
   mp.out = out;
-  mp.ws_ml = pl.total > 0 ? reinterpret_cast<float*>(workspace) : nullptr;
-  mp.ws_acc = pl.total > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.ml_bytes) : nullptr;
+  char* ws = static_cast<char*>(workspace);
+  mp.order = pl.order_bytes > 0 ? reinterpret_cast<const int32_t*>(ws) : nullptr;
+  mp.order_out = pl.order_bytes > 0 ? reinterpret_cast<int32_t*>(ws) : nullptr;
+  mp.ws_ml = pl.parts > 1 ? reinterpret_cast<float*>(ws + pl.order_bytes) : nullptr;
+  mp.ws_acc = pl.parts > 1 ? reinterpret_cast<float*>(ws + pl.order_bytes + pl.ml_bytes) : nullptr;
   mp.num_seqs = num_seqs;
   mp.total_q = total_q;
   mp.num_heads = num_heads;
@@ -475,7 +488,12 @@ pa_status pa_multi_query(const void* q, const void* k_cache, const void* v_cache
   mp.scale_log2e = (float)((double)scale * 1.4426950408889634074);
   const long long wgs = (pl.items * pl.parts + 7) / 8 * 8;
   void* args[] = {&mp};
-  hipError_t e = hipLaunchKernel(kmain, dim3((unsigned)wgs), dim3(256), args, 0, st);
+  hipError_t e;
+  if (pl.order_bytes > 0) {
+    e = hipLaunchKernel(multi_query_order_kernel(false), dim3(1), dim3(1024), args, 0, st);
+    if (e != hipSuccess) return hip_fail(e, "pa_multi_query order launch");
+  }
+  e = hipLaunchKernel(kmain, dim3((unsigned)wgs), dim3(256), args, 0, st);
   if (e != hipSuccess) return hip_fail(e, "pa_multi_query launch");
   if (pl.parts > 1) {
     const long long rows = (long long)total_q * num_heads;
@@ -494,6 +512,7 @@ MQPlan sp_plan(int num_seqs, int num_groups, int num_heads, int num_kv_heads, in
   MQPlan pl;
   const int group = num_heads / num_kv_heads;
   pl.split = true;
+  pl.rows = 16;
   pl.tq = 16 / group;
   pl.qblocks = max_group_size > 0 ? (max_group_size + pl.tq - 1) / pl.tq : 0;
   pl.items = (long long)num_groups * num_kv_heads * pl.qblocks;
@@ -504,11 +523,13 @@ MQPlan sp_plan(int num_seqs, int num_groups, int num_heads, int num_kv_heads, in
     if (parts > kMQMaxParts) parts = kMQMaxParts;
     pl.parts = parts < 1 ? 1 : (int)parts;
   }
+  if (num_groups > 0) pl.order_bytes = ((size_t)num_groups * sizeof(int32_t) + 255) / 256 * 256;
   if (pl.parts > 1) {
     const size_t slots = (size_t)num_seqs * num_heads * pl.parts;
     pl.ml_bytes = (slots * 2 * sizeof(float) + 255) / 256 * 256;
     pl.total = pl.ml_bytes + slots * head_dim * sizeof(float);
   }
+  pl.total += pl.order_bytes;
   return pl;
 }
 
@@ -611,7 +632,7 @@ pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void
   }
   const void* kmain = nullptr;
   const void* kmerge = nullptr;
-  if (!multi_query_kernels((int)dtype, head_dim, true, true, &kmain, &kmerge))
+  if (!multi_query_kernels((int)dtype, head_dim, 16, true, &kmain, &kmerge))
     return fail(PA_ERR_UNSUPPORTED, "%s: no kernel for this dtype and head_dim", who);
   MultiQueryParams mp;
   mp.q = q;
@@ -622,8 +643,11 @@ pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void
   mp.q_start = group_start;
   mp.prefix_lens = prefix_lens;
   mp.out = out;
-  mp.ws_ml = pl.total > 0 ? reinterpret_cast<float*>(workspace) : nullptr;
-  mp.ws_acc = pl.total > 0 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.ml_bytes) : nullptr;
+  char* ws = static_cast<char*>(workspace);
+  mp.order = pl.order_bytes > 0 ? reinterpret_cast<const int32_t*>(ws) : nullptr;
+  mp.order_out = pl.order_bytes > 0 ? reinterpret_cast<int32_t*>(ws) : nullptr;
+  mp.ws_ml = pl.parts > 1 ? reinterpret_cast<float*>(ws + pl.order_bytes) : nullptr;
+  mp.ws_acc = pl.parts > 1 ? reinterpret_cast<float*>(ws + pl.order_bytes + pl.ml_bytes) : nullptr;
   mp.num_seqs = num_groups;          // items run over groups
   mp.total_q = num_seqs;             // rows are member sequences
   mp.num_heads = num_heads;
@@ -642,7 +666,9 @@ pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void
   mp.scale_log2e = (float)((double)scale * 1.4426950408889634074);
   const long long wgs = (pl.items * pl.parts + 7) / 8 * 8;
   void* args[] = {&mp};
-  hipError_t e = hipLaunchKernel(kmain, dim3((unsigned)wgs), dim3(256), args, 0, st);
+  hipError_t e = hipLaunchKernel(multi_query_order_kernel(true), dim3(1), dim3(1024), args, 0, st);
+  if (e != hipSuccess) return hip_fail(e, "pa_decode_shared_prefix order launch");
+  e = hipLaunchKernel(kmain, dim3((unsigned)wgs), dim3(256), args, 0, st);
   if (e != hipSuccess) return hip_fail(e, "pa_decode_shared_prefix launch");
   if (pl.parts > 1) {
     const long long rows = (long long)num_seqs * num_heads;

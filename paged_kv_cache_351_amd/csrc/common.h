@@ -65,6 +65,9 @@ struct MultiQueryParams {
                                // [num_groups + 1] first member sequence of each group
   const int32_t* prefix_lens;  // shared-prefix decode: [num_groups] shared tokens
   void* out;                   // [total_q][num_heads][head_dim]
+  const int32_t* order;        // [num_seqs]: items' sequences (groups), longest first, or
+                               // null: workgroups in XCD-major order instead
+  int32_t* order_out;          // where the ordering pass writes `order`
   float* ws_ml;                // [total_q * num_heads][parts][2] running max and sum
   float* ws_acc;               // [total_q * num_heads][parts][head_dim]
   int num_seqs;
@@ -78,18 +81,22 @@ struct MultiQueryParams {
   int max_blocks_per_seq;
   int max_q_len;
   int max_seq_len;
-  int tq;                      // query tokens per workgroup: 64 rows / group, or
-                               // 16 / group when all four waves share 16 rows
+  int tq;                      // query tokens (or group members) per workgroup:
+                               // its rows (16, 64 or 128) / group
   int qblocks;                 // query blocks per (sequence, KV head): ceil(max_q_len / tq)
   int parts;                   // context partitions; 1 = no merge step
   long long items;             // num_seqs * num_kv_heads * qblocks
   float scale_log2e;
 };
 
-// The multi-query and partition-merge kernels for one element type and head_dim;
-// `split` picks the variant for blocks of at most 16 query rows, `shared` the
-// shared-prefix decode (both 16-bit types only).
-bool multi_query_kernels(int dtype, int head_dim, bool split, bool shared, const void** main,
+// The pass that orders the items' sequences (shared: groups) longest first.
+const void* multi_query_order_kernel(bool shared);
+
+// The multi-query and partition-merge kernels for one element type and head_dim.
+// rows = query rows per workgroup: 16 (the four waves split the context; 16-bit
+// types), 64 or 128 (16 or 32 rows per wave sharing K/V tiles); `shared` picks the
+// shared-prefix decode (16 rows, 16-bit types).
+bool multi_query_kernels(int dtype, int head_dim, int rows, bool shared, const void** main,
                          const void** merge);
 
 // Message returned by pa_last_error() on the calling thread.

@@ -121,10 +121,17 @@ struct Item {
   int s, kv, qb, part;
 };
 
+// Decode the workgroup's item.  With an ordering, workgroups take the items in
+// dispatch order, longest sequence (group) first, so that the last ones to start are
+// the shortest; otherwise every query block and partition of one (sequence, KV head)
+// goes to the same XCD (workgroup id mod 8), where they share its L2.
 __device__ __forceinline__ bool item_of(const MultiQueryParams& p, Item& it) {
-  const long long per = (long long)gridDim.x / 8;  // the grid is a multiple of 8
   const long long b = blockIdx.x;
-  const long long logical = (b % 8) * per + b / 8;
+  long long logical = b;
+  if (!p.order) {
+    const long long per = (long long)gridDim.x / 8;  // the grid is a multiple of 8
+    logical = (b % 8) * per + b / 8;
+  }
   if (logical >= (long long)p.items * p.parts) return false;
   it.part = (int)(logical % p.parts);
   long long r = logical / p.parts;
@@ -132,7 +139,67 @@ __device__ __forceinline__ bool item_of(const MultiQueryParams& p, Item& it) {
   r /= p.qblocks;
   it.kv = (int)(r % p.num_kv_heads);
   it.s = (int)(r / p.num_kv_heads);
-  return it.s < p.num_seqs;
+  if (it.s >= p.num_seqs) return false;
+  if (p.order) {
+    const int s = p.order[it.s];
+    if (s < 0 || s >= p.num_seqs) return false;
+    it.s = s;
+  }
+  return true;
+}
+
+// Longest-first ordering of the items' sequences (multi-query) or groups (shared
+// prefix), one workgroup: a counting sort on the number of 32-token tiles (capped),
+// written to order_out.  Equal keys may come out in any order; each item's result
+// does not depend on which workgroup computes it.
+constexpr int kOrderBuckets = 4096;
+
+template <bool SHARED>
+__global__ __launch_bounds__(1024) void item_order_kernel(MultiQueryParams p) {
+  __shared__ int hist[kOrderBuckets];
+  __shared__ int part[1024];
+  const int tid = threadIdx.x;
+  auto clamp_len = [&](int x) { return x < 0 ? 0 : (x > p.max_seq_len ? p.max_seq_len : x); };
+  auto bucket = [&](int s) {
+    int tiles;
+    if constexpr (!SHARED) {
+      tiles = (clamp_len(p.seq_lens[s]) + kTile - 1) / kTile;
+    } else {
+      const int a = p.q_start[s];
+      int n = p.q_start[s + 1] - a;
+      n = n < 0 ? 0 : (n > p.max_q_len ? p.max_q_len : n);
+      if (a < 0 || a + n > p.total_q) n = 0;
+      int lmin = 0x7fffffff;
+      for (int i = 0; i < n; ++i) lmin = min(lmin, clamp_len(p.seq_lens[a + i]));
+      const int P = n > 0 ? min(clamp_len(p.prefix_lens[s]), lmin) : 0;
+      tiles = (P + kTile - 1) / kTile;
+      for (int i = 0; i < n && tiles < kOrderBuckets; ++i)
+        tiles += (clamp_len(p.seq_lens[a + i]) - P + kTile - 1) / kTile;
+    }
+    return kOrderBuckets - 1 - min(tiles, kOrderBuckets - 1);  // ascending bucket = descending work
+  };
+  for (int i = tid; i < kOrderBuckets; i += 1024) hist[i] = 0;
+  __syncthreads();
+  for (int s = tid; s < p.num_seqs; s += 1024) atomicAdd(&hist[bucket(s)], 1);
+  __syncthreads();
+  // exclusive prefix sum of the histogram: thread t owns buckets 4t .. 4t+3
+  const int h0 = hist[4 * tid], h1 = hist[4 * tid + 1], h2 = hist[4 * tid + 2], h3 = hist[4 * tid + 3];
+  const int mine = h0 + h1 + h2 + h3;
+  part[tid] = mine;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int v = tid >= o ? part[tid - o] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  const int base = part[tid] - mine;
+  hist[4 * tid] = base;
+  hist[4 * tid + 1] = base + h0;
+  hist[4 * tid + 2] = base + h0 + h1;
+  hist[4 * tid + 3] = base + h0 + h1 + h2;
+  __syncthreads();
+  for (int s = tid; s < p.num_seqs; s += 1024) p.order_out[atomicAdd(&hist[bucket(s)], 1)] = s;
 }
 
 // Where the 32 tokens of one tile come from: tokens base .. base + count - 1 of
@@ -144,25 +211,29 @@ struct TileMap {
   int base, count, owner;
 };
 
-// SPLIT = false: the four waves own 16 rows each of a 64-row query block and
-// share every K/V tile through LDS (prefill-sized blocks).
-// SPLIT = true (16-bit types, at most 16 rows per block): the four waves work on
-// the same 16 rows and take every fourth tile of the partition each, K straight
-// from HBM into registers in the matrix-core layout and V through a
+// SPLIT = false: the four waves own 16 RB rows each of a 64 RB-row query block
+// and share every K/V tile through LDS (prefill-sized blocks); with RB = 2 every
+// K/V fragment read from LDS feeds two 16-row products, and registers are capped
+// for two waves per SIMD so that two workgroups share a CU across the barriers.
+// SPLIT = true (16-bit types, at most 16 rows per block, RB = 1): the four waves
+// work on the same 16 rows and take every fourth tile of the partition each, K
+// straight from HBM into registers in the matrix-core layout and V through a
 // wave-private LDS region, with no workgroup barrier in the loop; their four
 // partial results are merged through LDS at the end.
 // SHARED (split only): the item is a group of sequences whose first tokens sit in
 // the same blocks; rows are (member, head), and the tiles are the shared prefix
 // (read once, seen by every member) followed by each member's own tail (seen by
 // that member only), each padded to whole tiles.
-template <int DT, int D, bool SPLIT, bool SHARED>
-__global__ __launch_bounds__(256) void multi_query_kernel(MultiQueryParams p) {
+template <int DT, int D, bool SPLIT, bool SHARED, int RB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 2 ? 2 : 1)))
+void multi_query_kernel(MultiQueryParams p) {
   using S = Shape<DT, D>;
   constexpr int EB = S::EB, CR = S::CR, NKC = S::NKC, NJ = S::NJ;
   constexpr int VREG = D * S::VSTRIDE;                     // one transposed V tile
   constexpr int LDS_BYTES = SPLIT ? 4 * VREG : S::LDS;
   static_assert(!SPLIT || (DT != kF32 && 4 * 16 * (D + 2) * 4 <= LDS_BYTES), "split merge space");
   static_assert(SPLIT || !SHARED, "shared-prefix groups use the split variant");
+  static_assert(RB == 1 || (RB == 2 && !SPLIT), "two row blocks only with shared tiles");
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
 
   Item it;
@@ -186,14 +257,21 @@ __global__ __launch_bounds__(256) void multi_query_kernel(MultiQueryParams p) {
   const int tok1 = min(n, tok0 + p.tq);
   auto clamp_len = [&](int x) { return x < 0 ? 0 : (x > p.max_seq_len ? p.max_seq_len : x); };
 
-  // this lane's row (row col of the wave's 16)
-  const int rloc = SPLIT ? col : wave * 16 + col;
-  const int qtok = tok0 + rloc / g;
-  const int qh = rloc % g;
-  const bool row_ok = rloc < p.tq * g && qtok < tok1;
-  const size_t out_row = (size_t)(qa + qtok) * Hq + (size_t)it.kv * g + qh;
+  // this lane's rows: row col of each of the wave's RB blocks of 16
+  int qtok[RB], qh[RB];
+  bool row_ok[RB];
+  size_t out_row[RB];
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    const int rloc = SPLIT ? col : (wave * RB + b) * 16 + col;
+    qtok[b] = tok0 + rloc / g;
+    qh[b] = rloc % g;
+    row_ok[b] = rloc < p.tq * g && qtok[b] < tok1;
+    out_row[b] = (size_t)(qa + qtok[b]) * Hq + (size_t)it.kv * g + qh[b];
+  }
 
-  int L = 0, pos = 0, pos_lo = 0, t_end = 0;       // multi-query
+  int L = 0, pos_lo = 0, t_end = 0;                // multi-query
+  int pos[RB];                                      // each row's causal limit (inclusive)
   int P = 0, VP = 0, m_off = 0, m_tail = 0;        // shared prefix: lane i < tok1 - tok0 = member i
   const int32_t* tables = p.block_tables;
   const int32_t* seq_table = nullptr;
@@ -201,7 +279,8 @@ __global__ __launch_bounds__(256) void multi_query_kernel(MultiQueryParams p) {
     L = clamp_len(p.seq_lens[it.s]);
     const int pos_hi = L - n + tok1 - 1;           // last query position of the block
     pos_lo = L - n + tok0;                         // first query position of the block
-    pos = L - n + qtok;                            // the row's causal limit (inclusive)
+#pragma unroll
+    for (int b = 0; b < RB; ++b) pos[b] = L - n + qtok[b];
     t_end = min(L, pos_hi + 1);
     seq_table = tables + (size_t)it.s * p.max_blocks_per_seq;
   } else {
@@ -226,6 +305,8 @@ __global__ __launch_bounds__(256) void multi_query_kernel(MultiQueryParams p) {
     m_off = incl - padded;
     t_end = VP + __shfl(incl, 15);
     seq_table = tables + (size_t)(qa + tok0) * p.max_blocks_per_seq;  // the group's first member
+#pragma unroll
+    for (int b = 0; b < RB; ++b) pos[b] = 0;
   }
   // with several partitions, the item's own range is cut into equal whole tiles
   int t_begin = 0;
@@ -256,19 +337,26 @@ __global__ __launch_bounds__(256) void multi_query_kernel(MultiQueryParams p) {
   };
 
   // query fragments: the same chunks of the row as the K fragments
-  u32x4 qf[NKC];
+  u32x4 qf[RB][NKC];
 #pragma unroll
-  for (int c = 0; c < NKC; ++c) {
-    qf[c] = u32x4{0u, 0u, 0u, 0u};
-    if (row_ok)
-      qf[c] = *reinterpret_cast<const u32x4*>((const char*)p.q + out_row * S::ROWB +
-                                              chunk_of<DT, D>(c, grp) * 16);
-  }
+  for (int b = 0; b < RB; ++b)
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) {
+      qf[b][c] = u32x4{0u, 0u, 0u, 0u};
+      if (row_ok[b])
+        qf[b][c] = *reinterpret_cast<const u32x4*>((const char*)p.q + out_row[b] * S::ROWB +
+                                                   chunk_of<DT, D>(c, grp) * 16);
+    }
 
-  f32x4 acc[NJ];
+  f32x4 acc[RB][NJ];
+  float m[RB], l[RB];
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = kNegBig, l = 0.f;
+  for (int b = 0; b < RB; ++b) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) acc[b][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m[b] = kNegBig;
+    l[b] = 0.f;
+  }
 
   const int B = p.block_size;
   const size_t kv_off = (size_t)it.kv * S::ROWB;
@@ -277,9 +365,9 @@ __global__ __launch_bounds__(256) void multi_query_kernel(MultiQueryParams p) {
   // tile's count read its last valid token, so nothing outside a sequence is read
   auto row_addr = [&](const TileMap& mp, int i) -> size_t {
     const int t = mp.base + min(i, mp.count - 1);
-    int b = mp.table[t / B];
-    b = b < 0 ? 0 : (b >= p.num_blocks ? p.num_blocks - 1 : b);
-    return ((size_t)b * B + t % B) * slot_bytes + kv_off;
+    int bk = mp.table[t / B];
+    bk = bk < 0 ? 0 : (bk >= p.num_blocks ? p.num_blocks - 1 : bk);
+    return ((size_t)bk * B + t % B) * slot_bytes + kv_off;
   };
 
   // V rows of a tile as token pairs: `lanes` lanes take pair-chunks idx = me + lanes k
@@ -364,23 +452,27 @@ __global__ __launch_bounds__(256) void multi_query_kernel(MultiQueryParams p) {
     const int t0 = t_begin + k * kTile;
     const bool more = k + kstep < ntiles;
     const TileMap nxt = more ? tile_map(t0 + kstep * kTile) : cur;
-    // S^T = K Q^T for the two 16-token halves
-    f32x4 sc[2];
+    // S^T = K Q^T for the two 16-token halves and every row block
+    f32x4 sc[RB][2];
     auto qk = [&](int h, int c, u32x4 a) {
-      if constexpr (DT == kBF16) {
-        sc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                        __builtin_bit_cast(bf16x8, qf[c]), sc[h], 0, 0, 0);
-      } else if constexpr (DT == kF16) {
-        sc[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
-                                                       __builtin_bit_cast(f16x8, qf[c]), sc[h], 0, 0, 0);
-      } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          sc[h] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[e]), __uint_as_float(qf[c][e]),
-                                                       sc[h], 0, 0, 0);
+      for (int b = 0; b < RB; ++b) {
+        if constexpr (DT == kBF16) {
+          sc[b][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                             __builtin_bit_cast(bf16x8, qf[b][c]), sc[b][h], 0, 0, 0);
+        } else if constexpr (DT == kF16) {
+          sc[b][h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                            __builtin_bit_cast(f16x8, qf[b][c]), sc[b][h], 0, 0, 0);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            sc[b][h] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[e]), __uint_as_float(qf[b][c][e]),
+                                                            sc[b][h], 0, 0, 0);
+        }
       }
     };
-    sc[0] = sc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int b = 0; b < RB; ++b) sc[b][0] = sc[b][1] = f32x4{0.f, 0.f, 0.f, 0.f};
     if constexpr (SPLIT) {
       // this tile's K is in registers: stage its V and fetch the wave's next V,
       // multiply, then fetch the next K (no second copy of the K registers)
@@ -411,110 +503,135 @@ __global__ __launch_bounds__(256) void multi_query_kernel(MultiQueryParams p) {
     }
     // online softmax: tile token 16 h + 4 grp + i of row col; full tiles that every
     // row may see in full need no mask
-    float sv[8];
+    float pr[RB][8], alpha[RB];
     const bool whole = cur.count == kTile && (SHARED ? cur.owner < 0 : t0 + kTile - 1 <= pos_lo);
-    if (whole) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+    for (int b = 0; b < RB; ++b) {
+      float sv[8];
+      if (whole) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sv[4 * h + i] = sc[h][i] * sl2;
-    } else {
-      const bool row_sees = !SHARED || cur.owner < 0 || cur.owner == qtok - tok0;
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+          for (int i = 0; i < 4; ++i) sv[4 * h + i] = sc[b][h][i] * sl2;
+      } else {
+        const bool row_sees = !SHARED || cur.owner < 0 || cur.owner == qtok[b] - tok0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int u = 16 * h + 4 * grp + i;
-          const bool ok = SHARED ? (row_sees && u < cur.count) : (u < cur.count && t0 + u <= pos);
-          sv[4 * h + i] = ok ? sc[h][i] * sl2 : -__builtin_inff();
-        }
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int u = 16 * h + 4 * grp + i;
+            const bool ok = SHARED ? (row_sees && u < cur.count) : (u < cur.count && t0 + u <= pos[b]);
+            sv[4 * h + i] = ok ? sc[b][h][i] * sl2 : -__builtin_inff();
+          }
+      }
+      float mx = sv[0];
+#pragma unroll
+      for (int u = 1; u < 8; ++u) mx = fmaxf(mx, sv[u]);
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mn = fmaxf(m[b], mx);
+      alpha[b] = fast_exp2(m[b] - mn);
+      m[b] = mn;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) pr[b][u] = fast_exp2(sv[u] - mn);
     }
     cur = nxt;
-    float mx = sv[0];
+    bool moved = false;
 #pragma unroll
-    for (int u = 1; u < 8; ++u) mx = fmaxf(mx, sv[u]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mn = fmaxf(m, mx);
-    const float alpha = fast_exp2(m - mn);
-    m = mn;
-    float pr[8];
+    for (int b = 0; b < RB; ++b) moved = moved || alpha[b] != 1.0f;
+    if (__any(moved)) {  // rescale only when some row's maximum moved
 #pragma unroll
-    for (int u = 0; u < 8; ++u) pr[u] = fast_exp2(sv[u] - mn);
-    if (__any(alpha != 1.0f)) {  // rescale only when some row's maximum moved
+      for (int b = 0; b < RB; ++b)
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) acc[j] *= alpha;
+        for (int j = 0; j < NJ; ++j) acc[b][j] *= alpha[b];
     }
 
     if constexpr (DT == kF32) {
-      l = l * alpha + (((pr[0] + pr[1]) + (pr[2] + pr[3])) + ((pr[4] + pr[5]) + (pr[6] + pr[7])));
+#pragma unroll
+      for (int b = 0; b < RB; ++b)
+        l[b] = l[b] * alpha[b] + (((pr[b][0] + pr[b][1]) + (pr[b][2] + pr[b][3])) +
+                                  ((pr[b][4] + pr[b][5]) + (pr[b][6] + pr[b][7])));
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const char* vrow = ldsV + (16 * j + col) * S::VSTRIDE + grp * 32;
         const u32x4 a0 = *reinterpret_cast<const u32x4*>(vrow);
         const u32x4 a1 = *reinterpret_cast<const u32x4*>(vrow + 16);
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a0[u]), pr[u], acc[j], 0, 0, 0);
+        for (int b = 0; b < RB; ++b) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a1[u]), pr[4 + u], acc[j], 0, 0, 0);
+          for (int u = 0; u < 4; ++u)
+            acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a0[u]), pr[b][u], acc[b][j], 0, 0, 0);
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a1[u]), pr[b][4 + u], acc[b][j], 0, 0, 0);
+        }
       }
     } else {
       // P in the storage type; for bf16 (8 significant bits) as a sum of two bf16
       // values, the second the rounding error of the first, which carries about 16
       // significant bits through two products with the same V fragment
-      uint32_t pw[4], pw_lo[4];
-      float ps = 0.f;
+      u32x4 pb[RB], pb_lo[RB];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint16_t a = to_store<DT>(pr[2 * u]), b = to_store<DT>(pr[2 * u + 1]);
-        const float fa = from_store<DT>(a), fb = from_store<DT>(b);
-        pw[u] = (uint32_t)a | ((uint32_t)b << 16);
-        if constexpr (DT == kBF16) {
-          const uint16_t a2 = to_store<DT>(pr[2 * u] - fa), b2 = to_store<DT>(pr[2 * u + 1] - fb);
-          pw_lo[u] = (uint32_t)a2 | ((uint32_t)b2 << 16);
-          ps += (fa + from_store<DT>(a2)) + (fb + from_store<DT>(b2));
-        } else {
-          ps += fa + fb;
+      for (int b = 0; b < RB; ++b) {
+        uint32_t pw[4], pw_lo[4];
+        float ps = 0.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const uint16_t x = to_store<DT>(pr[b][2 * u]), y = to_store<DT>(pr[b][2 * u + 1]);
+          const float fx = from_store<DT>(x), fy = from_store<DT>(y);
+          pw[u] = (uint32_t)x | ((uint32_t)y << 16);
+          if constexpr (DT == kBF16) {
+            const uint16_t x2 = to_store<DT>(pr[b][2 * u] - fx), y2 = to_store<DT>(pr[b][2 * u + 1] - fy);
+            pw_lo[u] = (uint32_t)x2 | ((uint32_t)y2 << 16);
+            ps += (fx + from_store<DT>(x2)) + (fy + from_store<DT>(y2));
+          } else {
+            pw_lo[u] = 0u;
+            ps += fx + fy;
+          }
         }
+        l[b] = l[b] * alpha[b] + ps;
+        pb[b] = u32x4{pw[0], pw[1], pw[2], pw[3]};
+        pb_lo[b] = u32x4{pw_lo[0], pw_lo[1], pw_lo[2], pw_lo[3]};
       }
-      l = l * alpha + ps;
-      const u32x4 pb = u32x4{pw[0], pw[1], pw[2], pw[3]};
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const u32x4 a = *reinterpret_cast<const u32x4*>(ldsV + (16 * j + col) * S::VSTRIDE + grp * 16);
-        if constexpr (DT == kBF16) {
-          const u32x4 pb_lo = u32x4{pw_lo[0], pw_lo[1], pw_lo[2], pw_lo[3]};
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                           __builtin_bit_cast(bf16x8, pb), acc[j], 0, 0, 0);
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                           __builtin_bit_cast(bf16x8, pb_lo), acc[j], 0, 0, 0);
-        } else {
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
-                                                          __builtin_bit_cast(f16x8, pb), acc[j], 0, 0, 0);
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+          if constexpr (DT == kBF16) {
+            acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                                __builtin_bit_cast(bf16x8, pb[b]), acc[b][j], 0, 0, 0);
+            acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                                __builtin_bit_cast(bf16x8, pb_lo[b]), acc[b][j], 0, 0, 0);
+          } else {
+            acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                               __builtin_bit_cast(f16x8, pb[b]), acc[b][j], 0, 0, 0);
+          }
         }
       }
     }
     if constexpr (SPLIT) __builtin_amdgcn_wave_barrier();  // V reads above before the next stores
   }
 
-  // the row's sum over its four lanes; lane (grp, col) holds head_dim 16 j + 4 grp + i
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
+  // each row's sum over its four lanes; lane (grp, col) holds head_dim 16 j + 4 grp + i
+#pragma unroll
+  for (int b = 0; b < RB; ++b) {
+    l[b] += __shfl_xor(l[b], 16);
+    l[b] += __shfl_xor(l[b], 32);
+  }
   if constexpr (SPLIT) {
     // merge the four waves' results for the same 16 rows: wave w's (m, l) and
     // accumulator go to LDS region w; then wave w combines head_dim blocks j = w (mod 4)
     __syncthreads();   // every wave is done with its V region
     float* mine = reinterpret_cast<float*>(lds) + wave * 16 * (D + 2);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) *reinterpret_cast<f32x4*>(mine + col * D + 16 * j + 4 * grp) = acc[j];
+    for (int j = 0; j < NJ; ++j) *reinterpret_cast<f32x4*>(mine + col * D + 16 * j + 4 * grp) = acc[0][j];
     if (grp == 0) {
-      mine[16 * D + 2 * col] = m;
-      mine[16 * D + 2 * col + 1] = l;
+      mine[16 * D + 2 * col] = m[0];
+      mine[16 * D + 2 * col + 1] = l[0];
     }
     __syncthreads();
-    if (!row_ok) return;
+    if (!row_ok[0]) return;
     const float* part = reinterpret_cast<const float*>(lds);
     float M = kNegBig;
 #pragma unroll
@@ -533,29 +650,35 @@ __global__ __launch_bounds__(256) void multi_query_kernel(MultiQueryParams p) {
       for (int w = 0; w < 4; ++w)
         o += wt[w] * *reinterpret_cast<const f32x4*>(part + w * 16 * (D + 2) + col * D + 16 * j + 4 * grp);
       if (p.parts == 1) {
-        store4<DT>((char*)p.out + out_row * S::ROWB + (16 * j + 4 * grp) * EB, o * inv);
-      } else {
-        const size_t slot = out_row * p.parts + it.part;
+        store4<DT>((char*)p.out + out_row[0] * S::ROWB + (16 * j + 4 * grp) * EB, o * inv);
+      } else if (ntiles > 0) {  // the merge reads no accumulator of an empty partition
+        const size_t slot = out_row[0] * p.parts + it.part;
         *reinterpret_cast<f32x4*>(p.ws_acc + slot * D + 16 * j + 4 * grp) = o;
       }
     }
     if (p.parts > 1 && wave == 0 && grp == 0) {
-      const size_t slot = out_row * p.parts + it.part;
+      const size_t slot = out_row[0] * p.parts + it.part;
       *reinterpret_cast<u32x2*>(p.ws_ml + slot * 2) = u32x2{__float_as_uint(M), __float_as_uint(Lsum)};
     }
   } else {
-    if (!row_ok) return;
-    if (p.parts == 1) {
-      const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        store4<DT>((char*)p.out + out_row * S::ROWB + (16 * j + 4 * grp) * EB, acc[j] * inv);
-    } else {
-      const size_t slot = out_row * p.parts + it.part;
+    for (int b = 0; b < RB; ++b) {
+      if (!row_ok[b]) continue;
+      if (p.parts == 1) {
+        const float inv = l[b] > 0.f ? 1.f / l[b] : 0.f;
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        *reinterpret_cast<f32x4*>(p.ws_acc + slot * D + 16 * j + 4 * grp) = acc[j];
-      if (grp == 0) *reinterpret_cast<u32x2*>(p.ws_ml + slot * 2) = u32x2{__float_as_uint(m), __float_as_uint(l)};
+        for (int j = 0; j < NJ; ++j)
+          store4<DT>((char*)p.out + out_row[b] * S::ROWB + (16 * j + 4 * grp) * EB, acc[b][j] * inv);
+      } else {
+        const size_t slot = out_row[b] * p.parts + it.part;
+        if (ntiles > 0) {  // the merge reads no accumulator of an empty partition
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            *reinterpret_cast<f32x4*>(p.ws_acc + slot * D + 16 * j + 4 * grp) = acc[b][j];
+        }
+        if (grp == 0)
+          *reinterpret_cast<u32x2*>(p.ws_ml + slot * 2) = u32x2{__float_as_uint(m[b]), __float_as_uint(l[b])};
+      }
     }
   }
 }
@@ -575,6 +698,7 @@ __global__ __launch_bounds__(256) void multi_query_merge_kernel(MultiQueryParams
   float o[PER] = {};
   float lsum = 0.f;
   for (int q = 0; q < p.parts; ++q) {
+    if (!(ml[2 * q + 1] > 0.f)) continue;   // empty partition: no accumulator was written
     const float w = fast_exp2(ml[2 * q] - M);
     lsum += w * ml[2 * q + 1];
     const float* a = p.ws_acc + ((size_t)rh * p.parts + q) * D;
@@ -592,30 +716,31 @@ __global__ __launch_bounds__(256) void multi_query_merge_kernel(MultiQueryParams
 }
 
 template <int DT, int D>
-void pick_d(bool split, bool shared, const void** main, const void** merge) {
+void pick_d(int rows, bool shared, const void** main, const void** merge) {
   *merge = reinterpret_cast<const void*>(&multi_query_merge_kernel<DT, D>);
   if constexpr (DT != kF32) {
     if (shared) {
-      *main = reinterpret_cast<const void*>(&multi_query_kernel<DT, D, true, true>);
+      *main = reinterpret_cast<const void*>(&multi_query_kernel<DT, D, true, true, 1>);
       return;
     }
-    if (split) {
-      *main = reinterpret_cast<const void*>(&multi_query_kernel<DT, D, true, false>);
+    if (rows == 16) {
+      *main = reinterpret_cast<const void*>(&multi_query_kernel<DT, D, true, false, 1>);
       return;
     }
   }
-  *main = reinterpret_cast<const void*>(&multi_query_kernel<DT, D, false, false>);
+  if (rows == 128) *main = reinterpret_cast<const void*>(&multi_query_kernel<DT, D, false, false, 2>);
+  else *main = reinterpret_cast<const void*>(&multi_query_kernel<DT, D, false, false, 1>);
 }
 
 template <int DT>
-bool pick_dt(int head_dim, bool split, bool shared, const void** main, const void** merge) {
-  if ((split || shared) && DT == kF32) return false;
+bool pick_dt(int head_dim, int rows, bool shared, const void** main, const void** merge) {
+  if ((rows == 16 || shared) && DT == kF32) return false;
   if (head_dim == 64) {
-    pick_d<DT, 64>(split, shared, main, merge);
+    pick_d<DT, 64>(rows, shared, main, merge);
     return true;
   }
   if (head_dim == 128) {
-    pick_d<DT, 128>(split, shared, main, merge);
+    pick_d<DT, 128>(rows, shared, main, merge);
     return true;
   }
   return false;
@@ -623,12 +748,18 @@ bool pick_dt(int head_dim, bool split, bool shared, const void** main, const voi
 
 }  // namespace
 
-bool multi_query_kernels(int dtype, int head_dim, bool split, bool shared, const void** main,
+const void* multi_query_order_kernel(bool shared) {
+  return shared ? reinterpret_cast<const void*>(&item_order_kernel<true>)
+                : reinterpret_cast<const void*>(&item_order_kernel<false>);
+}
+
+bool multi_query_kernels(int dtype, int head_dim, int rows, bool shared, const void** main,
                          const void** merge) {
+  if (rows != 16 && rows != 64 && rows != 128) return false;
   switch (dtype) {
-    case kF32: return pick_dt<kF32>(head_dim, split, shared, main, merge);
-    case kF16: return pick_dt<kF16>(head_dim, split, shared, main, merge);
-    case kBF16: return pick_dt<kBF16>(head_dim, split, shared, main, merge);
+    case kF32: return pick_dt<kF32>(head_dim, rows, shared, main, merge);
+    case kF16: return pick_dt<kF16>(head_dim, rows, shared, main, merge);
+    case kBF16: return pick_dt<kBF16>(head_dim, rows, shared, main, merge);
     default: return false;
   }
 }

@@ -146,11 +146,15 @@ def test_multi_query_workspace_formula(pk, N, TQ, H, HKV, D, MQ, L):
     # partitions of >= 256 tokens, at most 64; with one partition nothing is needed,
     # else (m, l) and head_dim floats per row, head and partition
     g = H // HKV
-    tq = max(1, 64 // g)
+    # rows per workgroup: 128 when a block has more than 64 rows, else 64 (or 16 for the
+    # split variant, which gives one block exactly when 64 rows would)
+    tq = (128 if MQ * g > 64 else 64) // g
     items = N * HKV * (-(-MQ // tq))
     parts = max(1, min(-(-1024 // items), -(-L // 256), 64)) if items and L else 1
     up = lambda x: -(-x // 256) * 256
     want = 0 if parts == 1 else up(TQ * H * parts * 2 * 4) + TQ * H * parts * D * 4
+    if MQ * g <= 16 and N > 0:   # one block per item: a longest-first order of the sequences
+        want += up(4 * N)
     assert pk.pa_multi_query_workspace_size(N, TQ, H, HKV, D, MQ, L) == want
 
 
@@ -176,6 +180,7 @@ def call_mq(pk, **over):
     (dict(wsb=16), 3, "workspace"),
     (dict(ws=None, wsb=1 << 30), 3, "workspace"),
     (dict(BS=0), 1, "block_size"),
+    (dict(H=65, HKV=1), 2, "at most 64"),
 ])
 def test_multi_query_rejects_host_visible_errors(pk, over, status, words):
     assert call_mq(pk, **over) == status
