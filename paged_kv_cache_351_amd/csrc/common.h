@@ -77,6 +77,7 @@ struct MultiQueryParams {
   int group;
   int head_dim;
   int block_size;
+  float inv_block_size;        // 1 / block_size, rounded to nearest
   int num_blocks;
   int max_blocks_per_seq;
   int max_q_len;

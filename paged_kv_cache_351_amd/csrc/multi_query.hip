@@ -53,6 +53,7 @@ namespace pagedkv {
 namespace {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -60,6 +61,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kTile = 32;   // tokens per K/V tile
 constexpr float kNegBig = -1.0e30f;
+constexpr float kLazyMax = 8.0f;   // a row's reference maximum may trail by up to 2^8
 
 template <int DT, int D>
 struct Shape {
@@ -96,6 +98,19 @@ template <int DT>
 __device__ __forceinline__ uint16_t to_store(float x) {
   if constexpr (DT == kBF16) return __builtin_bit_cast(uint16_t, (__bf16)x);
   else return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+// Two values rounded to the storage type in one packed conversion, the first in the
+// low half.
+template <int DT>
+__device__ __forceinline__ uint32_t to_store2(float a, float b) {
+  if constexpr (DT == kBF16) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+  } else {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+  }
 }
 
 template <int DT>
@@ -214,7 +229,8 @@ struct TileMap {
 // SPLIT = false: the four waves own 16 RB rows each of a 64 RB-row query block
 // and share every K/V tile through LDS (prefill-sized blocks); with RB = 2 every
 // K/V fragment read from LDS feeds two 16-row products, and registers are capped
-// for two waves per SIMD so that two workgroups share a CU across the barriers.
+// for two waves per SIMD (16-bit types) so that two workgroups share a CU across
+// the barriers.
 // SPLIT = true (16-bit types, at most 16 rows per block, RB = 1): the four waves
 // work on the same 16 rows and take every fourth tile of the partition each, K
 // straight from HBM into registers in the matrix-core layout and V through a
@@ -225,7 +241,7 @@ struct TileMap {
 // (read once, seen by every member) followed by each member's own tail (seen by
 // that member only), each padded to whole tiles.
 template <int DT, int D, bool SPLIT, bool SHARED, int RB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 2 ? 2 : 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 2 && DT != kF32 ? 2 : 1)))
 void multi_query_kernel(MultiQueryParams p) {
   using S = Shape<DT, D>;
   constexpr int EB = S::EB, CR = S::CR, NKC = S::NKC, NJ = S::NJ;
@@ -363,30 +379,41 @@ void multi_query_kernel(MultiQueryParams p) {
   const size_t slot_bytes = (size_t)Hkv * S::ROWB;
   // byte offset of token i (0..31) of a mapped tile in the pool: tokens past the
   // tile's count read its last valid token, so nothing outside a sequence is read
+  const float inv_b = p.inv_block_size;
   auto row_addr = [&](const TileMap& mp, int i) -> size_t {
     const int t = mp.base + min(i, mp.count - 1);
-    int bk = mp.table[t / B];
+    // t / B without a branch or an integer division: t < 2^24 is exact in float, the
+    // product is off by at most one, and one correction each way fixes it
+    int j = (int)((float)t * inv_b);
+    int o = t - j * B;
+    j = o < 0 ? j - 1 : (o >= B ? j + 1 : j);
+    o = o < 0 ? o + B : (o >= B ? o - B : o);
+    int bk = mp.table[j];
     bk = bk < 0 ? 0 : (bk >= p.num_blocks ? p.num_blocks - 1 : bk);
-    return ((size_t)bk * B + t % B) * slot_bytes + kv_off;
+    return ((size_t)bk * B + o) * slot_bytes + kv_off;
   };
 
-  // V rows of a tile as token pairs: `lanes` lanes take pair-chunks idx = me + lanes k
-  constexpr int VLANES = SPLIT ? 64 : 256;
-  constexpr int VL = (16 * CR + VLANES - 1) / VLANES;
+  // Tile registers: K and V rows of one tile on their way from HBM.  The
+  // shared-tile variant keeps two sets (tiles k + 1 and k + 2 in flight while tile
+  // k is computed); the split variant one per wave.
+  constexpr int NSET = SPLIT ? 1 : 2;
+  constexpr int VLANES = SPLIT ? 64 : 256;                // V rows of a tile as token pairs:
+  constexpr int VL = (16 * CR + VLANES - 1) / VLANES;     // lanes take pair-chunks me + VLANES k
+  constexpr int KL = SPLIT ? 2 * NKC : S::KLOADS;
   const int vme = SPLIT ? lane : tid;
-  u32x4 va[VL], vb[VL];
-  auto load_v = [&](const TileMap& mp) {
+  u32x4 kr[NSET][KL], va[NSET][VL], vb[NSET][VL];
+  auto load_v = [&](u32x4 (&xa)[VL], u32x4 (&xb)[VL], const TileMap& mp) {
 #pragma unroll
     for (int k = 0; k < VL; ++k) {
       const int idx = vme + VLANES * k;
       if (idx < 16 * CR) {
         const int ch = idx / 16, pr = idx % 16;   // pairs fastest: conflict-free transposes
-        va[k] = *reinterpret_cast<const u32x4*>((const char*)p.v_cache + row_addr(mp, 2 * pr) + ch * 16);
-        vb[k] = *reinterpret_cast<const u32x4*>((const char*)p.v_cache + row_addr(mp, 2 * pr + 1) + ch * 16);
+        xa[k] = *reinterpret_cast<const u32x4*>((const char*)p.v_cache + row_addr(mp, 2 * pr) + ch * 16);
+        xb[k] = *reinterpret_cast<const u32x4*>((const char*)p.v_cache + row_addr(mp, 2 * pr + 1) + ch * 16);
       }
     }
   };
-  auto store_v = [&]() {
+  auto store_v = [&](const u32x4 (&xa)[VL], const u32x4 (&xb)[VL]) {
 #pragma unroll
     for (int k = 0; k < VL; ++k) {
       const int idx = vme + VLANES * k;
@@ -396,115 +423,86 @@ void multi_query_kernel(MultiQueryParams p) {
         if constexpr (DT == kF32) {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            *reinterpret_cast<u32x2*>(ldsV + (ch * 4 + e) * S::VSTRIDE + sl * 4) = u32x2{va[k][e], vb[k][e]};
+            *reinterpret_cast<u32x2*>(ldsV + (ch * 4 + e) * S::VSTRIDE + sl * 4) = u32x2{xa[k][e], xb[k][e]};
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const uint32_t lo = (va[k][e >> 1] >> (16 * (e & 1))) & 0xffffu;
-            const uint32_t hi = (vb[k][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+            const uint32_t lo = (xa[k][e >> 1] >> (16 * (e & 1))) & 0xffffu;
+            const uint32_t hi = (xb[k][e >> 1] >> (16 * (e & 1))) & 0xffffu;
             *reinterpret_cast<uint32_t*>(ldsV + (ch * 8 + e) * S::VSTRIDE + sl * 2) = lo | (hi << 16);
           }
         }
       }
     }
   };
-  // K: through LDS (shared tiles) or straight into the matrix-core layout (split)
-  constexpr int KL = SPLIT ? 2 * NKC : S::KLOADS;
-  u32x4 kr[KL];
-  auto load_k = [&](const TileMap& mp) {
+  // K: straight into the matrix-core layout (split) or through LDS (shared tiles)
+  auto load_k = [&](u32x4 (&xk)[KL], const TileMap& mp) {
     if constexpr (SPLIT) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const char* row = (const char*)p.k_cache + row_addr(mp, 16 * h + col);
 #pragma unroll
         for (int c = 0; c < NKC; ++c)
-          kr[h * NKC + c] = *reinterpret_cast<const u32x4*>(row + chunk_of<DT, D>(c, grp) * 16);
+          xk[h * NKC + c] = *reinterpret_cast<const u32x4*>(row + chunk_of<DT, D>(c, grp) * 16);
       }
     } else {
 #pragma unroll
       for (int k = 0; k < KL; ++k) {
         const int idx = tid + 256 * k;
         const int tk = idx / CR, ch = idx % CR;
-        kr[k] = *reinterpret_cast<const u32x4*>((const char*)p.k_cache + row_addr(mp, tk) + ch * 16);
+        xk[k] = *reinterpret_cast<const u32x4*>((const char*)p.k_cache + row_addr(mp, tk) + ch * 16);
       }
     }
   };
-  auto store_k = [&]() {
+  auto store_k = [&](const u32x4 (&xk)[KL]) {
     if constexpr (!SPLIT) {
 #pragma unroll
       for (int k = 0; k < KL; ++k) {
         const int idx = tid + 256 * k;
         const int tk = idx / CR, ch = idx % CR;
-        *reinterpret_cast<u32x4*>(ldsK + tk * S::KSTRIDE + ch * 16) = kr[k];
+        *reinterpret_cast<u32x4*>(ldsK + tk * S::KSTRIDE + ch * 16) = xk[k];
       }
     }
   };
 
   const float sl2 = p.scale_log2e;
   const int ntiles = t_end > t_begin ? (t_end - t_begin + kTile - 1) / kTile : 0;
-  const int k0 = SPLIT ? wave : 0, kstep = SPLIT ? 4 : 1;
-  TileMap cur = tile_map(t_begin + k0 * kTile);
-  if (k0 < ntiles) {
-    load_k(cur);
-    load_v(cur);
-  }
-  for (int k = k0; k < ntiles; k += kstep) {
-    const int t0 = t_begin + k * kTile;
-    const bool more = k + kstep < ntiles;
-    const TileMap nxt = more ? tile_map(t0 + kstep * kTile) : cur;
-    // S^T = K Q^T for the two 16-token halves and every row block
-    f32x4 sc[RB][2];
-    auto qk = [&](int h, int c, u32x4 a) {
-#pragma unroll
-      for (int b = 0; b < RB; ++b) {
-        if constexpr (DT == kBF16) {
-          sc[b][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                             __builtin_bit_cast(bf16x8, qf[b][c]), sc[b][h], 0, 0, 0);
-        } else if constexpr (DT == kF16) {
-          sc[b][h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
-                                                            __builtin_bit_cast(f16x8, qf[b][c]), sc[b][h], 0, 0, 0);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            sc[b][h] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[e]), __uint_as_float(qf[b][c][e]),
-                                                            sc[b][h], 0, 0, 0);
-        }
-      }
-    };
+
+  // S^T = K Q^T for the two 16-token halves and every row block; a(h, c) gives the
+  // K fragment of half h, step c
+  f32x4 sc[RB][2];
+  auto qk = [&](auto a) {
 #pragma unroll
     for (int b = 0; b < RB; ++b) sc[b][0] = sc[b][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if constexpr (SPLIT) {
-      // this tile's K is in registers: stage its V and fetch the wave's next V,
-      // multiply, then fetch the next K (no second copy of the K registers)
-      store_v();
-      if (more) load_v(nxt);
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int c = 0; c < NKC; ++c) qk(h, c, kr[h * NKC + c]);
-      if (more) load_k(nxt);
-      __builtin_amdgcn_wave_barrier();   // V stores above are read by other lanes below
-    } else {
-      __syncthreads();  // the previous tile is no longer read
-      store_k();
-      store_v();
-      __syncthreads();
-      if (more) {
-        load_k(nxt);
-        load_v(nxt);
+      for (int c = 0; c < NKC; ++c) {
+        const u32x4 kf = a(h, c);
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+          if constexpr (DT == kBF16) {
+            sc[b][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf),
+                                                               __builtin_bit_cast(bf16x8, qf[b][c]), sc[b][h], 0, 0, 0);
+          } else if constexpr (DT == kF16) {
+            sc[b][h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, kf),
+                                                              __builtin_bit_cast(f16x8, qf[b][c]), sc[b][h], 0, 0, 0);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              sc[b][h] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(kf[e]), __uint_as_float(qf[b][c][e]),
+                                                              sc[b][h], 0, 0, 0);
+          }
+        }
       }
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const char* krow = ldsK + (16 * h + col) * S::KSTRIDE;
-#pragma unroll
-        for (int c = 0; c < NKC; ++c)
-          qk(h, c, *reinterpret_cast<const u32x4*>(krow + chunk_of<DT, D>(c, grp) * 16));
-      }
-    }
-    // online softmax: tile token 16 h + 4 grp + i of row col; full tiles that every
-    // row may see in full need no mask
-    float pr[RB][8], alpha[RB];
-    const bool whole = cur.count == kTile && (SHARED ? cur.owner < 0 : t0 + kTile - 1 <= pos_lo);
+  };
+
+  // Online softmax of tile t0 (scores in sc) and O^T += V^T P^T from the V tile in LDS.
+  auto softmax_pv = [&](int t0, const TileMap& mp) {
+    // tile token 16 h + 4 grp + i of row col; full tiles that every row may see in
+    // full need no mask
+    float pr[RB][8], alpha[RB], tmax[RB], sv_keep[RB][8];
+    const bool whole = mp.count == kTile && (SHARED ? mp.owner < 0 : t0 + kTile - 1 <= pos_lo);
 #pragma unroll
     for (int b = 0; b < RB; ++b) {
       float sv[8];
@@ -514,13 +512,13 @@ void multi_query_kernel(MultiQueryParams p) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) sv[4 * h + i] = sc[b][h][i] * sl2;
       } else {
-        const bool row_sees = !SHARED || cur.owner < 0 || cur.owner == qtok[b] - tok0;
+        const bool row_sees = !SHARED || mp.owner < 0 || mp.owner == qtok[b] - tok0;
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int u = 16 * h + 4 * grp + i;
-            const bool ok = SHARED ? (row_sees && u < cur.count) : (u < cur.count && t0 + u <= pos[b]);
+            const bool ok = SHARED ? (row_sees && u < mp.count) : (u < mp.count && t0 + u <= pos[b]);
             sv[4 * h + i] = ok ? sc[b][h][i] * sl2 : -__builtin_inff();
           }
       }
@@ -529,17 +527,29 @@ void multi_query_kernel(MultiQueryParams p) {
       for (int u = 1; u < 8; ++u) mx = fmaxf(mx, sv[u]);
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mn = fmaxf(m[b], mx);
-      alpha[b] = fast_exp2(m[b] - mn);
+      tmax[b] = fmaxf(m[b], mx);
+      sv_keep[b][0] = sv[0];
+#pragma unroll
+      for (int u = 1; u < 8; ++u) sv_keep[b][u] = sv[u];
+    }
+    // The reference maximum of a row moves only when the tile's maximum exceeds it by
+    // more than kLazyMax (base 2), for every row of the wave at once; otherwise the
+    // weights are taken against the old reference, so they stay below 2^kLazyMax and
+    // the accumulators need no rescaling.  Any reference gives the same normalised
+    // result: acc and l are always relative to the same m.
+    bool grow = false;
+#pragma unroll
+    for (int b = 0; b < RB; ++b) grow = grow || tmax[b] > m[b] + kLazyMax;
+    const bool rescale = __any(grow);
+#pragma unroll
+    for (int b = 0; b < RB; ++b) {
+      const float mn = rescale ? tmax[b] : m[b];
+      alpha[b] = rescale ? fast_exp2(m[b] - mn) : 1.0f;
       m[b] = mn;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) pr[b][u] = fast_exp2(sv[u] - mn);
+      for (int u = 0; u < 8; ++u) pr[b][u] = fast_exp2(sv_keep[b][u] - mn);
     }
-    cur = nxt;
-    bool moved = false;
-#pragma unroll
-    for (int b = 0; b < RB; ++b) moved = moved || alpha[b] != 1.0f;
-    if (__any(moved)) {  // rescale only when some row's maximum moved
+    if (rescale) {
 #pragma unroll
       for (int b = 0; b < RB; ++b)
 #pragma unroll
@@ -577,13 +587,11 @@ void multi_query_kernel(MultiQueryParams p) {
         float ps = 0.f;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const uint16_t x = to_store<DT>(pr[b][2 * u]), y = to_store<DT>(pr[b][2 * u + 1]);
-          const float fx = from_store<DT>(x), fy = from_store<DT>(y);
-          pw[u] = (uint32_t)x | ((uint32_t)y << 16);
+          pw[u] = to_store2<DT>(pr[b][2 * u], pr[b][2 * u + 1]);
+          const float fx = from_store<DT>((uint16_t)pw[u]), fy = from_store<DT>((uint16_t)(pw[u] >> 16));
           if constexpr (DT == kBF16) {
-            const uint16_t x2 = to_store<DT>(pr[b][2 * u] - fx), y2 = to_store<DT>(pr[b][2 * u + 1] - fy);
-            pw_lo[u] = (uint32_t)x2 | ((uint32_t)y2 << 16);
-            ps += (fx + from_store<DT>(x2)) + (fy + from_store<DT>(y2));
+            pw_lo[u] = to_store2<DT>(pr[b][2 * u] - fx, pr[b][2 * u + 1] - fy);
+            ps += (fx + from_store<DT>((uint16_t)pw_lo[u])) + (fy + from_store<DT>((uint16_t)(pw_lo[u] >> 16)));
           } else {
             pw_lo[u] = 0u;
             ps += fx + fy;
@@ -610,7 +618,63 @@ void multi_query_kernel(MultiQueryParams p) {
         }
       }
     }
-    if constexpr (SPLIT) __builtin_amdgcn_wave_barrier();  // V reads above before the next stores
+  };
+
+  if constexpr (SPLIT) {
+    // every fourth tile, one set of registers: stage the tile's V and fetch the
+    // wave's next V, multiply with this tile's K, then fetch the next K
+    const int kstep = 4;
+    TileMap cur = tile_map(t_begin + wave * kTile);
+    if (wave < ntiles) {
+      load_k(kr[0], cur);
+      load_v(va[0], vb[0], cur);
+    }
+    for (int k = wave; k < ntiles; k += kstep) {
+      const int t0 = t_begin + k * kTile;
+      const bool more = k + kstep < ntiles;
+      const TileMap nxt = more ? tile_map(t0 + kstep * kTile) : cur;
+      store_v(va[0], vb[0]);
+      if (more) load_v(va[0], vb[0], nxt);
+      qk([&](int h, int c) { return kr[0][h * NKC + c]; });
+      if (more) load_k(kr[0], nxt);
+      __builtin_amdgcn_wave_barrier();   // V stores above are read by other lanes below
+      softmax_pv(t0, cur);
+      __builtin_amdgcn_wave_barrier();   // V reads above before the next stores
+      cur = nxt;
+    }
+  } else {
+    // all tiles, two sets of registers: while tile k is computed, tiles k + 1 and
+    // k + 2 are on their way
+    auto step = [&](int k, u32x4 (&xk)[KL], u32x4 (&xa)[VL], u32x4 (&xb)[VL]) {
+      const int t0 = t_begin + k * kTile;
+      __syncthreads();  // the previous tile is no longer read
+      store_k(xk);
+      store_v(xa, xb);
+      __syncthreads();
+      if (k + 2 < ntiles) {
+        const TileMap m2 = tile_map(t0 + 2 * kTile);
+        load_k(xk, m2);
+        load_v(xa, xb, m2);
+      }
+      qk([&](int h, int c) {
+        return *reinterpret_cast<const u32x4*>(ldsK + (16 * h + col) * S::KSTRIDE + chunk_of<DT, D>(c, grp) * 16);
+      });
+      softmax_pv(t0, tile_map(t0));
+    };
+    if (ntiles > 0) {
+      const TileMap m0 = tile_map(t_begin);
+      load_k(kr[0], m0);
+      load_v(va[0], vb[0], m0);
+    }
+    if (ntiles > 1) {
+      const TileMap m1 = tile_map(t_begin + kTile);
+      load_k(kr[NSET - 1], m1);
+      load_v(va[NSET - 1], vb[NSET - 1], m1);
+    }
+    for (int k = 0; k < ntiles; k += 2) {
+      step(k, kr[0], va[0], vb[0]);
+      if (k + 1 < ntiles) step(k + 1, kr[NSET - 1], va[NSET - 1], vb[NSET - 1]);
+    }
   }
 
   // each row's sum over its four lanes; lane (grp, col) holds head_dim 16 j + 4 grp + i
