@@ -40,7 +40,9 @@ import workloads  # noqa: E402
 METRIC = "paged-decode KV GB/s read (% of HBM peak) and seqs/s, Llama-3-8B-shaped, 1 GPU"
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, vendor figure
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_llama3_8b_traffic.json")
-KERNEL_SOURCES = ["decode_kernel.h", "split.h", "decode_bf16.hip", "common.h", "api.hip"]
+# the files that define the decode kernels and their launch (traffic is re-recorded when they change)
+KERNEL_SOURCES = ["decode_kernel.h", "split.h", "decode_bf16.hip", "decode_params.h", "decode_api.hip",
+                  "host_util.h", "common.h"]
 DECODE_KERNELS = ["decode_kernel", "reduce_kernel"]   # kernels one pa_decode call launches
 
 

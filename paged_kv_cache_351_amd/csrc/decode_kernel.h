@@ -56,7 +56,7 @@
 
 #include <type_traits>
 
-#include "common.h"
+#include "decode_params.h"
 #include "split.h"
 
 namespace pagedkv {

@@ -47,7 +47,7 @@
 //   inf - inf.
 #include <type_traits>
 
-#include "common.h"
+#include "multi_query.h"
 
 namespace pagedkv {
 namespace {

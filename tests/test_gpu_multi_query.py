@@ -126,6 +126,17 @@ def test_max_q_len_larger_than_needed_and_deterministic():
     assert_close(out1.float().cpu().double().numpy(), run_oracle(b), "f16", "slack")
 
 
+def test_many_short_sequences_in_longest_first_order():
+    # more sequences than the ordering pass has threads, lengths 1..80, 1..4 queries each
+    rng = np.random.default_rng(21)
+    lens = rng.integers(1, 81, 1500).tolist()
+    qn = [int(min(L, q)) for L, q in zip(lens, rng.integers(1, 5, 1500))]
+    b = batch(21, "bf16", lens, qn, 32, 8, 128, 16)
+    log("1500 short sequences")
+    out, _ = run_gpu(b)
+    assert_close(out.float().cpu().double().numpy(), run_oracle(b), "bf16", "many")
+
+
 @pytest.mark.parametrize("name,make", [
     ("spec", lambda: workloads.llama3_8b_spec(num_seqs=12, num_blocks=5000)),
     ("chunk", lambda: workloads.llama3_8b_chunk(num_seqs=2, chunk=96, max_prior=500)),

@@ -120,6 +120,17 @@ def test_groups_match_the_decode_oracle(case):
     assert_close(out.float().cpu().double().numpy(), oracle_out(b), dt, f"case {case}")
 
 
+def test_many_groups_in_longest_first_order():
+    # more groups than the ordering pass has threads
+    rng = np.random.default_rng(3)
+    groups = [(int(rng.integers(1, 40)), [int(x) for x in rng.integers(0, 20, int(rng.integers(1, 4)))])
+              for _ in range(1100)]
+    b = grouped_batch(3, "f16", groups, 8, 8, 64, 8)
+    log("1100 groups")
+    out, _ = run(b)
+    assert_close(out.float().cpu().double().numpy(), oracle_out(b), "f16", "many groups")
+
+
 def test_long_prefix_few_groups_uses_partitions_and_matches_pa_decode():
     b = grouped_batch(7, "f16", [(3000, [10, 200, 0, 77])], 8, 8, 128, 16)
     m = pk()
