@@ -23,11 +23,11 @@ int requested_waves() {
   return v;
 }
 
-// The last 1/12 of every wave's share goes to whichever wave is free first, in
+// The last 1/16 of every wave's share goes to whichever wave is free first, in
 // one part (smaller tails leave a longer finish, larger ones cost more chunk
 // starts and partial results); PA_DECODE_TAIL = d overrides the divisor (0 = no tails) and
 // PA_DECODE_TAIL_PIECES the number of parts (halving sizes), for tuning sweeps.
-constexpr int kDefaultTailDiv = 12;
+constexpr int kDefaultTailDiv = 16;
 int tail_pieces() {
   static const int v = std::min(env_int("PA_DECODE_TAIL_PIECES", 1), kMaxTailPieces);
   return v;
