@@ -190,3 +190,51 @@ def test_multi_query_rejects_host_visible_errors(pk, over, status, words):
 def test_multi_query_with_no_queries_is_a_no_op(pk):
     assert call_mq(pk, N=0, q=None, out=None) == 0
     assert call_mq(pk, TQ=0, MQ=0, q=None, out=None) == 0
+
+
+@pytest.mark.parametrize("N,G,H,HKV,D,MG,L", [(256, 32, 40, 40, 128, 8, 1280), (4, 1, 8, 8, 128, 4, 3200),
+                                             (8, 2, 32, 8, 128, 6, 150), (3, 3, 16, 1, 64, 1, 40)])
+def test_shared_prefix_workspace_formula(pk, N, G, H, HKV, D, MG, L):
+    # blocks of 16 / group members per item, about 1024 items wanted, partitions of >= 256
+    # tokens, at most 64; a longest-first order of the groups, then (with partitions) the
+    # partial results of every sequence, head and partition
+    g = H // HKV
+    items = G * HKV * (-(-MG // (16 // g)))
+    parts = max(1, min(-(-1024 // items), -(-L // 256), 64)) if items and L else 1
+    up = lambda x: -(-x // 256) * 256
+    want = up(4 * G) + (0 if parts == 1 else up(N * H * parts * 2 * 4) + N * H * parts * D * 4)
+    assert pk.pa_decode_shared_prefix_workspace_size(N, G, H, HKV, D, MG, L) == want
+
+
+def call_sp(pk, **over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, lens=FAKE, gs=FAKE, pre=FAKE, N=8, G=2, H=8, HKV=8, D=128,
+             BS=16, NB=100, MB=10, MG=4, L=160, scale=0.088, dt=1, out=FAKE, ws=FAKE, wsb=1 << 20,
+             stream=None)
+    a.update(over)
+    return pk.lib().pa_decode_shared_prefix(a["q"], a["k"], a["v"], a["bt"], a["lens"], a["gs"], a["pre"],
+                                            a["N"], a["G"], a["H"], a["HKV"], a["D"], a["BS"], a["NB"],
+                                            a["MB"], a["MG"], a["L"], a["scale"], a["dt"], a["out"], a["ws"],
+                                            a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("over,status,words", [
+    (dict(D=96), 2, "head_dim"),
+    (dict(dt=0), 2, "float32"),
+    (dict(dt=7), 1, "dtype"),
+    (dict(H=9), 1, "multiple"),
+    (dict(H=34, HKV=2), 2, "at most 16"),
+    (dict(L=161), 1, "max_seq_len"),
+    (dict(MG=9), 1, "max_group_size"),
+    (dict(pre=None), 1, "null"),
+    (dict(q=FAKE + 8), 1, "aligned"),
+    (dict(scale=float("nan")), 1, "finite"),
+    (dict(wsb=0, ws=None), 3, "workspace"),
+])
+def test_shared_prefix_rejects_host_visible_errors(pk, over, status, words):
+    assert call_sp(pk, **over) == status
+    assert words in pk.pa_last_error()
+
+
+def test_shared_prefix_with_no_groups_is_a_no_op(pk):
+    assert call_sp(pk, G=0, q=None, out=None) == 0
+    assert call_sp(pk, N=0, MG=0, q=None, out=None) == 0
