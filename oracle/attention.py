@@ -12,7 +12,7 @@ one shared pool, and a per-sequence block table gives logical -> physical
 ([PA-notes] §3; [vLLM-what] "2）PagedAttention 算子").  The softmax is
 normalised over *all* tokens of the sequence, across blocks ([PA-notes] §4).
 
-Readings where the pages are silent (each also listed in the design doc)
+Readings where the pages are silent
 --------------------------------------------------------------------
 * Pool layout: ``cache[num_blocks, block_size, num_kv_heads, head_dim]``, the
   per-block ``[block_size, heads, head_dim]`` shape of [PA-explainer]

@@ -22,7 +22,7 @@ that same draw; it is kept out of the pool and handed to the write instead.
 Pool slots that hold no token are filled with NaN by default, so any read of
 them poisons the result.
 
-Workloads (shapes of the pages' examples; see the design doc for the full recipe):
+Workloads (shapes of the pages' examples):
   tiny            fp32, 4 seqs {1,7,16,40} + 1 written token each, B=16, 32 blocks
   worked_5_2_9    the 40-token request on physical blocks 5, 2, 9
   llama7b         MHA 32 heads, D=128, fp16, 64 seqs, L ~ U{1..2048}
