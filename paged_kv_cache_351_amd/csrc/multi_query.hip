@@ -24,10 +24,9 @@
 //
 // Per tile of 32 tokens
 //   All 256 lanes load the tile's K and V rows (16 bytes per load, token ->
-//   block through the table) one tile ahead in registers and store them to LDS:
-//   K as [token][head_dim] rows, V transposed as [head_dim][slot] rows, where
-//   token t = 16 h + 4 grp + i (h in 0..1, grp and i in 0..3) sits in slot
-//   8 grp + 4 h + i (slot_of).  Then each wave, on the matrix cores:
+//   block through the table, table entries one step earlier than the rows) two
+//   tiles ahead in registers and store them to LDS as [token][head_dim] rows.
+//   Then each wave, on the matrix cores:
 //     S^T = K Q^T   v_mfma_f32_16x16x32_{bf16,f16} (16x16x4_f32 for fp32): A = K
 //                   rows of one 16-token half, B = the wave's 16 query rows, both
 //                   cut into the same head_dim chunks; lane (grp, col) gets the
@@ -36,13 +35,16 @@
 //                   that hold it, exponentials in base 2, the running sum kept
 //                   per lane (the four partial sums are added at the end).
 //     O^T += V^T P^T with A = V^T (16 head_dim rows x 32 slots) and B = P^T:
-//                   lane (grp, col) holds P for slots 8 grp .. 8 grp + 7, which
-//                   are exactly the tokens whose scores it computed, so the
-//                   scores never move between lanes.
+//                   slot 8 grp + 4 h + i stands for token 16 h + 4 grp + i, so
+//                   lane (grp, col) holds P for slots 8 grp .. 8 grp + 7, exactly
+//                   the tokens whose scores it computed, and the scores never move
+//                   between lanes.  The LDS transpose read (ds_read_b64_tr_b16)
+//                   turns the [token][head_dim] V rows into the A fragments.
 //   P is rounded to the storage type for the matrix cores: fp16 keeps 11
 //   significant bits, bf16 is split into two bf16 terms (about 16 bits) fed to
-//   two products, fp32 stays fp32.  The running sum adds the rounded values, so
-//   the output is a weighted mean with exactly the weights used.  Masked tokens
+//   two products, fp32 stays fp32.  The running sum adds the values used (for
+//   bf16 the fp32 values, within 2^-16 of the two terms), so the output is a
+//   weighted mean with the weights used.  Masked tokens
 //   get -inf, i.e. weight 0; running maxima start at -1e30 so no row ever forms
 //   inf - inf.
 #include <type_traits>
@@ -70,11 +72,12 @@ struct Shape {
   static constexpr int CR = ROWB / 16;            // 16-byte chunks per row
   static constexpr int NKC = CR / 4;              // chunks per lane of one row (4 lane groups)
   static constexpr int KSTRIDE = ROWB + 16;       // LDS bytes per K row, padded
-  static constexpr int VSTRIDE = kTile * EB + 16; // LDS bytes per transposed V row, padded
+  static constexpr int VSTRIDE = ROWB + 32;       // LDS bytes per V row: four rows' 32-byte
+                                                  // pieces fall in distinct banks
   static constexpr int KBYTES = kTile * KSTRIDE;
-  static constexpr int LDS = KBYTES + D * VSTRIDE;
-  static constexpr int KLOADS = kTile * CR / 256;         // K chunks per thread per tile
-  static constexpr int VLOADS = (16 * CR + 255) / 256;    // V token-pair chunks per thread
+  static constexpr int VBYTES = kTile * VSTRIDE;
+  static constexpr int LDS = KBYTES + VBYTES;
+  static constexpr int KLOADS = kTile * CR / 256;         // tokens per thread per tile
   static constexpr int NJ = D / 16;                       // 16-row head_dim blocks of O^T
   static_assert(KLOADS >= 1 && kTile * CR % 256 == 0, "tile does not split over 256 lanes");
 };
@@ -86,10 +89,14 @@ __device__ __forceinline__ int chunk_of(int c, int grp) {
   else return 4 * c + grp;                                        // 8 halves, one MFMA
 }
 
-// Slot of tile token t in the transposed V rows (see the file comment).
-__device__ __forceinline__ int slot_of(int t) {
-  const int h = t >> 4, r = t & 15;
-  return 8 * (r >> 2) + 4 * h + (r & 3);
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Four 16-bit elements through the LDS transpose read (ds_read_b64_tr_b16).  In each
+// group of 16 lanes, lane i names 8 bytes (elements M[i][0..3]); lane j receives
+// M[4q + j/4][j%4] for q = 0..3.
+__device__ __forceinline__ s16x4 lds_read_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -245,7 +252,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 2 && 
 void multi_query_kernel(MultiQueryParams p) {
   using S = Shape<DT, D>;
   constexpr int EB = S::EB, CR = S::CR, NKC = S::NKC, NJ = S::NJ;
-  constexpr int VREG = D * S::VSTRIDE;                     // one transposed V tile
+  constexpr int VREG = S::VBYTES;                          // one V tile
   constexpr int LDS_BYTES = SPLIT ? 4 * VREG : S::LDS;
   static_assert(!SPLIT || (DT != kF32 && 4 * 16 * (D + 2) * 4 <= LDS_BYTES), "split merge space");
   static_assert(SPLIT || !SHARED, "shared-prefix groups use the split variant");
@@ -377,92 +384,44 @@ void multi_query_kernel(MultiQueryParams p) {
   const int B = p.block_size;
   const size_t kv_off = (size_t)it.kv * S::ROWB;
   const size_t slot_bytes = (size_t)Hkv * S::ROWB;
-  // byte offset of token i (0..31) of a mapped tile in the pool: tokens past the
-  // tile's count read its last valid token, so nothing outside a sequence is read
+  // Each lane loads the K and V rows of NT tokens of a tile (the same tokens for both):
+  // the split variant tokens col and col + 16, NKC chunks each, straight in the matrix
+  // core layout of K; the shared-tile variant tokens tid / CR + (256 / CR) k, chunk
+  // tid % CR.  Tokens past a tile's count read its last valid token, so nothing outside
+  // a sequence is read.  A token's block-table entry is fetched one step before its
+  // rows, so that waiting for it never waits for the rows in flight.
+  constexpr int NT = SPLIT ? 2 : S::KLOADS;      // tokens per lane per tile
+  constexpr int CPT = SPLIT ? NKC : 1;           // 16-byte chunks per token
+  constexpr int KL = NT * CPT;
+  auto my_tok = [&](int k) { return SPLIT ? col + 16 * k : tid / CR + (256 / CR) * k; };
+  auto my_chunk = [&](int c) { return SPLIT ? chunk_of<DT, D>(c, grp) : tid % CR; };
   const float inv_b = p.inv_block_size;
-  auto row_addr = [&](const TileMap& mp, int i) -> size_t {
-    const int t = mp.base + min(i, mp.count - 1);
-    // t / B without a branch or an integer division: t < 2^24 is exact in float, the
-    // product is off by at most one, and one correction each way fixes it
-    int j = (int)((float)t * inv_b);
-    int o = t - j * B;
-    j = o < 0 ? j - 1 : (o >= B ? j + 1 : j);
-    o = o < 0 ? o + B : (o >= B ? o - B : o);
-    int bk = mp.table[j];
-    bk = bk < 0 ? 0 : (bk >= p.num_blocks ? p.num_blocks - 1 : bk);
-    return ((size_t)bk * B + o) * slot_bytes + kv_off;
-  };
-
-  // Tile registers: K and V rows of one tile on their way from HBM.  The
-  // shared-tile variant keeps two sets (tiles k + 1 and k + 2 in flight while tile
-  // k is computed); the split variant one per wave.
-  constexpr int NSET = SPLIT ? 1 : 2;
-  constexpr int VLANES = SPLIT ? 64 : 256;                // V rows of a tile as token pairs:
-  constexpr int VL = (16 * CR + VLANES - 1) / VLANES;     // lanes take pair-chunks me + VLANES k
-  constexpr int KL = SPLIT ? 2 * NKC : S::KLOADS;
-  const int vme = SPLIT ? lane : tid;
-  u32x4 kr[NSET][KL], va[NSET][VL], vb[NSET][VL];
-  auto load_v = [&](u32x4 (&xa)[VL], u32x4 (&xb)[VL], const TileMap& mp) {
+  // block-table entries (tb) and in-block offsets (to) of this lane's tokens of a tile
+  auto fetch_table = [&](int (&tb)[NT], int (&to)[NT], const TileMap& mp) {
 #pragma unroll
-    for (int k = 0; k < VL; ++k) {
-      const int idx = vme + VLANES * k;
-      if (idx < 16 * CR) {
-        const int ch = idx / 16, pr = idx % 16;   // pairs fastest: conflict-free transposes
-        xa[k] = *reinterpret_cast<const u32x4*>((const char*)p.v_cache + row_addr(mp, 2 * pr) + ch * 16);
-        xb[k] = *reinterpret_cast<const u32x4*>((const char*)p.v_cache + row_addr(mp, 2 * pr + 1) + ch * 16);
-      }
+    for (int k = 0; k < NT; ++k) {
+      const int t = mp.base + min(my_tok(k), mp.count - 1);
+      // t / B without a branch or an integer division: t < 2^24 is exact in float, the
+      // product is off by at most one, and one correction each way fixes it
+      int j = (int)((float)t * inv_b);
+      int o = t - j * B;
+      j = o < 0 ? j - 1 : (o >= B ? j + 1 : j);
+      to[k] = o < 0 ? o + B : (o >= B ? o - B : o);
+      tb[k] = mp.table[j];
     }
   };
-  auto store_v = [&](const u32x4 (&xa)[VL], const u32x4 (&xb)[VL]) {
+  u32x4 kr[2][KL], vr[2][KL];
+  // V rows go to LDS as they are ([token][head_dim], padded rows); the shared-tile
+  // variant stores K the same way
+  auto store_kv = [&](const u32x4 (&xk)[KL], const u32x4 (&xv)[KL]) {
 #pragma unroll
-    for (int k = 0; k < VL; ++k) {
-      const int idx = vme + VLANES * k;
-      if (idx < 16 * CR) {
-        const int ch = idx / 16, pr = idx % 16;
-        const int sl = slot_of(2 * pr);           // even; token 2 pr + 1 is the next slot
-        if constexpr (DT == kF32) {
+    for (int k = 0; k < NT; ++k)
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            *reinterpret_cast<u32x2*>(ldsV + (ch * 4 + e) * S::VSTRIDE + sl * 4) = u32x2{xa[k][e], xb[k][e]};
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const uint32_t lo = (xa[k][e >> 1] >> (16 * (e & 1))) & 0xffffu;
-            const uint32_t hi = (xb[k][e >> 1] >> (16 * (e & 1))) & 0xffffu;
-            *reinterpret_cast<uint32_t*>(ldsV + (ch * 8 + e) * S::VSTRIDE + sl * 2) = lo | (hi << 16);
-          }
-        }
+      for (int c = 0; c < CPT; ++c) {
+        *reinterpret_cast<u32x4*>(ldsV + my_tok(k) * S::VSTRIDE + my_chunk(c) * 16) = xv[k * CPT + c];
+        if constexpr (!SPLIT)
+          *reinterpret_cast<u32x4*>(ldsK + my_tok(k) * S::KSTRIDE + my_chunk(c) * 16) = xk[k * CPT + c];
       }
-    }
-  };
-  // K: straight into the matrix-core layout (split) or through LDS (shared tiles)
-  auto load_k = [&](u32x4 (&xk)[KL], const TileMap& mp) {
-    if constexpr (SPLIT) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const char* row = (const char*)p.k_cache + row_addr(mp, 16 * h + col);
-#pragma unroll
-        for (int c = 0; c < NKC; ++c)
-          xk[h * NKC + c] = *reinterpret_cast<const u32x4*>(row + chunk_of<DT, D>(c, grp) * 16);
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < KL; ++k) {
-        const int idx = tid + 256 * k;
-        const int tk = idx / CR, ch = idx % CR;
-        xk[k] = *reinterpret_cast<const u32x4*>((const char*)p.k_cache + row_addr(mp, tk) + ch * 16);
-      }
-    }
-  };
-  auto store_k = [&](const u32x4 (&xk)[KL]) {
-    if constexpr (!SPLIT) {
-#pragma unroll
-      for (int k = 0; k < KL; ++k) {
-        const int idx = tid + 256 * k;
-        const int tk = idx / CR, ch = idx % CR;
-        *reinterpret_cast<u32x4*>(ldsK + tk * S::KSTRIDE + ch * 16) = xk[k];
-      }
-    }
   };
 
   const float sl2 = p.scale_log2e;
@@ -561,49 +520,64 @@ void multi_query_kernel(MultiQueryParams p) {
       for (int b = 0; b < RB; ++b)
         l[b] = l[b] * alpha[b] + (((pr[b][0] + pr[b][1]) + (pr[b][2] + pr[b][3])) +
                                   ((pr[b][4] + pr[b][5]) + (pr[b][6] + pr[b][7])));
+      // product u takes slot 8 grp + u, i.e. tile token 16 (u / 4) + 4 grp + u % 4, at
+      // head_dim 16 j + col
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        const char* vrow = ldsV + (16 * j + col) * S::VSTRIDE + grp * 32;
-        const u32x4 a0 = *reinterpret_cast<const u32x4*>(vrow);
-        const u32x4 a1 = *reinterpret_cast<const u32x4*>(vrow + 16);
+        float a[8];
 #pragma unroll
-        for (int b = 0; b < RB; ++b) {
+        for (int u = 0; u < 8; ++u)
+          a[u] = *reinterpret_cast<const float*>(ldsV + (16 * (u >> 2) + 4 * grp + (u & 3)) * S::VSTRIDE +
+                                                 (16 * j + col) * 4);
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-            acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a0[u]), pr[b][u], acc[b][j], 0, 0, 0);
+        for (int b = 0; b < RB; ++b)
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-            acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a1[u]), pr[b][4 + u], acc[b][j], 0, 0, 0);
-        }
+          for (int u = 0; u < 8; ++u)
+            acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u], pr[b][u], acc[b][j], 0, 0, 0);
       }
     } else {
-      // P in the storage type; for bf16 (8 significant bits) as a sum of two bf16
-      // values, the second the rounding error of the first, which carries about 16
-      // significant bits through two products with the same V fragment
+      // P in the storage type.  bf16 keeps 8 significant bits, so P is split into two
+      // bf16 terms fed to two products with the same V fragment: the high term is P cut
+      // to its top 16 bits, which leaves an exact fp32 remainder, and the low term is
+      // that remainder rounded, about 16 significant bits in all; the running sum adds
+      // the fp32 values, which differ from the two terms by about 2^-16 relative.  fp16
+      // keeps 11 bits in one term, and the running sum adds the rounded values.
       u32x4 pb[RB], pb_lo[RB];
 #pragma unroll
       for (int b = 0; b < RB; ++b) {
         uint32_t pw[4], pw_lo[4];
-        float ps = 0.f;
+        float ps;
+        if constexpr (DT == kBF16) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          pw[u] = to_store2<DT>(pr[b][2 * u], pr[b][2 * u + 1]);
-          const float fx = from_store<DT>((uint16_t)pw[u]), fy = from_store<DT>((uint16_t)(pw[u] >> 16));
-          if constexpr (DT == kBF16) {
-            pw_lo[u] = to_store2<DT>(pr[b][2 * u] - fx, pr[b][2 * u + 1] - fy);
-            ps += (fx + from_store<DT>((uint16_t)pw_lo[u])) + (fy + from_store<DT>((uint16_t)(pw_lo[u] >> 16)));
-          } else {
+          for (int u = 0; u < 4; ++u) {
+            const uint32_t x = __float_as_uint(pr[b][2 * u]), y = __float_as_uint(pr[b][2 * u + 1]);
+            pw[u] = (x >> 16) | (y & 0xffff0000u);
+            pw_lo[u] = to_store2<DT>(pr[b][2 * u] - __uint_as_float(x & 0xffff0000u),
+                                     pr[b][2 * u + 1] - __uint_as_float(y & 0xffff0000u));
+          }
+          ps = ((pr[b][0] + pr[b][1]) + (pr[b][2] + pr[b][3])) + ((pr[b][4] + pr[b][5]) + (pr[b][6] + pr[b][7]));
+        } else {
+          ps = 0.f;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            pw[u] = to_store2<DT>(pr[b][2 * u], pr[b][2 * u + 1]);
             pw_lo[u] = 0u;
-            ps += fx + fy;
+            ps += from_store<DT>((uint16_t)pw[u]) + from_store<DT>((uint16_t)(pw[u] >> 16));
           }
         }
         l[b] = l[b] * alpha[b] + ps;
         pb[b] = u32x4{pw[0], pw[1], pw[2], pw[3]};
         pb_lo[b] = u32x4{pw_lo[0], pw_lo[1], pw_lo[2], pw_lo[3]};
       }
+      // A = V^T for head_dim 16 j .. 16 j + 15 through two transpose reads: slots
+      // 8 grp + 4 h + q hold tile tokens 16 h + 4 grp + q, and lane (grp, col) names the
+      // row 16 h + 4 grp + col / 4 at head_dim 16 j + 4 (col % 4)
+      const char* vbase = ldsV + (4 * grp + (col >> 2)) * S::VSTRIDE + (4 * (col & 3)) * 2;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(ldsV + (16 * j + col) * S::VSTRIDE + grp * 16);
+        const s16x4 a0 = lds_read_tr16(vbase + 32 * j);
+        const s16x4 a1 = lds_read_tr16(vbase + 16 * S::VSTRIDE + 32 * j);
+        const u32x4 a = __builtin_bit_cast(u32x4, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
         for (int b = 0; b < RB; ++b) {
           if constexpr (DT == kBF16) {
@@ -620,60 +594,88 @@ void multi_query_kernel(MultiQueryParams p) {
     }
   };
 
+  // pool byte offsets of this lane's tokens from their table entries
+  auto offsets = [&](const int (&tb)[NT], const int (&to)[NT], size_t (&off)[NT]) {
+#pragma unroll
+    for (int k = 0; k < NT; ++k) {
+      int bk = tb[k];
+      bk = bk < 0 ? 0 : (bk >= p.num_blocks ? p.num_blocks - 1 : bk);
+      off[k] = ((size_t)bk * B + to[k]) * slot_bytes + kv_off;
+    }
+  };
+  auto load_rows = [&](u32x4 (&x)[KL], const void* cache, const size_t (&off)[NT]) {
+#pragma unroll
+    for (int k = 0; k < NT; ++k)
+#pragma unroll
+      for (int c = 0; c < CPT; ++c)
+        x[k * CPT + c] = *reinterpret_cast<const u32x4*>((const char*)cache + off[k] + my_chunk(c) * 16);
+  };
+
   if constexpr (SPLIT) {
-    // every fourth tile, one set of registers: stage the tile's V and fetch the
-    // wave's next V, multiply with this tile's K, then fetch the next K
+    // every fourth tile, one set of registers.  Per tile: stage its V in the wave's
+    // LDS region, start the wave's next V, multiply with this tile's K (registers),
+    // start the next K and the table entries of the tile after that
     const int kstep = 4;
-    TileMap cur = tile_map(t_begin + wave * kTile);
+    int tb[NT], to[NT];
+    size_t off[NT];
     if (wave < ntiles) {
-      load_k(kr[0], cur);
-      load_v(va[0], vb[0], cur);
+      fetch_table(tb, to, tile_map(t_begin + wave * kTile));
+      offsets(tb, to, off);
+      load_rows(vr[0], p.v_cache, off);
+      load_rows(kr[0], p.k_cache, off);
+      if (wave + kstep < ntiles) fetch_table(tb, to, tile_map(t_begin + (wave + kstep) * kTile));
     }
     for (int k = wave; k < ntiles; k += kstep) {
       const int t0 = t_begin + k * kTile;
       const bool more = k + kstep < ntiles;
-      const TileMap nxt = more ? tile_map(t0 + kstep * kTile) : cur;
-      store_v(va[0], vb[0]);
-      if (more) load_v(va[0], vb[0], nxt);
+      store_kv(kr[0], vr[0]);
+      if (more) {
+        offsets(tb, to, off);
+        load_rows(vr[0], p.v_cache, off);
+      }
       qk([&](int h, int c) { return kr[0][h * NKC + c]; });
-      if (more) load_k(kr[0], nxt);
+      if (more) load_rows(kr[0], p.k_cache, off);
+      if (k + 2 * kstep < ntiles) fetch_table(tb, to, tile_map(t0 + 2 * kstep * kTile));
       __builtin_amdgcn_wave_barrier();   // V stores above are read by other lanes below
-      softmax_pv(t0, cur);
+      softmax_pv(t0, tile_map(t0));
       __builtin_amdgcn_wave_barrier();   // V reads above before the next stores
-      cur = nxt;
     }
   } else {
-    // all tiles, two sets of registers: while tile k is computed, tiles k + 1 and
-    // k + 2 are on their way
-    auto step = [&](int k, u32x4 (&xk)[KL], u32x4 (&xa)[VL], u32x4 (&xb)[VL]) {
+    // all tiles, two sets of registers: while tile k is computed, the rows of tiles
+    // k + 1 and k + 2 and the table entries of tile k + 3 are on their way
+    int tb[2][NT], to[2][NT];
+    auto step = [&](int k, u32x4 (&xk)[KL], u32x4 (&xv)[KL], const int (&tbc)[NT], const int (&toc)[NT],
+                    int (&tbn)[NT], int (&ton)[NT]) {
       const int t0 = t_begin + k * kTile;
       __syncthreads();  // the previous tile is no longer read
-      store_k(xk);
-      store_v(xa, xb);
+      store_kv(xk, xv);
       __syncthreads();
+      if (k + 3 < ntiles) fetch_table(tbn, ton, tile_map(t0 + 3 * kTile));
       if (k + 2 < ntiles) {
-        const TileMap m2 = tile_map(t0 + 2 * kTile);
-        load_k(xk, m2);
-        load_v(xa, xb, m2);
+        size_t off[NT];
+        offsets(tbc, toc, off);
+        load_rows(xk, p.k_cache, off);
+        load_rows(xv, p.v_cache, off);
       }
       qk([&](int h, int c) {
         return *reinterpret_cast<const u32x4*>(ldsK + (16 * h + col) * S::KSTRIDE + chunk_of<DT, D>(c, grp) * 16);
       });
       softmax_pv(t0, tile_map(t0));
     };
-    if (ntiles > 0) {
-      const TileMap m0 = tile_map(t_begin);
-      load_k(kr[0], m0);
-      load_v(va[0], vb[0], m0);
+    if (ntiles > 0) fetch_table(tb[0], to[0], tile_map(t_begin));
+    if (ntiles > 1) fetch_table(tb[1], to[1], tile_map(t_begin + kTile));
+    for (int i = 0; i < 2; ++i) {
+      if (i < ntiles) {
+        size_t off[NT];
+        offsets(tb[i], to[i], off);
+        load_rows(kr[i], p.k_cache, off);
+        load_rows(vr[i], p.v_cache, off);
+      }
     }
-    if (ntiles > 1) {
-      const TileMap m1 = tile_map(t_begin + kTile);
-      load_k(kr[NSET - 1], m1);
-      load_v(va[NSET - 1], vb[NSET - 1], m1);
-    }
+    if (ntiles > 2) fetch_table(tb[0], to[0], tile_map(t_begin + 2 * kTile));
     for (int k = 0; k < ntiles; k += 2) {
-      step(k, kr[0], va[0], vb[0]);
-      if (k + 1 < ntiles) step(k + 1, kr[NSET - 1], va[NSET - 1], vb[NSET - 1]);
+      step(k, kr[0], vr[0], tb[0], to[0], tb[1], to[1]);
+      if (k + 1 < ntiles) step(k + 1, kr[1], vr[1], tb[1], to[1], tb[0], to[0]);
     }
   }
 
