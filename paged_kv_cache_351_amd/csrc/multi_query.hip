@@ -101,6 +101,16 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const char* p) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Maximum over lanes i, i ^ 16, i ^ 32 and i ^ 48 with the gfx950 row swaps (no trip
+// through LDS): swapping a value with a copy of itself leaves one lane of each pair
+// in each result, so the maximum of the two results is the pair's maximum.
+__device__ __forceinline__ float max_over_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 template <int DT>
 __device__ __forceinline__ uint16_t to_store(float x) {
   if constexpr (DT == kBF16) return __builtin_bit_cast(uint16_t, (__bf16)x);
@@ -253,7 +263,7 @@ void multi_query_kernel(MultiQueryParams p) {
   using S = Shape<DT, D>;
   constexpr int EB = S::EB, CR = S::CR, NKC = S::NKC, NJ = S::NJ;
   constexpr int VREG = S::VBYTES;                          // one V tile
-  constexpr int LDS_BYTES = SPLIT ? 4 * VREG : S::LDS;
+  constexpr int LDS_BYTES = SPLIT ? 4 * VREG : 2 * S::LDS;   // shared tiles: two buffers
   static_assert(!SPLIT || (DT != kF32 && 4 * 16 * (D + 2) * 4 <= LDS_BYTES), "split merge space");
   static_assert(SPLIT || !SHARED, "shared-prefix groups use the split variant");
   static_assert(RB == 1 || (RB == 2 && !SPLIT), "two row blocks only with shared tiles");
@@ -265,8 +275,7 @@ void multi_query_kernel(MultiQueryParams p) {
   const int lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int g = p.group, Hq = p.num_heads, Hkv = p.num_kv_heads;
-  char* ldsK = lds;
-  char* ldsV = SPLIT ? lds + wave * VREG : lds + S::KBYTES;
+  char* const ldsV = lds + wave * VREG;   // the split variant's V region
 
   // The item's rows: query tokens qa + tok0 .. qa + tok1 - 1 of one sequence (multi-query),
   // or member sequences qa + tok0 .. qa + tok1 - 1 of one group (shared prefix), g heads
@@ -413,14 +422,14 @@ void multi_query_kernel(MultiQueryParams p) {
   u32x4 kr[2][KL], vr[2][KL];
   // V rows go to LDS as they are ([token][head_dim], padded rows); the shared-tile
   // variant stores K the same way
-  auto store_kv = [&](const u32x4 (&xk)[KL], const u32x4 (&xv)[KL]) {
+  auto store_kv = [&](const u32x4 (&xk)[KL], const u32x4 (&xv)[KL], char* kb, char* vb) {
 #pragma unroll
     for (int k = 0; k < NT; ++k)
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
-        *reinterpret_cast<u32x4*>(ldsV + my_tok(k) * S::VSTRIDE + my_chunk(c) * 16) = xv[k * CPT + c];
+        *reinterpret_cast<u32x4*>(vb + my_tok(k) * S::VSTRIDE + my_chunk(c) * 16) = xv[k * CPT + c];
         if constexpr (!SPLIT)
-          *reinterpret_cast<u32x4*>(ldsK + my_tok(k) * S::KSTRIDE + my_chunk(c) * 16) = xk[k * CPT + c];
+          *reinterpret_cast<u32x4*>(kb + my_tok(k) * S::KSTRIDE + my_chunk(c) * 16) = xk[k * CPT + c];
       }
   };
 
@@ -456,8 +465,9 @@ void multi_query_kernel(MultiQueryParams p) {
       }
   };
 
-  // Online softmax of tile t0 (scores in sc) and O^T += V^T P^T from the V tile in LDS.
-  auto softmax_pv = [&](int t0, const TileMap& mp) {
+  // Online softmax of tile t0 (scores in sc) and O^T += V^T P^T from the V tile at vb
+  // in LDS.
+  auto softmax_pv = [&](int t0, const TileMap& mp, const char* vb) {
     // tile token 16 h + 4 grp + i of row col; full tiles that every row may see in
     // full need no mask
     float pr[RB][8], alpha[RB], tmax[RB], sv_keep[RB][8];
@@ -484,8 +494,7 @@ void multi_query_kernel(MultiQueryParams p) {
       float mx = sv[0];
 #pragma unroll
       for (int u = 1; u < 8; ++u) mx = fmaxf(mx, sv[u]);
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = max_over_groups(mx);
       tmax[b] = fmaxf(m[b], mx);
       sv_keep[b][0] = sv[0];
 #pragma unroll
@@ -527,7 +536,7 @@ void multi_query_kernel(MultiQueryParams p) {
         float a[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u)
-          a[u] = *reinterpret_cast<const float*>(ldsV + (16 * (u >> 2) + 4 * grp + (u & 3)) * S::VSTRIDE +
+          a[u] = *reinterpret_cast<const float*>(vb + (16 * (u >> 2) + 4 * grp + (u & 3)) * S::VSTRIDE +
                                                  (16 * j + col) * 4);
 #pragma unroll
         for (int b = 0; b < RB; ++b)
@@ -572,7 +581,7 @@ void multi_query_kernel(MultiQueryParams p) {
       // A = V^T for head_dim 16 j .. 16 j + 15 through two transpose reads: slots
       // 8 grp + 4 h + q hold tile tokens 16 h + 4 grp + q, and lane (grp, col) names the
       // row 16 h + 4 grp + col / 4 at head_dim 16 j + 4 (col % 4)
-      const char* vbase = ldsV + (4 * grp + (col >> 2)) * S::VSTRIDE + (4 * (col & 3)) * 2;
+      const char* vbase = vb + (4 * grp + (col >> 2)) * S::VSTRIDE + (4 * (col & 3)) * 2;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const s16x4 a0 = lds_read_tr16(vbase + 32 * j);
@@ -628,7 +637,7 @@ void multi_query_kernel(MultiQueryParams p) {
     for (int k = wave; k < ntiles; k += kstep) {
       const int t0 = t_begin + k * kTile;
       const bool more = k + kstep < ntiles;
-      store_kv(kr[0], vr[0]);
+      store_kv(kr[0], vr[0], nullptr, ldsV);
       if (more) {
         offsets(tb, to, off);
         load_rows(vr[0], p.v_cache, off);
@@ -637,18 +646,21 @@ void multi_query_kernel(MultiQueryParams p) {
       if (more) load_rows(kr[0], p.k_cache, off);
       if (k + 2 * kstep < ntiles) fetch_table(tb, to, tile_map(t0 + 2 * kstep * kTile));
       __builtin_amdgcn_wave_barrier();   // V stores above are read by other lanes below
-      softmax_pv(t0, tile_map(t0));
+      softmax_pv(t0, tile_map(t0), ldsV);
       __builtin_amdgcn_wave_barrier();   // V reads above before the next stores
     }
   } else {
-    // all tiles, two sets of registers: while tile k is computed, the rows of tiles
-    // k + 1 and k + 2 and the table entries of tile k + 3 are on their way
+    // all tiles, two sets of registers and two LDS buffers: while tile k is computed,
+    // the rows of tiles k + 1 and k + 2 and the table entries of tile k + 3 are on
+    // their way.  Tile k goes to buffer k % 2, whose last readers (tile k - 2) have
+    // all passed the barrier of tile k - 1, so one barrier per tile suffices.
     int tb[2][NT], to[2][NT];
-    auto step = [&](int k, u32x4 (&xk)[KL], u32x4 (&xv)[KL], const int (&tbc)[NT], const int (&toc)[NT],
-                    int (&tbn)[NT], int (&ton)[NT]) {
+    auto step = [&](int k, char* buf, u32x4 (&xk)[KL], u32x4 (&xv)[KL], const int (&tbc)[NT],
+                    const int (&toc)[NT], int (&tbn)[NT], int (&ton)[NT]) {
       const int t0 = t_begin + k * kTile;
-      __syncthreads();  // the previous tile is no longer read
-      store_kv(xk, xv);
+      char* const kb = buf;
+      char* const vb = buf + S::KBYTES;
+      store_kv(xk, xv, kb, vb);
       __syncthreads();
       if (k + 3 < ntiles) fetch_table(tbn, ton, tile_map(t0 + 3 * kTile));
       if (k + 2 < ntiles) {
@@ -658,9 +670,9 @@ void multi_query_kernel(MultiQueryParams p) {
         load_rows(xv, p.v_cache, off);
       }
       qk([&](int h, int c) {
-        return *reinterpret_cast<const u32x4*>(ldsK + (16 * h + col) * S::KSTRIDE + chunk_of<DT, D>(c, grp) * 16);
+        return *reinterpret_cast<const u32x4*>(kb + (16 * h + col) * S::KSTRIDE + chunk_of<DT, D>(c, grp) * 16);
       });
-      softmax_pv(t0, tile_map(t0));
+      softmax_pv(t0, tile_map(t0), vb);
     };
     if (ntiles > 0) fetch_table(tb[0], to[0], tile_map(t_begin));
     if (ntiles > 1) fetch_table(tb[1], to[1], tile_map(t_begin + kTile));
@@ -674,8 +686,8 @@ void multi_query_kernel(MultiQueryParams p) {
     }
     if (ntiles > 2) fetch_table(tb[0], to[0], tile_map(t_begin + 2 * kTile));
     for (int k = 0; k < ntiles; k += 2) {
-      step(k, kr[0], vr[0], tb[0], to[0], tb[1], to[1]);
-      if (k + 1 < ntiles) step(k + 1, kr[1], vr[1], tb[1], to[1], tb[0], to[0]);
+      step(k, lds, kr[0], vr[0], tb[0], to[0], tb[1], to[1]);
+      if (k + 1 < ntiles) step(k + 1, lds + S::LDS, kr[1], vr[1], tb[1], to[1], tb[0], to[0]);
     }
   }
 
