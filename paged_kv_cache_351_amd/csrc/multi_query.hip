@@ -20,7 +20,8 @@
 //   partition the workgroup writes the output; otherwise it leaves (m, l, acc)
 //   per row and a second kernel merges the partitions in order.  Workgroups are
 //   numbered so that every query block and partition of one (sequence, KV head)
-//   runs on the same XCD (workgroup id mod 8), where they share its L2.
+//   runs on the same XCD (workgroup id mod 8), where they share its L2, and
+//   consecutive (sequence, KV head) units run on different XCDs.
 //
 // Per tile of 32 tokens
 //   All 256 lanes load the tile's K and V rows (16 bytes per load, token ->
@@ -155,14 +156,20 @@ struct Item {
 
 // Decode the workgroup's item.  With an ordering, workgroups take the items in
 // dispatch order, longest sequence (group) first, so that the last ones to start are
-// the shortest; otherwise every query block and partition of one (sequence, KV head)
-// goes to the same XCD (workgroup id mod 8), where they share its L2.
+// the shortest.  Otherwise the (sequence, KV head) units are dealt to the 8 XCDs in
+// turn (workgroup b runs on XCD b mod 8), unit u to XCD u mod 8, and every query block
+// and partition of a unit stays on its XCD, where they share its L2: the XCDs get
+// equal shares of every sequence's KV heads rather than whole sequences.  The grid is
+// then 8 * ceil(units / 8) * (query blocks * partitions) workgroups.
 __device__ __forceinline__ bool item_of(const MultiQueryParams& p, Item& it) {
   const long long b = blockIdx.x;
   long long logical = b;
   if (!p.order) {
-    const long long per = (long long)gridDim.x / 8;  // the grid is a multiple of 8
-    logical = (b % 8) * per + b / 8;
+    const long long ipu = (long long)p.qblocks * p.parts;   // items per unit
+    const long long j = b / 8;
+    const long long u = (j / ipu) * 8 + b % 8;
+    if (u >= (long long)p.num_seqs * p.num_kv_heads) return false;
+    logical = u * ipu + j % ipu;
   }
   if (logical >= (long long)p.items * p.parts) return false;
   it.part = (int)(logical % p.parts);

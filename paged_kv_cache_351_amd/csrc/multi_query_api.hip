@@ -115,7 +115,12 @@ pa_status pa_multi_query(const void* q, const void* k_cache, const void* v_cache
     return fail(PA_ERR_INVALID, "pa_multi_query: q, caches and out must be 16-byte aligned");
   const MQPlan pl = mq_plan(num_seqs, total_q, num_heads, num_kv_heads, head_dim, max_q_len, max_seq_len,
                             (int)dtype);
-  if (pl.items * pl.parts + 8 >= (1LL << 31))
+  // without an ordering the kernel deals (sequence, KV head) units to the 8 XCDs in
+  // turn, a multiple of 8 units times the items of a unit
+  const long long units = (long long)num_seqs * num_kv_heads;
+  const long long wgs = pl.order_bytes > 0 ? (pl.items * pl.parts + 7) / 8 * 8
+                                           : (units + 7) / 8 * 8 * ((long long)pl.qblocks * pl.parts);
+  if (wgs >= (1LL << 31))
     return fail(PA_ERR_UNSUPPORTED, "pa_multi_query: more than 2^31 workgroups");
   if (pl.total > 0 && (!workspace || workspace_bytes < pl.total))
     return fail(PA_ERR_WORKSPACE, "pa_multi_query: workspace of %zu bytes, %zu needed", workspace_bytes,
@@ -180,7 +185,6 @@ pa_status pa_multi_query(const void* q, const void* k_cache, const void* v_cache
   mp.parts = pl.parts;
   mp.items = pl.items;
   mp.scale_log2e = (float)((double)scale * 1.4426950408889634074);
-  const long long wgs = (pl.items * pl.parts + 7) / 8 * 8;
   void* args[] = {&mp};
   hipError_t e;
   if (pl.order_bytes > 0) {
