@@ -190,10 +190,9 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst_pa
  *                  q_start[num_seqs] = total_q
  *   seq_lens       device int32 [num_seqs], n_s <= L_s <= max_seq_len
  *   max_q_len      host bound on every n_s (no device sync is made)
- *   workspace      pa_multi_query_workspace_size(...) bytes (may be 0): a
- *                  longest-first order of the sequences when every sequence has
- *                  at most 16 / group queries, and partial results when the
- *                  context is partitioned; no zero-fill needed
+ *   workspace      pa_multi_query_workspace_size(...) bytes: a longest-first
+ *                  order of the sequences, and partial results when the context
+ *                  is partitioned; no zero-fill needed
  *
  * Work is cut into (sequence, KV head, block of query rows, context
  * partition) items; with few items the context is split into partitions that

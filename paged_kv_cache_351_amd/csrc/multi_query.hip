@@ -154,36 +154,30 @@ struct Item {
   int s, kv, qb, part;
 };
 
-// Decode the workgroup's item.  With an ordering, workgroups take the items in
-// dispatch order, longest sequence (group) first, so that the last ones to start are
-// the shortest.  Otherwise the (sequence, KV head) units are dealt to the 8 XCDs in
-// turn (workgroup b runs on XCD b mod 8), unit u to XCD u mod 8, and every query block
-// and partition of a unit stays on its XCD, where they share its L2: the XCDs get
-// equal shares of every sequence's KV heads rather than whole sequences.  The grid is
-// then 8 * ceil(units / 8) * (query blocks * partitions) workgroups.
+// Decode the workgroup's item.  The (sequence, KV head) units are dealt to the 8
+// XCDs in turn (workgroup b runs on XCD b mod 8), unit u to XCD u mod 8, and every
+// query block and partition of a unit stays on its XCD, where they share its L2: the
+// XCDs get equal shares of every sequence's KV heads rather than whole sequences.
+// Each XCD takes its units in order, a unit's last query block (the most context)
+// first; with an ordering the units' sequences (groups) come longest first, so that
+// the last items to start are the shortest.  The grid is 8 * ceil(units / 8) *
+// (query blocks * partitions) workgroups.
 __device__ __forceinline__ bool item_of(const MultiQueryParams& p, Item& it) {
   const long long b = blockIdx.x;
-  long long logical = b;
-  if (!p.order) {
-    const long long ipu = (long long)p.qblocks * p.parts;   // items per unit
-    const long long j = b / 8;
-    const long long u = (j / ipu) * 8 + b % 8;
-    if (u >= (long long)p.num_seqs * p.num_kv_heads) return false;
-    logical = u * ipu + j % ipu;
-  }
-  if (logical >= (long long)p.items * p.parts) return false;
-  it.part = (int)(logical % p.parts);
-  long long r = logical / p.parts;
-  it.qb = (int)(r % p.qblocks);
-  r /= p.qblocks;
-  it.kv = (int)(r % p.num_kv_heads);
-  it.s = (int)(r / p.num_kv_heads);
-  if (it.s >= p.num_seqs) return false;
+  const long long ipu = (long long)p.qblocks * p.parts;   // items per unit
+  const long long j = b / 8;
+  const long long u = (j / ipu) * 8 + b % 8;
+  if (u >= (long long)p.num_seqs * p.num_kv_heads) return false;
+  const long long r = j % ipu;
+  it.part = (int)(r % p.parts);
+  it.qb = p.qblocks - 1 - (int)(r / p.parts);
+  it.kv = (int)(u % p.num_kv_heads);
+  int s = (int)(u / p.num_kv_heads);
   if (p.order) {
-    const int s = p.order[it.s];
+    s = p.order[s];
     if (s < 0 || s >= p.num_seqs) return false;
-    it.s = s;
   }
+  it.s = s;
   return true;
 }
 

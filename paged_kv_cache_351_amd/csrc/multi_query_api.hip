@@ -44,9 +44,9 @@ MQPlan mq_plan(int num_seqs, int total_q, int num_heads, int num_kv_heads, int h
     if (parts > kMQMaxParts) parts = kMQMaxParts;
     pl.parts = parts < 1 ? 1 : (int)parts;
   }
-  // one query block per item (at most 16 rows): lengths alone set each item's work,
-  // so the items are taken longest first
-  if ((long long)max_q_len * group <= 16 && num_seqs > 0)
+  // the sequences are taken longest first (their lengths set most of the items' work),
+  // so the last items to start are the shortest
+  if (num_seqs > 0)
     pl.order_bytes = ((size_t)num_seqs * sizeof(int32_t) + 255) / 256 * 256;
   if (pl.parts > 1) {
     const size_t slots = (size_t)total_q * num_heads * pl.parts;
@@ -115,11 +115,10 @@ pa_status pa_multi_query(const void* q, const void* k_cache, const void* v_cache
     return fail(PA_ERR_INVALID, "pa_multi_query: q, caches and out must be 16-byte aligned");
   const MQPlan pl = mq_plan(num_seqs, total_q, num_heads, num_kv_heads, head_dim, max_q_len, max_seq_len,
                             (int)dtype);
-  // without an ordering the kernel deals (sequence, KV head) units to the 8 XCDs in
-  // turn, a multiple of 8 units times the items of a unit
+  // the kernel deals (sequence, KV head) units to the 8 XCDs in turn: a multiple of 8
+  // units times the items of a unit
   const long long units = (long long)num_seqs * num_kv_heads;
-  const long long wgs = pl.order_bytes > 0 ? (pl.items * pl.parts + 7) / 8 * 8
-                                           : (units + 7) / 8 * 8 * ((long long)pl.qblocks * pl.parts);
+  const long long wgs = (units + 7) / 8 * 8 * ((long long)pl.qblocks * pl.parts);
   if (wgs >= (1LL << 31))
     return fail(PA_ERR_UNSUPPORTED, "pa_multi_query: more than 2^31 workgroups");
   if (pl.total > 0 && (!workspace || workspace_bytes < pl.total))
@@ -286,7 +285,9 @@ pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void
     return fail(PA_ERR_INVALID, "%s: q, caches and out must be 16-byte aligned", who);
   const MQPlan pl = sp_plan(num_seqs, num_groups, num_heads, num_kv_heads, head_dim, max_group_size,
                             max_seq_len);
-  if (pl.items * pl.parts + 8 >= (1LL << 31))
+  // (group, KV head) units dealt to the 8 XCDs in turn, as for pa_multi_query
+  const long long wgs = ((long long)num_groups * num_kv_heads + 7) / 8 * 8 * ((long long)pl.qblocks * pl.parts);
+  if (wgs >= (1LL << 31))
     return fail(PA_ERR_UNSUPPORTED, "%s: more than 2^31 workgroups", who);
   if (pl.total > 0 && (!workspace || workspace_bytes < pl.total))
     return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed", who, workspace_bytes, pl.total);
@@ -363,7 +364,6 @@ pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void
   mp.parts = pl.parts;
   mp.items = pl.items;
   mp.scale_log2e = (float)((double)scale * 1.4426950408889634074);
-  const long long wgs = (pl.items * pl.parts + 7) / 8 * 8;
   void* args[] = {&mp};
   hipError_t e = hipLaunchKernel(multi_query_order_kernel(true), dim3(1), dim3(1024), args, 0, st);
   if (e != hipSuccess) return hip_fail(e, "pa_decode_shared_prefix order launch");

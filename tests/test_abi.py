@@ -153,7 +153,7 @@ def test_multi_query_workspace_formula(pk, N, TQ, H, HKV, D, MQ, L):
     parts = max(1, min(-(-1024 // items), -(-L // 256), 64)) if items and L else 1
     up = lambda x: -(-x // 256) * 256
     want = 0 if parts == 1 else up(TQ * H * parts * 2 * 4) + TQ * H * parts * D * 4
-    if MQ * g <= 16 and N > 0:   # one block per item: a longest-first order of the sequences
+    if N > 0:   # a longest-first order of the sequences
         want += up(4 * N)
     assert pk.pa_multi_query_workspace_size(N, TQ, H, HKV, D, MQ, L) == want
 
