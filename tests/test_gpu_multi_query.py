@@ -93,6 +93,24 @@ def test_shape_sweep(case):
     assert_close(out.float().cpu().double().numpy(), run_oracle(b), dt, f"sweep {case}")
 
 
+@pytest.mark.parametrize("dtype,scale,queries", [
+    ("bf16", -0.09, [4, 2, 1]),     # at most 16 rows per (sequence, KV head): split variant
+    ("bf16", -0.09, [40, 70, 1]),   # shared-tile variant
+    ("f16", 0.0, [4, 2, 1]),
+    ("f16", 0.0, [40, 70, 1]),
+    ("f32", -0.2, [40, 70, 1]),
+    ("bf16", 0.0, [40, 70, 1]),
+])
+def test_negative_and_zero_scale(dtype, scale, queries):
+    # a negative scale reverses the ordering of the scores (the kernel flips the sign of
+    # q and uses the magnitude); scale 0 gives every visible token the same weight
+    b = batch(31, dtype, [90, 200, 33], queries, 16, 4, 128, 16)
+    b.scale = scale
+    log(f"scale {scale} {dtype} queries {queries}")
+    out, _ = run_gpu(b)
+    assert_close(out.float().cpu().double().numpy(), run_oracle(b), dtype, f"scale {scale}")
+
+
 def test_long_context_few_queries_uses_partitions():
     # one sequence, 3 queries, 5000 tokens: few work items, so the context is split
     # into partitions and merged by the second kernel

@@ -120,6 +120,15 @@ def test_groups_match_the_decode_oracle(case):
     assert_close(out.float().cpu().double().numpy(), oracle_out(b), dt, f"case {case}")
 
 
+@pytest.mark.parametrize("scale", [-0.11, 0.0])
+def test_negative_and_zero_scale(scale):
+    b = grouped_batch(61, "bf16", [(64, [0, 5, 17, 40]), (33, [1, 0, 2])], 32, 8, 128, 16)
+    b.scale = scale
+    log(f"shared prefix, scale {scale}")
+    out, _ = run(b)
+    assert_close(out.float().cpu().double().numpy(), oracle_out(b), "bf16", f"scale {scale}")
+
+
 def test_many_groups_in_longest_first_order():
     # more groups than the ordering pass has threads
     rng = np.random.default_rng(3)
