@@ -112,8 +112,11 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, i
  *                bytes, 256-byte aligned, zero-filled before its first use.
  *                A call leaves it ready for the next one (the counter it
  *                uses to hand out work is back at 0), so it is zeroed once,
- *                not per call.  Calls that share a workspace must not run
- *                concurrently (put them on one stream).
+ *                not per call.  A first call on a workspace that was not
+ *                zeroed may give wrong results but keeps every access inside
+ *                the arrays, and still leaves the workspace ready.  Calls
+ *                that share a workspace must not run concurrently (put them
+ *                on one stream).
  *   max_seq_len  caller's upper bound on every seq_lens[s]; must be
  *                <= max_blocks_per_seq * block_size and <= 2^24.  Lengths
  *                above it are clamped to it, negative lengths to 0.

@@ -249,12 +249,14 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   int* const chunk_meta = p.ws_meta + 64;
   if (w == 0 && lane == 0) hdr[0] = (int)plan.chunks();
 
-  // Next tail part for this wave, or -1 when all are taken.
+  // Next tail part for this wave, or -1 when all are taken.  A counter that did not
+  // start at 0 (a workspace never zeroed) gives tickets outside [0, pieces * nw),
+  // which hand out nothing rather than a chunk outside the plan.
   auto next_tail = [&]() -> long long {
     int ticket = 0;
     if (lane == 0) ticket = atomicAdd(hdr + 32, 1);
     ticket = __builtin_amdgcn_readfirstlane(ticket);
-    return ticket < (long long)plan.pieces * nw ? plan.ticket_chunk(ticket) : -1;
+    return ticket >= 0 && ticket < (long long)plan.pieces * nw ? plan.ticket_chunk(ticket) : -1;
   };
 
   const size_t tok_stride = (size_t)Hkv * ROWB;
@@ -648,12 +650,17 @@ __global__ __launch_bounds__(256) void reduce_kernel(DecodeParams p) {
   if (blockIdx.x == 0 && threadIdx.x == 0) hdr[32] = 0;
   const int lane = threadIdx.x & 63;
   const int c = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (c >= hdr[0]) return;
+  const int nchunks = hdr[0];
+  if (c >= nchunks) return;
+  // A chunk record is written by the chunk's wave in this call; the checks keep a
+  // stale record (a workspace never zeroed, whose counter handed out no tail) inside
+  // the chunk list and the output.
   const int* meta = chunk_meta + 4 * (size_t)c;
-  const int parts = meta[2];
+  const int parts = min(meta[2], nchunks - c);
   if (parts < 2) return;
   const int s = meta[0];
   const int kv = meta[1];
+  if (s < 0 || s >= p.num_seqs || kv < 0 || kv >= p.num_kv_heads) return;
   const int g = p.group;
   const int h = lane / LPH;
   const int sub = lane % LPH;

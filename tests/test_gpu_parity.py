@@ -154,6 +154,29 @@ def test_deterministic_and_invariant_under_block_relabelling():
     assert_close(o1, oracle_decode(b), "bf16", "relabel")
 
 
+def test_workspace_not_zeroed_before_first_call():
+    # The contract asks for a zero-filled workspace before the first call.  One filled
+    # with 0xFF bytes instead starts the tail counter at -1: that ticket hands out no
+    # chunk, every tail part is still taken once, every access stays in bounds, and the
+    # call leaves the counter at 0, so both calls match the oracle.
+    rng = np.random.default_rng(29)
+    lens = rng.integers(500, 3000, 64).tolist()
+    b = random_batch(29, "bf16", lens, 32, 8, 128, 16)
+    d = to_dev(b)
+    m = pk()
+    ws = m.decode_workspace(d.q, b.num_kv_heads, max(lens))
+    assert ws is not None
+    ws.fill_(255)
+    log("decode with a 0xFF-filled workspace, twice")
+    ref = oracle_decode(b)
+    for call in range(2):
+        out = torch.empty_like(d.q)
+        m.pa_decode(d.q, d.kc, d.vc, d.bt, d.lens, b.num_kv_heads, b.scale, out,
+                    max_seq_len=max(lens), workspace=ws)
+        torch.cuda.synchronize()
+        assert_close(out.float().cpu().double().numpy(), ref, "bf16", f"0xFF workspace, call {call}")
+
+
 def test_write_kv_is_bit_exact_on_arbitrary_bit_patterns():
     torch.manual_seed(0)
     NB, B, H, D, T = 50, 16, 8, 128, 300
