@@ -33,14 +33,25 @@
 //     positions to MFMA k-slots gives the same dot products, so the chunking
 //     only has to match between A and B.  The result lands as
 //     S[token 4*grp + r][head col], r = 0..3, in lane (grp, col).
-//   Online softmax: lane (grp, col) keeps its own running max m and sum l for
-//     head col over the tokens 4*grp + r of every tile, i.e. four independent
-//     streams per head; they are merged once at the end of the segment.
-//   P.V on the vector ALU: lane (grp, col) owns head_dim/16 consecutive
-//     elements (at col * head_dim/16) of tokens 4*grp + j, j = 0..3, and
-//     accumulates acc[h][.] for every head h of the group.  The weight p of
-//     (head h, token 4*grp + j) sits in lane (grp, h); DPP row_newbcast:h
-//     broadcasts it to the 16 lanes of the row -- no LDS, no barrier.
+//   P.V on the matrix cores (16-bit types, groups of 3 or more query heads):
+//     O^T += V^T P^T with v_mfma_f32_16x16x16_{bf16,f16}, one product per
+//     element e of the lane's V slice: the A operand is element col * head_dim/16
+//     + e of the lane's four token rows (gathered with v_perm), the B operand is
+//     the lane's own four weights, so no weight moves between lanes.  Lane
+//     (grp, col) ends with head col over elements (4*grp + r) * head_dim/16 + e.
+//     All 16 tokens of a tile meet in one sum, so every head keeps one reference
+//     maximum for the four row groups (row swaps v_permlane{32,16}_swap), moved
+//     only when a tile exceeds it by 2^8: weights stay below 256 and the
+//     accumulators are rescaled on few tiles.  bf16 weights are split into two
+//     bf16 terms (about 16 significant bits), fp16 weights are rounded once.
+//   P.V on the vector ALU (fp32, and groups of 1 or 2): lane (grp, col) keeps its
+//     own running max m and sum l for head col over the tokens 4*grp + r of
+//     every tile, i.e. four independent streams per head, merged once at the end
+//     of the segment.  It owns head_dim/16 consecutive elements (at col *
+//     head_dim/16) of tokens 4*grp + j, j = 0..3, and accumulates acc[h][.] for
+//     every head h of the group.  The weight p of (head h, token 4*grp + j) sits
+//     in lane (grp, h); DPP row_newbcast:h broadcasts it to the 16 lanes of the
+//     row -- no LDS, no barrier.
 //   Block ids: lane i holds the id of the segment's block 64 w + i for the
 //     current window w (v_readlane picks it per tile) and the next 64 ids are
 //     fetched a window ahead, so the two-tile pipeline runs through a whole
@@ -67,8 +78,26 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kNegBig = -1.0e30f;
+#ifndef PA_DECODE_PIPE
+#define PA_DECODE_PIPE 2
+#endif
+// K/V tiles in flight per wave (3 measured no faster than 2 on the Llama-3-8B shape)
+constexpr int kDecodePipe = PA_DECODE_PIPE;
+#ifndef PA_DECODE_MPV_MIN_GP
+#define PA_DECODE_MPV_MIN_GP 4
+#endif
+// P.V on the matrix cores for 16-bit types from this padded group size on; smaller
+// groups keep it on the vector ALU (with one or two heads most of the 16 product
+// rows would be padding).
+template <int DT, int GP>
+constexpr bool kMatrixPV = DT != kF32 && GP >= PA_DECODE_MPV_MIN_GP;
+// A reference maximum moves only when a tile's maximum exceeds it by more than this
+// (log2 units), so weights stay below 2^8 and the accumulators are rescaled rarely.
+constexpr float kLazyMax = 8.0f;
 
 template <int DT>
 struct Elem {
@@ -90,6 +119,39 @@ __device__ __forceinline__ float row_bcast(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Maximum over lanes i, i ^ 16, i ^ 32 and i ^ 48 (the four 16-lane rows) with the
+// gfx950 row swaps: swapping a value with a copy of itself leaves one lane of each
+// pair in each result, so the larger of the two is the pair's maximum.
+__device__ __forceinline__ float max_over_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Two floats rounded to nearest even in a 16-bit type, the first in the low half.
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  if constexpr (DT == kBF16) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+  } else {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+  }
+}
+
+// One 16x16x16 product on the matrix cores, 16-bit inputs, fp32 accumulate.
+template <int DT>
+__device__ __forceinline__ f32x4 mfma16(uint32_t a0, uint32_t a1, uint32_t b0, uint32_t b1, f32x4 c) {
+  if constexpr (DT == kBF16)
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, u32x2{a0, a1}),
+                                                     __builtin_bit_cast(s16x4, u32x2{b0, b1}), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, u32x2{a0, a1}),
+                                                 __builtin_bit_cast(f16x4, u32x2{b0, b1}), c, 0, 0, 0);
+}
 
 // Inclusive prefix sum over the 64 lanes, in registers: shifts by 1, 2, 4, 8
 // inside each 16-lane row (lanes shifted in from outside the row read 0), then
@@ -376,11 +438,18 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
 
       float m = kNegBig;
       float l = 0.f;
-      float acc[GP][VE];
+      // P.V accumulators.  Vector ALU: acc[h][e] = head h, element col*VE + e, over
+      // this lane's tokens.  Matrix cores (MPV): oacc[i][r] = head col, element
+      // (4*grp + r)*VE + i, over all tokens.
+      constexpr bool MPV = kMatrixPV<DT, GP>;
+      float acc[MPV ? 1 : GP][VE];
+      f32x4 oacc[MPV ? VE : 1];
 #pragma unroll
-      for (int h = 0; h < GP; ++h)
+      for (int h = 0; h < (MPV ? 1 : GP); ++h)
 #pragma unroll
         for (int e = 0; e < VE; ++e) acc[h][e] = 0.f;
+#pragma unroll
+      for (int i = 0; i < (MPV ? VE : 1); ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
       // Issue the loads of lc's tile, then step lc (the chunk's last tile is
       // loaded again rather than stepping past it).  A token index past the pair's
@@ -455,8 +524,64 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
         }
       };
 
+      // Record a finished piece of a split pair: owner bookkeeping shared by both
+      // accumulator layouts.
+      auto note_piece = [&](int s, int kv, int jb, int n_pair, long long tseg) __attribute__((always_inline)) {
+        if (jb == 0) {
+          meta_s = s;
+          meta_kv = kv;
+          meta_parts = (int)(plan.chunk_of(tseg + n_pair - 1) - ck + 1);
+        } else {
+          meta_first = 1;
+        }
+      };
+
+      // Matrix-core layout: every row group already holds the full sums of head col
+      // for its 4*VE elements, and the reference maximum m is the same in all four
+      // groups; only the running sums are added over the groups.
+      auto flush_mpv = [&](int s, int kv, int jb, int je, int L, long long tseg) __attribute__((always_inline)) {
+        float ls = l;
+        ls += __shfl_xor(ls, 16);
+        ls += __shfl_xor(ls, 32);
+        const int n_pair = tiles_of(L);
+        const int d0 = 4 * grp * VE;  // first element of this lane's run
+        if (col < g) {
+          float o[4 * VE];
+          if (jb == 0 && je == n_pair) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+              for (int i = 0; i < VE; ++i) o[r * VE + i] = oacc[i][r] / ls;
+            store_row<DT, 4 * VE>((char*)p.out + ((size_t)s * p.num_heads + kv * g + col) * ROWB + d0 * EB, o);
+          } else {
+            const size_t slot = 2 * (size_t)ck + (jb == 0 ? 1 : 0);
+            float* dst = p.ws_acc + (slot * g + col) * D + d0;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+              for (int i = 0; i < VE; i += 4)
+                *reinterpret_cast<f32x4*>(dst + r * VE + i) =
+                    f32x4{oacc[i][r], oacc[i + 1][r], oacc[i + 2][r], oacc[i + 3][r]};
+            if (grp == 0) {
+              float* ml = p.ws_ml + (slot * g + col) * 2;
+              ml[0] = m;
+              ml[1] = ls;
+            }
+          }
+        }
+        if (!(jb == 0 && je == n_pair)) note_piece(s, kv, jb, n_pair, tseg);
+        m = kNegBig;
+        l = 0.f;
+#pragma unroll
+        for (int i = 0; i < VE; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      };
+
       // Normalise or store the finished segment [jb, je) of pair (s, kv).
       auto flush = [&](int s, int kv, int jb, int je, int L, long long tseg) __attribute__((always_inline)) {
+        if constexpr (MPV) {
+          flush_mpv(s, kv, jb, je, L, tseg);
+          return;
+        }
         // Merge the four per-group streams of every head.
         float M = fmaxf(m, __shfl_xor(m, 16));
         M = fmaxf(M, __shfl_xor(M, 32));
@@ -509,18 +634,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
             ml[0] = M;
             ml[1] = ls;
           }
-          if (owner) {
-            meta_s = s;
-            meta_kv = kv;
-            meta_parts = (int)(plan.chunk_of(tseg + n_pair - 1) - ck + 1);
-          } else {
-            meta_first = 1;
-          }
+          note_piece(s, kv, jb, n_pair, tseg);
         }
         m = kNegBig;
         l = 0.f;
 #pragma unroll
-        for (int h = 0; h < GP; ++h)
+        for (int h = 0; h < (MPV ? 1 : GP); ++h)
 #pragma unroll
           for (int e = 0; e < VE; ++e) acc[h][e] = 0.f;
       };
@@ -550,33 +669,87 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
         float sv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) sv[r] = r < lim ? sc[r] * sl2 : -__builtin_inff();
-        const float mn = fmaxf(m, fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
-        const float alpha = fast_exp2(m - mn);
-        float pr[4];
+        if constexpr (MPV) {
+          // One reference maximum per head for all 16 tokens (the product below sums
+          // over every row group), moved only when the tile exceeds it by kLazyMax.
+          const float tmx = max_over_rows(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+          if (__any(tmx > m + kLazyMax)) {
+            const float mn = tmx > m + kLazyMax ? tmx : m;
+            const float alpha = fast_exp2(m - mn);
+            l *= alpha;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(sv[r] - mn);
-        l = l * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
-        m = mn;
-        // rescale the accumulators only when some running max moved
-        if (__any(col < GP && alpha != 1.0f)) {
-          static_for<GP>([&](auto hc) {
-            constexpr int h = decltype(hc)::value;
-            const float a = row_bcast<h>(alpha);
+            for (int i = 0; i < VE; ++i) oacc[i] *= alpha;
+            m = mn;
+          }
+          float pr[4];
 #pragma unroll
-            for (int e = 0; e < VE; ++e) acc[h][e] *= a;
-          });
-        }
-        // P V on the vector ALU
+          for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(sv[r] - m);
+          // P^T as the B operand (tokens 4*grp + r of head col).  bf16 keeps 8
+          // significant bits, so P is split in two: the high term is P cut to its top
+          // 16 bits (the remainder is exact in fp32) and the low term that remainder
+          // rounded; the running sum adds the fp32 weights.  fp16 keeps 11 bits in one
+          // term and the running sum adds the rounded weights.
+          uint32_t ph[2], pl[2];
+          if constexpr (DT == kBF16) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float vf[VE];
-          unpack<DT, VW>(Tl.v[j], vf);
-          static_for<GP>([&](auto hc) {
-            constexpr int h = decltype(hc)::value;
-            const float pj = row_bcast<h>(pr[j]);
+            for (int u = 0; u < 2; ++u) {
+              const uint32_t x = __float_as_uint(pr[2 * u]), y = __float_as_uint(pr[2 * u + 1]);
+              ph[u] = (x >> 16) | (y & 0xffff0000u);
+              pl[u] = pack2<DT>(pr[2 * u] - __uint_as_float(x & 0xffff0000u),
+                                pr[2 * u + 1] - __uint_as_float(y & 0xffff0000u));
+            }
+            l += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+          } else {
+            float ps = 0.f;
 #pragma unroll
-            for (int e = 0; e < VE; ++e) acc[h][e] = fmaf(pj, vf[e], acc[h][e]);
-          });
+            for (int u = 0; u < 2; ++u) {
+              ph[u] = pack2<DT>(pr[2 * u], pr[2 * u + 1]);
+              const f16x2 h = __builtin_bit_cast(f16x2, ph[u]);
+              ps += (float)h.x + (float)h.y;
+              pl[u] = 0u;
+            }
+            l += ps;
+          }
+          // O^T += V^T P^T: the A operand of product i is element col*VE + i of the
+          // lane's four token rows (row m = col of the 16x16 tile), so the result row
+          // 4*grp + r stands for element (4*grp + r)*VE + i.
+#pragma unroll
+          for (int i = 0; i < VE; ++i) {
+            const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
+            const uint32_t a0 = __builtin_amdgcn_perm(Tl.v[1][i >> 1], Tl.v[0][i >> 1], sel);
+            const uint32_t a1 = __builtin_amdgcn_perm(Tl.v[3][i >> 1], Tl.v[2][i >> 1], sel);
+            oacc[i] = mfma16<DT>(a0, a1, ph[0], ph[1], oacc[i]);
+            if constexpr (DT == kBF16) oacc[i] = mfma16<DT>(a0, a1, pl[0], pl[1], oacc[i]);
+          }
+        } else {
+          const float mn = fmaxf(m, fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+          const float alpha = fast_exp2(m - mn);
+          float pr[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) pr[r] = fast_exp2(sv[r] - mn);
+          l = l * alpha + ((pr[0] + pr[1]) + (pr[2] + pr[3]));
+          m = mn;
+          // rescale the accumulators only when some running max moved
+          if (__any(col < GP && alpha != 1.0f)) {
+            static_for<GP>([&](auto hc) {
+              constexpr int h = decltype(hc)::value;
+              const float a = row_bcast<h>(alpha);
+#pragma unroll
+              for (int e = 0; e < VE; ++e) acc[h][e] *= a;
+            });
+          }
+          // P V on the vector ALU
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            float vf[VE];
+            unpack<DT, VW>(Tl.v[j], vf);
+            static_for<GP>([&](auto hc) {
+              constexpr int h = decltype(hc)::value;
+              const float pj = row_bcast<h>(pr[j]);
+#pragma unroll
+              for (int e = 0; e < VE; ++e) acc[h][e] = fmaf(pj, vf[e], acc[h][e]);
+            });
+          }
         }
 
         TileCursor nx = cc;  // as for lc, the step succeeds whenever a tile is left
@@ -602,24 +775,23 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
         }
       };
 
-      // Two tiles in flight: while one is reduced the next two are being fetched.
-      // Loads are unconditional so no tile register is ever copied, and the
-      // scheduling barriers keep a refill after the last use of the registers it
-      // overwrites.
-      Tile A, B;
-      load_next(A);
-      __builtin_amdgcn_sched_barrier(0);
-      load_next(B);
-      __builtin_amdgcn_sched_barrier(0);
-      for (int tt = 0; tt < nt; tt += 2) {
-        compute_next(A);
+      // kDecodePipe tiles in flight: while one is reduced the next ones are being
+      // fetched.  Loads are unconditional so no tile register is ever copied, and
+      // the scheduling barriers keep a refill after the last use of the registers
+      // it overwrites.
+      Tile tl[kDecodePipe];
+      static_for<kDecodePipe>([&](auto ic) {
+        load_next(tl[decltype(ic)::value]);
         __builtin_amdgcn_sched_barrier(0);
-        load_next(A);
-        __builtin_amdgcn_sched_barrier(0);
-        if (tt + 1 < nt) compute_next(B);
-        __builtin_amdgcn_sched_barrier(0);
-        load_next(B);
-        __builtin_amdgcn_sched_barrier(0);
+      });
+      for (int tt = 0; tt < nt; tt += kDecodePipe) {
+        static_for<kDecodePipe>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          if (i == 0 || tt + i < nt) compute_next(tl[i]);
+          __builtin_amdgcn_sched_barrier(0);
+          load_next(tl[i]);
+          __builtin_amdgcn_sched_barrier(0);
+        });
       }
     }
     // Every chunk states whether it owns a split pair (parts >= 2) and whether it
