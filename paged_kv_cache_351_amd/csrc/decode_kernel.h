@@ -98,6 +98,10 @@ constexpr bool kMatrixPV = DT != kF32 && GP >= PA_DECODE_MPV_MIN_GP;
 // A reference maximum moves only when a tile's maximum exceeds it by more than this
 // (log2 units), so weights stay below 2^8 and the accumulators are rescaled rarely.
 constexpr float kLazyMax = 8.0f;
+// Batches of at most this many sequences keep every sequence's length and tile
+// prefix sum in LDS (each wave its own copy), so locating a chunk and stepping to
+// the next sequence read LDS instead of global memory.
+constexpr int kLdsSeqs = 2048;
 
 template <int DT>
 struct Elem {
@@ -290,16 +294,35 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   // Tiles of sequence s as seen by this lane (0 past the batch).
   auto lane_tiles = [&](int s) { return s < N ? tiles_of(seq_len_at(p, s)) : 0; };
 
+  // This wave's LDS copy of the lengths and of the tiles before each sequence (one
+  // KV head's worth: pair (s, kv) starts at tile Hkv * pre[s] + kv * n_s).
+  __shared__ int lds_pre[4][kLdsSeqs + 1];
+  __shared__ int lds_len[4][kLdsSeqs];
+  int* const pre = lds_pre[threadIdx.x >> 6];
+  int* const lenl = lds_len[threadIdx.x >> 6];
+  bool in_lds = N <= kLdsSeqs;
+
   // Total tiles of the step; the lengths of the next 64 sequences are loaded
-  // while the current 64 are summed.
+  // while the current 64 are summed (and, for a batch that fits, stored in LDS
+  // with their exclusive prefix sums).
   long long seq_tiles = 0;
   {
-    int n_cur = lane_tiles(lane);
+    int L_cur = lane < N ? seq_len_at(p, lane) : 0;
     for (int c = 0; c < N; c += 64) {
-      const int n_nxt = lane_tiles(c + 64 + lane);
-      seq_tiles += wave_sum(n_cur);
-      n_cur = n_nxt;
+      const int L_nxt = c + 64 + lane < N ? seq_len_at(p, c + 64 + lane) : 0;
+      const int n_cur = tiles_of(L_cur);
+      const int incl = wave_inclusive_scan(n_cur);
+      if (in_lds && c + lane < N) {
+        pre[c + lane] = (int)(seq_tiles + incl - n_cur);
+        lenl[c + lane] = L_cur;
+      }
+      seq_tiles += __builtin_amdgcn_readlane(incl, 63);
+      L_cur = L_nxt;
     }
+    // prefix sums must fit in an int; the writes above complete before any read
+    in_lds = in_lds && seq_tiles < (1ll << 31) - 1;
+    if (in_lds && lane == 0) pre[N] = (int)seq_tiles;
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
   }
   const long long T = seq_tiles * Hkv;
   const long long nw = waves_used(T, launched);
@@ -324,7 +347,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   const size_t tok_stride = (size_t)Hkv * ROWB;
   const size_t blk_bytes = (size_t)BS * tok_stride;
   const float sl2 = p.scale_log2e;
-  auto lenf = [&](int s) { return seq_len_at(p, s); };
+  auto lenf = [&](int s) { return in_lds ? lenl[s] : seq_len_at(p, s); };
   auto valid_id = [&](int id) __attribute__((always_inline)) {
     return (unsigned)id < (unsigned)p.num_blocks ? id : 0;
   };
@@ -339,7 +362,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   auto blocks_of = [&](int L) { return (L + BS - 1) / BS; };
   auto next_seq = [&](int s) {  // next non-empty sequence after s (N if none)
     int t = s + 1;
-    while (t < N && seq_len_at(p, t) == 0) ++t;
+    while (t < N && lenf(t) == 0) ++t;
     return t;
   };
   // Query fragments (MFMA B operand) of pair (s, kv): head kv g + col, chunks 4c + grp.
@@ -368,13 +391,24 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     const long long t0 = plan.begin(ck);
     const long long t1 = plan.begin(ck + 1);
     int meta_s = 0, meta_kv = 0, meta_parts = 0, meta_first = 0;
-    // Find the pair and tile of t0: the first sequence whose tiles end past t0.
-    // The scan goes 64 sequences at a time (the next 64 lengths load while the
-    // current ones are scanned) and resumes from the block of 64 where this
-    // wave's previous chunk began when t0 lies past it.
+    // Find the pair and tile of t0: the first sequence whose tiles end past t0,
+    // i.e. the last s < N with Hkv * pre[s] <= t0 (such an s is never empty).
+    // From LDS: one ballot over every 64th prefix sum, then one over the 64
+    // sequences of the block it picks.  Otherwise a scan 64 sequences at a time
+    // (the next 64 lengths load while the current ones are scanned) that resumes
+    // from the block of 64 where this wave's previous chunk began when t0 lies
+    // past it.
     int s0 = -1;
     long long pair_base = 0;
-    if (t0 < t1) {
+    if (t0 < t1 && in_lds) {
+      const int i1 = 64 * lane;
+      const unsigned long long b1 = __ballot(i1 < N && (long long)pre[i1] * Hkv <= t0);
+      const int k1 = 63 - __clzll(b1 | 1ull);
+      const int i2 = 64 * k1 + lane;
+      const unsigned long long b2 = __ballot(i2 < N && (long long)pre[i2] * Hkv <= t0);
+      s0 = 64 * k1 + (63 - __clzll(b2 | 1ull));
+      pair_base = (long long)pre[s0] * Hkv;
+    } else if (t0 < t1) {
       if (t0 < scan_base) {
         scan_c = 0;
         scan_base = 0;
@@ -399,7 +433,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     }
     // s0 >= 0 and 0 <= off < Hkv * n0 always for a non-empty chunk (t0 < T); the
     // tests only guard against reading past the lengths or the pool
-    const int L0 = s0 >= 0 ? seq_len_at(p, s0) : 0;
+    const int L0 = s0 >= 0 ? lenf(s0) : 0;
     int n0 = tiles_of(L0);
     const long long off = t0 - pair_base;
     if (t0 >= t1 || off < 0 || off >= (long long)Hkv * n0) n0 = 0;
@@ -422,7 +456,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
       int ids_row0 = fetch_ids(l_seq, l_nblk, 0);
       int ids_row1 = fetch_ids(l_seq, l_nblk, 1);
       int pf_seq = next_seq(l_seq);
-      int pf_nblk = pf_seq < N ? blocks_of(seq_len_at(p, pf_seq)) : 0;
+      int pf_nblk = pf_seq < N ? blocks_of(lenf(pf_seq)) : 0;
       int ids_pf0 = pf_seq < N ? fetch_ids(pf_seq, pf_nblk, 0) : 0;
       int ids_pf1 = pf_seq < N ? fetch_ids(pf_seq, pf_nblk, 1) : 0;
       int l_pair = 0, l_count = 0;
@@ -509,7 +543,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
                 ids_row1 = fetch_ids(l_seq, l_nblk, 1);
               }
               pf_seq = next_seq(l_seq);
-              pf_nblk = pf_seq < N ? blocks_of(seq_len_at(p, pf_seq)) : 0;
+              pf_nblk = pf_seq < N ? blocks_of(lenf(pf_seq)) : 0;
               ids_pf0 = pf_seq < N ? fetch_ids(pf_seq, pf_nblk, 0) : 0;
               ids_pf1 = pf_seq < N ? fetch_ids(pf_seq, pf_nblk, 1) : 0;
             }
@@ -580,68 +614,68 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
       auto flush = [&](int s, int kv, int jb, int je, int L, long long tseg) __attribute__((always_inline)) {
         if constexpr (MPV) {
           flush_mpv(s, kv, jb, je, L, tseg);
-          return;
-        }
-        // Merge the four per-group streams of every head.
-        float M = fmaxf(m, __shfl_xor(m, 16));
-        M = fmaxf(M, __shfl_xor(M, 32));
-        const float f = fast_exp2(m - M);
-        float ls = l * f;
-        ls += __shfl_xor(ls, 16);
-        ls += __shfl_xor(ls, 32);
-        static_for<GP>([&](auto hc) {
-          constexpr int h = decltype(hc)::value;
-          const float fh = row_bcast<h>(f);
-#pragma unroll
-          for (int e = 0; e < VE; ++e) {
-            float x = acc[h][e] * fh;
-            x += __shfl_xor(x, 16);
-            x += __shfl_xor(x, 32);
-            acc[h][e] = x;
-          }
-        });
-        const int head0 = kv * g;
-        const int n_pair = tiles_of(L);
-        if (jb == 0 && je == n_pair) {
-          // whole pair in this chunk: every row now holds the full sums; row grp
-          // stores heads h = grp (mod 4)
-          static_for<GP>([&](auto hc) {
-            constexpr int h = decltype(hc)::value;
-            const float lh = row_bcast<h>(ls);
-            if (h < g && (h & 3) == grp) {
-              float o[VE];
-#pragma unroll
-              for (int e = 0; e < VE; ++e) o[e] = acc[h][e] / lh;
-              store_row<DT, VE>((char*)p.out + ((size_t)s * p.num_heads + head0 + h) * ROWB + col * (VE * EB), o);
-            }
-          });
         } else {
-          // one piece of a pair split over chunks: the owner (first tile) writes to
-          // slot 2c + 1, every other piece is its chunk's first segment, slot 2c
-          const bool owner = jb == 0;
-          const size_t slot = 2 * (size_t)ck + (owner ? 1 : 0);
+          // Merge the four per-group streams of every head.
+          float M = fmaxf(m, __shfl_xor(m, 16));
+          M = fmaxf(M, __shfl_xor(M, 32));
+          const float f = fast_exp2(m - M);
+          float ls = l * f;
+          ls += __shfl_xor(ls, 16);
+          ls += __shfl_xor(ls, 32);
           static_for<GP>([&](auto hc) {
             constexpr int h = decltype(hc)::value;
-            if (h < g && (h & 3) == grp) {
-              float* dst = p.ws_acc + (slot * g + h) * D + col * VE;
+            const float fh = row_bcast<h>(f);
 #pragma unroll
-              for (int e = 0; e < VE; e += 4)
-                *reinterpret_cast<f32x4*>(dst + e) = f32x4{acc[h][e], acc[h][e + 1], acc[h][e + 2], acc[h][e + 3]};
+            for (int e = 0; e < VE; ++e) {
+              float x = acc[h][e] * fh;
+              x += __shfl_xor(x, 16);
+              x += __shfl_xor(x, 32);
+              acc[h][e] = x;
             }
           });
-          if (grp == 0 && col < g) {
-            float* ml = p.ws_ml + (slot * g + col) * 2;
-            ml[0] = M;
-            ml[1] = ls;
+          const int head0 = kv * g;
+          const int n_pair = tiles_of(L);
+          if (jb == 0 && je == n_pair) {
+            // whole pair in this chunk: every row now holds the full sums; row grp
+            // stores heads h = grp (mod 4)
+            static_for<GP>([&](auto hc) {
+              constexpr int h = decltype(hc)::value;
+              const float lh = row_bcast<h>(ls);
+              if (h < g && (h & 3) == grp) {
+                float o[VE];
+#pragma unroll
+                for (int e = 0; e < VE; ++e) o[e] = acc[h][e] / lh;
+                store_row<DT, VE>((char*)p.out + ((size_t)s * p.num_heads + head0 + h) * ROWB + col * (VE * EB), o);
+              }
+            });
+          } else {
+            // one piece of a pair split over chunks: the owner (first tile) writes to
+            // slot 2c + 1, every other piece is its chunk's first segment, slot 2c
+            const bool owner = jb == 0;
+            const size_t slot = 2 * (size_t)ck + (owner ? 1 : 0);
+            static_for<GP>([&](auto hc) {
+              constexpr int h = decltype(hc)::value;
+              if (h < g && (h & 3) == grp) {
+                float* dst = p.ws_acc + (slot * g + h) * D + col * VE;
+#pragma unroll
+                for (int e = 0; e < VE; e += 4)
+                  *reinterpret_cast<f32x4*>(dst + e) = f32x4{acc[h][e], acc[h][e + 1], acc[h][e + 2], acc[h][e + 3]};
+              }
+            });
+            if (grp == 0 && col < g) {
+              float* ml = p.ws_ml + (slot * g + col) * 2;
+              ml[0] = M;
+              ml[1] = ls;
+            }
+            note_piece(s, kv, jb, n_pair, tseg);
           }
-          note_piece(s, kv, jb, n_pair, tseg);
+          m = kNegBig;
+          l = 0.f;
+#pragma unroll
+          for (int h = 0; h < (MPV ? 1 : GP); ++h)
+#pragma unroll
+            for (int e = 0; e < VE; ++e) acc[h][e] = 0.f;
         }
-        m = kNegBig;
-        l = 0.f;
-#pragma unroll
-        for (int h = 0; h < (MPV ? 1 : GP); ++h)
-#pragma unroll
-          for (int e = 0; e < VE; ++e) acc[h][e] = 0.f;
       };
 
       // Fold cc's tile into the running softmax, flush at the end of a segment,

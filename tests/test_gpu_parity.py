@@ -130,6 +130,22 @@ def test_shape_sweep(dt, D, B, Hq, Hkv):
     assert_close(gpu_decode(b, d), oracle_decode(b), dt, "sweep")
 
 
+@pytest.mark.parametrize("num_seqs", [2048, 2100])
+def test_many_sequences_around_the_lds_limit(num_seqs):
+    # up to 2048 sequences the decode kernel keeps lengths and tile prefix sums in LDS;
+    # beyond that it scans the lengths in global memory.  Short lengths, some empty.
+    g = torch.Generator().manual_seed(num_seqs)
+    lens = torch.randint(0, 41, (num_seqs,), generator=g)
+    lens[torch.randint(0, num_seqs, (64,), generator=g)] = 0
+    b = random_batch(300 + num_seqs, "bf16", lens.tolist(), 8, 2, 128, 16)
+    d = to_dev(b)
+    log(f"{num_seqs} sequences")
+    got = gpu_decode(b, d)
+    empty = np.where(np.asarray(lens) == 0)[0]
+    assert np.array_equal(got[empty], np.zeros_like(got[empty]))
+    assert_close(got, oracle_decode(b), "bf16", f"{num_seqs} sequences")
+
+
 # ---------------------------------------------------------------------------- invariants
 
 
