@@ -155,6 +155,18 @@ def test_many_short_sequences_in_longest_first_order():
     assert_close(out.float().cpu().double().numpy(), run_oracle(b), "bf16", "many")
 
 
+def test_more_sequences_than_the_ordering_pass_sorts_in_one_sweep():
+    # 2100 short sequences (more than twice the ordering pass's 1024 threads), up to 16
+    # (query, head) rows per KV head (the split variant); some sequences have no queries
+    rng = np.random.default_rng(23)
+    lens = rng.integers(1, 61, 2100).tolist()
+    qn = [int(min(L, q)) for L, q in zip(lens, rng.integers(0, 5, 2100))]
+    b = batch(23, "f16", lens, qn, 16, 4, 64, 8)
+    log("2100 sequences")
+    out, _ = run_gpu(b)
+    assert_close(out.float().cpu().double().numpy(), run_oracle(b), "f16", "2100")
+
+
 @pytest.mark.parametrize("name,make", [
     ("spec", lambda: workloads.llama3_8b_spec(num_seqs=12, num_blocks=5000)),
     ("chunk", lambda: workloads.llama3_8b_chunk(num_seqs=2, chunk=96, max_prior=500)),
