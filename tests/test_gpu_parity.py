@@ -130,6 +130,21 @@ def test_shape_sweep(dt, D, B, Hq, Hkv):
     assert_close(gpu_decode(b, d), oracle_decode(b), dt, "sweep")
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (16, 4), (16, 2)])
+@pytest.mark.parametrize("scale", [-0.09, 0.0, 2.0])
+def test_negative_zero_and_large_scales(dtype, Hq, Hkv, scale):
+    # groups of 1 (P.V on the vector ALU), 4 and 8 (matrix cores, one reference maximum
+    # per head that moves only when a tile exceeds it by 2^8).  A negative scale reverses
+    # the score order, 0 gives uniform weights, 2.0 spreads the scores over about +-70 in
+    # log2 units so the reference maximum moves often and most weights underflow.
+    b = random_batch(400 + Hq + Hkv, dtype, [1, 17, 300, 1031, 64], Hq, Hkv, 128, 16)
+    b.scale = scale
+    d = to_dev(b)
+    log(f"scale {scale} {dtype} {Hq}/{Hkv}")
+    assert_close(gpu_decode(b, d), oracle_decode(b), dtype, f"scale {scale}")
+
+
 @pytest.mark.parametrize("num_seqs", [2048, 2100])
 def test_many_sequences_around_the_lds_limit(num_seqs):
     # up to 2048 sequences the decode kernel keeps lengths and tile prefix sums in LDS;
