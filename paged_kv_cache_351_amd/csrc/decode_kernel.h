@@ -876,25 +876,48 @@ __global__ __launch_bounds__(256) void reduce_kernel(DecodeParams p) {
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-  for (int i = 0; i < parts; ++i) {
-    size_t sl;
-    if (i == 0) {
-      sl = 2 * (size_t)c + 1;
-    } else {
-      if (!chunk_meta[4 * ((size_t)c + i) + 3]) continue;
-      sl = 2 * ((size_t)c + i);
-    }
-    const size_t r = sl * g + hr;
-    const float mi = p.ws_ml[2 * r];
-    const float li = p.ws_ml[2 * r + 1];
-    const float* a = p.ws_acc + r * D + sub * EPL;
-    const float mn = fmaxf(m, mi);
-    const float fa = fast_exp2(m - mn);
-    const float fb = fast_exp2(mi - mn);
-    l = fmaf(li, fb, l * fa);
+  // Piece i of the pair: i = 0 is the owner's (slot 2c + 1), i >= 1 the first piece of
+  // chunk c + i (slot 2(c + i)) if that chunk left one.  The flags of 64 chunks are read
+  // at once, and the pieces are loaded four at a time before they are folded, so a pair
+  // cut into many pieces costs a few dependent loads, not two per piece.  The fold order
+  // is the chunk order.
+  constexpr int kBatch = 4;
+  for (int i0 = 0; i0 < parts; i0 += 64) {
+    const int i = i0 + lane;
+    unsigned long long has = __ballot(i < parts && (i == 0 || chunk_meta[4 * ((size_t)c + i) + 3] != 0));
+    while (has) {
+      int bi[kBatch];
+      bool ok[kBatch];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] = fmaf(a[e], fb, acc[e] * fa);
-    m = mn;
+      for (int k = 0; k < kBatch; ++k) {
+        ok[k] = has != 0;
+        bi[k] = ok[k] ? i0 + __ffsll(has) - 1 : 0;
+        has &= has - 1;
+      }
+      float mi[kBatch], li[kBatch], av[kBatch][EPL];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        if (!ok[k]) continue;
+        const size_t sl = bi[k] == 0 ? 2 * (size_t)c + 1 : 2 * ((size_t)c + bi[k]);
+        const size_t r = sl * g + hr;
+        mi[k] = p.ws_ml[2 * r];
+        li[k] = p.ws_ml[2 * r + 1];
+        const float* a = p.ws_acc + r * D + sub * EPL;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) av[k][e] = a[e];
+      }
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        if (!ok[k]) continue;
+        const float mn = fmaxf(m, mi[k]);
+        const float fa = fast_exp2(m - mn);
+        const float fb = fast_exp2(mi[k] - mn);
+        l = fmaf(li[k], fb, l * fa);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[e] = fmaf(av[k][e], fb, acc[e] * fa);
+        m = mn;
+      }
+    }
   }
   if (h < g) {
     float o[EPL];
