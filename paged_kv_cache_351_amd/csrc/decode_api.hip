@@ -25,7 +25,9 @@ int requested_waves() {
 
 // The last 1/16 of every wave's share goes to whichever wave is free first, in
 // one part (smaller tails leave a longer finish, larger ones cost more chunk
-// starts and partial results); PA_DECODE_TAIL = d overrides the divisor (0 = no tails) and
+// starts and partial results); with short shares the kernel lowers the divisor so a
+// part keeps at least 16 tiles (split.h, effective_tail_div), down to 1/8.
+// PA_DECODE_TAIL = d overrides the divisor (0 = no tails) and
 // PA_DECODE_TAIL_PIECES the number of parts (halving sizes), for tuning sweeps.
 constexpr int kDefaultTailDiv = 16;
 int tail_pieces() {

@@ -326,7 +326,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   }
   const long long T = seq_tiles * Hkv;
   const long long nw = waves_used(T, launched);
-  const ChunkPlan plan{T, nw, p.tail_div, p.tail_pieces};
+  const ChunkPlan plan{T, nw, effective_tail_div(T, nw, p.tail_div), p.tail_pieces};
 
   // Workspace header: [0] = chunks of this call (for the merge kernel), [32] =
   // counter of tail parts handed out (the merge kernel sets it back to 0).

@@ -63,6 +63,23 @@ __host__ __device__ inline long long wave_of(long long t, long long T, long long
   return ((t + 1) * nw + T - 1) / T - 1;
 }
 
+// Tail parts shorter than this many tiles do not pay for the chunk start they cost,
+// so the divisor of a call with short shares is lowered (to at least kMinTailDiv):
+// with 1/16 of a 128-tile share a part would be 8 tiles.
+constexpr int kMinTailTiles = 16;
+constexpr int kMinTailDiv = 8;
+
+// The tail divisor used for T tiles over nw shares when tail_div is asked for: at
+// most tail_div, lowered toward kMinTailDiv while a part would have fewer than
+// kMinTailTiles tiles (a function of T and nw only, so every kernel agrees).
+__host__ __device__ inline int effective_tail_div(long long T, long long nw, int tail_div) {
+  if (tail_div <= 0 || nw <= 0) return tail_div;
+  long long d = T / nw / kMinTailTiles;
+  if (d > tail_div) d = tail_div;
+  const int floor_div = kMinTailDiv < tail_div ? kMinTailDiv : tail_div;
+  return d < floor_div ? floor_div : (int)d;
+}
+
 // Chunk layout of one call: nw shares, each a head and `pieces` tail parts.
 struct ChunkPlan {
   long long T;    // tiles of the step

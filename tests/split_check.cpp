@@ -34,6 +34,7 @@ static int fail(const char* what, int c) {
   return 1;
 }
 
+// td < 0: the kernels' default, effective_tail_div(T, nw, -td)
 int check(const std::vector<int>& lens, int Hkv, long long launched, int c, int td, int pieces) {
   const int N = (int)lens.size();
   std::vector<long long> C(N + 1, 0);  // C[s] = tiles of sequences before s
@@ -44,6 +45,12 @@ int check(const std::vector<int>& lens, int Hkv, long long launched, int c, int 
   if (T == 0 && nw != 0) return fail("waves for an empty batch", c);
 
   std::vector<int> seen(T, 0);  // visits of each tile, by its global index
+  if (td < 0) {
+    const int want = -td;
+    td = effective_tail_div(T, nw, want);
+    if (T > 0 && (td > want || td < (want < kMinTailDiv ? want : kMinTailDiv)))
+      return fail("effective tail divisor out of range", c);
+  }
   const ChunkPlan plan{T, nw, td, pieces};
   const long long nc = plan.chunks();
   // tail tickets name every tail chunk exactly once, first parts first
@@ -180,7 +187,7 @@ int main() {
     }
     for (int Hkv : hkv_set)
       for (long long launched : launched_set)
-        for (int td : {0, 4, 8})
+        for (int td : {0, 4, 8, -16})
           for (int pieces : {1, 3, 4}) {
             if (td == 0 && pieces != 1) continue;
             if (check(lens, Hkv, launched, cases, td, pieces)) return 1;
@@ -188,7 +195,7 @@ int main() {
           }
   }
   // all empty, single token, one huge sequence
-  for (int td : {0, 8})
+  for (int td : {0, 8, -16})
     for (int pieces : {1, 3}) {
       if (check(std::vector<int>(5, 0), 2, 3072, cases++, td, pieces)) return 1;
       if (check(std::vector<int>{1}, 1, 3072, cases++, td, pieces)) return 1;
