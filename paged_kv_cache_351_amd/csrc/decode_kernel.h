@@ -862,6 +862,9 @@ __global__ __launch_bounds__(256) void reduce_kernel(DecodeParams p) {
   // stale record (a workspace never zeroed, whose counter handed out no tail) inside
   // the chunk list and the output.
   const int* meta = chunk_meta + 4 * (size_t)c;
+  // the "left a first piece" flags of the next 63 chunks load together with the record
+  // (only those below c + parts are used)
+  const int flag1 = lane >= 1 && c + lane < nchunks ? chunk_meta[4 * ((size_t)c + lane) + 3] : 0;
   const int parts = min(meta[2], nchunks - c);
   if (parts < 2) return;
   const int s = meta[0];
@@ -878,13 +881,14 @@ __global__ __launch_bounds__(256) void reduce_kernel(DecodeParams p) {
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
   // Piece i of the pair: i = 0 is the owner's (slot 2c + 1), i >= 1 the first piece of
   // chunk c + i (slot 2(c + i)) if that chunk left one.  The flags of 64 chunks are read
-  // at once, and the pieces are loaded four at a time before they are folded, so a pair
-  // cut into many pieces costs a few dependent loads, not two per piece.  The fold order
-  // is the chunk order.
-  constexpr int kBatch = 4;
+  // at once, and the pieces are loaded in batches (8, or 4 for the widest rows) before
+  // they are folded, so a pair cut into many pieces costs a few dependent loads, not two
+  // per piece.  The fold order is the chunk order.
+  constexpr int kBatch = EPL <= 16 ? 8 : 4;
   for (int i0 = 0; i0 < parts; i0 += 64) {
     const int i = i0 + lane;
-    unsigned long long has = __ballot(i < parts && (i == 0 || chunk_meta[4 * ((size_t)c + i) + 3] != 0));
+    const int flag = i0 == 0 ? flag1 : (i < parts ? chunk_meta[4 * ((size_t)c + i) + 3] : 0);
+    unsigned long long has = __ballot(i < parts && (i == 0 || flag != 0));
     while (has) {
       int bi[kBatch];
       bool ok[kBatch];
