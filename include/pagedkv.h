@@ -94,10 +94,11 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, i
  *
  * Work split: the step's (sequence, KV head) pairs are cut into 16-token tiles
  * and the launched waves (as many as the device holds at once) take equal runs
- * of consecutive tiles, whatever the length mix; the last eighth of every run,
- * cut into parts of halving size, is handed to whichever wave is free first.  A pair cut by a run boundary is
- * finished by a second kernel on the same stream, which merges the pieces'
- * running maxima, sums and accumulators with the same rule.  The boundaries
+ * of consecutive tiles, whatever the length mix; the last sixteenth of every
+ * run (up to an eighth when runs are short, so that a part keeps at least 16
+ * tiles) is handed to whichever wave is free first.  A pair cut by a run
+ * boundary is finished by a second kernel on the same stream, which merges the
+ * pieces' running maxima, sums and accumulators with the same rule.  The boundaries
  * depend only on the lengths, so which wave did which part never changes the
  * result.
  *
@@ -122,7 +123,10 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, i
  *                above it are clamped to it, negative lengths to 0.
  * Supported: head_dim in {64, 128}; block_size in {8, 16, 32}; num_heads a
  * multiple of num_kv_heads with group size num_heads / num_kv_heads <= 16.
- * Accumulation is float32; the output is rounded once, to nearest even.
+ * Accumulation is float32; the output is rounded once, to nearest even.  For
+ * fp16 and bf16 with 3 or more query heads per KV head, P.V runs on the matrix
+ * cores with the softmax weights in the storage type (two bf16 terms, about 16
+ * significant bits, or one fp16 term).
  * Results are deterministic on a given device: the same inputs give the same
  * bits (the split depends on the lengths and the device's wave capacity).
  * The current HIP device must be the stream's device.
