@@ -139,6 +139,33 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_no_alloc -- pa_decode for callers that cannot allocate device memory
+ * (code recorded into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments, result and errors as pa_decode, without the
+ * workspace: the call uses a workspace built into the library, one array of
+ * PA_DECODE_NO_ALLOC_SCRATCH_BYTES bytes of device memory per GPU, which that GPU
+ * holds from the first call on it until the process ends.  The call allocates and
+ * frees nothing.  The first call on a device looks the array up and clears its
+ * header on `stream` (make that first call outside a stream capture); later calls
+ * reuse it as a caller-owned workspace is reused.  Every call on one GPU shares
+ * that GPU's array, so calls that may overlap on one GPU (different streams,
+ * different threads) race and give wrong results: serialise them, e.g. on one
+ * stream.  The array holds the workspace of every shape pa_decode supports with
+ * the default work split on an MI355X (at most 1,024 waves, two chunks each); a
+ * call that would need more (a device with more compute units, or the tuning
+ * overrides of the split) returns PA_ERR_WORKSPACE before enqueuing anything.
+ * Results are bit-identical to pa_decode's for the same inputs on the same device.
+ */
+#define PA_DECODE_NO_ALLOC_SCRATCH_BYTES ((size_t)34 << 20)
+size_t pa_decode_no_alloc_scratch_bytes(void); /* = PA_DECODE_NO_ALLOC_SCRATCH_BYTES */
+pa_status pa_decode_no_alloc(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, const int32_t* seq_lens,
+                             int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                             int block_size, int num_blocks, int max_blocks_per_seq,
+                             int max_seq_len, float scale, pa_dtype dtype, void* out,
+                             void* stream);
+
+/*
  * pa_write_kv -- store new tokens' K and V rows into their slots.
  *
  * For every i with 0 <= slot_mapping[i] < num_blocks * block_size:

@@ -65,20 +65,23 @@ struct WorkspaceLayout {
   size_t total;
 };
 
-WorkspaceLayout plan_workspace(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
-                               int max_seq_len) {
+WorkspaceLayout layout_for(long long waves, int pieces, int group, int head_dim) {
   WorkspaceLayout w{0, 0, 0, 0};
-  const long long t_max = (long long)num_seqs * num_kv_heads * tiles_of(max_seq_len);
-  long long waves = waves_used(t_max, kMaxWaves);
   if (waves < 1) waves = 1;
-  const size_t g = (size_t)(num_heads / num_kv_heads);
-  const size_t chunks = (size_t)waves * (kMaxTailPieces + 1);
+  const size_t g = (size_t)group;
+  const size_t chunks = (size_t)waves * (pieces + 1);
   const size_t slots = 2 * chunks;
   w.waves = (int)waves;
   w.ml_offset = align_up(256 + chunks * 16, 256);
   w.acc_offset = w.ml_offset + align_up(slots * g * 2 * sizeof(float), 256);
   w.total = w.acc_offset + slots * g * head_dim * sizeof(float);
   return w;
+}
+
+WorkspaceLayout plan_workspace(int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                               int max_seq_len) {
+  const long long t_max = (long long)num_seqs * num_kv_heads * tiles_of(max_seq_len);
+  return layout_for(waves_used(t_max, kMaxWaves), kMaxTailPieces, num_heads / num_kv_heads, head_dim);
 }
 
 // Decode waves to launch on the current device: one per SIMD (4 per CU), or
@@ -122,61 +125,82 @@ size_t pa_decode_workspace_size(int num_seqs, int num_heads, int num_kv_heads, i
   return plan_workspace(num_seqs, num_heads, num_kv_heads, head_dim, max_seq_len).total;
 }
 
-pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
-                    const int32_t* block_tables, const int32_t* seq_lens, int num_seqs,
-                    int num_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
-                    int max_blocks_per_seq, int max_seq_len, float scale, pa_dtype dtype, void* out,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+// ---------------------------------------------------------------------------------
+// The decode path for callers that cannot allocate.  Its workspace is this file-scope
+// device array: every GPU the library runs on holds its own copy, at its own address,
+// until the process ends.  In host code `scratch` names a host-side stand-in, never
+// the device memory: host code uses only the address hipGetSymbolAddress returns for
+// the current device.
+static __device__ __align__(256) char scratch[PA_DECODE_NO_ALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr size_t kNoAllocScratchBytes = PA_DECODE_NO_ALLOC_SCRATCH_BYTES;
+
+// Everything pa_decode and pa_decode_no_alloc share: argument checks, the kernels, the
+// debug checks of the index data and the launch parameters (DecodeParams without the
+// workspace pointers).  Returns PA_OK with *skip set when there is nothing to launch.
+pa_status prepare_decode(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* seq_lens, int num_seqs,
+                         int num_heads, int num_kv_heads, int head_dim, int block_size,
+                         int num_blocks, int max_blocks_per_seq, int max_seq_len, float scale,
+                         pa_dtype dtype, void* out, hipStream_t st, const char* who,
+                         const void* workspace, size_t workspace_bytes, bool check_workspace,
+                         DecodeParams* p, const void** dec, const void** red, bool* skip) {
+  *skip = false;
   if (dtype != PA_F32 && dtype != PA_F16 && dtype != PA_BF16)
-    return fail(PA_ERR_INVALID, "pa_decode: unknown dtype %d", (int)dtype);
+    return fail(PA_ERR_INVALID, "%s: unknown dtype %d", who, (int)dtype);
   if (num_seqs < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
       max_blocks_per_seq <= 0 || max_seq_len < 0)
     return fail(PA_ERR_INVALID,
-                "pa_decode: need num_seqs >= 0, num_heads, num_kv_heads, num_blocks, "
-                "max_blocks_per_seq > 0 and max_seq_len >= 0");
+                "%s: need num_seqs >= 0, num_heads, num_kv_heads, num_blocks, "
+                "max_blocks_per_seq > 0 and max_seq_len >= 0", who);
   if (num_heads % num_kv_heads != 0)
-    return fail(PA_ERR_INVALID, "pa_decode: num_heads (%d) is not a multiple of num_kv_heads (%d)",
+    return fail(PA_ERR_INVALID, "%s: num_heads (%d) is not a multiple of num_kv_heads (%d)", who,
                 num_heads, num_kv_heads);
   if (!(scale == scale) || scale > 3.0e38f || scale < -3.0e38f)
-    return fail(PA_ERR_INVALID, "pa_decode: scale must be finite");
+    return fail(PA_ERR_INVALID, "%s: scale must be finite", who);
   if (head_dim != 64 && head_dim != 128)
-    return fail(PA_ERR_UNSUPPORTED, "pa_decode: head_dim %d not in {64, 128}", head_dim);
+    return fail(PA_ERR_UNSUPPORTED, "%s: head_dim %d not in {64, 128}", who, head_dim);
   if (!valid_block_size(block_size))
-    return fail(PA_ERR_UNSUPPORTED, "pa_decode: block_size %d not in {8, 16, 32}", block_size);
+    return fail(PA_ERR_UNSUPPORTED, "%s: block_size %d not in {8, 16, 32}", who, block_size);
   const int group = num_heads / num_kv_heads;
   if (padded_group(group) == 0)
-    return fail(PA_ERR_UNSUPPORTED, "pa_decode: %d query heads per KV head (at most 16)", group);
+    return fail(PA_ERR_UNSUPPORTED, "%s: %d query heads per KV head (at most 16)", who, group);
   if ((long long)max_seq_len > (long long)max_blocks_per_seq * block_size)
-    return fail(PA_ERR_INVALID, "pa_decode: max_seq_len %d exceeds max_blocks_per_seq * block_size (%lld)",
-                max_seq_len, (long long)max_blocks_per_seq * block_size);
+    return fail(PA_ERR_INVALID, "%s: max_seq_len %d exceeds max_blocks_per_seq * block_size (%lld)",
+                who, max_seq_len, (long long)max_blocks_per_seq * block_size);
   if (max_seq_len > kMaxSeqLen)
-    return fail(PA_ERR_UNSUPPORTED, "pa_decode: max_seq_len %d above %d", max_seq_len, kMaxSeqLen);
+    return fail(PA_ERR_UNSUPPORTED, "%s: max_seq_len %d above %d", who, max_seq_len, kMaxSeqLen);
   if ((long long)num_seqs * num_kv_heads * tiles_of(max_seq_len) >= (1LL << 40))
-    return fail(PA_ERR_UNSUPPORTED, "pa_decode: batch of more than 2^40 tiles");
-  if (num_seqs == 0) return PA_OK;
+    return fail(PA_ERR_UNSUPPORTED, "%s: batch of more than 2^40 tiles", who);
+  if (num_seqs == 0) {
+    *skip = true;
+    return PA_OK;
+  }
   if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !out)
-    return fail(PA_ERR_INVALID, "pa_decode: null pointer argument");
+    return fail(PA_ERR_INVALID, "%s: null pointer argument", who);
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
-    return fail(PA_ERR_INVALID, "pa_decode: q, caches and out must be 16-byte aligned");
+    return fail(PA_ERR_INVALID, "%s: q, caches and out must be 16-byte aligned", who);
+  if (check_workspace) {
+    const WorkspaceLayout ws = plan_workspace(num_seqs, num_heads, num_kv_heads, head_dim, max_seq_len);
+    if (!workspace || workspace_bytes < ws.total)
+      return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", who, ws.total,
+                  workspace ? workspace_bytes : (size_t)0);
+    if (((uintptr_t)workspace & 255u) != 0)
+      return fail(PA_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", who);
+  }
 
-  const WorkspaceLayout ws = plan_workspace(num_seqs, num_heads, num_kv_heads, head_dim, max_seq_len);
-  if (!workspace || workspace_bytes < ws.total)
-    return fail(PA_ERR_WORKSPACE, "pa_decode: workspace of %zu bytes needed, %zu given", ws.total,
-                workspace ? workspace_bytes : (size_t)0);
-  if (((uintptr_t)workspace & 255u) != 0)
-    return fail(PA_ERR_WORKSPACE, "pa_decode: workspace must be 256-byte aligned");
-
-  const void* dec = nullptr;
-  const void* red = nullptr;
   const int gp = padded_group(group);
   bool found;
   switch (dtype) {
-    case PA_F32: found = decode_kernels_f32(head_dim, block_size, gp, &dec, &red); break;
-    case PA_F16: found = decode_kernels_f16(head_dim, block_size, gp, &dec, &red); break;
-    default: found = decode_kernels_bf16(head_dim, block_size, gp, &dec, &red); break;
+    case PA_F32: found = decode_kernels_f32(head_dim, block_size, gp, dec, red); break;
+    case PA_F16: found = decode_kernels_f16(head_dim, block_size, gp, dec, red); break;
+    default: found = decode_kernels_bf16(head_dim, block_size, gp, dec, red); break;
   }
-  if (!found) return fail(PA_ERR_UNSUPPORTED, "pa_decode: no kernel for this shape");
-  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!found) return fail(PA_ERR_UNSUPPORTED, "%s: no kernel for this shape", who);
 
   if (debug_checks()) {
     pa_status bad = PA_OK;
@@ -185,55 +209,149 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
     if (!to_host(tab, block_tables, (size_t)num_seqs * max_blocks_per_seq, st, &bad)) return bad;
     for (int s = 0; s < num_seqs; ++s) {
       if (lens[s] < 0 || lens[s] > max_seq_len)
-        return fail(PA_ERR_INVALID, "pa_decode: seq_lens[%d] = %d outside [0, %d]", s, lens[s], max_seq_len);
+        return fail(PA_ERR_INVALID, "%s: seq_lens[%d] = %d outside [0, %d]", who, s, lens[s],
+                    max_seq_len);
       const int nb = (lens[s] + block_size - 1) / block_size;
       for (int j = 0; j < nb; ++j) {
         const int id = tab[(size_t)s * max_blocks_per_seq + j];
         if (id < 0 || id >= num_blocks)
-          return fail(PA_ERR_INVALID, "pa_decode: block_tables[%d][%d] = %d outside [0, %d)", s, j, id,
-                      num_blocks);
+          return fail(PA_ERR_INVALID, "%s: block_tables[%d][%d] = %d outside [0, %d)", who, s, j,
+                      id, num_blocks);
       }
     }
   }
 
+  // the most waves any call with these shapes may use, then what the device holds at once
+  const long long t_max = (long long)num_seqs * num_kv_heads * tiles_of(max_seq_len);
   int waves = 0;
-  hipError_t e = decode_waves(dec, &waves);
+  hipError_t e = decode_waves(*dec, &waves);
   if (e != hipSuccess) return hip_fail(e, "pa_decode occupancy query");
-  waves = std::min(waves, ws.waves);
+  waves = (int)std::min<long long>(waves, std::max<long long>(1, waves_used(t_max, kMaxWaves)));
   if (requested_waves() > 0) waves = std::min(waves, requested_waves());
 
-  DecodeParams p;
-  p.q = q;
-  p.k_cache = k_cache;
-  p.v_cache = v_cache;
-  p.block_tables = block_tables;
-  p.seq_lens = seq_lens;
-  p.out = out;
-  p.ws_meta = static_cast<int*>(workspace);
-  p.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.ml_offset);
-  p.ws_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.acc_offset);
-  p.num_seqs = num_seqs;
-  p.num_heads = num_heads;
-  p.num_kv_heads = num_kv_heads;
-  p.group = group;
-  p.head_dim = head_dim;
-  p.block_size = block_size;
-  p.num_blocks = num_blocks;
-  p.max_blocks_per_seq = max_blocks_per_seq;
-  p.max_seq_len = max_seq_len;
-  p.num_waves = waves;
-  p.tail_div = tail_divisor();
-  p.tail_pieces = tail_pieces();
-  p.scale_log2e = (float)((double)scale * 1.4426950408889634074);
+  p->q = q;
+  p->k_cache = k_cache;
+  p->v_cache = v_cache;
+  p->block_tables = block_tables;
+  p->seq_lens = seq_lens;
+  p->out = out;
+  p->ws_meta = nullptr;
+  p->ws_ml = nullptr;
+  p->ws_acc = nullptr;
+  p->num_seqs = num_seqs;
+  p->num_heads = num_heads;
+  p->num_kv_heads = num_kv_heads;
+  p->group = group;
+  p->head_dim = head_dim;
+  p->block_size = block_size;
+  p->num_blocks = num_blocks;
+  p->max_blocks_per_seq = max_blocks_per_seq;
+  p->max_seq_len = max_seq_len;
+  p->num_waves = waves;
+  p->tail_div = tail_divisor();
+  p->tail_pieces = tail_pieces();
+  p->scale_log2e = (float)((double)scale * 1.4426950408889634074);
+  return PA_OK;
+}
 
-  void* kargs[] = {&p};
+// Point the parameters at a workspace laid out as `ws` describes, then launch the decode
+// kernel and the merge kernel (which also resets the tail counter for the next call).
+pa_status launch_decode(DecodeParams* p, const void* dec, const void* red, char* base,
+                        const WorkspaceLayout& ws, hipStream_t st) {
+  p->ws_meta = reinterpret_cast<int*>(base);
+  p->ws_ml = reinterpret_cast<float*>(base + ws.ml_offset);
+  p->ws_acc = reinterpret_cast<float*>(base + ws.acc_offset);
+  void* kargs[] = {p};
   // four waves per workgroup: one workgroup per CU, one wave per SIMD
-  e = hipLaunchKernel(dec, dim3((waves + 3) / 4), dim3(256), kargs, 0, st);
+  hipError_t e = hipLaunchKernel(dec, dim3((p->num_waves + 3) / 4), dim3(256), kargs, 0, st);
   if (e != hipSuccess) return hip_fail(e, "pa_decode launch");
-  // always: it also resets the tail counter for the next call
-  e = hipLaunchKernel(red, dim3((waves * (p.tail_pieces + 1) + 3) / 4), dim3(256), kargs, 0, st);
+  e = hipLaunchKernel(red, dim3((p->num_waves * (p->tail_pieces + 1) + 3) / 4), dim3(256), kargs, 0, st);
   if (e != hipSuccess) return hip_fail(e, "pa_decode merge launch");
   return PA_OK;
+}
+
+// Clears the workspace header (the tail counter must start at 0) with a kernel rather
+// than hipMemsetAsync, so the set-up is also valid inside a stream capture.
+__global__ void clear_header_kernel(int* hdr) { hdr[threadIdx.x] = 0; }
+
+// Device address of `scratch` on the current device, looked up (and its header
+// cleared, on `st`) the first time this device is seen.
+pa_status scratch_address(hipStream_t st, char** out) {
+  static std::mutex mu;
+  static std::map<int, char*> by_device;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "pa_decode_no_alloc: hipGetDevice");
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = by_device.find(dev);
+  if (it != by_device.end()) {
+    *out = it->second;
+    return PA_OK;
+  }
+  void* ptr = nullptr;
+  e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || ptr == nullptr)
+    return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "pa_decode_no_alloc: hipGetSymbolAddress");
+  hipLaunchKernelGGL(clear_header_kernel, dim3(1), dim3(64), 0, st, static_cast<int*>(ptr));
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "pa_decode_no_alloc: clearing the workspace header");
+  by_device[dev] = static_cast<char*>(ptr);
+  *out = static_cast<char*>(ptr);
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* seq_lens, int num_seqs,
+                    int num_heads, int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                    int max_blocks_per_seq, int max_seq_len, float scale, pa_dtype dtype, void* out,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  DecodeParams p;
+  const void* dec = nullptr;
+  const void* red = nullptr;
+  bool skip = false;
+  pa_status r = prepare_decode(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads,
+                               num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                               max_seq_len, scale, dtype, out, st, "pa_decode", workspace,
+                               workspace_bytes, true, &p, &dec, &red, &skip);
+  if (r != PA_OK || skip) return r;
+  const WorkspaceLayout ws = plan_workspace(num_seqs, num_heads, num_kv_heads, head_dim, max_seq_len);
+  return launch_decode(&p, dec, red, static_cast<char*>(workspace), ws, st);
+}
+
+size_t pa_decode_no_alloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+pa_status pa_decode_no_alloc(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_tables, const int32_t* seq_lens, int num_seqs,
+                             int num_heads, int num_kv_heads, int head_dim, int block_size,
+                             int num_blocks, int max_blocks_per_seq, int max_seq_len, float scale,
+                             pa_dtype dtype, void* out, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  DecodeParams p;
+  const void* dec = nullptr;
+  const void* red = nullptr;
+  bool skip = false;
+  pa_status r = prepare_decode(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads,
+                               num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
+                               max_seq_len, scale, dtype, out, st, "pa_decode_no_alloc", nullptr, 0,
+                               false, &p, &dec, &red, &skip);
+  if (r != PA_OK || skip) return r;
+  // laid out for the waves this launch actually uses and its tail parts
+  const WorkspaceLayout ws = layout_for(p.num_waves, p.tail_pieces, p.group, p.head_dim);
+  if (ws.total > kNoAllocScratchBytes)
+    return fail(PA_ERR_WORKSPACE,
+                "pa_decode_no_alloc: this call needs %zu bytes of workspace, above the built-in "
+                "%zu (%d waves, %d query heads per KV head, head_dim %d); use pa_decode with a "
+                "caller-owned workspace", ws.total, kNoAllocScratchBytes, p.num_waves, p.group,
+                p.head_dim);
+  char* base = nullptr;
+  r = scratch_address(st, &base);
+  if (r != PA_OK) return r;
+  return launch_decode(&p, dec, red, base, ws, st);
 }
 
 }  // extern "C"

@@ -54,7 +54,7 @@ def test_binding_names_match_the_abi(pk):
 
 
 def test_version(pk):
-    assert pk.pa_version() == 6
+    assert pk.pa_version() == 7
 
 
 @pytest.mark.parametrize("N,H,HKV,D,L", [(256, 32, 8, 128, 4096), (32, 64, 8, 128, 32768),
