@@ -9,9 +9,14 @@ head_dim 128, bf16 KV and q, fp32 accumulation, block size 16, lengths uniform i
 copies, if any, before the write).
 
 Prints ONE JSON line.  ``value`` is the K/V bytes the decode step must read
-(each (token, KV head) row of K and V once) divided by the measured step time;
-``roofline`` reports the decode call alone, timed with HIP events on the stream it
-runs on; ``cpu_baseline`` times the float64 CPU oracle on the host.
+(each (token, KV head) row of K and V once) divided by the wall time per step of K
+back-to-back steps; ``step_us`` gives the median / p10 / p90 of the same steps from HIP
+events.  ``roofline`` reports the decode call alone: K further calls, each preceded by
+an untimed read of a 1 GiB buffer that evicts the caches (L2 and the 256 MiB Infinity
+Cache; a read leaves no dirty lines to write back), timed with HIP events on the stream
+it runs on; ``achieved`` uses the median.  ``cache_ops`` times pa_write_kv (the step's
+new tokens) and pa_copy_blocks (224 copy-on-write pairs of OPT-13B-shaped blocks) the
+same way.  ``cpu_baseline`` times the float64 CPU oracle on the host.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME [--block-size B]]
     python bench.py --workload opt13b_shared --shared-prefix   # shared-prefix decode
@@ -48,6 +53,53 @@ DECODE_KERNELS = ["decode_kernel", "reduce_kernel"]   # kernels one pa_decode ca
 
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+FLUSH_BYTES = 1 << 30            # > 8 x 4 MiB L2 + 256 MiB Infinity Cache
+
+
+class CacheFlush:
+    """Evicts the GPU caches by reading (not writing) a 1 GiB buffer: a write would leave
+    dirty lines whose write-back lands in the next timed call."""
+
+    def __init__(self, dev):
+        self.buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+        self.sink = torch.empty((), dtype=torch.float32, device=dev)
+
+    def __call__(self):
+        torch.sum(self.buf, dim=0, out=self.sink)
+
+
+def pct(ms):
+    """median / p10 / p90 of event timings in ms, as microseconds."""
+    a = np.asarray(ms, dtype=np.float64) * 1e3
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90)), "mean": float(a.mean()), "n": int(a.size)}
+
+
+def timed_calls(fn, n, stream, flush=None):
+    """Event timings (ms) of n calls of fn on stream, each after an untimed flush."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for a, z in ev:
+        if flush is not None:
+            flush()
+        a.record(stream)
+        fn()
+        z.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(z) for a, z in ev]
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def kernel_sha():
@@ -239,7 +291,7 @@ def cpu_baseline(b, gpu_out, time_cap=25.0):
             "sample": f"{steps} of the first {done} of {b.num_seqs} sequences of the "
                       f"same workload (numpy float64, {kv / 1e9:.3f} GB of K/V)",
             "seqs_per_s": done / wall, "wall_s": wall, "cpu_s": cpu,
-            "host_cpus": len(os.sched_getaffinity(0)),
+            "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model(),
             "max_abs_err_gpu_vs_oracle": err}
 
 
@@ -269,7 +321,8 @@ def cpu_baseline_multi_query(b, gpu_out, time_cap=25.0):
     return {"value": kv / wall / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"write of all {len(b.slot_mapping)} new tokens, then the queries of the first "
                       f"{done} of {b.num_seqs} sequences of the same workload (numpy float64)",
-            "seqs_per_s": done / wall, "wall_s": wall, "max_abs_err_gpu_vs_oracle": err}
+            "seqs_per_s": done / wall, "wall_s": wall, "host_cpus": len(os.sched_getaffinity(0)),
+            "cpu_model": cpu_model(), "max_abs_err_gpu_vs_oracle": err}
 
 
 def unique_kv_bytes(b):
@@ -285,6 +338,40 @@ def unique_kv_bytes(b):
         slots[blk] = max(slots.get(blk, 0), fill)
     esize = 4 if b.dtype == "f32" else 2
     return sum(slots.values()) * b.num_kv_heads * b.head_dim * 2 * esize
+
+
+def cache_op_lines(dev, stream, K, flush, nk, nv, slots, kc, vc):
+    """pa_write_kv of the step's new tokens, and pa_copy_blocks of 224 copy-on-write pairs of
+    OPT-13B-shaped blocks (16 tokens x 40 KV heads x 128, fp16: 160 KiB per block per pool),
+    each call after a cache flush; GB/s on the bytes each call must read plus write."""
+    res = {}
+    # the write is idempotent (the same rows to the same slots)
+    w_ms = timed_calls(lambda: pk.pa_write_kv(nk, nv, slots, kc, vc), K, stream, flush)
+    wb = 2 * 2 * nk.numel() * nk.element_size()              # K and V rows, read + written
+    w = pct(w_ms)
+    res["pa_write_kv"] = {"workload": f"{nk.shape[0]} new tokens of the Llama-3-8B shape",
+                          "bytes_read_plus_written": wb, "us": w,
+                          "gbs": wb / (w["median"] * 1e-6) / 1e9,
+                          "frac_of_hbm_peak": wb / (w["median"] * 1e-6) / 1e9 / HBM_PEAK_GBS}
+    # 32 prompts x 7 copying samples: sources are the prompts' last blocks, destinations
+    # fresh blocks; a pool of 32 + 224 blocks plus slack, on the device
+    nb, B, H, D = 320, 16, 40, 128
+    g = torch.Generator(device=dev).manual_seed(0)
+    ck = torch.randn((nb, B, H, D), device=dev, generator=g).to(torch.float16)
+    cv = torch.randn((nb, B, H, D), device=dev, generator=g).to(torch.float16)
+    perm = torch.randperm(nb, generator=torch.Generator().manual_seed(0))
+    src = perm[:32].repeat_interleave(7)
+    dst = perm[32:32 + 224]
+    pairs = torch.stack([src, dst], 1).int().to(dev)
+    c_ms = timed_calls(lambda: pk.pa_copy_blocks(ck, cv, pairs), K, stream, flush)
+    cb = 224 * 2 * 2 * B * H * D * 2                         # K and V blocks, read + written
+    c = pct(c_ms)
+    res["pa_copy_blocks"] = {"workload": "224 copy-on-write pairs of OPT-13B-shaped fp16 blocks "
+                                         "(32 prompts x 7 copying samples)",
+                             "bytes_read_plus_written": cb, "us": c,
+                             "gbs": cb / (c["median"] * 1e-6) / 1e9,
+                             "frac_of_hbm_peak": cb / (c["median"] * 1e-6) / 1e9 / HBM_PEAK_GBS}
+    return res
 
 
 WORKLOADS = {
@@ -421,18 +508,28 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     log(f"timing {K} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        step(*ev[i])
+        ev[i][0].record(stream)
+        step(ev[i][1], ev[i][2])
     torch.cuda.synchronize()
     total = time.perf_counter() - t0
-    dec_ms = np.array([a.elapsed_time(z) for a, z in ev])
-    dec_avg = float(dec_ms.mean())
+    step_ms = [a.elapsed_time(z) for a, _, z in ev]          # whole step, back to back
+    call_ms_warm = [a.elapsed_time(z) for _, a, z in ev]     # its attention call
     eager_total = total
+
+    # the roofline leg: the attention call alone, K times, each after an untimed read of
+    # 1 GiB that evicts L2 and the Infinity Cache (the step's write and copies are done,
+    # and repeating the call changes nothing)
+    log(f"timing {K} calls, each after a cache flush")
+    flush = CacheFlush(dev)
+    call_ms = timed_calls(attend, K, stream, flush)
+    call = pct(call_ms)
+    dec_avg = call["median"] * 1e-3                          # ms
     if args.graph:
         # a serving loop records its step once and replays it; inputs stay where they were
         # captured, and the copies and writes are idempotent, so replays repeat the step
@@ -460,6 +557,9 @@ def main():
     value = kv_bytes / (total / K) / 1e9
     achieved = kv_bytes / (dec_avg * 1e-3) / 1e9
     traffic = measured_traffic()
+    cache_ops = None
+    if args.workload == "llama3_8b":
+        cache_ops = cache_op_lines(dev, stream, K, flush, nk, nv, slots, kc, vc)
     res = {
         "metric": METRIC, "value": value, "unit": "GB/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
@@ -472,12 +572,15 @@ def main():
         "step_mode": "graph" if args.graph else "eager",
         "eager_ms_per_step": eager_total * 1e3 / K,
         "seqs_per_s": b.num_seqs / (total / K),
+        "step_us": pct(step_ms),
         "roofline": {"kernel": "pa_decode (decode_kernel + reduce_kernel)", "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": kv_bytes,
-                     "avg_launch_us": dec_avg * 1e3, "p10_us": float(np.percentile(dec_ms, 10)) * 1e3,
-                     "p90_us": float(np.percentile(dec_ms, 90)) * 1e3},
+                     "timing": "median of K calls, each after a 1 GiB read that evicts the caches",
+                     "call_us": call, "call_us_back_to_back": pct(call_ms_warm),
+                     "avg_launch_us": call["mean"], "p10_us": call["p10"], "p90_us": call["p90"]},
+        "cache_ops": cache_ops,
         "cpu_baseline": None,
     }
     if args.workload != "llama3_8b":

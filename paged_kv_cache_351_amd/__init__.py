@@ -118,6 +118,18 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _scratch(nbytes, device, stream, zero):
+    """A uint8 device tensor of nbytes allocated (and zero-filled, if asked) on the stream
+    the call will run on, so that the fill is ordered before the kernels and the caching
+    allocator hands the memory to no other stream's work after this function returns."""
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    with torch.cuda.stream(stream):
+        if zero:
+            return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+        return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
@@ -140,14 +152,15 @@ def pa_decode_workspace_size(num_seqs, num_heads, num_kv_heads, head_dim, max_se
                                               int(head_dim), int(max_seq_len)))
 
 
-def decode_workspace(q, num_kv_heads, max_seq_len):
+def decode_workspace(q, num_kv_heads, max_seq_len, stream=None):
     """A zero-filled workspace tensor sized for ``pa_decode`` with these arguments (None if
-    the arguments are invalid; pa_decode then reports why).  Reuse it across calls on one
-    stream: each call leaves it ready for the next."""
+    the arguments are invalid; pa_decode then reports why), allocated and filled on
+    ``stream`` (default: the current stream).  Reuse it across calls on that stream: each
+    call leaves it ready for the next."""
     n = pa_decode_workspace_size(q.shape[0], q.shape[1], num_kv_heads, q.shape[2], max_seq_len)
     if n == 0:
         return None
-    return torch.zeros(n, dtype=torch.uint8, device=q.device)
+    return _scratch(n, q.device, stream, zero=True)
 
 
 def pa_decode(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, scale, out, *,
@@ -160,7 +173,8 @@ def pa_decode(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, scale, 
     block_tables: int32 [num_seqs, max_blocks_per_seq]; seq_lens: int32 [num_seqs];
     max_seq_len: host int bound on seq_lens (no device sync is made);
     workspace: uint8 tensor of at least pa_decode_workspace_size(...) bytes, allocated
-    here if omitted (pass one to keep allocation off the hot path).
+    (zero-filled) here on ``stream`` if omitted (pass one to keep allocation off the hot
+    path); stream: a torch.cuda.Stream, default the current one.
     """
     _dev("q", q, ndim=3)
     if q.dtype not in _DTYPE:
@@ -180,7 +194,7 @@ def pa_decode(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, scale, 
     if out.shape != q.shape or block_tables.shape[0] != num_seqs or seq_lens.shape[0] != num_seqs:
         raise ValueError("q, out, block_tables and seq_lens disagree on num_seqs or shape")
     if workspace is None:
-        workspace = decode_workspace(q, num_kv_heads, max_seq_len)
+        workspace = decode_workspace(q, num_kv_heads, max_seq_len, stream)
     if workspace is not None:
         _dev("workspace", workspace)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
@@ -265,7 +279,7 @@ def pa_multi_query(q, k_cache, v_cache, block_tables, seq_lens, q_start, num_kv_
     need = pa_multi_query_workspace_size(num_seqs, total_q, num_heads, num_kv_heads, head_dim,
                                          max_q_len, max_seq_len)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _scratch(need, q.device, stream, zero=False)
     if workspace is not None:
         _dev("workspace", workspace)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
@@ -315,7 +329,7 @@ def pa_decode_shared_prefix(q, k_cache, v_cache, block_tables, seq_lens, group_s
     need = pa_decode_shared_prefix_workspace_size(num_seqs, num_groups, num_heads, num_kv_heads,
                                                   head_dim, max_group_size, max_seq_len)
     if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _scratch(need, q.device, stream, zero=False)
     if workspace is not None:
         _dev("workspace", workspace)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0

@@ -1,7 +1,7 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the benchmark
-times.  The oracle recomputes a seeded sample of sequences (always including the
-shortest and the longest); writes and block copies are checked bit for bit over the
-whole pool."""
+times.  The oracle recomputes every sequence of every workload (pairs split across
+waves and tail chunks only arise at these sizes, and any of them may be wrong);
+writes and block copies are checked bit for bit over the whole pool."""
 
 import numpy as np
 import pytest
@@ -20,14 +20,6 @@ def _need_gpu():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     pk()
-
-
-def sample(b, n, seed=0):
-    lens = b.seq_lens.numpy()
-    rng = np.random.default_rng(seed)
-    pick = set(rng.choice(len(lens), size=min(n, len(lens)), replace=False).tolist())
-    pick |= {int(lens.argmin()), int(lens.argmax())}
-    return sorted(pick)
 
 
 def apply_write_and_check(b, d, with_copy=False):
@@ -49,14 +41,18 @@ def apply_write_and_check(b, d, with_copy=False):
     b.k_cache, b.v_cache = ek, ev
 
 
-def check_sampled(b, d, n, what):
-    seqs = sample(b, n)
-    log(f"{what}: decode, oracle on sequences {seqs}")
+def check_all(b, d, what):
+    """pa_decode against the oracle on every sequence of the batch."""
     got = gpu_decode(b, d)
-    ref = oracle_decode(b, seqs=seqs)
-    err = assert_close(got[seqs], ref, b.dtype, what)
     assert np.isfinite(got).all()
-    log(f"{what}: max abs err {err:.3e}")
+    log(f"{what}: oracle on all {b.num_seqs} sequences")
+    ref = oracle_decode(b)
+    err = assert_close(got, ref, b.dtype, what)
+    big = np.abs(ref) >= 4          # where rounding the output to bf16 alone can exceed 8e-3
+    small_err = float(np.abs(got - ref)[~big].max()) if (~big).any() else 0.0
+    log(f"{what}: {b.num_seqs} sequences x {b.num_heads} heads compared, max abs err {err:.3e}; "
+        f"{int(big.sum())} outputs with |ref| >= 4 (bound: half a bf16 ulp), max abs err on the "
+        f"rest {small_err:.3e}")
 
 
 def test_llama3_8b_full():
@@ -64,17 +60,17 @@ def test_llama3_8b_full():
     d = to_dev(b)
     log("llama3_8b full: write 256 tokens")
     apply_write_and_check(b, d)
-    check_sampled(b, d, 14, "llama3_8b full")
+    check_all(b, d, "llama3_8b full")
 
 
 def test_llama7b_full():
     b = workloads.llama7b()
-    check_sampled(b, to_dev(b), 10, "llama7b full")
+    check_all(b, to_dev(b), "llama7b full")
 
 
 def test_opt13b_shared_full():
     b = workloads.opt13b_shared()
-    check_sampled(b, to_dev(b), 10, "opt13b_shared full")
+    check_all(b, to_dev(b), "opt13b_shared full")
 
 
 def test_opt13b_cow_full():
@@ -83,10 +79,10 @@ def test_opt13b_cow_full():
     log("opt13b_cow full: copy 224 blocks, write 256 tokens")
     assert len(b.cow_pairs) == 224
     apply_write_and_check(b, d, with_copy=True)
-    check_sampled(b, d, 10, "opt13b_cow full")
+    check_all(b, d, "opt13b_cow full")
 
 
 @pytest.mark.parametrize("block_size", [8, 16, 32])
 def test_llama2_70b_full(block_size):
     b = workloads.llama2_70b(block_size=block_size)
-    check_sampled(b, to_dev(b), 2, f"llama2_70b B={block_size} full")
+    check_all(b, to_dev(b), f"llama2_70b B={block_size} full")

@@ -178,32 +178,56 @@ def test_workloads_reduced(name, make):
     assert_close(out.float().cpu().double().numpy(), run_oracle(b), "bf16", name)
 
 
-def sampled_rows(b, rows):
-    """Oracle output for sampled query rows only (full-size batches)."""
+def oracle_rows(b, rows):
+    """Oracle output for the given query rows (full-size batches): each sequence's K/V is
+    gathered once, and each row attends to its causal prefix of it."""
     kc, vc = written(b)
     qs = b.q_start.tolist()
     lens = b.seq_lens.tolist()
     bt = as_numpy(b.block_tables)
-    res = []
+    by_seq = {}
     for r in rows:
-        s = int(np.searchsorted(qs, r, side="right") - 1)
+        by_seq.setdefault(int(np.searchsorted(qs, r, side="right") - 1), []).append(r)
+    res = {}
+    for s, rs in by_seq.items():
         n, L = qs[s + 1] - qs[s], lens[s]
-        pos = L - n + (r - qs[s])
-        K = oracle.to_f64(oracle.gather(kc, bt[s], pos + 1, b.block_size), b.dtype)
-        V = oracle.to_f64(oracle.gather(vc, bt[s], pos + 1, b.block_size), b.dtype)
-        res.append(oracle.attend(oracle.to_f64(as_numpy(b.q[r]), b.dtype), K, V, b.scale))
-    return np.stack(res)
+        last = max(L - n + (r - qs[s]) for r in rs)
+        K = oracle.to_f64(oracle.gather(kc, bt[s], last + 1, b.block_size), b.dtype)
+        V = oracle.to_f64(oracle.gather(vc, bt[s], last + 1, b.block_size), b.dtype)
+        for r in rs:
+            pos = L - n + (r - qs[s])
+            res[r] = oracle.attend(oracle.to_f64(as_numpy(b.q[r]), b.dtype), K[:pos + 1], V[:pos + 1],
+                                   b.scale)
+    return np.stack([res[r] for r in rows])
 
 
-@pytest.mark.parametrize("name", ["llama3_8b_spec", "llama3_8b_chunk"])
-def test_full_size_workloads_on_sampled_rows(name):
-    b = workloads.WORKLOADS[name]()
-    log(f"{name} full size")
+def test_full_size_speculative_verification_every_row():
+    b = workloads.WORKLOADS["llama3_8b_spec"]()
+    log("llama3_8b_spec full size")
+    out, _ = run_gpu(b)
+    got = out.float().cpu().double().numpy()
+    assert np.isfinite(got).all()
+    rows = list(range(b.q.shape[0]))
+    err = assert_close(got, oracle_rows(b, rows), "bf16", "llama3_8b_spec")
+    log(f"llama3_8b_spec: all {len(rows)} query rows x {b.num_heads} heads compared, max abs err {err:.3e}")
+
+
+def test_full_size_chunked_prefill_every_query_block():
+    # one row from every 16-query block of every sequence (a different offset in each
+    # block), plus each sequence's first and last query
+    b = workloads.WORKLOADS["llama3_8b_chunk"]()
+    log("llama3_8b_chunk full size")
     out, _ = run_gpu(b)
     got = out.float().cpu().double().numpy()
     assert np.isfinite(got).all()
     rng = np.random.default_rng(0)
     qs = b.q_start.tolist()
-    rows = sorted(set(rng.choice(b.q.shape[0], 48, replace=False).tolist()
-                      + [0, b.q.shape[0] - 1] + [qs[s] for s in range(0, b.num_seqs, 7)]))
-    assert_close(got[rows], sampled_rows(b, rows), "bf16", name)
+    rows = set()
+    for s in range(b.num_seqs):
+        rows |= {qs[s], qs[s + 1] - 1}
+        for a in range(qs[s], qs[s + 1], 16):
+            rows.add(int(a + rng.integers(0, min(16, qs[s + 1] - a))))
+    rows = sorted(rows)
+    err = assert_close(got[rows], oracle_rows(b, rows), "bf16", "llama3_8b_chunk")
+    log(f"llama3_8b_chunk: {len(rows)} of {b.q.shape[0]} query rows x {b.num_heads} heads compared "
+        f"(every 16-query block of all {b.num_seqs} sequences), max abs err {err:.3e}")

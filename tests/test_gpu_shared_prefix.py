@@ -178,12 +178,11 @@ def test_workloads_reduced(name, make):
     assert_close(out.float().cpu().double().numpy(), ref, "f16", name)
 
 
-def test_full_size_opt13b_shared_on_sampled_sequences():
+def test_full_size_opt13b_shared_every_sequence():
     b = workloads.opt13b_shared()
     log("opt13b_shared full size")
     out, _ = run(b)
     got = out.float().cpu().double().numpy()
     assert np.isfinite(got).all()
-    rng = np.random.default_rng(1)
-    seqs = sorted(set(rng.choice(b.num_seqs, 24, replace=False).tolist() + [0, 7, 8, b.num_seqs - 1]))
-    assert_close(got[seqs], oracle_out(b, seqs=seqs), "f16", "opt13b_shared")
+    err = assert_close(got, oracle_out(b), "f16", "opt13b_shared")
+    log(f"opt13b_shared: all {b.num_seqs} sequences x {b.num_heads} heads compared, max abs err {err:.3e}")
