@@ -20,10 +20,11 @@
 //   wave, so each K/V row is read from HBM once.
 //
 // Prologue
-//   Each wave sums the tile counts of all sequences (64 at a time, one per lane)
-//   to get the total T, and scans them again to find the pair and tile where its
-//   range begins.  Sequences of length 0 have no tiles; their zero outputs are
-//   written by wave s mod (number of waves).
+//   Each wave loads the lengths of all sequences (512 at a time, in one round
+//   trip) and sums their tile counts to get the total T, keeping each sequence's
+//   length and tile prefix sum in LDS, where it locates the pair and tile its range
+//   begins with.  Sequences of length 0 have no tiles; their zero outputs are
+//   written by wave s mod (number of waves) during that pass.
 //
 // Lane roles inside a segment (lane = 16 * grp + col, grp = 0..3, col = 0..15)
 //   q.K^T on the matrix cores: v_mfma_f32_16x16x32_{bf16,f16} (or 16x16x4_f32)
@@ -282,15 +283,6 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   const int Hkv = p.num_kv_heads;
   const int g = p.group;
 
-  // Zero outputs of empty sequences.
-  for (int s = w; s < N; s += launched) {
-    if (seq_len_at(p, s) == 0) {
-      u32x4* o = reinterpret_cast<u32x4*>((char*)p.out + (size_t)s * p.num_heads * ROWB);
-      const int n16 = p.num_heads * ROWB / 16;
-      for (int i = lane; i < n16; i += 64) o[i] = u32x4{0, 0, 0, 0};
-    }
-  }
-
   // Tiles of sequence s as seen by this lane (0 past the batch).
   auto lane_tiles = [&](int s) { return s < N ? tiles_of(seq_len_at(p, s)) : 0; };
 
@@ -302,22 +294,40 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   int* const lenl = lds_len[threadIdx.x >> 6];
   bool in_lds = N <= kLdsSeqs;
 
-  // Total tiles of the step; the lengths of the next 64 sequences are loaded
-  // while the current 64 are summed (and, for a batch that fits, stored in LDS
-  // with their exclusive prefix sums).
+  // Total tiles of the step (and, for a batch that fits, every sequence's length and
+  // exclusive tile prefix sum in LDS).  The lengths of kLenRound * 64 sequences are
+  // loaded at once, unconditionally (indices past the batch read its last length and
+  // are masked afterwards), so the pass costs one memory round trip per round rather
+  // than one per 64 sequences.
   long long seq_tiles = 0;
   {
-    int L_cur = lane < N ? seq_len_at(p, lane) : 0;
-    for (int c = 0; c < N; c += 64) {
-      const int L_nxt = c + 64 + lane < N ? seq_len_at(p, c + 64 + lane) : 0;
-      const int n_cur = tiles_of(L_cur);
-      const int incl = wave_inclusive_scan(n_cur);
-      if (in_lds && c + lane < N) {
-        pre[c + lane] = (int)(seq_tiles + incl - n_cur);
-        lenl[c + lane] = L_cur;
+    constexpr int kLenRound = 8;
+    for (int c0 = 0; c0 < N; c0 += 64 * kLenRound) {
+      int raw[kLenRound];
+#pragma unroll
+      for (int i = 0; i < kLenRound; ++i) raw[i] = p.seq_lens[min(c0 + 64 * i + lane, N - 1)];
+#pragma unroll
+      for (int i = 0; i < kLenRound; ++i) {
+        const int c = c0 + 64 * i;
+        if (c >= N) break;
+        const int L = c + lane < N ? (raw[i] < 0 ? 0 : min(raw[i], p.max_seq_len)) : 0;
+        const int n_cur = tiles_of(L);
+        const int incl = wave_inclusive_scan(n_cur);
+        if (in_lds && c + lane < N) {
+          pre[c + lane] = (int)(seq_tiles + incl - n_cur);
+          lenl[c + lane] = L;
+        }
+        seq_tiles += __builtin_amdgcn_readlane(incl, 63);
+        // outputs of empty sequences are zeros: sequence s is zeroed by wave s mod launched
+        unsigned long long empty = __ballot(c + lane < N && L == 0 && (c + lane) % launched == w);
+        while (empty) {
+          const int s = c + __ffsll(empty) - 1;
+          empty &= empty - 1;
+          u32x4* o = reinterpret_cast<u32x4*>((char*)p.out + (size_t)s * p.num_heads * ROWB);
+          const int n16 = p.num_heads * ROWB / 16;
+          for (int i2 = lane; i2 < n16; i2 += 64) o[i2] = u32x4{0, 0, 0, 0};
+        }
       }
-      seq_tiles += __builtin_amdgcn_readlane(incl, 63);
-      L_cur = L_nxt;
     }
     // prefix sums must fit in an int; the writes above complete before any read
     in_lds = in_lds && seq_tiles < (1ll << 31) - 1;
