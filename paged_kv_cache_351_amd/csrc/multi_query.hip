@@ -41,13 +41,20 @@
 //                   the tokens whose scores it computed, and the scores never move
 //                   between lanes.  The LDS transpose read (ds_read_b64_tr_b16)
 //                   turns the [token][head_dim] V rows into the A fragments.
-//   P is rounded to the storage type for the matrix cores: fp16 keeps 11
-//   significant bits, bf16 is split into two bf16 terms (about 16 bits) fed to
-//   two products, fp32 stays fp32.  The running sum adds the values used (for
-//   bf16 the fp32 values, within 2^-16 of the two terms), so the output is a
-//   weighted mean with the weights used.  Masked tokens
-//   get -inf, i.e. weight 0; running maxima start at -1e30 so no row ever forms
-//   inf - inf.
+//   P enters the second product in a 16-bit type.  fp16 data: P rounded to fp16
+//   (11 significant bits).  bf16 data with shared tiles (prefill-sized blocks): V
+//   is staged in LDS as fp16 (exact for |v| < 2^16) and P rounded to fp16, one
+//   product; a V value beyond fp16's range becomes inf, the workgroup's result
+//   comes out non-finite, and the workgroup runs its tiles again with bf16 V and
+//   the two-term P below (so every finite input is handled, the common case at one
+//   product per tile instead of two).  bf16 data in the split variant: P split into
+//   two bf16 terms (about 16 significant bits) fed to two products.  fp32 stays
+//   fp32.  The running sum adds the values used (for two-term bf16 the fp32
+//   values, within 2^-16 of the two terms), so the output is a weighted mean with
+//   the weights used.  Scores stay raw until the exponent, p = 2^(s * |scale|
+//   log2 e - m) in one fused multiply-add (a negative scale is folded into q's
+//   signs).  Masked tokens get -inf, i.e. weight 0; running maxima start at -1e30
+//   so no row ever forms inf - inf.
 #include <type_traits>
 
 #include "multi_query.h"
@@ -61,6 +68,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kTile = 32;   // tokens per K/V tile
 constexpr float kNegBig = -1.0e30f;
@@ -269,6 +277,12 @@ void multi_query_kernel(MultiQueryParams p) {
   static_assert(SPLIT || !SHARED, "shared-prefix groups use the split variant");
   static_assert(RB == 1 || (RB == 2 && !SPLIT), "two row blocks only with shared tiles");
   __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+  // bf16 with shared tiles: V is staged in LDS as fp16 and P.V runs as one fp16 product
+  // (see softmax_pv); a workgroup whose result comes out non-finite (a V value beyond
+  // fp16's range, or non-finite input) runs its tiles again with bf16 V (see the end of
+  // the tile loop)
+  constexpr bool PVH = DT == kBF16 && !SPLIT;
+  __shared__ uint32_t redo_flag[4];
 
   Item it;
   if (!item_of(p, it)) return;
@@ -369,7 +383,12 @@ void multi_query_kernel(MultiQueryParams p) {
     return mp;
   };
 
-  // query fragments: the same chunks of the row as the K fragments
+  // query fragments: the same chunks of the row as the K fragments.  A negative scale is
+  // folded into q (every sign flipped, which negates each score exactly), so the scores
+  // are scaled by |scale| log2(e) > 0 and the maximum of the raw scores is the maximum of
+  // the scaled ones.
+  const bool neg_scale = p.scale_log2e < 0.f;
+  const uint32_t qsign = neg_scale ? (DT == kF32 ? 0x80000000u : 0x80008000u) : 0u;
   u32x4 qf[RB][NKC];
 #pragma unroll
   for (int b = 0; b < RB; ++b)
@@ -378,7 +397,7 @@ void multi_query_kernel(MultiQueryParams p) {
       qf[b][c] = u32x4{0u, 0u, 0u, 0u};
       if (row_ok[b])
         qf[b][c] = *reinterpret_cast<const u32x4*>((const char*)p.q + out_row[b] * S::ROWB +
-                                                   chunk_of<DT, D>(c, grp) * 16);
+                                                   chunk_of<DT, D>(c, grp) * 16) ^ qsign;
     }
 
   f32x4 acc[RB][NJ];
@@ -423,18 +442,29 @@ void multi_query_kernel(MultiQueryParams p) {
   u32x4 kr[2][KL], vr[2][KL];
   // V rows go to LDS as they are ([token][head_dim], padded rows); the shared-tile
   // variant stores K the same way
-  auto store_kv = [&](const u32x4 (&xk)[KL], const u32x4 (&xv)[KL], char* kb, char* vb) {
+  // Stage a tile's K/V rows in LDS.  For PVH, V goes in as fp16 unless SAFE: bf16 ->
+  // fp16 is exact for |v| < 2^16 (8 significant bits fit in 11; below 2^-17 the fp16
+  // spacing 2^-24 bounds the change); a larger value becomes inf and makes the result
+  // non-finite, which sends the workgroup through its tiles again with SAFE set.
+  auto store_kv = [&](auto safe_c, const u32x4 (&xk)[KL], const u32x4 (&xv)[KL], char* kb, char* vb) {
+    constexpr bool SAFE = decltype(safe_c)::value;
 #pragma unroll
     for (int k = 0; k < NT; ++k)
 #pragma unroll
       for (int c = 0; c < CPT; ++c) {
-        *reinterpret_cast<u32x4*>(vb + my_tok(k) * S::VSTRIDE + my_chunk(c) * 16) = xv[k * CPT + c];
+        u32x4 v = xv[k * CPT + c];
+        if constexpr (PVH && !SAFE) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            v[i] = to_store2<kF16>(__uint_as_float(v[i] << 16), __uint_as_float(v[i] & 0xffff0000u));
+        }
+        *reinterpret_cast<u32x4*>(vb + my_tok(k) * S::VSTRIDE + my_chunk(c) * 16) = v;
         if constexpr (!SPLIT)
           *reinterpret_cast<u32x4*>(kb + my_tok(k) * S::KSTRIDE + my_chunk(c) * 16) = xk[k * CPT + c];
       }
   };
 
-  const float sl2 = p.scale_log2e;
+  const float sl2 = neg_scale ? -p.scale_log2e : p.scale_log2e;   // >= 0
   const int ntiles = t_end > t_begin ? (t_end - t_begin + kTile - 1) / kTile : 0;
 
   // S^T = K Q^T for the two 16-token halves and every row block; a(h, c) gives the
@@ -467,20 +497,21 @@ void multi_query_kernel(MultiQueryParams p) {
   };
 
   // Online softmax of tile t0 (scores in sc) and O^T += V^T P^T from the V tile at vb
-  // in LDS.
-  auto softmax_pv = [&](int t0, const TileMap& mp, const char* vb) {
+  // in LDS (fp16 for PVH unless SAFE; see store_kv).
+  auto softmax_pv = [&](auto safe_c, int t0, const TileMap& mp, const char* vb) {
+    constexpr bool SAFE = decltype(safe_c)::value;
     // tile token 16 h + 4 grp + i of row col; full tiles that every row may see in
-    // full need no mask
-    float pr[RB][8], alpha[RB], tmax[RB], sv_keep[RB][8];
+    // full need no mask.  The raw scores are kept (masked ones -inf) and scaled inside
+    // the exponent's fused multiply-add: p = 2^(s sl2 - m).
+    float pr[RB][8], alpha[RB], tmax[RB], sv[RB][8];
     const bool whole = mp.count == kTile && (SHARED ? mp.owner < 0 : t0 + kTile - 1 <= pos_lo);
 #pragma unroll
     for (int b = 0; b < RB; ++b) {
-      float sv[8];
       if (whole) {
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sv[4 * h + i] = sc[b][h][i] * sl2;
+          for (int i = 0; i < 4; ++i) sv[b][4 * h + i] = sc[b][h][i];
       } else {
         const bool row_sees = !SHARED || mp.owner < 0 || mp.owner == qtok[b] - tok0;
 #pragma unroll
@@ -489,17 +520,15 @@ void multi_query_kernel(MultiQueryParams p) {
           for (int i = 0; i < 4; ++i) {
             const int u = 16 * h + 4 * grp + i;
             const bool ok = SHARED ? (row_sees && u < mp.count) : (u < mp.count && t0 + u <= pos[b]);
-            sv[4 * h + i] = ok ? sc[b][h][i] * sl2 : -__builtin_inff();
+            sv[b][4 * h + i] = ok ? sc[b][h][i] : -__builtin_inff();
           }
       }
-      float mx = sv[0];
-#pragma unroll
-      for (int u = 1; u < 8; ++u) mx = fmaxf(mx, sv[u]);
+      float mx = fmaxf(fmaxf(fmaxf(sv[b][0], sv[b][1]), fmaxf(sv[b][2], sv[b][3])),
+                       fmaxf(fmaxf(sv[b][4], sv[b][5]), fmaxf(sv[b][6], sv[b][7])));
       mx = max_over_groups(mx);
-      tmax[b] = fmaxf(m[b], mx);
-      sv_keep[b][0] = sv[0];
-#pragma unroll
-      for (int u = 1; u < 8; ++u) sv_keep[b][u] = sv[u];
+      // a row with no visible token here has mx = -inf; with a zero scale that product is
+      // NaN, which fmaxf drops
+      tmax[b] = fmaxf(m[b], mx * sl2);
     }
     // The reference maximum of a row moves only when the tile's maximum exceeds it by
     // more than kLazyMax (base 2), for every row of the wave at once; otherwise the
@@ -516,7 +545,15 @@ void multi_query_kernel(MultiQueryParams p) {
       alpha[b] = rescale ? fast_exp2(m[b] - mn) : 1.0f;
       m[b] = mn;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) pr[b][u] = fast_exp2(sv_keep[b][u] - mn);
+      for (int u = 0; u < 8; ++u) pr[b][u] = fast_exp2(fmaf(sv[b][u], sl2, -mn));
+    }
+    // a masked score (-inf) gives exactly 0 as long as sl2 > 0; with a zero scale
+    // -inf * 0 is NaN, so those weights are cleared here (a uniform, rare branch)
+    if (sl2 == 0.f && !whole) {
+#pragma unroll
+      for (int b = 0; b < RB; ++b)
+#pragma unroll
+        for (int u = 0; u < 8; ++u) pr[b][u] = sv[b][u] == -__builtin_inff() ? 0.f : pr[b][u];
     }
     if (rescale) {
 #pragma unroll
@@ -525,13 +562,13 @@ void multi_query_kernel(MultiQueryParams p) {
         for (int j = 0; j < NJ; ++j) acc[b][j] *= alpha[b];
     }
 
-    if constexpr (DT == kF32) {
+    // fp32 products: product u takes slot 8 grp + u, i.e. tile token 16 (u / 4) + 4 grp +
+    // u % 4, at head_dim 16 j + col
+    auto pv_f32 = [&]() {
 #pragma unroll
       for (int b = 0; b < RB; ++b)
         l[b] = l[b] * alpha[b] + (((pr[b][0] + pr[b][1]) + (pr[b][2] + pr[b][3])) +
                                   ((pr[b][4] + pr[b][5]) + (pr[b][6] + pr[b][7])));
-      // product u takes slot 8 grp + u, i.e. tile token 16 (u / 4) + 4 grp + u % 4, at
-      // head_dim 16 j + col
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         float a[8];
@@ -545,63 +582,80 @@ void multi_query_kernel(MultiQueryParams p) {
           for (int u = 0; u < 8; ++u)
             acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[u], pr[b][u], acc[b][j], 0, 0, 0);
       }
-    } else {
-      // P in the storage type.  bf16 keeps 8 significant bits, so P is split into two
-      // bf16 terms fed to two products with the same V fragment: the high term is P cut
-      // to its top 16 bits, which leaves an exact fp32 remainder, and the low term is
-      // that remainder rounded, about 16 significant bits in all; the running sum adds
-      // the fp32 values, which differ from the two terms by about 2^-16 relative.  fp16
-      // keeps 11 bits in one term, and the running sum adds the rounded values.
+    };
+    // A = V^T for head_dim 16 j .. 16 j + 15 through two transpose reads: slots
+    // 8 grp + 4 h + q hold tile tokens 16 h + 4 grp + q, and lane (grp, col) names the
+    // row 16 h + 4 grp + col / 4 at head_dim 16 j + 4 (col % 4)
+    const char* vbase = vb + (4 * grp + (col >> 2)) * S::VSTRIDE + (4 * (col & 3)) * 2;
+    auto vfrag = [&](int j) {
+      const s16x4 a0 = lds_read_tr16(vbase + 32 * j);
+      const s16x4 a1 = lds_read_tr16(vbase + 16 * S::VSTRIDE + 32 * j);
+      return __builtin_bit_cast(u32x4, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    // P rounded once to fp16 (11 significant bits; the weights are below 2^8, so no
+    // overflow), V in fp16 (its own type, or bf16 widened exactly): one product.  The
+    // running sum adds the rounded weights, two at a time.
+    auto pv_f16 = [&]() {
+      const f16x2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
+      u32x4 pb[RB];
+#pragma unroll
+      for (int b = 0; b < RB; ++b) {
+        uint32_t pw[4];
+        float ps = l[b] * alpha[b];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          pw[u] = to_store2<kF16>(pr[b][2 * u], pr[b][2 * u + 1]);
+          ps = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pw[u]), one2, ps, false);
+        }
+        l[b] = ps;
+        pb[b] = u32x4{pw[0], pw[1], pw[2], pw[3]};
+      }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const u32x4 a = vfrag(j);
+#pragma unroll
+        for (int b = 0; b < RB; ++b)
+          acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                             __builtin_bit_cast(f16x8, pb[b]), acc[b][j], 0, 0, 0);
+      }
+    };
+    // bf16 P split into two bf16 terms fed to two products with the same bf16 V fragment
+    // (bf16 alone keeps 8 significant bits): the high term is P cut to its top 16 bits,
+    // which leaves an exact fp32 remainder, and the low term is that remainder rounded,
+    // about 16 significant bits in all; the running sum adds the fp32 values, which
+    // differ from the two terms by about 2^-16 relative.
+    auto pv_bf16_split = [&]() {
       u32x4 pb[RB], pb_lo[RB];
 #pragma unroll
       for (int b = 0; b < RB; ++b) {
         uint32_t pw[4], pw_lo[4];
-        float ps;
-        if constexpr (DT == kBF16) {
 #pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const uint32_t x = __float_as_uint(pr[b][2 * u]), y = __float_as_uint(pr[b][2 * u + 1]);
-            pw[u] = (x >> 16) | (y & 0xffff0000u);
-            pw_lo[u] = to_store2<DT>(pr[b][2 * u] - __uint_as_float(x & 0xffff0000u),
-                                     pr[b][2 * u + 1] - __uint_as_float(y & 0xffff0000u));
-          }
-          ps = ((pr[b][0] + pr[b][1]) + (pr[b][2] + pr[b][3])) + ((pr[b][4] + pr[b][5]) + (pr[b][6] + pr[b][7]));
-        } else {
-          ps = 0.f;
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            pw[u] = to_store2<DT>(pr[b][2 * u], pr[b][2 * u + 1]);
-            pw_lo[u] = 0u;
-            ps += from_store<DT>((uint16_t)pw[u]) + from_store<DT>((uint16_t)(pw[u] >> 16));
-          }
+        for (int u = 0; u < 4; ++u) {
+          const uint32_t x = __float_as_uint(pr[b][2 * u]), y = __float_as_uint(pr[b][2 * u + 1]);
+          pw[u] = (x >> 16) | (y & 0xffff0000u);
+          pw_lo[u] = to_store2<kBF16>(pr[b][2 * u] - __uint_as_float(x & 0xffff0000u),
+                                      pr[b][2 * u + 1] - __uint_as_float(y & 0xffff0000u));
         }
-        l[b] = l[b] * alpha[b] + ps;
+        l[b] = l[b] * alpha[b] + (((pr[b][0] + pr[b][1]) + (pr[b][2] + pr[b][3])) +
+                                  ((pr[b][4] + pr[b][5]) + (pr[b][6] + pr[b][7])));
         pb[b] = u32x4{pw[0], pw[1], pw[2], pw[3]};
         pb_lo[b] = u32x4{pw_lo[0], pw_lo[1], pw_lo[2], pw_lo[3]};
       }
-      // A = V^T for head_dim 16 j .. 16 j + 15 through two transpose reads: slots
-      // 8 grp + 4 h + q hold tile tokens 16 h + 4 grp + q, and lane (grp, col) names the
-      // row 16 h + 4 grp + col / 4 at head_dim 16 j + 4 (col % 4)
-      const char* vbase = vb + (4 * grp + (col >> 2)) * S::VSTRIDE + (4 * (col & 3)) * 2;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
-        const s16x4 a0 = lds_read_tr16(vbase + 32 * j);
-        const s16x4 a1 = lds_read_tr16(vbase + 16 * S::VSTRIDE + 32 * j);
-        const u32x4 a = __builtin_bit_cast(u32x4, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+        const u32x4 a = vfrag(j);
 #pragma unroll
         for (int b = 0; b < RB; ++b) {
-          if constexpr (DT == kBF16) {
-            acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                                __builtin_bit_cast(bf16x8, pb[b]), acc[b][j], 0, 0, 0);
-            acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                                __builtin_bit_cast(bf16x8, pb_lo[b]), acc[b][j], 0, 0, 0);
-          } else {
-            acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
-                                                               __builtin_bit_cast(f16x8, pb[b]), acc[b][j], 0, 0, 0);
-          }
+          acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                              __builtin_bit_cast(bf16x8, pb[b]), acc[b][j], 0, 0, 0);
+          acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                              __builtin_bit_cast(bf16x8, pb_lo[b]), acc[b][j], 0, 0, 0);
         }
       }
-    }
+    };
+    if constexpr (DT == kF32) pv_f32();
+    else if constexpr (DT == kF16 || (PVH && !SAFE)) pv_f16();
+    else pv_bf16_split();
   };
 
   // pool byte offsets of this lane's tokens from their table entries
@@ -638,7 +692,7 @@ void multi_query_kernel(MultiQueryParams p) {
     for (int k = wave; k < ntiles; k += kstep) {
       const int t0 = t_begin + k * kTile;
       const bool more = k + kstep < ntiles;
-      store_kv(kr[0], vr[0], nullptr, ldsV);
+      store_kv(std::false_type{}, kr[0], vr[0], nullptr, ldsV);
       if (more) {
         offsets(tb, to, off);
         load_rows(vr[0], p.v_cache, off);
@@ -647,7 +701,7 @@ void multi_query_kernel(MultiQueryParams p) {
       if (more) load_rows(kr[0], p.k_cache, off);
       if (k + 2 * kstep < ntiles) fetch_table(tb, to, tile_map(t0 + 2 * kstep * kTile));
       __builtin_amdgcn_wave_barrier();   // V stores above are read by other lanes below
-      softmax_pv(t0, tile_map(t0), ldsV);
+      softmax_pv(std::false_type{}, t0, tile_map(t0), ldsV);
       __builtin_amdgcn_wave_barrier();   // V reads above before the next stores
     }
   } else {
@@ -655,40 +709,72 @@ void multi_query_kernel(MultiQueryParams p) {
     // the rows of tiles k + 1 and k + 2 and the table entries of tile k + 3 are on
     // their way.  Tile k goes to buffer k % 2, whose last readers (tile k - 2) have
     // all passed the barrier of tile k - 1, so one barrier per tile suffices.
-    int tb[2][NT], to[2][NT];
-    auto step = [&](int k, char* buf, u32x4 (&xk)[KL], u32x4 (&xv)[KL], const int (&tbc)[NT],
-                    const int (&toc)[NT], int (&tbn)[NT], int (&ton)[NT]) {
-      const int t0 = t_begin + k * kTile;
-      char* const kb = buf;
-      char* const vb = buf + S::KBYTES;
-      store_kv(xk, xv, kb, vb);
-      __syncthreads();
-      if (k + 3 < ntiles) fetch_table(tbn, ton, tile_map(t0 + 3 * kTile));
-      if (k + 2 < ntiles) {
-        size_t off[NT];
-        offsets(tbc, toc, off);
-        load_rows(xk, p.k_cache, off);
-        load_rows(xv, p.v_cache, off);
+    auto run_tiles = [&](auto safe_c) {
+      int tb[2][NT], to[2][NT];
+      auto step = [&](int k, char* buf, u32x4 (&xk)[KL], u32x4 (&xv)[KL], const int (&tbc)[NT],
+                      const int (&toc)[NT], int (&tbn)[NT], int (&ton)[NT]) {
+        const int t0 = t_begin + k * kTile;
+        char* const kb = buf;
+        char* const vb = buf + S::KBYTES;
+        store_kv(safe_c, xk, xv, kb, vb);
+        __syncthreads();
+        if (k + 3 < ntiles) fetch_table(tbn, ton, tile_map(t0 + 3 * kTile));
+        if (k + 2 < ntiles) {
+          size_t off[NT];
+          offsets(tbc, toc, off);
+          load_rows(xk, p.k_cache, off);
+          load_rows(xv, p.v_cache, off);
+        }
+        qk([&](int h, int c) {
+          return *reinterpret_cast<const u32x4*>(kb + (16 * h + col) * S::KSTRIDE + chunk_of<DT, D>(c, grp) * 16);
+        });
+        softmax_pv(safe_c, t0, tile_map(t0), vb);
+      };
+      if (ntiles > 0) fetch_table(tb[0], to[0], tile_map(t_begin));
+      if (ntiles > 1) fetch_table(tb[1], to[1], tile_map(t_begin + kTile));
+      for (int i = 0; i < 2; ++i) {
+        if (i < ntiles) {
+          size_t off[NT];
+          offsets(tb[i], to[i], off);
+          load_rows(kr[i], p.k_cache, off);
+          load_rows(vr[i], p.v_cache, off);
+        }
       }
-      qk([&](int h, int c) {
-        return *reinterpret_cast<const u32x4*>(kb + (16 * h + col) * S::KSTRIDE + chunk_of<DT, D>(c, grp) * 16);
-      });
-      softmax_pv(t0, tile_map(t0), vb);
+      if (ntiles > 2) fetch_table(tb[0], to[0], tile_map(t_begin + 2 * kTile));
+      for (int k = 0; k < ntiles; k += 2) {
+        step(k, lds, kr[0], vr[0], tb[0], to[0], tb[1], to[1]);
+        if (k + 1 < ntiles) step(k + 1, lds + S::LDS, kr[1], vr[1], tb[1], to[1], tb[0], to[0]);
+      }
     };
-    if (ntiles > 0) fetch_table(tb[0], to[0], tile_map(t_begin));
-    if (ntiles > 1) fetch_table(tb[1], to[1], tile_map(t_begin + kTile));
-    for (int i = 0; i < 2; ++i) {
-      if (i < ntiles) {
-        size_t off[NT];
-        offsets(tb[i], to[i], off);
-        load_rows(kr[i], p.k_cache, off);
-        load_rows(vr[i], p.v_cache, off);
+    run_tiles(std::false_type{});
+    if constexpr (PVH) {
+      // A V value of 2^16 or more became inf in fp16, so every accumulator it reached
+      // is inf or NaN (p inf, or 0 inf for a masked token).  Any non-finite accumulator
+      // in the workgroup sends all four waves through the tiles again with V staged as
+      // bf16 and P split into two bf16 terms (exact for every finite input; input that
+      // is itself non-finite gives the same non-finite result either way).  The flag
+      // words are written by every wave before the barrier and read after it.
+      bool bad = false;
+#pragma unroll
+      for (int b = 0; b < RB; ++b)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) bad = bad || !__builtin_isfinite(acc[b][j][i]);
+      const bool wave_bad = __any(bad);
+      if (lane == 0) redo_flag[wave] = wave_bad ? 1u : 0u;
+      __syncthreads();
+      const uint32_t any_bad = redo_flag[0] | redo_flag[1] | redo_flag[2] | redo_flag[3];
+      if (__builtin_amdgcn_readfirstlane(any_bad) != 0u) {
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) acc[b][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+          m[b] = kNegBig;
+          l[b] = 0.f;
+        }
+        run_tiles(std::true_type{});
       }
-    }
-    if (ntiles > 2) fetch_table(tb[0], to[0], tile_map(t_begin + 2 * kTile));
-    for (int k = 0; k < ntiles; k += 2) {
-      step(k, lds, kr[0], vr[0], tb[0], to[0], tb[1], to[1]);
-      if (k + 1 < ntiles) step(k + 1, lds + S::LDS, kr[1], vr[1], tb[1], to[1], tb[0], to[0]);
     }
   }
 

@@ -15,7 +15,7 @@ import torch
 import oracle
 import workloads
 from workloads import as_numpy
-from _gpu import TOL, assert_close, bits, log, pk, to_dev
+from _gpu import TOL, allowance, assert_close, bits, log, pk, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -176,6 +176,38 @@ def test_workloads_reduced(name, make):
     log(f"{name} reduced")
     out, _ = run_gpu(b)
     assert_close(out.float().cpu().double().numpy(), run_oracle(b), "bf16", name)
+
+
+@pytest.mark.parametrize("exp2", [16, 20, 100])
+def test_bf16_values_far_outside_the_unit_range(exp2):
+    # bf16 prefill-sized blocks stage V in LDS as fp16, which holds |v| < 2^16 exactly; a
+    # larger value turns the workgroup's result non-finite and the workgroup runs again with
+    # bf16 V.  One V row (every KV head) of two sequences is multiplied by 2^exp2 (exact in
+    # bf16) and every query of those sequences attends to it (it is in the prompt), so the
+    # outputs range from O(1) to about 2^exp2.  All must be finite, and within the usual
+    # bound plus 2^-9 of the largest |V| the sequence holds: bf16 precision at the scale of
+    # the values being averaged.
+    b = batch(41 + exp2, "bf16", [300, 90, 700], [40, 64, 33], 32, 8, 128, 16)
+    vflat = b.v_cache.view(-1, 8, 128)
+    for s, t in ((0, 5), (2, 70)):
+        slot = int(b.block_tables[s, t // 16]) * 16 + t % 16
+        vflat[slot] = (vflat[slot].float() * 2.0 ** exp2).to(torch.bfloat16)
+    log(f"bf16 V rows x 2^{exp2}")
+    out, _ = run_gpu(b)
+    got = out.float().cpu().double().numpy()
+    assert np.isfinite(got).all()
+    ref = run_oracle(b)
+    qs = b.q_start.tolist()
+    _, vc = written(b)
+    vmax = np.zeros(b.q.shape[0])
+    for s in range(b.num_seqs):
+        V = oracle.to_f64(oracle.gather(vc, as_numpy(b.block_tables)[s], int(b.seq_lens[s]), b.block_size),
+                          "bf16")
+        vmax[qs[s]:qs[s + 1]] = np.abs(V).max()
+    bound = allowance(ref, "bf16") + 2.0 ** -9 * vmax[:, None, None]
+    err = np.abs(got - ref)
+    assert (err <= bound).all(), f"{(err > bound).sum()} outputs over the bound, max err {err.max():.3e}"
+    log(f"V x 2^{exp2}: max err {err.max():.3e}, max |out| {np.abs(ref).max():.3e}")
 
 
 def oracle_rows(b, rows):
