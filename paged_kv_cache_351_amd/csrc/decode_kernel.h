@@ -129,10 +129,12 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // gfx950 row swaps: swapping a value with a copy of itself leaves one lane of each
 // pair in each result, so the larger of the two is the pair's maximum.
 __device__ __forceinline__ float max_over_rows(float x) {
+  // (left-leaning chains, so that each step is one v_max3 and the swapped values are not
+  // first passed through a canonicalising maximum of their own)
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  x = fmaxf(fmaxf(x, __uint_as_float(a[0])), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return fmaxf(fmaxf(x, __uint_as_float(b[0])), __uint_as_float(b[1]));
 }
 
 // Two floats rounded to nearest even in a 16-bit type, the first in the low half.
@@ -716,7 +718,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
         if constexpr (MPV) {
           // One reference maximum per head for all 16 tokens (the product below sums
           // over every row group), moved only when the tile exceeds it by kLazyMax.
-          const float tmx = max_over_rows(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+          const float tmx = max_over_rows(fmaxf(fmaxf(fmaxf(sv[0], sv[1]), sv[2]), sv[3]));
           if (__any(tmx > m + kLazyMax)) {
             const float mn = tmx > m + kLazyMax ? tmx : m;
             const float alpha = fast_exp2(m - mn);
@@ -766,7 +768,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
             if constexpr (DT == kBF16) oacc[i] = mfma16<DT>(a0, a1, pl[0], pl[1], oacc[i]);
           }
         } else {
-          const float mn = fmaxf(m, fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])));
+          const float mn = fmaxf(fmaxf(fmaxf(fmaxf(m, sv[0]), sv[1]), sv[2]), sv[3]);
           const float alpha = fast_exp2(m - mn);
           float pr[4];
 #pragma unroll

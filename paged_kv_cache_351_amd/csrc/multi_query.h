@@ -31,6 +31,7 @@ struct MultiQueryParams {
   int head_dim;
   int block_size;
   float inv_block_size;        // 1 / block_size, rounded to nearest
+  int log2_block_size;         // log2(block_size) for a power of two, else -1
   int num_blocks;
   int max_blocks_per_seq;
   int max_q_len;

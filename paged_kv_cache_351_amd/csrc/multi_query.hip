@@ -114,10 +114,12 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // through LDS): swapping a value with a copy of itself leaves one lane of each pair
 // in each result, so the maximum of the two results is the pair's maximum.
 __device__ __forceinline__ float max_over_groups(float x) {
+  // (left-leaning chains, so that each step is one v_max3 and the swapped values are not
+  // first passed through a canonicalising maximum of their own)
   const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  x = fmaxf(fmaxf(x, __uint_as_float(a[0])), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return fmaxf(fmaxf(x, __uint_as_float(b[0])), __uint_as_float(b[1]));
 }
 
 template <int DT>
@@ -425,17 +427,25 @@ void multi_query_kernel(MultiQueryParams p) {
   auto my_tok = [&](int k) { return SPLIT ? col + 16 * k : tid / CR + (256 / CR) * k; };
   auto my_chunk = [&](int c) { return SPLIT ? chunk_of<DT, D>(c, grp) : tid % CR; };
   const float inv_b = p.inv_block_size;
+  const int log2_b = p.log2_block_size;
   // block-table entries (tb) and in-block offsets (to) of this lane's tokens of a tile
   auto fetch_table = [&](int (&tb)[NT], int (&to)[NT], const TileMap& mp) {
 #pragma unroll
     for (int k = 0; k < NT; ++k) {
       const int t = mp.base + min(my_tok(k), mp.count - 1);
-      // t / B without a branch or an integer division: t < 2^24 is exact in float, the
-      // product is off by at most one, and one correction each way fixes it
-      int j = (int)((float)t * inv_b);
-      int o = t - j * B;
-      j = o < 0 ? j - 1 : (o >= B ? j + 1 : j);
-      to[k] = o < 0 ? o + B : (o >= B ? o - B : o);
+      int j, o;
+      if (log2_b >= 0) {   // a power-of-two block size (uniform): a shift and a mask
+        j = t >> log2_b;
+        o = t & (B - 1);
+      } else {
+        // t / B without a branch or an integer division: t < 2^24 is exact in float,
+        // the product is off by at most one, and one correction each way fixes it
+        j = (int)((float)t * inv_b);
+        o = t - j * B;
+        j = o < 0 ? j - 1 : (o >= B ? j + 1 : j);
+        o = o < 0 ? o + B : (o >= B ? o - B : o);
+      }
+      to[k] = o;
       tb[k] = mp.table[j];
     }
   };
@@ -523,8 +533,9 @@ void multi_query_kernel(MultiQueryParams p) {
             sv[b][4 * h + i] = ok ? sc[b][h][i] : -__builtin_inff();
           }
       }
-      float mx = fmaxf(fmaxf(fmaxf(sv[b][0], sv[b][1]), fmaxf(sv[b][2], sv[b][3])),
-                       fmaxf(fmaxf(sv[b][4], sv[b][5]), fmaxf(sv[b][6], sv[b][7])));
+      // a left-leaning chain: the compiler makes it one maximum and three v_max3
+      float mx = fmaxf(fmaxf(fmaxf(sv[b][0], sv[b][1]), sv[b][2]), sv[b][3]);
+      mx = fmaxf(fmaxf(fmaxf(fmaxf(mx, sv[b][4]), sv[b][5]), sv[b][6]), sv[b][7]);
       mx = max_over_groups(mx);
       // a row with no visible token here has mx = -inf; with a zero scale that product is
       // NaN, which fmaxf drops

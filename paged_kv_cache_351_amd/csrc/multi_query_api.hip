@@ -175,6 +175,7 @@ pa_status pa_multi_query(const void* q, const void* k_cache, const void* v_cache
   mp.head_dim = head_dim;
   mp.block_size = block_size;
   mp.inv_block_size = 1.0f / (float)block_size;
+  mp.log2_block_size = (block_size & (block_size - 1)) == 0 ? __builtin_ctz((unsigned)block_size) : -1;
   mp.num_blocks = num_blocks;
   mp.max_blocks_per_seq = max_blocks_per_seq;
   mp.max_q_len = max_q_len;
@@ -355,6 +356,7 @@ pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void
   mp.head_dim = head_dim;
   mp.block_size = block_size;
   mp.inv_block_size = 1.0f / (float)block_size;
+  mp.log2_block_size = (block_size & (block_size - 1)) == 0 ? __builtin_ctz((unsigned)block_size) : -1;
   mp.num_blocks = num_blocks;
   mp.max_blocks_per_seq = max_blocks_per_seq;
   mp.max_q_len = max_group_size;
