@@ -274,7 +274,10 @@ void multi_query_kernel(MultiQueryParams p) {
   using S = Shape<DT, D>;
   constexpr int EB = S::EB, CR = S::CR, NKC = S::NKC, NJ = S::NJ;
   constexpr int VREG = S::VBYTES;                          // one V tile
-  constexpr int LDS_BYTES = SPLIT ? 4 * VREG : 2 * S::LDS;   // shared tiles: two buffers
+  // shared tiles of 16-bit types run the pipelined loop below on three LDS buffers; fp32
+  // runs the plain loop on two
+  constexpr bool PIPE = !SPLIT && DT != kF32;
+  constexpr int LDS_BYTES = SPLIT ? 4 * VREG : (PIPE ? 3 : 2) * S::LDS;
   static_assert(!SPLIT || (DT != kF32 && 4 * 16 * (D + 2) * 4 <= LDS_BYTES), "split merge space");
   static_assert(SPLIT || !SHARED, "shared-prefix groups use the split variant");
   static_assert(RB == 1 || (RB == 2 && !SPLIT), "two row blocks only with shared tiles");
@@ -480,7 +483,7 @@ void multi_query_kernel(MultiQueryParams p) {
   // S^T = K Q^T for the two 16-token halves and every row block; a(h, c) gives the
   // K fragment of half h, step c
   f32x4 sc[RB][2];
-  auto qk = [&](auto a) {
+  auto qk_to = [&](f32x4 (&sc)[RB][2], auto a) {
 #pragma unroll
     for (int b = 0; b < RB; ++b) sc[b][0] = sc[b][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -505,6 +508,7 @@ void multi_query_kernel(MultiQueryParams p) {
         }
       }
   };
+  auto qk = [&](auto a) { qk_to(sc, a); };
 
   // Online softmax of tile t0 (scores in sc) and O^T += V^T P^T from the V tile at vb
   // in LDS (fp16 for PVH unless SAFE; see store_kv).
@@ -720,7 +724,7 @@ void multi_query_kernel(MultiQueryParams p) {
     // the rows of tiles k + 1 and k + 2 and the table entries of tile k + 3 are on
     // their way.  Tile k goes to buffer k % 2, whose last readers (tile k - 2) have
     // all passed the barrier of tile k - 1, so one barrier per tile suffices.
-    auto run_tiles = [&](auto safe_c) {
+    auto run_plain = [&](auto safe_c) {
       int tb[2][NT], to[2][NT];
       auto step = [&](int k, char* buf, u32x4 (&xk)[KL], u32x4 (&xv)[KL], const int (&tbc)[NT],
                       const int (&toc)[NT], int (&tbn)[NT], int (&ton)[NT]) {
@@ -755,6 +759,276 @@ void multi_query_kernel(MultiQueryParams p) {
       for (int k = 0; k < ntiles; k += 2) {
         step(k, lds, kr[0], vr[0], tb[0], to[0], tb[1], to[1]);
         if (k + 1 < ntiles) step(k + 1, lds + S::LDS, kr[1], vr[1], tb[1], to[1], tb[0], to[0]);
+      }
+    };
+    // Pipelined loop (16-bit types), three LDS buffers.  Entering step k, tile k's scores
+    // are in registers (masked if it needs a mask), its rows' reference maxima are settled
+    // and `resc` says whether they moved.  Step k fetches the table entries of tile k + 4,
+    // stages tile k + 1 in buffer (k + 1) mod 3 and passes one barrier; rescales the
+    // accumulators if `resc` (rare); then one branch-free stretch: tile k + 1's scores on
+    // the matrix cores, tile k's weights, tile k's P.V, tile k + 1's mask (last tiles only)
+    // and row maxima, and the loads of tile k + 3, with the matrix instructions spread among
+    // the vector ones (the groups are placed explicitly), so that neither unit waits for
+    // the other.  Buffer j mod 3 is written again at step j + 2, after every wave passed the
+    // barrier of step j + 1 and so finished step j, its last reader.  A tile index past the
+    // last stands for the last tile (loaded, staged and scored again, never used), so the
+    // stretch does not branch on the count.  A zero scale makes every visible score 0 (the
+    // masked variant runs on every tile, and the softmax with scale 1), so the exponent's
+    // argument is never -inf * 0.
+    auto run_pipelined = [&](auto safe_c) {
+      constexpr bool SAFE = decltype(safe_c)::value;
+      if (ntiles <= 0) return;
+      const bool zero_scale = sl2 == 0.f;
+      const float sl2e = zero_scale ? 1.f : sl2;
+      auto tmap = [&](int k) { return tile_map(t_begin + min(k, ntiles - 1) * kTile); };
+      auto buf = [&](int k) { return lds + (k % 3) * S::LDS; };
+      // tiles 0 .. nwhole - 1 are full and every row sees all of their tokens
+      const int wl = min(pos_lo, t_end - 1) - t_begin - (kTile - 1);
+      const int nwhole = zero_scale ? 0 : (wl >= 0 ? min(ntiles, wl / kTile + 1) : 0);
+      constexpr int NQK = RB * 2 * NKC;                    // matrix instructions of one tile's scores
+      constexpr int NPV = RB * NJ;                         // of one tile's P.V (twice that for SAFE)
+      int tb[2][NT], to[2][NT];
+      f32x4 sA[RB][2], sB[RB][2];
+      float alpha[RB];
+      bool resc = false;
+      auto load_tile = [&](const int (&tbx)[NT], const int (&tox)[NT], u32x4 (&xk)[KL], u32x4 (&xv)[KL]) {
+        size_t off[NT];
+        offsets(tbx, tox, off);
+        load_rows(xk, p.k_cache, off);
+        load_rows(xv, p.v_cache, off);
+      };
+      auto scores = [&](f32x4 (&dst)[RB][2], const char* kb) {
+        qk_to(dst, [&](int h, int c) {
+          return *reinterpret_cast<const u32x4*>(kb + (16 * h + col) * S::KSTRIDE + chunk_of<DT, D>(c, grp) * 16);
+        });
+      };
+      // tile k's mask on raw scores: row b sees tile token u iff u < count and t0 + u <= pos[b]
+      // (a tile past the last sees nothing)
+      auto mask = [&](f32x4 (&sc)[RB][2], int k) {
+        const int t0 = t_begin + k * kTile;
+        const int cnt = min(kTile, t_end - t0);
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+          const int lim = min(pos[b] - t0, cnt - 1);
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              sc[b][h][i] = 16 * h + 4 * grp + i <= lim ? (zero_scale ? 0.f : sc[b][h][i]) : -__builtin_inff();
+        }
+      };
+      // a tile's row maxima: the reference of a row moves only when the tile exceeds it by
+      // more than kLazyMax, for every row of the wave at once (as in softmax_pv); alpha is
+      // then the factor for the accumulators and the running sums (exactly 1 otherwise)
+      auto maxima = [&](f32x4 (&sc)[RB][2]) {
+        float tmax[RB];
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+          float mx = fmaxf(fmaxf(fmaxf(sc[b][0][0], sc[b][0][1]), sc[b][0][2]), sc[b][0][3]);
+          mx = fmaxf(fmaxf(fmaxf(fmaxf(mx, sc[b][1][0]), sc[b][1][1]), sc[b][1][2]), sc[b][1][3]);
+          mx = max_over_groups(mx);
+          tmax[b] = fmaxf(m[b], mx * sl2e);
+        }
+        bool grow = false;
+#pragma unroll
+        for (int b = 0; b < RB; ++b) grow = grow || tmax[b] > m[b] + kLazyMax;
+        resc = __any(grow);
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+          const float mn = resc ? tmax[b] : m[b];
+          alpha[b] = fast_exp2(m[b] - mn);
+          m[b] = mn;
+        }
+      };
+      auto mfma16 = [&](const u32x4& x, const u32x4& y, const f32x4& c) {
+        if constexpr (DT == kBF16)
+          return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, x), __builtin_bit_cast(bf16x8, y), c, 0, 0, 0);
+        else
+          return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, x), __builtin_bit_cast(f16x8, y), c, 0, 0, 0);
+      };
+      u32x4 pb[RB], pb_lo[RB];
+      const uint32_t vlane = (4 * grp + (col >> 2)) * S::VSTRIDE + (4 * (col & 3)) * 2;
+      // One step.  The two products are written as chunks of one matrix instruction (two for
+      // the two-term P.V) and a share of the vector work, fenced so that the compiler keeps
+      // the order; the matrix unit runs each instruction while the vector unit works.
+      auto step = [&](auto mask_next_c, int k, f32x4 (&scur)[RB][2], f32x4 (&snext)[RB][2], u32x4 (&xk)[KL],
+                      u32x4 (&xv)[KL], const int (&tbl)[NT], const int (&tol)[NT], int (&tbf)[NT], int (&tof)[NT]) {
+        constexpr bool MASK_NEXT = decltype(mask_next_c)::value;
+        char* const bn = buf(k + 1);
+        fetch_table(tbf, tof, tmap(k + 4));
+        store_kv(safe_c, xk, xv, bn, bn + S::KBYTES);   // tile k + 1
+        __syncthreads();
+        if (resc) {
+#pragma unroll
+          for (int b = 0; b < RB; ++b)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) acc[b][j] *= alpha[b];
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        // Part 1: tile k + 1's scores, chunk i = (c, h, b), with tile k's weights.  The weights
+        // of a pair of scores take two half-steps: two exponentials, then the packing and the
+        // running sum.
+        // K fragments of step c are read one step ahead
+        u32x4 kf[2][NKC];
+        auto kread = [&](int c) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            kf[h][c] = *reinterpret_cast<const u32x4*>(bn + (16 * h + col) * S::KSTRIDE + chunk_of<DT, D>(c, grp) * 16);
+        };
+#pragma unroll
+        for (int b = 0; b < RB; ++b) snext[b][0] = snext[b][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        float pr[RB][8], ps[RB];
+        uint32_t pw[RB][4], pw_lo[RB][4];
+        auto weight_half = [&](int hs) {
+          const int pair = hs >> 1, b = pair >> 2, u = pair & 3;
+          const int h = u >> 1, i0 = 2 * (u & 1);
+          if ((hs & 1) == 0) {
+            if (u == 0) ps[b] = l[b] * alpha[b];
+            pr[b][2 * u] = fast_exp2(fmaf(scur[b][h][i0], sl2e, -m[b]));
+            pr[b][2 * u + 1] = fast_exp2(fmaf(scur[b][h][i0 + 1], sl2e, -m[b]));
+          } else if constexpr (!SAFE) {
+            const f16x2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
+            pw[b][u] = to_store2<kF16>(pr[b][2 * u], pr[b][2 * u + 1]);
+            ps[b] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pw[b][u]), one2, ps[b], false);
+          } else {
+            const uint32_t x = __float_as_uint(pr[b][2 * u]), y = __float_as_uint(pr[b][2 * u + 1]);
+            pw[b][u] = (x >> 16) | (y & 0xffff0000u);
+            pw_lo[b][u] = to_store2<kBF16>(pr[b][2 * u] - __uint_as_float(x & 0xffff0000u),
+                                           pr[b][2 * u + 1] - __uint_as_float(y & 0xffff0000u));
+            ps[b] += pr[b][2 * u] + pr[b][2 * u + 1];
+          }
+        };
+        constexpr int HS = RB * 8;                     // half-steps of the weights
+        constexpr int PER1 = (HS + NQK - 1) / NQK;
+#pragma unroll
+        for (int i = 0; i < NQK; ++i) {
+          const int c = i / (2 * RB), h = (i / RB) % 2, b = i % RB;
+          if (i == 0) kread(0);
+          if (i % (2 * RB) == 0 && c + 1 < NKC) kread(c + 1);
+          snext[b][h] = mfma16(kf[h][c], qf[b][c], snext[b][h]);
+#pragma unroll
+          for (int q = 0; q < PER1; ++q)
+            if (i * PER1 + q < HS) weight_half(i * PER1 + q);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int b = 0; b < RB; ++b) {
+          l[b] = ps[b];
+          pb[b] = u32x4{pw[b][0], pw[b][1], pw[b][2], pw[b][3]};
+          if constexpr (SAFE) pb_lo[b] = u32x4{pw_lo[b][0], pw_lo[b][1], pw_lo[b][2], pw_lo[b][3]};
+        }
+
+        // Part 2: tile k's P.V, chunk j = one head_dim block (every row block), with tile k + 1's
+        // mask (last tiles only), row maxima and settled references, and the loads of tile k + 3
+        // into the registers just staged.  V fragments are read two chunks ahead.
+        // one address register per step, so that the fragments' offsets stay immediates
+        uint32_t voff = (uint32_t)((k % 3) * S::LDS + S::KBYTES) + vlane;
+        asm volatile("" : "+v"(voff));
+        const char* vbase = lds + voff;
+        u32x4 vf[NJ];
+        auto vread = [&](int j) {
+          const s16x4 a0 = lds_read_tr16(vbase + 32 * j);
+          const s16x4 a1 = lds_read_tr16(vbase + 16 * S::VSTRIDE + 32 * j);
+          vf[j] = __builtin_bit_cast(u32x4, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        float mx[RB];
+        const int t1 = t_begin + (k + 1) * kTile;
+        constexpr int NMASK = MASK_NEXT ? RB : 0;
+        constexpr int NW = NMASK + 2 * RB + 1 + NT;   // pieces of vector work
+        auto work = [&](int w) {
+          if (w < NMASK) {                              // mask of row block w
+            const int b = w;
+            const int lim = min(pos[b] - t1, min(kTile, t_end - t1) - 1);
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                snext[b][h][i] = 16 * h + 4 * grp + i <= lim ? (zero_scale ? 0.f : snext[b][h][i]) : -__builtin_inff();
+          } else if (w < NMASK + RB) {                  // a row block's maximum over its lane
+            const int b = w - NMASK;
+            float x = fmaxf(fmaxf(fmaxf(snext[b][0][0], snext[b][0][1]), snext[b][0][2]), snext[b][0][3]);
+            mx[b] = fmaxf(fmaxf(fmaxf(fmaxf(x, snext[b][1][0]), snext[b][1][1]), snext[b][1][2]), snext[b][1][3]);
+          } else if (w < NMASK + 2 * RB) {              // ... and over the row's four lanes
+            const int b = w - NMASK - RB;
+            mx[b] = max_over_groups(mx[b]);
+          } else if (w == NMASK + 2 * RB) {             // settle the references (as in maxima)
+            float tmax[RB];
+            bool grow = false;
+#pragma unroll
+            for (int b = 0; b < RB; ++b) {
+              tmax[b] = fmaxf(m[b], mx[b] * sl2e);
+              grow = grow || tmax[b] > m[b] + kLazyMax;
+            }
+            resc = __any(grow);
+#pragma unroll
+            for (int b = 0; b < RB; ++b) {
+              const float mn = resc ? tmax[b] : m[b];
+              alpha[b] = fast_exp2(m[b] - mn);
+              m[b] = mn;
+            }
+          } else {                                      // one token's K and V rows of tile k + 3
+            const int t = w - NMASK - 2 * RB - 1;
+            int bk = tbl[t];
+            bk = bk < 0 ? 0 : (bk >= p.num_blocks ? p.num_blocks - 1 : bk);
+            const size_t off = ((size_t)bk * B + tol[t]) * slot_bytes + kv_off + my_chunk(0) * 16;
+            xk[t] = *reinterpret_cast<const u32x4*>((const char*)p.k_cache + off);
+            xv[t] = *reinterpret_cast<const u32x4*>((const char*)p.v_cache + off);
+          }
+        };
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+          if (j == 0) {
+#pragma unroll
+            for (int r = 0; r < 2 && r < NJ; ++r) vread(r);
+          }
+          if (j + 2 < NJ) vread(j + 2);
+#pragma unroll
+          for (int b = 0; b < RB; ++b) {
+            if constexpr (!SAFE) {   // fp16 V (stored or widened) and fp16 weights
+              acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, vf[j]),
+                                                                 __builtin_bit_cast(f16x8, pb[b]), acc[b][j], 0, 0, 0);
+            } else {
+              acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf[j]),
+                                                                  __builtin_bit_cast(bf16x8, pb[b]), acc[b][j], 0, 0, 0);
+              acc[b][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, vf[j]),
+                                                                  __builtin_bit_cast(bf16x8, pb_lo[b]), acc[b][j], 0, 0, 0);
+            }
+          }
+#pragma unroll
+          for (int w = j * NW / NJ; w < (j + 1) * NW / NJ; ++w) work(w);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      fetch_table(tb[0], to[0], tmap(0));
+      fetch_table(tb[1], to[1], tmap(1));
+      load_tile(tb[0], to[0], kr[0], vr[0]);
+      load_tile(tb[1], to[1], kr[1], vr[1]);
+      fetch_table(tb[0], to[0], tmap(2));
+      store_kv(safe_c, kr[0], vr[0], lds, lds + S::KBYTES);   // tile 0 -> buffer 0
+      __syncthreads();
+      load_tile(tb[0], to[0], kr[0], vr[0]);                    // tile 2
+      fetch_table(tb[1], to[1], tmap(3));
+      scores(sA, lds);
+      if (nwhole == 0) mask(sA, 0);
+      maxima(sA);
+      // whole tiles with a whole successor, in pairs; then the rest with masks
+      const int nfast = max(0, nwhole - 1) & ~1;
+      int k = 0;
+      for (; k < nfast; k += 2) {
+        step(std::false_type{}, k, sA, sB, kr[1], vr[1], tb[1], to[1], tb[0], to[0]);
+        step(std::false_type{}, k + 1, sB, sA, kr[0], vr[0], tb[0], to[0], tb[1], to[1]);
+      }
+      for (; k < ntiles; k += 2) {
+        step(std::true_type{}, k, sA, sB, kr[1], vr[1], tb[1], to[1], tb[0], to[0]);
+        if (k + 1 < ntiles) step(std::true_type{}, k + 1, sB, sA, kr[0], vr[0], tb[0], to[0], tb[1], to[1]);
+      }
+    };
+    auto run_tiles = [&](auto safe_c) {
+      if constexpr (!PIPE) {
+        run_plain(safe_c);
+      } else {
+        run_pipelined(safe_c);
       }
     };
     run_tiles(std::false_type{});
