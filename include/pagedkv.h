@@ -231,7 +231,9 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst_pa
  * Work is cut into (sequence, KV head, block of query rows, context
  * partition) items; with few items the context is split into partitions that
  * a second kernel merges, in a fixed order.  Head_dim 64 or 128; at most 64
- * query heads per KV head (PA_ERR_UNSUPPORTED above).  Errors as for pa_decode; index data violating the contract above
+ * query heads per KV head; a cache slot (num_kv_heads * head_dim elements)
+ * below 2^24 bytes and a block below 2^32 bytes (PA_ERR_UNSUPPORTED beyond
+ * these).  Errors as for pa_decode; index data violating the contract above
  * is clamped so that no access leaves the arrays, with unspecified results
  * (PA_DEBUG_CHECK=1 rejects it).  Results are deterministic.
  */

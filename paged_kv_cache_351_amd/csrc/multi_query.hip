@@ -424,11 +424,14 @@ void multi_query_kernel(MultiQueryParams p) {
   // tid % CR.  Tokens past a tile's count read its last valid token, so nothing outside
   // a sequence is read.  A token's block-table entry is fetched one step before its
   // rows, so that waiting for it never waits for the rows in flight.
-  constexpr int NT = SPLIT ? 2 : S::KLOADS;      // tokens per lane per tile
-  constexpr int CPT = SPLIT ? NKC : 1;           // 16-byte chunks per token
+  // (the pipelined loop: eight lanes per token, CR / 8 chunks each, so that a lane looks up
+  // one token per tile)
+  static_assert(!PIPE || CR % 8 == 0, "eight lanes per row");
+  constexpr int NT = SPLIT ? 2 : (PIPE ? 1 : S::KLOADS);      // tokens per lane per tile
+  constexpr int CPT = SPLIT ? NKC : (PIPE ? CR / 8 : 1);      // 16-byte chunks per token
   constexpr int KL = NT * CPT;
-  auto my_tok = [&](int k) { return SPLIT ? col + 16 * k : tid / CR + (256 / CR) * k; };
-  auto my_chunk = [&](int c) { return SPLIT ? chunk_of<DT, D>(c, grp) : tid % CR; };
+  auto my_tok = [&](int k) { return SPLIT ? col + 16 * k : (PIPE ? tid >> 3 : tid / CR + (256 / CR) * k); };
+  auto my_chunk = [&](int c) { return SPLIT ? chunk_of<DT, D>(c, grp) : (PIPE ? (tid & 7) + 8 * c : tid % CR); };
   const float inv_b = p.inv_block_size;
   const int log2_b = p.log2_block_size;
   // block-table entries (tb) and in-block offsets (to) of this lane's tokens of a tile
@@ -848,6 +851,8 @@ void multi_query_kernel(MultiQueryParams p) {
       };
       u32x4 pb[RB], pb_lo[RB];
       const uint32_t vlane = (4 * grp + (col >> 2)) * S::VSTRIDE + (4 * (col & 3)) * 2;
+      const uint32_t slot32 = (uint32_t)slot_bytes, blk32 = (uint32_t)(slot_bytes * B);
+      const uint32_t lane_kv = (uint32_t)kv_off + (uint32_t)my_chunk(0) * 16;
       // One step.  The two products are written as chunks of one matrix instruction (two for
       // the two-term P.V) and a share of the vector work, fenced so that the compiler keeps
       // the order; the matrix unit runs each instruction while the vector unit works.
@@ -967,13 +972,18 @@ void multi_query_kernel(MultiQueryParams p) {
               alpha[b] = fast_exp2(m[b] - mn);
               m[b] = mn;
             }
-          } else {                                      // one token's K and V rows of tile k + 3
+          } else {                                      // the lane's token of tile k + 3: K and V rows
             const int t = w - NMASK - 2 * RB - 1;
-            int bk = tbl[t];
-            bk = bk < 0 ? 0 : (bk >= p.num_blocks ? p.num_blocks - 1 : bk);
-            const size_t off = ((size_t)bk * B + tol[t]) * slot_bytes + kv_off + my_chunk(0) * 16;
-            xk[t] = *reinterpret_cast<const u32x4*>((const char*)p.k_cache + off);
-            xv[t] = *reinterpret_cast<const u32x4*>((const char*)p.v_cache + off);
+            const int bk = min(max(tbl[t], 0), p.num_blocks - 1);
+            // block * block bytes (one 32x32 -> 64-bit multiply-add) + slot row and chunk offset
+            // (block bytes < 2^32 and slot bytes < 2^24, checked by the host)
+            const uint32_t lo = __umul24((uint32_t)tol[t], slot32) + lane_kv;
+            const size_t off = (size_t)(uint32_t)bk * blk32 + lo;
+#pragma unroll
+            for (int c = 0; c < CPT; ++c) {
+              xk[t * CPT + c] = *reinterpret_cast<const u32x4*>((const char*)p.k_cache + off + 128 * c);
+              xv[t * CPT + c] = *reinterpret_cast<const u32x4*>((const char*)p.v_cache + off + 128 * c);
+            }
           }
         };
 #pragma unroll

@@ -108,6 +108,13 @@ pa_status pa_multi_query(const void* q, const void* k_cache, const void* v_cache
     return fail(PA_ERR_INVALID, "pa_multi_query: max_q_len %d above max_seq_len %d", max_q_len, max_seq_len);
   if ((long long)total_q * num_heads >= (1LL << 31))
     return fail(PA_ERR_UNSUPPORTED, "pa_multi_query: total_q * num_heads above 2^31");
+  {
+    // the shared-tile kernels address a cache block with 32-bit block and 24-bit row offsets
+    const long long row = (long long)num_kv_heads * head_dim * (dtype == PA_F32 ? 4 : 2);
+    if (row >= (1LL << 24) || row * block_size >= (1LL << 32))
+      return fail(PA_ERR_UNSUPPORTED, "pa_multi_query: %lld bytes per cache slot and %lld per block "
+                  "(at most 2^24 - 1 and 2^32 - 1)", row, row * block_size);
+  }
   if (num_seqs == 0 || total_q == 0 || max_q_len == 0) return PA_OK;
   if (!q || !k_cache || !v_cache || !block_tables || !seq_lens || !q_start || !out)
     return fail(PA_ERR_INVALID, "pa_multi_query: null pointer argument");
