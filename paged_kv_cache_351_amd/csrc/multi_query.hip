@@ -122,6 +122,20 @@ __device__ __forceinline__ float max_over_groups(float x) {
   return fmaxf(fmaxf(x, __uint_as_float(b[0])), __uint_as_float(b[1]));
 }
 
+// The same with the IEEE maximum (NaN-propagating, gfx950 v_maximum3_f32): no canonicalising
+// instruction before each maximum.  Used where a NaN score makes the row's result non-finite
+// either way.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float max_over_groups_nan(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = vmax(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return vmax(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float vmax8(const f32x4& a, const f32x4& b) {
+  return vmax(vmax(vmax(vmax(vmax(vmax(vmax(a[0], a[1]), a[2]), a[3]), b[0]), b[1]), b[2]), b[3]);
+}
+
 template <int DT>
 __device__ __forceinline__ uint16_t to_store(float x) {
   if constexpr (DT == kBF16) return __builtin_bit_cast(uint16_t, (__bf16)x);
@@ -792,7 +806,12 @@ void multi_query_kernel(MultiQueryParams p) {
       constexpr int NPV = RB * NJ;                         // of one tile's P.V (twice that for SAFE)
       int tb[2][NT], to[2][NT];
       f32x4 sA[RB][2], sB[RB][2];
-      float alpha[RB];
+      // running sums as matrix products (P times a block of ones), so they come out summed
+      // over the row's four lanes; the reference each row had before the last move
+      f32x4 lacc[RB];
+      float mprev[RB];
+#pragma unroll
+      for (int b = 0; b < RB; ++b) lacc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
       bool resc = false;
       auto load_tile = [&](const int (&tbx)[NT], const int (&tox)[NT], u32x4 (&xk)[KL], u32x4 (&xv)[KL]) {
         size_t off[NT];
@@ -820,28 +839,29 @@ void multi_query_kernel(MultiQueryParams p) {
               sc[b][h][i] = 16 * h + 4 * grp + i <= lim ? (zero_scale ? 0.f : sc[b][h][i]) : -__builtin_inff();
         }
       };
-      // a tile's row maxima: the reference of a row moves only when the tile exceeds it by
-      // more than kLazyMax, for every row of the wave at once (as in softmax_pv); alpha is
-      // then the factor for the accumulators and the running sums (exactly 1 otherwise)
-      auto maxima = [&](f32x4 (&sc)[RB][2]) {
+      // settle the references from the row maxima mx of a tile's raw scores: a row's reference
+      // moves only when the tile exceeds it by more than kLazyMax, for every row of the wave at
+      // once (as in softmax_pv); resc says whether they moved (mprev keeps the old ones)
+      auto settle = [&](const float (&mx)[RB]) {
         float tmax[RB];
-#pragma unroll
-        for (int b = 0; b < RB; ++b) {
-          float mx = fmaxf(fmaxf(fmaxf(sc[b][0][0], sc[b][0][1]), sc[b][0][2]), sc[b][0][3]);
-          mx = fmaxf(fmaxf(fmaxf(fmaxf(mx, sc[b][1][0]), sc[b][1][1]), sc[b][1][2]), sc[b][1][3]);
-          mx = max_over_groups(mx);
-          tmax[b] = fmaxf(m[b], mx * sl2e);
-        }
         bool grow = false;
 #pragma unroll
-        for (int b = 0; b < RB; ++b) grow = grow || tmax[b] > m[b] + kLazyMax;
+        for (int b = 0; b < RB; ++b) {
+          tmax[b] = vmax(m[b], mx[b] * sl2e);
+          grow = grow || tmax[b] > m[b] + kLazyMax;
+        }
         resc = __any(grow);
 #pragma unroll
         for (int b = 0; b < RB; ++b) {
-          const float mn = resc ? tmax[b] : m[b];
-          alpha[b] = fast_exp2(m[b] - mn);
-          m[b] = mn;
+          mprev[b] = m[b];
+          m[b] = resc ? tmax[b] : m[b];
         }
+      };
+      auto maxima = [&](f32x4 (&sc)[RB][2]) {
+        float mx[RB];
+#pragma unroll
+        for (int b = 0; b < RB; ++b) mx[b] = max_over_groups_nan(vmax8(sc[b][0], sc[b][1]));
+        settle(mx);
       };
       auto mfma16 = [&](const u32x4& x, const u32x4& y, const f32x4& c) {
         if constexpr (DT == kBF16)
@@ -853,6 +873,8 @@ void multi_query_kernel(MultiQueryParams p) {
       const uint32_t vlane = (4 * grp + (col >> 2)) * S::VSTRIDE + (4 * (col & 3)) * 2;
       const uint32_t slot32 = (uint32_t)slot_bytes, blk32 = (uint32_t)(slot_bytes * B);
       const uint32_t lane_kv = (uint32_t)kv_off + (uint32_t)my_chunk(0) * 16;
+      const u32x4 ones16 = {0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u};    // fp16 1.0
+      const u32x4 onesb16 = {0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u};   // bf16 1.0
       // One step.  The two products are written as chunks of one matrix instruction (two for
       // the two-term P.V) and a share of the vector work, fenced so that the compiler keeps
       // the order; the matrix unit runs each instruction while the vector unit works.
@@ -865,15 +887,17 @@ void multi_query_kernel(MultiQueryParams p) {
         __syncthreads();
         if (resc) {
 #pragma unroll
-          for (int b = 0; b < RB; ++b)
+          for (int b = 0; b < RB; ++b) {
+            const float alpha = fast_exp2(mprev[b] - m[b]);
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) acc[b][j] *= alpha[b];
+            for (int j = 0; j < NJ; ++j) acc[b][j] *= alpha;
+            lacc[b] *= alpha;
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
 
         // Part 1: tile k + 1's scores, chunk i = (c, h, b), with tile k's weights.  The weights
-        // of a pair of scores take two half-steps: two exponentials, then the packing and the
-        // running sum.
+        // of a pair of scores take two half-steps: two exponentials, then the packing.
         // K fragments of step c are read one step ahead
         u32x4 kf[2][NKC];
         auto kread = [&](int c) {
@@ -883,25 +907,21 @@ void multi_query_kernel(MultiQueryParams p) {
         };
 #pragma unroll
         for (int b = 0; b < RB; ++b) snext[b][0] = snext[b][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-        float pr[RB][8], ps[RB];
+        float pr[RB][8];
         uint32_t pw[RB][4], pw_lo[RB][4];
         auto weight_half = [&](int hs) {
           const int pair = hs >> 1, b = pair >> 2, u = pair & 3;
           const int h = u >> 1, i0 = 2 * (u & 1);
           if ((hs & 1) == 0) {
-            if (u == 0) ps[b] = l[b] * alpha[b];
             pr[b][2 * u] = fast_exp2(fmaf(scur[b][h][i0], sl2e, -m[b]));
             pr[b][2 * u + 1] = fast_exp2(fmaf(scur[b][h][i0 + 1], sl2e, -m[b]));
           } else if constexpr (!SAFE) {
-            const f16x2 one2 = {(_Float16)1.0f, (_Float16)1.0f};
             pw[b][u] = to_store2<kF16>(pr[b][2 * u], pr[b][2 * u + 1]);
-            ps[b] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pw[b][u]), one2, ps[b], false);
           } else {
             const uint32_t x = __float_as_uint(pr[b][2 * u]), y = __float_as_uint(pr[b][2 * u + 1]);
             pw[b][u] = (x >> 16) | (y & 0xffff0000u);
             pw_lo[b][u] = to_store2<kBF16>(pr[b][2 * u] - __uint_as_float(x & 0xffff0000u),
                                            pr[b][2 * u + 1] - __uint_as_float(y & 0xffff0000u));
-            ps[b] += pr[b][2 * u] + pr[b][2 * u + 1];
           }
         };
         constexpr int HS = RB * 8;                     // half-steps of the weights
@@ -919,7 +939,6 @@ void multi_query_kernel(MultiQueryParams p) {
         }
 #pragma unroll
         for (int b = 0; b < RB; ++b) {
-          l[b] = ps[b];
           pb[b] = u32x4{pw[b][0], pw[b][1], pw[b][2], pw[b][3]};
           if constexpr (SAFE) pb_lo[b] = u32x4{pw_lo[b][0], pw_lo[b][1], pw_lo[b][2], pw_lo[b][3]};
         }
@@ -952,26 +971,12 @@ void multi_query_kernel(MultiQueryParams p) {
                 snext[b][h][i] = 16 * h + 4 * grp + i <= lim ? (zero_scale ? 0.f : snext[b][h][i]) : -__builtin_inff();
           } else if (w < NMASK + RB) {                  // a row block's maximum over its lane
             const int b = w - NMASK;
-            float x = fmaxf(fmaxf(fmaxf(snext[b][0][0], snext[b][0][1]), snext[b][0][2]), snext[b][0][3]);
-            mx[b] = fmaxf(fmaxf(fmaxf(fmaxf(x, snext[b][1][0]), snext[b][1][1]), snext[b][1][2]), snext[b][1][3]);
+            mx[b] = vmax8(snext[b][0], snext[b][1]);
           } else if (w < NMASK + 2 * RB) {              // ... and over the row's four lanes
             const int b = w - NMASK - RB;
-            mx[b] = max_over_groups(mx[b]);
-          } else if (w == NMASK + 2 * RB) {             // settle the references (as in maxima)
-            float tmax[RB];
-            bool grow = false;
-#pragma unroll
-            for (int b = 0; b < RB; ++b) {
-              tmax[b] = fmaxf(m[b], mx[b] * sl2e);
-              grow = grow || tmax[b] > m[b] + kLazyMax;
-            }
-            resc = __any(grow);
-#pragma unroll
-            for (int b = 0; b < RB; ++b) {
-              const float mn = resc ? tmax[b] : m[b];
-              alpha[b] = fast_exp2(m[b] - mn);
-              m[b] = mn;
-            }
+            mx[b] = max_over_groups_nan(mx[b]);
+          } else if (w == NMASK + 2 * RB) {             // settle the references
+            settle(mx);
           } else {                                      // the lane's token of tile k + 3: K and V rows
             const int t = w - NMASK - 2 * RB - 1;
             const int bk = min(max(tbl[t], 0), p.num_blocks - 1);
@@ -1005,6 +1010,20 @@ void multi_query_kernel(MultiQueryParams p) {
                                                                   __builtin_bit_cast(bf16x8, pb_lo[b]), acc[b][j], 0, 0, 0);
             }
           }
+          if (j == NJ - 1) {                            // the running sums
+#pragma unroll
+            for (int b = 0; b < RB; ++b) {
+              if constexpr (!SAFE) {
+                lacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, ones16),
+                                                                 __builtin_bit_cast(f16x8, pb[b]), lacc[b], 0, 0, 0);
+              } else {
+                lacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, onesb16),
+                                                                  __builtin_bit_cast(bf16x8, pb[b]), lacc[b], 0, 0, 0);
+                lacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, onesb16),
+                                                                  __builtin_bit_cast(bf16x8, pb_lo[b]), lacc[b], 0, 0, 0);
+              }
+            }
+          }
 #pragma unroll
           for (int w = j * NW / NJ; w < (j + 1) * NW / NJ; ++w) work(w);
           __builtin_amdgcn_sched_barrier(0);
@@ -1033,6 +1052,9 @@ void multi_query_kernel(MultiQueryParams p) {
         step(std::true_type{}, k, sA, sB, kr[1], vr[1], tb[1], to[1], tb[0], to[0]);
         if (k + 1 < ntiles) step(std::true_type{}, k + 1, sB, sA, kr[0], vr[0], tb[0], to[0], tb[1], to[1]);
       }
+      // every element of a running-sum block holds the row's whole sum
+#pragma unroll
+      for (int b = 0; b < RB; ++b) l[b] = lacc[b][0];
     };
     auto run_tiles = [&](auto safe_c) {
       if constexpr (!PIPE) {
@@ -1076,8 +1098,10 @@ void multi_query_kernel(MultiQueryParams p) {
   // each row's sum over its four lanes; lane (grp, col) holds head_dim 16 j + 4 grp + i
 #pragma unroll
   for (int b = 0; b < RB; ++b) {
-    l[b] += __shfl_xor(l[b], 16);
-    l[b] += __shfl_xor(l[b], 32);
+    if constexpr (!PIPE) {   // (the pipelined loop's sums are whole already)
+      l[b] += __shfl_xor(l[b], 16);
+      l[b] += __shfl_xor(l[b], 32);
+    }
   }
   if constexpr (SPLIT) {
     // merge the four waves' results for the same 16 rows: wave w's (m, l) and
