@@ -809,7 +809,6 @@ void multi_query_kernel(MultiQueryParams p) {
       // running sums as matrix products (P times a block of ones), so they come out summed
       // over the row's four lanes; the reference each row had before the last move
       f32x4 lacc[RB];
-      float mprev[RB];
 #pragma unroll
       for (int b = 0; b < RB; ++b) lacc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
       bool resc = false;
@@ -839,29 +838,33 @@ void multi_query_kernel(MultiQueryParams p) {
               sc[b][h][i] = 16 * h + 4 * grp + i <= lim ? (zero_scale ? 0.f : sc[b][h][i]) : -__builtin_inff();
         }
       };
-      // settle the references from the row maxima mx of a tile's raw scores: a row's reference
-      // moves only when the tile exceeds it by more than kLazyMax, for every row of the wave at
-      // once (as in softmax_pv); resc says whether they moved (mprev keeps the old ones)
-      auto settle = [&](const float (&mx)[RB]) {
-        float tmax[RB];
+      // A row's reference moves only when a tile's scores exceed it by more than kLazyMax,
+      // and then for every row of the wave at once (as in softmax_pv).  The test needs only
+      // each lane's own maximum lmx: any lane over the bound sets resc for the wave.  The
+      // moves (the maxima over each row's four lanes, new references, rescaled accumulators)
+      // happen in the rare branch at the start of the next step, before the tile's weights.
+      float lmx[RB];
+      auto test_grow = [&]() {
         bool grow = false;
 #pragma unroll
-        for (int b = 0; b < RB; ++b) {
-          tmax[b] = vmax(m[b], mx[b] * sl2e);
-          grow = grow || tmax[b] > m[b] + kLazyMax;
-        }
+        for (int b = 0; b < RB; ++b) grow = grow || lmx[b] * sl2e > m[b] + kLazyMax;
         resc = __any(grow);
+      };
+      auto move_refs = [&]() {
 #pragma unroll
         for (int b = 0; b < RB; ++b) {
-          mprev[b] = m[b];
-          m[b] = resc ? tmax[b] : m[b];
+          const float mn = vmax(m[b], max_over_groups_nan(lmx[b]) * sl2e);
+          const float alpha = fast_exp2(m[b] - mn);
+          m[b] = mn;
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) acc[b][j] *= alpha;
+          lacc[b] *= alpha;
         }
       };
       auto maxima = [&](f32x4 (&sc)[RB][2]) {
-        float mx[RB];
 #pragma unroll
-        for (int b = 0; b < RB; ++b) mx[b] = max_over_groups_nan(vmax8(sc[b][0], sc[b][1]));
-        settle(mx);
+        for (int b = 0; b < RB; ++b) lmx[b] = vmax8(sc[b][0], sc[b][1]);
+        test_grow();
       };
       auto mfma16 = [&](const u32x4& x, const u32x4& y, const f32x4& c) {
         if constexpr (DT == kBF16)
@@ -885,15 +888,7 @@ void multi_query_kernel(MultiQueryParams p) {
         fetch_table(tbf, tof, tmap(k + 4));
         store_kv(safe_c, xk, xv, bn, bn + S::KBYTES);   // tile k + 1
         __syncthreads();
-        if (resc) {
-#pragma unroll
-          for (int b = 0; b < RB; ++b) {
-            const float alpha = fast_exp2(mprev[b] - m[b]);
-#pragma unroll
-            for (int j = 0; j < NJ; ++j) acc[b][j] *= alpha;
-            lacc[b] *= alpha;
-          }
-        }
+        if (resc) move_refs();
         __builtin_amdgcn_sched_barrier(0);
 
         // Part 1: tile k + 1's scores, chunk i = (c, h, b), with tile k's weights.  The weights
@@ -956,10 +951,9 @@ void multi_query_kernel(MultiQueryParams p) {
           const s16x4 a1 = lds_read_tr16(vbase + 16 * S::VSTRIDE + 32 * j);
           vf[j] = __builtin_bit_cast(u32x4, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
         };
-        float mx[RB];
         const int t1 = t_begin + (k + 1) * kTile;
         constexpr int NMASK = MASK_NEXT ? RB : 0;
-        constexpr int NW = NMASK + 2 * RB + 1 + NT;   // pieces of vector work
+        constexpr int NW = NMASK + RB + 1 + NT;       // pieces of vector work
         auto work = [&](int w) {
           if (w < NMASK) {                              // mask of row block w
             const int b = w;
@@ -971,14 +965,11 @@ void multi_query_kernel(MultiQueryParams p) {
                 snext[b][h][i] = 16 * h + 4 * grp + i <= lim ? (zero_scale ? 0.f : snext[b][h][i]) : -__builtin_inff();
           } else if (w < NMASK + RB) {                  // a row block's maximum over its lane
             const int b = w - NMASK;
-            mx[b] = vmax8(snext[b][0], snext[b][1]);
-          } else if (w < NMASK + 2 * RB) {              // ... and over the row's four lanes
-            const int b = w - NMASK - RB;
-            mx[b] = max_over_groups_nan(mx[b]);
-          } else if (w == NMASK + 2 * RB) {             // settle the references
-            settle(mx);
+            lmx[b] = vmax8(snext[b][0], snext[b][1]);
+          } else if (w == NMASK + RB) {                 // does any reference have to move?
+            test_grow();
           } else {                                      // the lane's token of tile k + 3: K and V rows
-            const int t = w - NMASK - 2 * RB - 1;
+            const int t = w - NMASK - RB - 1;
             const int bk = min(max(tbl[t], 0), p.num_blocks - 1);
             // block * block bytes (one 32x32 -> 64-bit multiply-add) + slot row and chunk offset
             // (block bytes < 2^32 and slot bytes < 2^24, checked by the host)
