@@ -954,7 +954,9 @@ void multi_query_kernel(MultiQueryParams p) {
         const int t1 = t_begin + (k + 1) * kTile;
         constexpr int NMASK = MASK_NEXT ? RB : 0;
         constexpr int NW = NMASK + RB + 1 + NT;       // pieces of vector work
-        auto work = [&](int w) {
+        auto work = [&](int w0) {
+          // the loads first, so that they have most of a step more to arrive
+          const int w = w0 < NT ? NMASK + RB + 1 + w0 : w0 - NT;
           if (w < NMASK) {                              // mask of row block w
             const int b = w;
             const int lim = min(pos[b] - t1, min(kTile, t_end - t1) - 1);
@@ -1027,8 +1029,11 @@ void multi_query_kernel(MultiQueryParams p) {
       fetch_table(tb[0], to[0], tmap(2));
       store_kv(safe_c, kr[0], vr[0], lds, lds + S::KBYTES);   // tile 0 -> buffer 0
       __syncthreads();
-      load_tile(tb[0], to[0], kr[0], vr[0]);                    // tile 2
+      // tile 3's table entries before tile 2's rows: the order of a step (table entries of
+      // tile k + 4 before the rows of tile k + 3), so that the waits the compiler places at the
+      // loop head, which must hold for the first entry too, wait only for what a step needs
       fetch_table(tb[1], to[1], tmap(3));
+      load_tile(tb[0], to[0], kr[0], vr[0]);                    // tile 2
       scores(sA, lds);
       if (nwhole == 0) mask(sA, 0);
       maxima(sA);
