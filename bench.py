@@ -333,9 +333,11 @@ def cpu_baseline(b, gpu_out, time_cap=25.0):
             "max_abs_err_gpu_vs_oracle": err, **split.report(b.dtype)}
 
 
-def cpu_baseline_multi_query(b, gpu_out, time_cap=25.0):
+def cpu_baseline_multi_query(b, gpu_out, flops_unit=False, time_cap=25.0):
     """The float64 oracle on the host for a multi-query step: the write of the new tokens, then
-    attention for the workload's sequences in order until done or the time cap is reached."""
+    attention for the workload's sequences in order until done or the time cap is reached.  The
+    rate is in the workload's metric: GB/s of K/V, or (flops_unit) causal TFLOP/s, 4 x pairs x
+    heads x head_dim over the sequences done."""
     import oracle
     from workloads import as_numpy
     try:
@@ -347,10 +349,12 @@ def cpu_baseline_multi_query(b, gpu_out, time_cap=25.0):
     t0 = time.time()
     kc, vc = oracle.write_kv(as_numpy(b.new_k), as_numpy(b.new_v), as_numpy(b.slot_mapping),
                              as_numpy(b.k_cache), as_numpy(b.v_cache))
-    done, err, kv = 0, 0.0, 0
+    done, err, kv, pairs = 0, 0.0, 0, 0
     split = ErrSplit()
     while done < b.num_seqs and time.time() - t0 < time_cap:
         a, z = qs[done], qs[done + 1]
+        n, L = z - a, int(lens[done])
+        pairs += n * (L - n) + n * (n + 1) // 2
         ref = oracle.paged_multi_query(q[a:z], kc, vc, bt[done:done + 1], lens[done:done + 1],
                                        np.array([0, z - a]), b.scale, b.dtype)
         err = max(err, float(np.abs(gpu_out[a:z] - ref).max()))
@@ -358,7 +362,11 @@ def cpu_baseline_multi_query(b, gpu_out, time_cap=25.0):
         kv += int(lens[done]) * b.num_kv_heads * b.head_dim * 2 * 2
         done += 1
     wall = time.time() - t0
-    return {"value": kv / wall / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+    if flops_unit:
+        rate = {"value": 4.0 * pairs * b.num_heads * b.head_dim / wall / 1e12, "unit": "TFLOP/s"}
+    else:
+        rate = {"value": kv / wall / 1e9, "unit": "GB/s"}
+    return {**rate, "cores": threads, "kind": "oracle",
             "sample": f"write of all {len(b.slot_mapping)} new tokens, then the queries of the first "
                       f"{done} of {b.num_seqs} sequences of the same workload (numpy float64)",
             "seqs_per_s": done / wall, "wall_s": wall, "host_cpus": len(os.sched_getaffinity(0)),
@@ -665,7 +673,8 @@ def main():
         log("cpu baseline: float64 oracle on the host")
         torch.cuda.synchronize()
         gpu_out = out.float().cpu().double().numpy()
-        res["cpu_baseline"] = (cpu_baseline_multi_query(b, gpu_out) if multi else cpu_baseline(b, gpu_out))
+        res["cpu_baseline"] = (cpu_baseline_multi_query(b, gpu_out, flops_unit=args.workload.endswith("chunk"))
+                               if multi else cpu_baseline(b, gpu_out))
     print(json.dumps(res))
 
 
