@@ -181,6 +181,10 @@ def call_mq(pk, **over):
     (dict(ws=None, wsb=1 << 30), 3, "workspace"),
     (dict(BS=0), 1, "block_size"),
     (dict(H=65, HKV=1), 2, "at most 64"),
+    # a cache slot of 2^24 bytes, or a block of 2^32 bytes (the kernels' 24-bit row and 32-bit
+    # block offsets)
+    (dict(H=65536, HKV=65536), 2, "per cache slot"),
+    (dict(H=8192, HKV=8192, BS=2048, MB=16), 2, "per cache slot"),
 ])
 def test_multi_query_rejects_host_visible_errors(pk, over, status, words):
     assert call_mq(pk, **over) == status

@@ -122,6 +122,21 @@ def test_long_context_few_queries_uses_partitions():
     assert_close(out.float().cpu().double().numpy(), run_oracle(b), "bf16", "partitions")
 
 
+@pytest.mark.parametrize("dtype,B,scale", [("bf16", 16, None), ("f16", 7, None), ("bf16", 16, 0.0)])
+def test_long_context_many_queries_partitions_on_shared_tiles(dtype, B, scale):
+    # one sequence of 5000 tokens whose last 40 are queries, 4 heads per KV head: 160 rows per
+    # KV head, so the shared-tile loop runs (two 128-row blocks), and with 4 items the context
+    # of each is cut into partitions; the masked last tiles fall inside the last partition
+    b = batch(8, dtype, [5000], [40], 8, 2, 128, B)
+    if scale is not None:
+        b.scale = scale
+    m = pk()
+    assert m.pa_multi_query_workspace_size(1, 40, 8, 2, 128, 40, 5000) > 0
+    log(f"partitioned shared tiles {dtype} B={B} scale={b.scale}")
+    out, _ = run_gpu(b)
+    assert_close(out.float().cpu().double().numpy(), run_oracle(b), dtype, "partitions, shared tiles")
+
+
 def test_one_query_per_sequence_matches_decode():
     b = batch(9, "bf16", [1, 17, 300, 1000, 64, 2], [1] * 6, 32, 8, 128, 16)
     m = pk()
