@@ -13,34 +13,37 @@
 //
 // Work decomposition
 //   A workgroup (4 waves) owns one (sequence, KV head, query block, context
-//   partition).  A query block is 64 rows: up to floor(64 / g) consecutive query
-//   tokens times the g query heads of the KV head's group, row = token * g +
-//   head; wave w computes rows 16w .. 16w+15.  The context up to the block's
-//   last query position is cut into `parts` equal partitions of whole tiles.  With one
-//   partition the workgroup writes the output; otherwise it leaves (m, l, acc)
-//   per row and a second kernel merges the partitions in order.  Workgroups are
-//   numbered so that every query block and partition of one (sequence, KV head)
-//   runs on the same XCD (workgroup id mod 8), where they share its L2, and
-//   consecutive (sequence, KV head) units run on different XCDs.
+//   partition).  A query block is 16 rows (the split variant below), 64 rows (16
+//   per wave) or 128 rows (32 per wave, two row blocks of 16): consecutive query
+//   tokens times the g query heads of the KV head's group, row = token * g + head.
+//   The context up to the block's last query position is cut into `parts` equal
+//   partitions of whole tiles.  With one partition the workgroup writes the output;
+//   otherwise it leaves (m, l, acc) per row and a second kernel merges the
+//   partitions in order.  Workgroups are numbered so that every query block and
+//   partition of one (sequence, KV head) runs on the same XCD (workgroup id mod 8),
+//   where they share its L2, and consecutive (sequence, KV head) units run on
+//   different XCDs.
 //
 // Per tile of 32 tokens
-//   All 256 lanes load the tile's K and V rows (16 bytes per load, token ->
-//   block through the table, table entries one step earlier than the rows) two
-//   tiles ahead in registers and store them to LDS as [token][head_dim] rows.
-//   Then each wave, on the matrix cores:
+//   The tile's K and V rows (16 bytes per load, token -> block through the table,
+//   table entries one step earlier than the rows) are loaded ahead into registers
+//   and stored to LDS as [token][head_dim] rows.  Then each wave, on the matrix
+//   cores:
 //     S^T = K Q^T   v_mfma_f32_16x16x32_{bf16,f16} (16x16x4_f32 for fp32): A = K
 //                   rows of one 16-token half, B = the wave's 16 query rows, both
 //                   cut into the same head_dim chunks; lane (grp, col) gets the
 //                   scores of tokens 16 h + 4 grp + i, i = 0..3, for row col.
-//     online softmax per row: the row's maximum over the four lanes (grp 0..3)
-//                   that hold it, exponentials in base 2, the running sum kept
-//                   per lane (the four partial sums are added at the end).
+//     online softmax per row: exponentials in base 2 against a reference maximum
+//                   that moves only when a tile exceeds it by 2^8.
 //     O^T += V^T P^T with A = V^T (16 head_dim rows x 32 slots) and B = P^T:
 //                   slot 8 grp + 4 h + i stands for token 16 h + 4 grp + i, so
 //                   lane (grp, col) holds P for slots 8 grp .. 8 grp + 7, exactly
 //                   the tokens whose scores it computed, and the scores never move
 //                   between lanes.  The LDS transpose read (ds_read_b64_tr_b16)
 //                   turns the [token][head_dim] V rows into the A fragments.
+//   Shared tiles of 16-bit types run a pipelined loop: tile k + 1's scores are
+//   computed while tile k's weights are formed, in explicitly interleaved chunks of
+//   matrix and vector instructions (see run_pipelined).
 //   P enters the second product in a 16-bit type.  fp16 data: P rounded to fp16
 //   (11 significant bits).  bf16 data with shared tiles (prefill-sized blocks): V
 //   is staged in LDS as fp16 (exact for |v| < 2^16) and P rounded to fp16, one
@@ -49,7 +52,8 @@
 //   the two-term P below (so every finite input is handled, the common case at one
 //   product per tile instead of two).  bf16 data in the split variant: P split into
 //   two bf16 terms (about 16 significant bits) fed to two products.  fp32 stays
-//   fp32.  The running sum adds the values used (for two-term bf16 the fp32
+//   fp32.  The running sum adds the weights used (in the pipelined loop as a matrix
+//   product of P with a block of ones; elsewhere, for two-term bf16, the fp32
 //   values, within 2^-16 of the two terms), so the output is a weighted mean with
 //   the weights used.  Scores stay raw until the exponent, p = 2^(s * |scale|
 //   log2 e - m) in one fused multiply-add (a negative scale is folded into q's
