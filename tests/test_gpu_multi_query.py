@@ -93,6 +93,31 @@ def test_shape_sweep(case):
     assert_close(out.float().cpu().double().numpy(), run_oracle(b), dt, f"sweep {case}")
 
 
+def _random_shared_tile_case(seed):
+    # a seeded draw of shapes that take the shared-tile (pipelined for 16-bit types) path:
+    # more than 16 rows per (sequence, KV head) in the longest sequence
+    r = np.random.default_rng(seed)
+    dt = ["bf16", "f16", "bf16", "f16", "f32"][seed % 5]
+    D = int(r.choice([64, 128]))
+    g = int(r.choice([1, 2, 4, 8]))
+    Hkv = int(r.choice([1, 2, 4]))
+    B = int(r.choice([4, 5, 8, 11, 16, 32]))
+    n = int(r.integers(1, 5))
+    queries = [int(r.integers(0, 90)) for _ in range(n)]
+    queries[int(r.integers(0, n))] = int(r.integers(max(17, 17 // g + 1), 150))   # one long chunk
+    lens = [q + int(r.integers(0, 400)) for q in queries]
+    return dt, D, B, g * Hkv, Hkv, lens, queries
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_shared_tile_shapes(seed):
+    dt, D, B, Hq, Hkv, lens, qn = _random_shared_tile_case(seed)
+    b = batch(300 + seed, dt, lens, qn, Hq, Hkv, D, B)
+    log(f"random shared-tile case {seed}: {dt} D={D} B={B} Hq={Hq} Hkv={Hkv} lens={lens} queries={qn}")
+    out, _ = run_gpu(b)
+    assert_close(out.float().cpu().double().numpy(), run_oracle(b), dt, f"random case {seed}")
+
+
 @pytest.mark.parametrize("dtype,scale,queries", [
     ("bf16", -0.09, [4, 2, 1]),     # at most 16 rows per (sequence, KV head): split variant
     ("bf16", -0.09, [40, 70, 1]),   # shared-tile variant
