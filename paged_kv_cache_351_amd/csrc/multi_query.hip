@@ -783,14 +783,14 @@ void multi_query_kernel(MultiQueryParams p) {
       }
     };
     // Pipelined loop (16-bit types), three LDS buffers.  Entering step k, tile k's scores
-    // are in registers (masked if it needs a mask), its rows' reference maxima are settled
-    // and `resc` says whether they moved.  Step k fetches the table entries of tile k + 4,
-    // stages tile k + 1 in buffer (k + 1) mod 3 and passes one barrier; rescales the
-    // accumulators if `resc` (rare); then one branch-free stretch: tile k + 1's scores on
-    // the matrix cores, tile k's weights, tile k's P.V, tile k + 1's mask (last tiles only)
-    // and row maxima, and the loads of tile k + 3, with the matrix instructions spread among
-    // the vector ones (the groups are placed explicitly), so that neither unit waits for
-    // the other.  Buffer j mod 3 is written again at step j + 2, after every wave passed the
+    // are in registers (masked if it needs a mask) and `resc` says whether some row's
+    // reference must move for them.  Step k fetches the table entries of tile k + 4, stages
+    // tile k + 1 in buffer (k + 1) mod 3 and passes one barrier; moves the references and
+    // rescales the accumulators if `resc` (rare); then two branch-free stretches: tile k + 1's
+    // scores with tile k's weights, and tile k's P.V with the loads of tile k + 3, tile
+    // k + 1's mask (last tiles only) and its lanes' maxima, each matrix instruction followed
+    // by a share of the vector work, so that the matrix unit runs while the vector unit
+    // works.  Buffer j mod 3 is written again at step j + 2, after every wave passed the
     // barrier of step j + 1 and so finished step j, its last reader.  A tile index past the
     // last stands for the last tile (loaded, staged and scored again, never used), so the
     // stretch does not branch on the count.  A zero scale makes every visible score 0 (the
@@ -807,11 +807,10 @@ void multi_query_kernel(MultiQueryParams p) {
       const int wl = min(pos_lo, t_end - 1) - t_begin - (kTile - 1);
       const int nwhole = zero_scale ? 0 : (wl >= 0 ? min(ntiles, wl / kTile + 1) : 0);
       constexpr int NQK = RB * 2 * NKC;                    // matrix instructions of one tile's scores
-      constexpr int NPV = RB * NJ;                         // of one tile's P.V (twice that for SAFE)
       int tb[2][NT], to[2][NT];
       f32x4 sA[RB][2], sB[RB][2];
       // running sums as matrix products (P times a block of ones), so they come out summed
-      // over the row's four lanes; the reference each row had before the last move
+      // over the row's four lanes
       f32x4 lacc[RB];
 #pragma unroll
       for (int b = 0; b < RB; ++b) lacc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
