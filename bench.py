@@ -1,8 +1,10 @@
 """Benchmark: paged decode attention on one MI355X, Llama-3-8B-shaped GQA layer.
 
-One step = pa_write_kv of 256 new tokens (one per sequence) followed by pa_decode
-over all 256 sequences (decode kernel + merge kernel), on one stream, with every
-input already resident in HBM.  Workload: 256 sequences, 32 query / 8 KV heads,
+One step = the write of 256 new tokens (one per sequence, at its newest position) and
+the decode over all 256 sequences, as one pa_decode_append call (decode kernel + merge
+kernel), on one stream, with every input already resident in HBM.  ``--unfused`` runs
+them as two calls, pa_write_kv then pa_decode; the default line also times that form
+(``write_plus_decode_ms_per_step``).  Workload: 256 sequences, 32 query / 8 KV heads,
 head_dim 128, bf16 KV and q, fp32 accumulation, block size 16, lengths uniform in
 [512, 4096] (seed 0), 70,000-block pool with random block placement.
 --workload picks one of the other workloads instead (its step also runs its block
@@ -10,8 +12,9 @@ copies, if any, before the write).
 
 Prints ONE JSON line.  ``value`` is the K/V bytes the decode step must read
 (each (token, KV head) row of K and V once) divided by the wall time per step of K
-back-to-back steps; ``step_us`` gives the median / p10 / p90 of the same steps from HIP
-events.  ``roofline`` reports the decode call alone: K further calls, each preceded by
+back-to-back steps, timed with no event between them; ``step_us`` gives the median / p10 /
+p90 of K steps from HIP events around each one, run before them (``events_ms_per_step`` is
+their wall time: an event record costs GPU time of its own).  ``roofline`` reports the decode call alone: K further calls, each preceded by
 an untimed read of a 1 GiB buffer that evicts the caches (L2 and the 256 MiB Infinity
 Cache; a read leaves no dirty lines to write back), timed with HIP events on the stream
 it runs on; ``achieved`` uses the median.  ``cache_ops`` times pa_write_kv (the step's
@@ -388,6 +391,18 @@ def unique_kv_bytes(b):
     return sum(slots.values()) * b.num_kv_heads * b.head_dim * 2 * esize
 
 
+def write_is_newest(b):
+    """True when the step's write stores one token per sequence, at its position L - 1 (the
+    slot the block table gives that position), so write and decode can run as one call."""
+    if b.slot_mapping is None or len(b.slot_mapping) != b.num_seqs:
+        return False
+    B = b.block_size
+    for s, L in enumerate(b.seq_lens.tolist()):
+        if L < 1 or int(b.slot_mapping[s]) != int(b.block_tables[s, (L - 1) // B]) * B + (L - 1) % B:
+            return False
+    return True
+
+
 def cache_op_lines(dev, stream, K, flush, nk, nv, slots, kc, vc):
     """pa_write_kv of the step's new tokens, and pa_copy_blocks of 224 copy-on-write pairs of
     OPT-13B-shaped blocks (16 tokens x 40 KV heads x 128, fp16: 160 KiB per block per pool),
@@ -472,6 +487,9 @@ def main():
                          "of the same study, measured the same way")
     ap.add_argument("--block-size", type=int, default=16, choices=[8, 16, 32],
                     help="block size of the llama2_70b workload")
+    ap.add_argument("--unfused", action="store_true",
+                    help="run the step's write and decode as two calls (pa_write_kv, pa_decode) "
+                         "instead of one pa_decode_append")
     ap.add_argument("--graph", action="store_true",
                     help="time the step as replays of a HIP graph captured once (the roofline "
                          "still times the eager decode call)")
@@ -534,19 +552,31 @@ def main():
     else:
         ws = pk.decode_workspace(q, b.num_kv_heads, max_len)
 
-        def attend():
+        def decode():
             pk.pa_decode(q, kc, vc, bt, lens, b.num_kv_heads, b.scale, out, max_seq_len=max_len,
                          workspace=ws)
 
-    def step(ev0=None, ev1=None):
+        def decode_append():
+            pk.pa_decode_append(q, nk, nv, kc, vc, bt, lens, b.num_kv_heads, b.scale, out,
+                                max_seq_len=max_len, workspace=ws)
+        attend = decode
+    # A step whose write stores exactly each sequence's newest token (position L - 1) runs
+    # write and decode as one pa_decode_append, unless --unfused.
+    fused = (not multi and not shared and has_write and not args.unfused
+             and write_is_newest(b))
+    two_calls = None
+    if fused:
+        attend, two_calls = decode_append, decode
+
+    def step(ev0=None, ev1=None, unfused=False):
         # copies and writes are idempotent, so every step repeats the same state change
         if pairs is not None:
             pk.pa_copy_blocks(kc, vc, pairs)
-        if has_write:
+        if has_write and (unfused or not fused):
             pk.pa_write_kv(nk, nv, slots, kc, vc)
         if ev0 is not None:
             ev0.record(stream)
-        attend()
+        (two_calls if unfused else attend)()
         if ev1 is not None:
             ev1.record(stream)
 
@@ -556,19 +586,46 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
+    # The per-step spread first: K steps with HIP events around each step and its attention
+    # call.  They also carry the GPU past its first ~20 ms of this kernel, which run slower
+    # than the steady state (the first 20 steps after 5 warm-up steps take about 7 µs more
+    # each than every later 20).  An event record takes GPU time of its own (a few µs
+    # each), so the wall-clock steps below run without them.
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
            torch.cuda.Event(enable_timing=True)) for _ in range(K)]
-    log(f"timing {K} steps")
+    log(f"timing {K} steps with events")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
         ev[i][0].record(stream)
         step(ev[i][1], ev[i][2])
     torch.cuda.synchronize()
-    total = time.perf_counter() - t0
+    events_total = time.perf_counter() - t0
     step_ms = [a.elapsed_time(z) for a, _, z in ev]          # whole step, back to back
     call_ms_warm = [a.elapsed_time(z) for _, a, z in ev]     # its attention call
+
+    log(f"timing {K} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    total = time.perf_counter() - t0
     eager_total = total
+
+    unfused_total = None
+    if fused:
+        # the same step as two calls (pa_write_kv, then pa_decode), for comparison; its
+        # kernels are warmed up first like the step's
+        for _ in range(args.warmup):
+            step(unfused=True)
+        log(f"timing {K} steps as write + decode")
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(K):
+            step(unfused=True)
+        torch.cuda.synchronize()
+        unfused_total = time.perf_counter() - t0
 
     # the roofline leg: the attention call alone, K times, each after an untimed read of
     # 1 GiB that evicts L2 and the Infinity Cache (the step's write and copies are done,
@@ -619,9 +676,18 @@ def main():
         "pct_of_hbm_peak": 100.0 * value / HBM_PEAK_GBS,
         "step_mode": "graph" if args.graph else "eager",
         "eager_ms_per_step": eager_total * 1e3 / K,
+        "events_ms_per_step": events_total * 1e3 / K,
+        "timing_order": (f"{args.warmup} warm-up steps; {K} steps with events (step_us); {K} "
+                         "wall-clock steps (value)" + (f"; {K} write + decode steps" if fused else "")
+                         + f"; {K} flushed calls (roofline)"),
+        "step_calls": ("pa_decode_append" if fused else
+                       ("pa_write_kv + " if has_write else "") + ("pa_multi_query" if multi else
+                       "pa_decode_shared_prefix" if shared else "pa_decode")),
+        "write_plus_decode_ms_per_step": unfused_total * 1e3 / K if fused else None,
         "seqs_per_s": b.num_seqs / (total / K),
         "step_us": pct(step_ms),
-        "roofline": {"kernel": "pa_decode (decode_kernel + reduce_kernel)", "bound": "hbm",
+        "roofline": {"kernel": ("pa_decode_append" if fused else "pa_decode") +
+                               " (decode_kernel + reduce_kernel)", "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": kv_bytes,

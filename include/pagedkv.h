@@ -64,7 +64,7 @@ typedef enum {
   PA_ERR_NO_BLOCKS = 5    /* block manager: the pool has no free block left */
 } pa_status;
 
-/* Library ABI version (incremented on any signature change). */
+/* Library ABI version (incremented on any signature change or new entry point). */
 int pa_version(void);
 
 /* Message for the last non-PA_OK status returned on the calling thread
@@ -185,6 +185,41 @@ pa_status pa_write_kv(const void* k, const void* v, const int32_t* slot_mapping,
                       void* k_cache, void* v_cache, int num_tokens,
                       int num_kv_heads, int head_dim, int block_size,
                       int num_blocks, pa_dtype dtype, void* stream);
+
+/*
+ * pa_decode_append -- the append and the decode of one step in one call: each
+ * sequence's newest token (position L - 1, already counted in seq_lens) is stored
+ * into its slot, and then every sequence is decoded as by pa_decode.
+ *
+ * Results are bit-identical to pa_write_kv(new_k, new_v, slots) followed by
+ * pa_decode with the same arguments, where slots[s] is the slot the block table
+ * assigns to position L - 1 of sequence s: block_tables[s][(L-1) / block_size]
+ * * block_size + (L-1) % block_size ([PA-notes] §5 ②: the new token goes to the
+ * next free slot of the sequence's last block; the decode itself is [PA-notes]
+ * §4).  Sequences with L = 0 append nothing.  The decode kernel reads that
+ * token from new_k/new_v instead of the slot, and the merge kernel that follows
+ * it on the stream stores the rows into the slot, so the step needs no write
+ * launch of its own and no ordering between the write and the decode's reads.
+ *
+ *   new_k, new_v  [num_seqs][num_kv_heads][head_dim] dtype, 16-byte aligned;
+ *                 must not alias the caches
+ *   k_cache, v_cache  written at each sequence's newest slot, read elsewhere
+ *   other arguments, errors and workspace as for pa_decode
+ * Each newest slot must belong to its sequence alone: no two sequences may
+ * append into one slot, and no other (sequence, position) of the batch may read
+ * it (the copy-on-write contract: a shared last block is copied first).  With
+ * PA_DEBUG_CHECK=1 a violation returns PA_ERR_INVALID before anything is
+ * enqueued.  Without it the result is undefined but every access stays inside
+ * the arrays; a table entry outside [0, num_blocks) at position L - 1 writes
+ * nothing.
+ */
+pa_status pa_decode_append(const void* q, const void* new_k, const void* new_v,
+                           void* k_cache, void* v_cache, const int32_t* block_tables,
+                           const int32_t* seq_lens, int num_seqs, int num_heads,
+                           int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                           int max_blocks_per_seq, int max_seq_len, float scale,
+                           pa_dtype dtype, void* out, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /*
  * pa_copy_blocks -- copy-on-write block duplication.

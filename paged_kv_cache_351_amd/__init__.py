@@ -51,6 +51,9 @@ def lib():
     L.pa_decode.restype = i32
     L.pa_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32,
                             vp, vp, sz, vp]
+    L.pa_decode_append.restype = i32
+    L.pa_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
+                                   f32, i32, vp, vp, sz, vp]
     L.pa_decode_no_alloc.restype = i32
     L.pa_decode_no_alloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32,
                                      i32, vp, vp]
@@ -201,6 +204,50 @@ def pa_decode(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, scale, 
     _check(lib().pa_decode(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens),
         num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+        block_tables.shape[1], int(max_seq_len), float(scale), _DTYPE[q.dtype], _ptr(out),
+        _ptr(workspace), ws_bytes, _stream(stream)))
+    return out
+
+
+def pa_decode_append(q, new_k, new_v, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, scale,
+                     out, *, max_seq_len, workspace=None, stream=None):
+    """Store each sequence's newest token (position seq_lens[s] - 1) into the slot its block
+    table gives that position, then pa_decode, in one call: bit-identical to pa_write_kv
+    into those slots followed by pa_decode (see include/pagedkv.h).
+
+    new_k, new_v: [num_seqs, num_kv_heads, head_dim], same dtype as q; the other arguments
+    as for pa_decode.  Each newest slot must belong to its sequence alone.
+    """
+    _dev("q", q, ndim=3)
+    if q.dtype not in _DTYPE:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _dev(name, t, q.dtype, 4)
+    if k_cache.shape != v_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+    _dev("block_tables", block_tables, torch.int32, 2)
+    _dev("seq_lens", seq_lens, torch.int32, 1)
+    _dev("out", out, q.dtype)
+    num_seqs, num_heads, head_dim = q.shape
+    num_blocks, block_size, nkv, hd = k_cache.shape
+    if nkv != num_kv_heads or hd != head_dim:
+        raise ValueError(f"cache shape {tuple(k_cache.shape)} does not match num_kv_heads="
+                         f"{num_kv_heads}, head_dim={head_dim}")
+    for name, t in (("new_k", new_k), ("new_v", new_v)):
+        _dev(name, t, q.dtype, 3)
+        if tuple(t.shape) != (num_seqs, num_kv_heads, head_dim):
+            raise ValueError(f"{name} must be [num_seqs, num_kv_heads, head_dim] = "
+                             f"{(num_seqs, num_kv_heads, head_dim)}, got {tuple(t.shape)}")
+    if out.shape != q.shape or block_tables.shape[0] != num_seqs or seq_lens.shape[0] != num_seqs:
+        raise ValueError("q, out, block_tables and seq_lens disagree on num_seqs or shape")
+    if workspace is None:
+        workspace = decode_workspace(q, num_kv_heads, max_seq_len, stream)
+    if workspace is not None:
+        _dev("workspace", workspace)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().pa_decode_append(
+        _ptr(q), _ptr(new_k), _ptr(new_v), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables),
+        _ptr(seq_lens), num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
         block_tables.shape[1], int(max_seq_len), float(scale), _DTYPE[q.dtype], _ptr(out),
         _ptr(workspace), ws_bytes, _stream(stream)))
     return out
@@ -546,7 +593,7 @@ class BlockManager:
         return tables, lens
 
 
-__all__ = ["pa_decode", "pa_decode_no_alloc", "pa_decode_no_alloc_scratch_bytes", "pa_multi_query", "pa_multi_query_workspace_size", "pa_decode_shared_prefix",
+__all__ = ["pa_decode", "pa_decode_append", "pa_decode_no_alloc", "pa_decode_no_alloc_scratch_bytes", "pa_multi_query", "pa_multi_query_workspace_size", "pa_decode_shared_prefix",
            "pa_decode_shared_prefix_workspace_size", "pa_write_kv",
            "pa_copy_blocks", "pa_swap_blocks", "pa_decode_workspace_size",
            "decode_workspace", "pa_last_error", "pa_version",

@@ -76,7 +76,7 @@ using namespace pagedkv;
 
 extern "C" {
 
-int pa_version(void) { return 7; }
+int pa_version(void) { return 8; }
 
 const char* pa_last_error(void) { return g_err.c_str(); }
 

@@ -1,10 +1,12 @@
-// pa_decode and pa_decode_workspace_size: validation, workspace layout and the
-// launch plan of the decode and merge kernels (decode_kernel.h, split.h).
+// pa_decode, pa_decode_append and pa_decode_workspace_size: validation, workspace layout
+// and the launch plan of the decode and merge kernels (decode_kernel.h, split.h).
 #include <stdlib.h>
 
 #include <algorithm>
 #include <map>
 #include <mutex>
+#include <unordered_map>
+#include <unordered_set>
 #include <utility>
 #include <vector>
 
@@ -139,11 +141,48 @@ namespace {
 
 constexpr size_t kNoAllocScratchBytes = PA_DECODE_NO_ALLOC_SCRATCH_BYTES;
 
-// Everything pa_decode and pa_decode_no_alloc share: argument checks, the kernels, the
-// debug checks of the index data and the launch parameters (DecodeParams without the
-// workspace pointers).  Returns PA_OK with *skip set when there is nothing to launch.
+// With debug checks on, for pa_decode_append: every sequence's newest slot (position
+// seq_lens[s] - 1) belongs to it alone.  No two sequences append into one slot, and no
+// other (sequence, position) of the batch reads it, so the write needs no ordering
+// against the reads of other waves.  The ids are already known to be in the pool.
+pa_status check_append_slots(const std::vector<int32_t>& lens, const std::vector<int32_t>& tab,
+                             int num_seqs, int block_size, int max_blocks_per_seq, const char* who) {
+  std::unordered_map<long long, int> owner;  // appended slot -> its sequence
+  std::unordered_set<int> blocks;            // blocks holding an appended slot
+  for (int s = 0; s < num_seqs; ++s) {
+    if (lens[s] == 0) continue;
+    const int t = lens[s] - 1;
+    const int id = tab[(size_t)s * max_blocks_per_seq + t / block_size];
+    const long long slot = (long long)id * block_size + t % block_size;
+    auto ins = owner.emplace(slot, s);
+    if (!ins.second)
+      return fail(PA_ERR_INVALID, "%s: sequences %d and %d both append into slot %lld", who,
+                  ins.first->second, s, slot);
+    blocks.insert(id);
+  }
+  for (int s = 0; s < num_seqs; ++s) {
+    const int nb = (lens[s] + block_size - 1) / block_size;
+    for (int j = 0; j < nb; ++j) {
+      const int id = tab[(size_t)s * max_blocks_per_seq + j];
+      if (blocks.count(id) == 0) continue;
+      for (int t = j * block_size; t < std::min(lens[s], (j + 1) * block_size); ++t) {
+        auto it = owner.find((long long)id * block_size + t % block_size);
+        if (it != owner.end() && !(it->second == s && t == lens[s] - 1))
+          return fail(PA_ERR_INVALID,
+                      "%s: slot %lld, appended by sequence %d, is also read by sequence %d at "
+                      "position %d", who, it->first, it->second, s, t);
+      }
+    }
+  }
+  return PA_OK;
+}
+
+// Everything pa_decode, pa_decode_append and pa_decode_no_alloc share: argument checks,
+// the kernels, the debug checks of the index data and the launch parameters
+// (DecodeParams without the workspace pointers).  new_k and new_v are null except for
+// pa_decode_append.  Returns PA_OK with *skip set when there is nothing to launch.
 pa_status prepare_decode(const void* q, const void* k_cache, const void* v_cache,
-                         const int32_t* block_tables, const int32_t* seq_lens, int num_seqs,
+                         const void* new_k, const void* new_v, const int32_t* block_tables, const int32_t* seq_lens, int num_seqs,
                          int num_heads, int num_kv_heads, int head_dim, int block_size,
                          int num_blocks, int max_blocks_per_seq, int max_seq_len, float scale,
                          pa_dtype dtype, void* out, hipStream_t st, const char* who,
@@ -184,6 +223,10 @@ pa_status prepare_decode(const void* q, const void* k_cache, const void* v_cache
     return fail(PA_ERR_INVALID, "%s: null pointer argument", who);
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
     return fail(PA_ERR_INVALID, "%s: q, caches and out must be 16-byte aligned", who);
+  if ((new_k == nullptr) != (new_v == nullptr))
+    return fail(PA_ERR_INVALID, "%s: new_k and new_v must both be given", who);
+  if (new_k && (!aligned16(new_k) || !aligned16(new_v)))
+    return fail(PA_ERR_INVALID, "%s: new_k and new_v must be 16-byte aligned", who);
   if (check_workspace) {
     const WorkspaceLayout ws = plan_workspace(num_seqs, num_heads, num_kv_heads, head_dim, max_seq_len);
     if (!workspace || workspace_bytes < ws.total)
@@ -196,9 +239,9 @@ pa_status prepare_decode(const void* q, const void* k_cache, const void* v_cache
   const int gp = padded_group(group);
   bool found;
   switch (dtype) {
-    case PA_F32: found = decode_kernels_f32(head_dim, block_size, gp, dec, red); break;
-    case PA_F16: found = decode_kernels_f16(head_dim, block_size, gp, dec, red); break;
-    default: found = decode_kernels_bf16(head_dim, block_size, gp, dec, red); break;
+    case PA_F32: found = decode_kernels_f32(head_dim, block_size, gp, new_k != nullptr, dec, red); break;
+    case PA_F16: found = decode_kernels_f16(head_dim, block_size, gp, new_k != nullptr, dec, red); break;
+    default: found = decode_kernels_bf16(head_dim, block_size, gp, new_k != nullptr, dec, red); break;
   }
   if (!found) return fail(PA_ERR_UNSUPPORTED, "%s: no kernel for this shape", who);
 
@@ -219,6 +262,10 @@ pa_status prepare_decode(const void* q, const void* k_cache, const void* v_cache
                       id, num_blocks);
       }
     }
+    if (new_k) {
+      const pa_status r = check_append_slots(lens, tab, num_seqs, block_size, max_blocks_per_seq, who);
+      if (r != PA_OK) return r;
+    }
   }
 
   // the most waves any call with these shapes may use, then what the device holds at once
@@ -235,6 +282,8 @@ pa_status prepare_decode(const void* q, const void* k_cache, const void* v_cache
   p->block_tables = block_tables;
   p->seq_lens = seq_lens;
   p->out = out;
+  p->new_k = new_k;
+  p->new_v = new_v;
   p->ws_meta = nullptr;
   p->ws_ml = nullptr;
   p->ws_acc = nullptr;
@@ -251,6 +300,12 @@ pa_status prepare_decode(const void* q, const void* k_cache, const void* v_cache
   p->tail_div = tail_divisor();
   p->tail_pieces = tail_pieces();
   p->scale_log2e = (float)((double)scale * 1.4426950408889634074);
+  p->merge_blocks = (waves * (p->tail_pieces + 1) + 3) / 4;
+  // one 16-byte piece of a newest K and V row per thread
+  const long long pieces = (long long)num_seqs * num_kv_heads * head_dim * (dtype == PA_F32 ? 4 : 2) / 16;
+  if (new_k && (pieces + 255) / 256 > (1LL << 30))
+    return fail(PA_ERR_UNSUPPORTED, "%s: more than 2^38 bytes of new rows", who);
+  p->append_blocks = new_k ? (int)((pieces + 255) / 256) : 0;
   return PA_OK;
 }
 
@@ -265,7 +320,7 @@ pa_status launch_decode(DecodeParams* p, const void* dec, const void* red, char*
   // four waves per workgroup: one workgroup per CU, one wave per SIMD
   hipError_t e = hipLaunchKernel(dec, dim3((p->num_waves + 3) / 4), dim3(256), kargs, 0, st);
   if (e != hipSuccess) return hip_fail(e, "pa_decode launch");
-  e = hipLaunchKernel(red, dim3((p->num_waves * (p->tail_pieces + 1) + 3) / 4), dim3(256), kargs, 0, st);
+  e = hipLaunchKernel(red, dim3(p->merge_blocks + p->append_blocks), dim3(256), kargs, 0, st);
   if (e != hipSuccess) return hip_fail(e, "pa_decode merge launch");
   return PA_OK;
 }
@@ -314,10 +369,33 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
   const void* dec = nullptr;
   const void* red = nullptr;
   bool skip = false;
-  pa_status r = prepare_decode(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads,
-                               num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
-                               max_seq_len, scale, dtype, out, st, "pa_decode", workspace,
-                               workspace_bytes, true, &p, &dec, &red, &skip);
+  pa_status r = prepare_decode(q, k_cache, v_cache, nullptr, nullptr, block_tables, seq_lens,
+                               num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                               max_blocks_per_seq, max_seq_len, scale, dtype, out, st, "pa_decode",
+                               workspace, workspace_bytes, true, &p, &dec, &red, &skip);
+  if (r != PA_OK || skip) return r;
+  const WorkspaceLayout ws = plan_workspace(num_seqs, num_heads, num_kv_heads, head_dim, max_seq_len);
+  return launch_decode(&p, dec, red, static_cast<char*>(workspace), ws, st);
+}
+
+pa_status pa_decode_append(const void* q, const void* new_k, const void* new_v, void* k_cache,
+                           void* v_cache, const int32_t* block_tables, const int32_t* seq_lens,
+                           int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                           int block_size, int num_blocks, int max_blocks_per_seq, int max_seq_len,
+                           float scale, pa_dtype dtype, void* out, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  DecodeParams p;
+  const void* dec = nullptr;
+  const void* red = nullptr;
+  bool skip = false;
+  if (num_seqs > 0 && (!new_k || !new_v))
+    return fail(PA_ERR_INVALID, "pa_decode_append: null pointer argument");
+  pa_status r = prepare_decode(q, k_cache, v_cache, new_k, new_v, block_tables, seq_lens, num_seqs,
+                               num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                               max_blocks_per_seq, max_seq_len, scale, dtype, out, st,
+                               "pa_decode_append", workspace, workspace_bytes, true, &p, &dec, &red,
+                               &skip);
   if (r != PA_OK || skip) return r;
   const WorkspaceLayout ws = plan_workspace(num_seqs, num_heads, num_kv_heads, head_dim, max_seq_len);
   return launch_decode(&p, dec, red, static_cast<char*>(workspace), ws, st);
@@ -335,10 +413,10 @@ pa_status pa_decode_no_alloc(const void* q, const void* k_cache, const void* v_c
   const void* dec = nullptr;
   const void* red = nullptr;
   bool skip = false;
-  pa_status r = prepare_decode(q, k_cache, v_cache, block_tables, seq_lens, num_seqs, num_heads,
-                               num_kv_heads, head_dim, block_size, num_blocks, max_blocks_per_seq,
-                               max_seq_len, scale, dtype, out, st, "pa_decode_no_alloc", nullptr, 0,
-                               false, &p, &dec, &red, &skip);
+  pa_status r = prepare_decode(q, k_cache, v_cache, nullptr, nullptr, block_tables, seq_lens,
+                               num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                               max_blocks_per_seq, max_seq_len, scale, dtype, out, st,
+                               "pa_decode_no_alloc", nullptr, 0, false, &p, &dec, &red, &skip);
   if (r != PA_OK || skip) return r;
   // laid out for the waves this launch actually uses and its tail parts
   const WorkspaceLayout ws = layout_for(p.num_waves, p.tail_pieces, p.group, p.head_dim);

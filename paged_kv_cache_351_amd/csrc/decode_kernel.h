@@ -58,6 +58,11 @@
 //     fetched a window ahead, so the two-tile pipeline runs through a whole
 //     segment without draining at window boundaries.
 //
+// Append variant (APPEND, for pa_decode_append): the newest token of every pair
+// (position L - 1) is read from the new rows passed with the call instead of its
+// slot, and the merge kernel's extra workgroups store those rows into the slot
+// after this kernel has finished.  The plain variant's code is unchanged by it.
+//
 // Logits are taken in base 2 (scale * log2 e folded in), so every exponential is
 // one v_exp_f32.  Running maxima start at a finite -1e30 so that a stream with
 // no valid token yet never forms inf - inf.  Tokens past the end of a window in
@@ -266,7 +271,7 @@ __device__ __forceinline__ void load_dwords(const char* src, uint32_t (&w)[NW]) 
   }
 }
 
-template <int DT, int D, int BS, int GP>
+template <int DT, int D, int BS, int GP, bool APPEND>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   constexpr int EB = Elem<DT>::bytes;
   constexpr int ROWB = D * EB;       // bytes of one (token, KV head) row
@@ -531,11 +536,28 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
         const char* kp = (const char*)p.k_cache + (size_t)lc.kv * ROWB + (size_t)pk * blk_bytes +
                          (size_t)(tk % BS) * tok_stride;
         const char* vb = (const char*)p.v_cache + (size_t)lc.kv * ROWB + col * (VE * EB);
+        if constexpr (APPEND) {
+          // In the pair's last tile the newest token is read from the appended rows (the
+          // merge kernel, which runs after this one, stores them into their slot).  The
+          // addresses are selected without a branch.
+          const bool newest = lc.j + 1 == lc.n;
+          const size_t nrow = ((size_t)lc.s * Hkv + lc.kv) * ROWB;
+          const char* nv = (const char*)p.new_v + nrow + col * (VE * EB);
+          kp = newest && tk == last ? (const char*)p.new_k + nrow : kp;
 #pragma unroll
-        for (int c = 0; c < NKC; ++c) Tl.k[c] = *reinterpret_cast<const u32x4*>(kp + (4 * c + grp) * 16);
+          for (int c = 0; c < NKC; ++c) Tl.k[c] = *reinterpret_cast<const u32x4*>(kp + (4 * c + grp) * 16);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          load_dwords<VW>(vb + (size_t)pv[j] * blk_bytes + (size_t)(tv[j] % BS) * tok_stride, Tl.v[j]);
+          for (int j = 0; j < 4; ++j) {
+            const char* vp = vb + (size_t)pv[j] * blk_bytes + (size_t)(tv[j] % BS) * tok_stride;
+            load_dwords<VW>(newest && tv[j] == last ? nv : vp, Tl.v[j]);
+          }
+        } else {
+#pragma unroll
+          for (int c = 0; c < NKC; ++c) Tl.k[c] = *reinterpret_cast<const u32x4*>(kp + (4 * c + grp) * 16);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            load_dwords<VW>(vb + (size_t)pv[j] * blk_bytes + (size_t)(tv[j] % BS) * tok_stride, Tl.v[j]);
+        }
 
         TileCursor nx = lc;  // a chunk never ends past the batch, so the step succeeds
         if (l_count + 1 < nt && nx.next(N, Hkv, lenf)) {
@@ -858,11 +880,36 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
 //     m' = max(m, m_i),  l' = 2^(m - m') l + 2^(m_i - m') l_i,
 //     acc' = 2^(m - m') acc + 2^(m_i - m') a_i,      out = acc / l,
 // so the result does not depend on timing.
+//
+// For pa_decode_append the workgroups from merge_blocks on store each sequence's
+// newest K and V rows (read from new_k/new_v by the decode kernel, which has
+// finished) into the slot of position L - 1, 16 bytes per lane, alongside the merges.
 template <int DT, int D, int GP>
 __global__ __launch_bounds__(256) void reduce_kernel(DecodeParams p) {
   constexpr int LPH = 64 / GP;   // lanes per head
   constexpr int EPL = D / LPH;   // accumulator elements per lane
   constexpr int EB = Elem<DT>::bytes;
+  if ((int)blockIdx.x >= p.merge_blocks) {
+    constexpr int PPR = D * EB / 16;  // 16-byte pieces per row
+    const long long x = (long long)(blockIdx.x - p.merge_blocks) * 256 + threadIdx.x;
+    if (x >= (long long)p.num_seqs * p.num_kv_heads * PPR) return;
+    const long long row = x / PPR;  // row (s, kv) of new_k and new_v
+    const int piece = (int)(x % PPR);
+    const int s = (int)(row / p.num_kv_heads);
+    const int kv = (int)(row % p.num_kv_heads);
+    const int L = seq_len_at(p, s);
+    if (L == 0) return;
+    const int id = p.block_tables[(size_t)s * p.max_blocks_per_seq + (L - 1) / p.block_size];
+    if ((unsigned)id >= (unsigned)p.num_blocks) return;  // contract violation: no write
+    const size_t slot = (size_t)id * p.block_size + (L - 1) % p.block_size;
+    const size_t dst = (slot * p.num_kv_heads + kv) * (D * EB) + piece * 16;
+    const size_t src = (size_t)row * (D * EB) + piece * 16;
+    const u32x4 k = *reinterpret_cast<const u32x4*>((const char*)p.new_k + src);
+    const u32x4 v = *reinterpret_cast<const u32x4*>((const char*)p.new_v + src);
+    *reinterpret_cast<u32x4*>((char*)p.k_cache + dst) = k;
+    *reinterpret_cast<u32x4*>((char*)p.v_cache + dst) = v;
+    return;
+  }
   int* const hdr = p.ws_meta;
   const int* const chunk_meta = p.ws_meta + 64;
   if (blockIdx.x == 0 && threadIdx.x == 0) hdr[32] = 0;
@@ -945,39 +992,40 @@ __global__ __launch_bounds__(256) void reduce_kernel(DecodeParams p) {
 
 // The decode and merge kernels of one shape (nullptr if not compiled).
 template <int DT, int D, int BS, int GP>
-bool pick(const void** dec, const void** red) {
-  *dec = reinterpret_cast<const void*>(&decode_kernel<DT, D, BS, GP>);
+bool pick(bool append, const void** dec, const void** red) {
+  *dec = append ? reinterpret_cast<const void*>(&decode_kernel<DT, D, BS, GP, true>)
+                : reinterpret_cast<const void*>(&decode_kernel<DT, D, BS, GP, false>);
   *red = reinterpret_cast<const void*>(&reduce_kernel<DT, D, GP>);
   return true;
 }
 
 template <int DT, int D, int BS>
-bool pick_group(int gp, const void** dec, const void** red) {
+bool pick_group(int gp, bool append, const void** dec, const void** red) {
   switch (gp) {
-    case 1: return pick<DT, D, BS, 1>(dec, red);
-    case 2: return pick<DT, D, BS, 2>(dec, red);
-    case 4: return pick<DT, D, BS, 4>(dec, red);
-    case 8: return pick<DT, D, BS, 8>(dec, red);
-    case 16: return pick<DT, D, BS, 16>(dec, red);
+    case 1: return pick<DT, D, BS, 1>(append, dec, red);
+    case 2: return pick<DT, D, BS, 2>(append, dec, red);
+    case 4: return pick<DT, D, BS, 4>(append, dec, red);
+    case 8: return pick<DT, D, BS, 8>(append, dec, red);
+    case 16: return pick<DT, D, BS, 16>(append, dec, red);
     default: return false;
   }
 }
 
 template <int DT, int D>
-bool pick_block(int bs, int gp, const void** dec, const void** red) {
+bool pick_block(int bs, int gp, bool append, const void** dec, const void** red) {
   switch (bs) {
-    case 8: return pick_group<DT, D, 8>(gp, dec, red);
-    case 16: return pick_group<DT, D, 16>(gp, dec, red);
-    case 32: return pick_group<DT, D, 32>(gp, dec, red);
+    case 8: return pick_group<DT, D, 8>(gp, append, dec, red);
+    case 16: return pick_group<DT, D, 16>(gp, append, dec, red);
+    case 32: return pick_group<DT, D, 32>(gp, append, dec, red);
     default: return false;
   }
 }
 
 template <int DT>
-bool pick_decode_kernels(int head_dim, int bs, int gp, const void** dec, const void** red) {
+bool pick_decode_kernels(int head_dim, int bs, int gp, bool append, const void** dec, const void** red) {
   switch (head_dim) {
-    case 64: return pick_block<DT, 64>(bs, gp, dec, red);
-    case 128: return pick_block<DT, 128>(bs, gp, dec, red);
+    case 64: return pick_block<DT, 64>(bs, gp, append, dec, red);
+    case 128: return pick_block<DT, 128>(bs, gp, append, dec, red);
     default: return false;
   }
 }

@@ -32,13 +32,25 @@ struct DecodeParams {
                        // demand; 0 = none
   int tail_pieces;     // parts the tail is cut into (halving sizes), 1..kMaxTailPieces
   float scale_log2e;   // scale * log2(e): logits are taken in base 2
+  // pa_decode_append only (null otherwise): the K and V rows of each sequence's newest
+  // token, position seq_lens[s] - 1, as [num_seqs][num_kv_heads][head_dim].  The decode
+  // kernel reads that token from here; the merge kernel's last append_blocks
+  // workgroups then store these rows into their slots of the caches.
+  const void* new_k;
+  const void* new_v;
+  int merge_blocks;    // workgroups of the merge kernel that merge (one wave per chunk)
+  int append_blocks;   // workgroups after them that store the newest rows (0 = none)
 };
 
 // The decode and merge kernels for one shape, one translation unit per element
-// type; false for a shape outside the compiled set.  `gp` is the padded group.
-bool decode_kernels_f32(int head_dim, int block_size, int gp, const void** dec, const void** red);
-bool decode_kernels_f16(int head_dim, int block_size, int gp, const void** dec, const void** red);
-bool decode_kernels_bf16(int head_dim, int block_size, int gp, const void** dec, const void** red);
+// type; false for a shape outside the compiled set.  `gp` is the padded group;
+// `append` picks the decode kernel variant of pa_decode_append.
+bool decode_kernels_f32(int head_dim, int block_size, int gp, bool append, const void** dec,
+                        const void** red);
+bool decode_kernels_f16(int head_dim, int block_size, int gp, bool append, const void** dec,
+                        const void** red);
+bool decode_kernels_bf16(int head_dim, int block_size, int gp, bool append, const void** dec,
+                         const void** red);
 
 // Smallest group size of the compiled decode variants that can hold `group`
 // query heads (1, 2, 4, 8, 16), or 0 if none can.

@@ -2,7 +2,8 @@
 environment before anything touches the GPU.
 
 It hands every entry point index data that breaks the contract of include/pagedkv.h
-(block ids outside the pool, slots outside the pool or named twice, copy pairs that
+(block ids outside the pool, slots outside the pool or named twice, newest slots that
+are shared, copy pairs that
 overlap, swap pairs with a repeated destination, bad q_start / group_start /
 prefix_lens) and records, per case, the status, the message and whether the output or
 the pool was left untouched (a rejected call must launch nothing).  Then it runs the
@@ -78,6 +79,12 @@ def run_valid(dec, mq, sh, dev="cuda"):
                                sh.prefix_lens.to(dev), sh.num_kv_heads, sh.scale, so, max_group_size=3,
                                max_seq_len=sh.max_seq_len)
     out["shared_prefix"] = bits(so)
+    ak, av = dec.k_cache.to(dev), dec.v_cache.to(dev)
+    ao = torch.empty_like(q)
+    pk.pa_decode_append(q, dec.new_k.to(dev), dec.new_v.to(dev), ak, av, bt, lens, dec.num_kv_heads,
+                        dec.scale, ao, max_seq_len=300)
+    out["decode_append"] = bits(ao)
+    out["append_pool_k"], out["append_pool_v"] = bits(ak), bits(av)
     torch.cuda.synchronize()
     return out
 
@@ -117,6 +124,24 @@ def main():
     bt = dec.block_tables.to(dev)
     expect_invalid("decode seq_len above max_seq_len",
                    lambda: pk.pa_decode(q, kc, vc, bt, lens, 2, dec.scale, o, max_seq_len=299), [o])
+
+    # ---- pa_decode_append: two sequences appending into one slot, a newest slot that
+    # another sequence reads (sequence 0 appends at position 0 of its block 0, sequence 1
+    # at position 16 = offset 0 of its block 1; sequence 2 at position 39 = offset 7 of its
+    # block 2, which sequence 3 then also maps as its block 0)
+    nk, nv = dec.new_k.to(dev), dec.new_v.to(dev)
+    bt = dec.block_tables.clone()
+    bt[1, 1] = bt[0, 0]
+    btd = bt.to(dev)
+    expect_invalid("decode_append two sequences append into one slot",
+                   lambda: pk.pa_decode_append(q, nk, nv, kc, vc, btd, lens, 2, dec.scale, o,
+                                               max_seq_len=300), [o, kc, vc])
+    bt = dec.block_tables.clone()
+    bt[3, 0] = bt[2, 2]
+    btd2 = bt.to(dev)
+    expect_invalid("decode_append newest slot read by another sequence",
+                   lambda: pk.pa_decode_append(q, nk, nv, kc, vc, btd2, lens, 2, dec.scale, o,
+                                               max_seq_len=300), [o, kc, vc])
 
     # ---- pa_write_kv: a slot outside the pool, a slot named twice
     nk, nv = dec.new_k.to(dev), dec.new_v.to(dev)

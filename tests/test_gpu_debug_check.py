@@ -29,6 +29,8 @@ EXPECTED = {
     "decode_no_alloc table id = num_blocks": "outside",
     "decode_no_alloc table id = -1": "outside",
     "decode seq_len above max_seq_len": "seq_lens[3]",
+    "decode_append two sequences append into one slot": "both append into slot",
+    "decode_append newest slot read by another sequence": "is also read by sequence 3",
     "write slot outside the pool": "beyond the pool",
     "write slot named twice": "named twice",
     "copy src == dst": "onto itself",
