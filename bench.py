@@ -1,12 +1,11 @@
 """Benchmark: paged decode attention on one MI355X, Llama-3-8B-shaped GQA layer.
 
-One step = the write of 256 new tokens (one per sequence, at its newest position) and
-the decode over all 256 sequences, as one pa_decode_append call (decode kernel + merge
-kernel), on one stream, with every input already resident in HBM.  ``--unfused`` runs
-them as two calls, pa_write_kv then pa_decode; the default line also times that form
-(``write_plus_decode_ms_per_step``).  Workload: 256 sequences, 32 query / 8 KV heads,
-head_dim 128, bf16 KV and q, fp32 accumulation, block size 16, lengths uniform in
-[512, 4096] (seed 0), 70,000-block pool with random block placement.
+One step = pa_write_kv of 256 new tokens (one per sequence) followed by pa_decode
+over all 256 sequences (decode kernel + merge kernel), on one stream, with every
+input already resident in HBM; ``--fused`` runs the two as one pa_decode_append call.
+Workload: 256 sequences, 32 query / 8 KV heads, head_dim 128, bf16 KV and q, fp32
+accumulation, block size 16, lengths uniform in [512, 4096] (seed 0), 70,000-block
+pool with random block placement.
 --workload picks one of the other workloads instead (its step also runs its block
 copies, if any, before the write).
 
@@ -22,6 +21,7 @@ new tokens) and pa_copy_blocks (224 copy-on-write pairs of OPT-13B-shaped blocks
 same way.  ``cpu_baseline`` times the float64 CPU oracle on the host.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME [--block-size B]]
+    python bench.py --fused              # the step as one pa_decode_append
     python bench.py --workload opt13b_shared --shared-prefix   # shared-prefix decode
     python bench.py --workload llama3_8b_spec                  # multi-query (also llama3_8b_chunk)
     python bench.py --swap               # pa_swap_blocks HBM <-> pinned host throughput
@@ -80,10 +80,62 @@ def pct(ms):
             "p90": float(np.percentile(a, 90)), "mean": float(a.mean()), "n": int(a.size)}
 
 
+class HipEvent:
+    """A HIP timing event created with hipEventDisableSystemFence, recorded on a torch stream.
+
+    A default event (torch.cuda.Event included) performs a system-scope fence when it is
+    recorded: the L2 is written back and invalidated, which costs the timed interval a few
+    µs and slows the work after it.  HIP documents this flag for events used only to
+    measure time; every reading here follows a device synchronisation, so nothing needs
+    the fence.  The events come from the HIP runtime torch has loaded."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+    _hip = None
+
+    @classmethod
+    def _lib(cls):
+        if cls._hip is None:
+            import ctypes
+            with open("/proc/self/maps") as f:
+                path = next((ln.split()[-1] for ln in f if "libamdhip64" in ln), "libamdhip64.so.7")
+            L = ctypes.CDLL(path)
+            vp = ctypes.c_void_p
+            L.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(vp), ctypes.c_uint]
+            L.hipEventRecord.argtypes = [vp, vp]
+            L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+            L.hipEventDestroy.argtypes = [vp]
+            cls._hip = L
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+        self._ct = ctypes
+        self.h = ctypes.c_void_p()
+        e = self._lib().hipEventCreateWithFlags(ctypes.byref(self.h), self.DISABLE_SYSTEM_FENCE)
+        if e != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({e})")
+
+    def record(self, stream):
+        e = self._lib().hipEventRecord(self.h, self._ct.c_void_p(stream.cuda_stream))
+        if e != 0:
+            raise RuntimeError(f"hipEventRecord failed ({e})")
+
+    def elapsed_time(self, end):
+        """ms from this event to `end` (both recorded and complete)."""
+        ms = self._ct.c_float()
+        e = self._lib().hipEventElapsedTime(self._ct.byref(ms), self.h, end.h)
+        if e != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({e})")
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and self.h:
+            self._hip.hipEventDestroy(self.h)
+
+
 def timed_calls(fn, n, stream, flush=None):
     """Event timings (ms) of n calls of fn on stream, each after an untimed flush."""
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(n)]
+    ev = [(HipEvent(), HipEvent()) for _ in range(n)]
     for a, z in ev:
         if flush is not None:
             flush()
@@ -487,9 +539,10 @@ def main():
                          "of the same study, measured the same way")
     ap.add_argument("--block-size", type=int, default=16, choices=[8, 16, 32],
                     help="block size of the llama2_70b workload")
-    ap.add_argument("--unfused", action="store_true",
-                    help="run the step's write and decode as two calls (pa_write_kv, pa_decode) "
-                         "instead of one pa_decode_append")
+    ap.add_argument("--fused", action="store_true",
+                    help="run the step's write and decode as one pa_decode_append instead of "
+                         "two calls (pa_write_kv, pa_decode); the write must store each "
+                         "sequence's newest token")
     ap.add_argument("--graph", action="store_true",
                     help="time the step as replays of a HIP graph captured once (the roofline "
                          "still times the eager decode call)")
@@ -551,32 +604,35 @@ def main():
                                        max_group_size=max_group, max_seq_len=max_len, workspace=ws)
     else:
         ws = pk.decode_workspace(q, b.num_kv_heads, max_len)
+        # batches whose sequences share blocks read them with the default cache policy
+        decode_fn = pk.pa_decode_cached if b.group_start is not None else pk.pa_decode
 
         def decode():
-            pk.pa_decode(q, kc, vc, bt, lens, b.num_kv_heads, b.scale, out, max_seq_len=max_len,
-                         workspace=ws)
+            decode_fn(q, kc, vc, bt, lens, b.num_kv_heads, b.scale, out, max_seq_len=max_len,
+                      workspace=ws)
 
         def decode_append():
             pk.pa_decode_append(q, nk, nv, kc, vc, bt, lens, b.num_kv_heads, b.scale, out,
                                 max_seq_len=max_len, workspace=ws)
         attend = decode
-    # A step whose write stores exactly each sequence's newest token (position L - 1) runs
-    # write and decode as one pa_decode_append, unless --unfused.
-    fused = (not multi and not shared and has_write and not args.unfused
-             and write_is_newest(b))
-    two_calls = None
+    # --fused: a step whose write stores exactly each sequence's newest token (position
+    # L - 1) runs write and decode as one pa_decode_append
+    fused = args.fused
     if fused:
-        attend, two_calls = decode_append, decode
+        if multi or shared or not has_write or not write_is_newest(b):
+            raise SystemExit("--fused needs a decode workload whose write stores each sequence's "
+                             "newest token")
+        attend = decode_append
 
-    def step(ev0=None, ev1=None, unfused=False):
+    def step(ev0=None, ev1=None):
         # copies and writes are idempotent, so every step repeats the same state change
         if pairs is not None:
             pk.pa_copy_blocks(kc, vc, pairs)
-        if has_write and (unfused or not fused):
+        if has_write and not fused:
             pk.pa_write_kv(nk, nv, slots, kc, vc)
         if ev0 is not None:
             ev0.record(stream)
-        (two_calls if unfused else attend)()
+        attend()
         if ev1 is not None:
             ev1.record(stream)
 
@@ -589,10 +645,9 @@ def main():
     # The per-step spread first: K steps with HIP events around each step and its attention
     # call.  They also carry the GPU past its first ~20 ms of this kernel, which run slower
     # than the steady state (the first 20 steps after 5 warm-up steps take about 7 µs more
-    # each than every later 20).  An event record takes GPU time of its own (a few µs
-    # each), so the wall-clock steps below run without them.
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    # each than every later 20).  An event record takes GPU time of its own, so the
+    # wall-clock steps below run without them.
+    ev = [(HipEvent(), HipEvent(), HipEvent()) for _ in range(K)]
     log(f"timing {K} steps with events")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -612,20 +667,6 @@ def main():
     torch.cuda.synchronize()
     total = time.perf_counter() - t0
     eager_total = total
-
-    unfused_total = None
-    if fused:
-        # the same step as two calls (pa_write_kv, then pa_decode), for comparison; its
-        # kernels are warmed up first like the step's
-        for _ in range(args.warmup):
-            step(unfused=True)
-        log(f"timing {K} steps as write + decode")
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(K):
-            step(unfused=True)
-        torch.cuda.synchronize()
-        unfused_total = time.perf_counter() - t0
 
     # the roofline leg: the attention call alone, K times, each after an untimed read of
     # 1 GiB that evicts L2 and the Infinity Cache (the step's write and copies are done,
@@ -678,20 +719,22 @@ def main():
         "eager_ms_per_step": eager_total * 1e3 / K,
         "events_ms_per_step": events_total * 1e3 / K,
         "timing_order": (f"{args.warmup} warm-up steps; {K} steps with events (step_us); {K} "
-                         "wall-clock steps (value)" + (f"; {K} write + decode steps" if fused else "")
-                         + f"; {K} flushed calls (roofline)"),
+                         f"wall-clock steps (value); {K} flushed calls (roofline)"),
         "step_calls": ("pa_decode_append" if fused else
+                       ("pa_copy_blocks + " if pairs is not None else "") +
                        ("pa_write_kv + " if has_write else "") + ("pa_multi_query" if multi else
-                       "pa_decode_shared_prefix" if shared else "pa_decode")),
-        "write_plus_decode_ms_per_step": unfused_total * 1e3 / K if fused else None,
+                       "pa_decode_shared_prefix" if shared else
+                       "pa_decode_cached" if b.group_start is not None else "pa_decode")),
         "seqs_per_s": b.num_seqs / (total / K),
         "step_us": pct(step_ms),
-        "roofline": {"kernel": ("pa_decode_append" if fused else "pa_decode") +
+        "roofline": {"kernel": ("pa_decode_append" if fused else "pa_decode_cached"
+                                if b.group_start is not None else "pa_decode") +
                                " (decode_kernel + reduce_kernel)", "bound": "hbm",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": kv_bytes,
-                     "timing": "median of K calls, each after a 1 GiB read that evicts the caches",
+                     "timing": "median of K calls, each after a 1 GiB read that evicts the caches; "
+                               "HIP events without the system-scope fence",
                      "call_us": call, "call_us_back_to_back": pct(call_ms_warm),
                      "avg_launch_us": call["mean"], "p10_us": call["p10"], "p90_us": call["p90"]},
         "cache_ops": cache_ops,

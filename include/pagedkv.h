@@ -139,6 +139,26 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pa_decode_cached -- pa_decode for batches whose sequences share blocks.
+ *
+ * Same arguments, result (bit for bit), errors and workspace as pa_decode; only
+ * the cache policy of the K/V loads differs.  pa_decode reads K/V with the
+ * non-temporal hint, since each row is read once per call: the streamed lines
+ * do not take room in L2 and the Infinity Cache, which makes it faster when
+ * sequences share no blocks.  When sequences of the batch share blocks
+ * (parallel samples or beams of one prompt reading its blocks, [PA-notes] §6.1
+ * and §6.2), those rows are read once per sequence and the default policy lets
+ * the repeated reads hit in the caches: use this call, or
+ * pa_decode_shared_prefix, which reads a group's shared blocks once.
+ */
+pa_status pa_decode_cached(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, const int32_t* seq_lens,
+                           int num_seqs, int num_heads, int num_kv_heads, int head_dim,
+                           int block_size, int num_blocks, int max_blocks_per_seq,
+                           int max_seq_len, float scale, pa_dtype dtype, void* out,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * pa_decode_no_alloc -- pa_decode for callers that cannot allocate device memory
  * (code recorded into a HIP graph, tight serving loops, harnesses that forbid
  * hipMalloc).  Same arguments, result and errors as pa_decode, without the

@@ -51,6 +51,8 @@ def lib():
     L.pa_decode.restype = i32
     L.pa_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32,
                             vp, vp, sz, vp]
+    L.pa_decode_cached.restype = i32
+    L.pa_decode_cached.argtypes = L.pa_decode.argtypes
     L.pa_decode_append.restype = i32
     L.pa_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
                                    f32, i32, vp, vp, sz, vp]
@@ -179,6 +181,21 @@ def pa_decode(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, scale, 
     (zero-filled) here on ``stream`` if omitted (pass one to keep allocation off the hot
     path); stream: a torch.cuda.Stream, default the current one.
     """
+    return _decode("pa_decode", q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, scale,
+                   out, max_seq_len, workspace, stream)
+
+
+def pa_decode_cached(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, scale, out, *,
+                     max_seq_len, workspace=None, stream=None):
+    """pa_decode for batches whose sequences share blocks: the same result bit for bit, with
+    the K/V loads under the default cache policy, so that rows read by several sequences
+    can hit in the caches (pa_decode streams them; see include/pagedkv.h)."""
+    return _decode("pa_decode_cached", q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads,
+                   scale, out, max_seq_len, workspace, stream)
+
+
+def _decode(entry, q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, scale, out,
+            max_seq_len, workspace, stream):
     _dev("q", q, ndim=3)
     if q.dtype not in _DTYPE:
         raise TypeError(f"unsupported dtype {q.dtype}")
@@ -201,7 +218,7 @@ def pa_decode(q, k_cache, v_cache, block_tables, seq_lens, num_kv_heads, scale, 
     if workspace is not None:
         _dev("workspace", workspace)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(lib().pa_decode(
+    _check(getattr(lib(), entry)(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens),
         num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
         block_tables.shape[1], int(max_seq_len), float(scale), _DTYPE[q.dtype], _ptr(out),
@@ -593,7 +610,7 @@ class BlockManager:
         return tables, lens
 
 
-__all__ = ["pa_decode", "pa_decode_append", "pa_decode_no_alloc", "pa_decode_no_alloc_scratch_bytes", "pa_multi_query", "pa_multi_query_workspace_size", "pa_decode_shared_prefix",
+__all__ = ["pa_decode", "pa_decode_cached", "pa_decode_append", "pa_decode_no_alloc", "pa_decode_no_alloc_scratch_bytes", "pa_multi_query", "pa_multi_query_workspace_size", "pa_decode_shared_prefix",
            "pa_decode_shared_prefix_workspace_size", "pa_write_kv",
            "pa_copy_blocks", "pa_swap_blocks", "pa_decode_workspace_size",
            "decode_workspace", "pa_last_error", "pa_version",

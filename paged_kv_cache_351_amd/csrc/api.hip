@@ -76,7 +76,7 @@ using namespace pagedkv;
 
 extern "C" {
 
-int pa_version(void) { return 8; }
+int pa_version(void) { return 9; }
 
 const char* pa_last_error(void) { return g_err.c_str(); }
 

@@ -1,5 +1,6 @@
-// pa_decode, pa_decode_append and pa_decode_workspace_size: validation, workspace layout
-// and the launch plan of the decode and merge kernels (decode_kernel.h, split.h).
+// pa_decode, pa_decode_cached, pa_decode_append and pa_decode_workspace_size: validation,
+// workspace layout and the launch plan of the decode and merge kernels (decode_kernel.h,
+// split.h).
 #include <stdlib.h>
 
 #include <algorithm>
@@ -177,12 +178,13 @@ pa_status check_append_slots(const std::vector<int32_t>& lens, const std::vector
   return PA_OK;
 }
 
-// Everything pa_decode, pa_decode_append and pa_decode_no_alloc share: argument checks,
-// the kernels, the debug checks of the index data and the launch parameters
-// (DecodeParams without the workspace pointers).  new_k and new_v are null except for
-// pa_decode_append.  Returns PA_OK with *skip set when there is nothing to launch.
-pa_status prepare_decode(const void* q, const void* k_cache, const void* v_cache,
-                         const void* new_k, const void* new_v, const int32_t* block_tables, const int32_t* seq_lens, int num_seqs,
+// Everything pa_decode, pa_decode_cached, pa_decode_append and pa_decode_no_alloc share:
+// argument checks, the kernels, the debug checks of the index data and the launch
+// parameters (DecodeParams without the workspace pointers).  new_k and new_v are null
+// except for pa_decode_append (variant kAppend).  Returns PA_OK with *skip set when there is nothing to launch.
+pa_status prepare_decode(DecodeVariant variant, const void* q, const void* k_cache,
+                         const void* v_cache, const void* new_k, const void* new_v,
+                         const int32_t* block_tables, const int32_t* seq_lens, int num_seqs,
                          int num_heads, int num_kv_heads, int head_dim, int block_size,
                          int num_blocks, int max_blocks_per_seq, int max_seq_len, float scale,
                          pa_dtype dtype, void* out, hipStream_t st, const char* who,
@@ -239,9 +241,9 @@ pa_status prepare_decode(const void* q, const void* k_cache, const void* v_cache
   const int gp = padded_group(group);
   bool found;
   switch (dtype) {
-    case PA_F32: found = decode_kernels_f32(head_dim, block_size, gp, new_k != nullptr, dec, red); break;
-    case PA_F16: found = decode_kernels_f16(head_dim, block_size, gp, new_k != nullptr, dec, red); break;
-    default: found = decode_kernels_bf16(head_dim, block_size, gp, new_k != nullptr, dec, red); break;
+    case PA_F32: found = decode_kernels_f32(head_dim, block_size, gp, variant, dec, red); break;
+    case PA_F16: found = decode_kernels_f16(head_dim, block_size, gp, variant, dec, red); break;
+    default: found = decode_kernels_bf16(head_dim, block_size, gp, variant, dec, red); break;
   }
   if (!found) return fail(PA_ERR_UNSUPPORTED, "%s: no kernel for this shape", who);
 
@@ -369,10 +371,32 @@ pa_status pa_decode(const void* q, const void* k_cache, const void* v_cache,
   const void* dec = nullptr;
   const void* red = nullptr;
   bool skip = false;
-  pa_status r = prepare_decode(q, k_cache, v_cache, nullptr, nullptr, block_tables, seq_lens,
-                               num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                               max_blocks_per_seq, max_seq_len, scale, dtype, out, st, "pa_decode",
-                               workspace, workspace_bytes, true, &p, &dec, &red, &skip);
+  pa_status r = prepare_decode(DecodeVariant::kStream, q, k_cache, v_cache, nullptr, nullptr,
+                               block_tables, seq_lens, num_seqs, num_heads, num_kv_heads, head_dim,
+                               block_size, num_blocks, max_blocks_per_seq, max_seq_len, scale, dtype,
+                               out, st, "pa_decode", workspace, workspace_bytes, true, &p, &dec, &red,
+                               &skip);
+  if (r != PA_OK || skip) return r;
+  const WorkspaceLayout ws = plan_workspace(num_seqs, num_heads, num_kv_heads, head_dim, max_seq_len);
+  return launch_decode(&p, dec, red, static_cast<char*>(workspace), ws, st);
+}
+
+pa_status pa_decode_cached(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, const int32_t* seq_lens, int num_seqs,
+                           int num_heads, int num_kv_heads, int head_dim, int block_size,
+                           int num_blocks, int max_blocks_per_seq, int max_seq_len, float scale,
+                           pa_dtype dtype, void* out, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  DecodeParams p;
+  const void* dec = nullptr;
+  const void* red = nullptr;
+  bool skip = false;
+  pa_status r = prepare_decode(DecodeVariant::kCached, q, k_cache, v_cache, nullptr, nullptr,
+                               block_tables, seq_lens, num_seqs, num_heads, num_kv_heads, head_dim,
+                               block_size, num_blocks, max_blocks_per_seq, max_seq_len, scale, dtype,
+                               out, st, "pa_decode_cached", workspace, workspace_bytes, true, &p,
+                               &dec, &red, &skip);
   if (r != PA_OK || skip) return r;
   const WorkspaceLayout ws = plan_workspace(num_seqs, num_heads, num_kv_heads, head_dim, max_seq_len);
   return launch_decode(&p, dec, red, static_cast<char*>(workspace), ws, st);
@@ -391,11 +415,11 @@ pa_status pa_decode_append(const void* q, const void* new_k, const void* new_v, 
   bool skip = false;
   if (num_seqs > 0 && (!new_k || !new_v))
     return fail(PA_ERR_INVALID, "pa_decode_append: null pointer argument");
-  pa_status r = prepare_decode(q, k_cache, v_cache, new_k, new_v, block_tables, seq_lens, num_seqs,
-                               num_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                               max_blocks_per_seq, max_seq_len, scale, dtype, out, st,
-                               "pa_decode_append", workspace, workspace_bytes, true, &p, &dec, &red,
-                               &skip);
+  pa_status r = prepare_decode(DecodeVariant::kAppend, q, k_cache, v_cache, new_k, new_v,
+                               block_tables, seq_lens, num_seqs, num_heads, num_kv_heads, head_dim,
+                               block_size, num_blocks, max_blocks_per_seq, max_seq_len, scale, dtype,
+                               out, st, "pa_decode_append", workspace, workspace_bytes, true, &p, &dec,
+                               &red, &skip);
   if (r != PA_OK || skip) return r;
   const WorkspaceLayout ws = plan_workspace(num_seqs, num_heads, num_kv_heads, head_dim, max_seq_len);
   return launch_decode(&p, dec, red, static_cast<char*>(workspace), ws, st);
@@ -413,10 +437,11 @@ pa_status pa_decode_no_alloc(const void* q, const void* k_cache, const void* v_c
   const void* dec = nullptr;
   const void* red = nullptr;
   bool skip = false;
-  pa_status r = prepare_decode(q, k_cache, v_cache, nullptr, nullptr, block_tables, seq_lens,
-                               num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
-                               max_blocks_per_seq, max_seq_len, scale, dtype, out, st,
-                               "pa_decode_no_alloc", nullptr, 0, false, &p, &dec, &red, &skip);
+  pa_status r = prepare_decode(DecodeVariant::kStream, q, k_cache, v_cache, nullptr, nullptr,
+                               block_tables, seq_lens, num_seqs, num_heads, num_kv_heads, head_dim,
+                               block_size, num_blocks, max_blocks_per_seq, max_seq_len, scale, dtype,
+                               out, st, "pa_decode_no_alloc", nullptr, 0, false, &p, &dec, &red,
+                               &skip);
   if (r != PA_OK || skip) return r;
   // laid out for the waves this launch actually uses and its tail parts
   const WorkspaceLayout ws = layout_for(p.num_waves, p.tail_pieces, p.group, p.head_dim);

@@ -42,15 +42,19 @@ struct DecodeParams {
   int append_blocks;   // workgroups after them that store the newest rows (0 = none)
 };
 
+// Decode kernel variants: K/V loads with the non-temporal hint (pa_decode), the same
+// with the append of the newest tokens (pa_decode_append), and K/V loads with the
+// default cache policy (pa_decode_cached).
+enum class DecodeVariant { kStream, kAppend, kCached };
+
 // The decode and merge kernels for one shape, one translation unit per element
-// type; false for a shape outside the compiled set.  `gp` is the padded group;
-// `append` picks the decode kernel variant of pa_decode_append.
-bool decode_kernels_f32(int head_dim, int block_size, int gp, bool append, const void** dec,
-                        const void** red);
-bool decode_kernels_f16(int head_dim, int block_size, int gp, bool append, const void** dec,
-                        const void** red);
-bool decode_kernels_bf16(int head_dim, int block_size, int gp, bool append, const void** dec,
-                         const void** red);
+// type; false for a shape outside the compiled set.  `gp` is the padded group.
+bool decode_kernels_f32(int head_dim, int block_size, int gp, DecodeVariant variant,
+                        const void** dec, const void** red);
+bool decode_kernels_f16(int head_dim, int block_size, int gp, DecodeVariant variant,
+                        const void** dec, const void** red);
+bool decode_kernels_bf16(int head_dim, int block_size, int gp, DecodeVariant variant,
+                         const void** dec, const void** red);
 
 // Smallest group size of the compiled decode variants that can hold `group`
 // query heads (1, 2, 4, 8, 16), or 0 if none can.

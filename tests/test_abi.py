@@ -48,13 +48,13 @@ def test_library_exports_every_declared_symbol(pk):
 
 
 def test_binding_names_match_the_abi(pk):
-    for n in ["pa_decode", "pa_decode_append", "pa_write_kv", "pa_copy_blocks",
+    for n in ["pa_decode", "pa_decode_cached", "pa_decode_append", "pa_write_kv", "pa_copy_blocks",
               "pa_decode_workspace_size", "pa_last_error", "pa_version"]:
         assert callable(getattr(pk, n))
 
 
 def test_version(pk):
-    assert pk.pa_version() == 8
+    assert pk.pa_version() == 9
 
 
 @pytest.mark.parametrize("N,H,HKV,D,L", [(256, 32, 8, 128, 4096), (32, 64, 8, 128, 32768),
@@ -114,6 +114,21 @@ def test_decode_rejects_host_visible_errors(pk, over, status, words):
 
 def test_decode_with_no_sequences_is_a_no_op(pk):
     assert call_decode(pk, N=0, q=None, out=None) == 0
+
+
+@pytest.mark.parametrize("over,status,words", [
+    (dict(D=96), 2, "head_dim"),
+    (dict(q=None), 1, "null"),
+    (dict(L=1000, MB=100, wsb=16), 3, "workspace"),
+])
+def test_decode_cached_rejects_host_visible_errors(pk, over, status, words):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, lens=FAKE, N=4, H=8, HKV=2, D=128, BS=16, NB=100,
+             MB=10, L=160, scale=0.088, dt=2, out=FAKE, ws=FAKE, wsb=0, stream=None)
+    a.update(over)
+    assert pk.lib().pa_decode_cached(a["q"], a["k"], a["v"], a["bt"], a["lens"], a["N"], a["H"],
+                                     a["HKV"], a["D"], a["BS"], a["NB"], a["MB"], a["L"], a["scale"],
+                                     a["dt"], a["out"], a["ws"], a["wsb"], a["stream"]) == status
+    assert words in pk.pa_last_error() and "pa_decode_cached" in pk.pa_last_error()
 
 
 def call_decode_append(pk, **over):
