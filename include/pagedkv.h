@@ -279,13 +279,19 @@ pa_status pa_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst_pa
  *                  q_start[num_seqs] = total_q
  *   seq_lens       device int32 [num_seqs], n_s <= L_s <= max_seq_len
  *   max_q_len      host bound on every n_s (no device sync is made)
- *   workspace      pa_multi_query_workspace_size(...) bytes: a longest-first
- *                  order of the sequences, and partial results when the context
- *                  is partitioned; no zero-fill needed
+ *   workspace      pa_multi_query_workspace_size(...) bytes, 16-byte aligned:
+ *                  the work plan and partial results; no zero-fill needed (the
+ *                  call clears what it counts on)
  *
- * Work is cut into (sequence, KV head, block of query rows, context
- * partition) items; with few items the context is split into partitions that
- * a second kernel merges, in a fixed order.  Head_dim 64 or 128; at most 64
+ * With at most 16 (query, head) rows per (sequence, KV head) (max_q_len *
+ * num_heads / num_kv_heads <= 16: verification of a few drafted tokens), fp16
+ * or bf16, and block_size 8, 16 or 32, the call runs on the decode kernels:
+ * each pair's rows take the 16 columns of the decode's score tile, each row
+ * with its own causal limit, and the step is split evenly over the waves as
+ * for pa_decode (a clear of the workspace header, the decode kernel, the
+ * merge kernel).  Otherwise work is cut into (sequence, KV head, block of query
+ * rows, context partition) items; with few items the context is split into
+ * partitions that a second kernel merges, in a fixed order.  Head_dim 64 or 128; at most 64
  * query heads per KV head; a cache slot (num_kv_heads * head_dim elements)
  * below 2^24 bytes and a block below 2^32 bytes (PA_ERR_UNSUPPORTED beyond
  * these).  Errors as for pa_decode; index data violating the contract above

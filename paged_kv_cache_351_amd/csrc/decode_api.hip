@@ -51,6 +51,15 @@ int tail_divisor() {
 
 bool valid_block_size(int bs) { return bs == 8 || bs == 16 || bs == 32; }
 
+// The multi-query rows mode hands out no tail parts by default: its pieces carry up to 16
+// rows, and the fewer pieces of a static split (two per wave rather than about three)
+// cost less than the longer finish (Llama-3-8B verification: 439 against 445 us for
+// 1/16 tails).  PA_MULTI_QUERY_ROWS_TAIL = d sets a divisor, for tuning sweeps.
+int rows_tail_divisor() {
+  static const int v = std::max(0, std::min(env_int("PA_MULTI_QUERY_ROWS_TAIL", 0), 1024));
+  return v;
+}
+
 // Workspace of one pa_decode call.  Each launched wave's share of the step is
 // cut into chunks (a head and up to kMaxTailPieces tail parts); each chunk has
 // a 16-byte record (the pair it owns, if split, and whether it left a first
@@ -238,7 +247,7 @@ pa_status prepare_decode(DecodeVariant variant, const void* q, const void* k_cac
       return fail(PA_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", who);
   }
 
-  const int gp = padded_group(group);
+  const int gp = variant == DecodeVariant::kRows ? 16 : padded_group(group);
   bool found;
   switch (dtype) {
     case PA_F32: found = decode_kernels_f32(head_dim, block_size, gp, variant, dec, red); break;
@@ -286,6 +295,9 @@ pa_status prepare_decode(DecodeVariant variant, const void* q, const void* k_cac
   p->out = out;
   p->new_k = new_k;
   p->new_v = new_v;
+  p->q_start = nullptr;
+  p->rows = group;
+  p->total_q = 0;
   p->ws_meta = nullptr;
   p->ws_ml = nullptr;
   p->ws_acc = nullptr;
@@ -358,6 +370,58 @@ pa_status scratch_address(hipStream_t st, char** out) {
 }
 
 }  // namespace
+
+namespace pagedkv {
+
+size_t multi_query_rows_workspace(int num_seqs, int num_kv_heads, int head_dim, int max_seq_len,
+                                  int rows) {
+  const long long t_max = (long long)num_seqs * num_kv_heads * tiles_of(max_seq_len);
+  return layout_for(waves_used(t_max, kMaxWaves), kMaxTailPieces, rows, head_dim).total;
+}
+
+bool multi_query_rows_apply(pa_dtype dtype, int num_seqs, int num_heads, int num_kv_heads,
+                            int head_dim, int block_size, int max_q_len, int max_seq_len) {
+  const long long rows = (long long)max_q_len * (num_heads / num_kv_heads);
+  return dtype != PA_F32 && rows >= 1 && rows <= 16 && (head_dim == 64 || head_dim == 128) &&
+         valid_block_size(block_size) && num_seqs <= kLdsSeqs &&
+         (long long)num_seqs * tiles_of(max_seq_len) < (1LL << 31) - 1;
+}
+
+pa_status multi_query_rows(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, const int32_t* seq_lens,
+                           const int32_t* q_start, int num_seqs, int total_q, int num_heads,
+                           int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                           int max_blocks_per_seq, int max_q_len, int max_seq_len, float scale,
+                           pa_dtype dtype, void* out,
+                           void* workspace, size_t workspace_bytes, hipStream_t st) {
+  DecodeParams p;
+  const void* dec = nullptr;
+  const void* red = nullptr;
+  bool skip = false;
+  pa_status r = prepare_decode(DecodeVariant::kRows, q, k_cache, v_cache, nullptr, nullptr,
+                               block_tables, seq_lens, num_seqs, num_heads, num_kv_heads, head_dim,
+                               block_size, num_blocks, max_blocks_per_seq, max_seq_len, scale, dtype,
+                               out, st, "pa_multi_query", nullptr, 0, false, &p, &dec, &red, &skip);
+  if (r != PA_OK || skip) return r;
+  p.q_start = q_start;
+  p.rows = max_q_len * (num_heads / num_kv_heads);
+  p.total_q = total_q;
+  p.tail_div = rows_tail_divisor();
+  const long long t_max = (long long)num_seqs * num_kv_heads * tiles_of(max_seq_len);
+  const WorkspaceLayout ws = layout_for(waves_used(t_max, kMaxWaves), kMaxTailPieces, p.rows, head_dim);
+  if (!workspace || workspace_bytes < ws.total)
+    return fail(PA_ERR_WORKSPACE, "pa_multi_query: workspace of %zu bytes, %zu needed",
+                workspace ? workspace_bytes : (size_t)0, ws.total);
+  // the workspace carries no state between pa_multi_query calls: the counter that hands
+  // out tail parts is cleared first (a kernel, not a memset, so that a capture stays valid)
+  char* base = static_cast<char*>(workspace);
+  hipLaunchKernelGGL(clear_header_kernel, dim3(1), dim3(64), 0, st, reinterpret_cast<int*>(base));
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "pa_multi_query: clearing the workspace header");
+  return launch_decode(&p, dec, red, base, ws, st);
+}
+
+}  // namespace pagedkv
 
 extern "C" {
 

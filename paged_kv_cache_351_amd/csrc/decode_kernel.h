@@ -104,10 +104,6 @@ constexpr bool kMatrixPV = DT != kF32 && GP >= PA_DECODE_MPV_MIN_GP;
 // A reference maximum moves only when a tile's maximum exceeds it by more than this
 // (log2 units), so weights stay below 2^8 and the accumulators are rescaled rarely.
 constexpr float kLazyMax = 8.0f;
-// Batches of at most this many sequences keep every sequence's length and tile
-// prefix sum in LDS (each wave its own copy), so locating a chunk and stepping to
-// the next sequence read LDS instead of global memory.
-constexpr int kLdsSeqs = 2048;
 
 template <int DT>
 struct Elem {
@@ -283,7 +279,7 @@ __device__ __forceinline__ void load_dwords(const char* src, uint32_t (&w)[NW]) 
   }
 }
 
-template <int DT, int D, int BS, int GP, bool APPEND, bool STREAM>
+template <int DT, int D, int BS, int GP, bool APPEND, bool STREAM, bool ROWS>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   constexpr int EB = Elem<DT>::bytes;
   constexpr int ROWB = D * EB;       // bytes of one (token, KV head) row
@@ -291,6 +287,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   constexpr int VE = D / 16;         // V elements per lane per token
   constexpr int VW = VE * EB / 4;    // V dwords per lane per token
   static_assert(ROWB % 64 == 0 && (BS == 8 || BS == 16 || BS == 32), "shape");
+  static_assert(!ROWS || (kMatrixPV<DT, GP> && !APPEND), "multi-query rows use the matrix-core P.V");
 
   const int lane = threadIdx.x & 63;
   const int grp = lane >> 4;
@@ -312,6 +309,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   int* const pre = lds_pre[threadIdx.x >> 6];
   int* const lenl = lds_len[threadIdx.x >> 6];
   bool in_lds = N <= kLdsSeqs;
+  // ROWS: the query starts q_start[0..N] as well, loaded with the lengths
+  __shared__ int lds_qs[4][ROWS ? kLdsSeqs + 1 : 1];
+  int* const qsl = lds_qs[threadIdx.x >> 6];
+  int q_end = 0;
+  if constexpr (ROWS) q_end = p.q_start[N];
 
   // Total tiles of the step (and, for a batch that fits, every sequence's length and
   // exclusive tile prefix sum in LDS).  The lengths of kLenRound * 64 sequences are
@@ -322,9 +324,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   {
     constexpr int kLenRound = 8;
     for (int c0 = 0; c0 < N; c0 += 64 * kLenRound) {
-      int raw[kLenRound];
+      int raw[kLenRound], rawq[kLenRound];
 #pragma unroll
-      for (int i = 0; i < kLenRound; ++i) raw[i] = p.seq_lens[min(c0 + 64 * i + lane, N - 1)];
+      for (int i = 0; i < kLenRound; ++i) {
+        raw[i] = p.seq_lens[min(c0 + 64 * i + lane, N - 1)];
+        if constexpr (ROWS) rawq[i] = p.q_start[min(c0 + 64 * i + lane, N - 1)];
+      }
 #pragma unroll
       for (int i = 0; i < kLenRound; ++i) {
         const int c = c0 + 64 * i;
@@ -335,10 +340,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
         if (in_lds && c + lane < N) {
           pre[c + lane] = (int)(seq_tiles + incl - n_cur);
           lenl[c + lane] = L;
+          if constexpr (ROWS) qsl[c + lane] = rawq[i];
         }
         seq_tiles += __builtin_amdgcn_readlane(incl, 63);
         // outputs of empty sequences are zeros: sequence s is zeroed by wave s mod launched
-        unsigned long long empty = __ballot(c + lane < N && L == 0 && (c + lane) % launched == w);
+        // (ROWS: an empty sequence has no query rows)
+        unsigned long long empty =
+            __ballot(!ROWS && c + lane < N && L == 0 && (c + lane) % launched == w);
         while (empty) {
           const int s = c + __ffsll(empty) - 1;
           empty &= empty - 1;
@@ -351,6 +359,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     // prefix sums must fit in an int; the writes above complete before any read
     in_lds = in_lds && seq_tiles < (1ll << 31) - 1;
     if (in_lds && lane == 0) pre[N] = (int)seq_tiles;
+    if (ROWS && in_lds && lane == 0) qsl[N] = q_end;
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
   }
   const long long T = seq_tiles * Hkv;
@@ -377,6 +386,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   const size_t blk_bytes = (size_t)BS * tok_stride;
   const float sl2 = p.scale_log2e;
   auto lenf = [&](int s) { return in_lds ? lenl[s] : seq_len_at(p, s); };
+  // ROWS: first query row of sequence s (s <= N), and this lane's row of a pair: query
+  // row_i, head row_h of the KV head's group (columns at and past p.rows are padding)
+  // (the host runs the rows mode only for batches whose tables fit LDS, so qsl is
+  // always filled; reading it alone keeps these reads off the vector memory counter)
+  auto qsf = [&](int s) { return min(max(qsl[s], 0), p.total_q); };
+  const int row_i = ROWS ? col / g : 0;
+  const int row_h = ROWS ? col - row_i * g : col;
   auto valid_id = [&](int id) __attribute__((always_inline)) {
     return (unsigned)id < (unsigned)p.num_blocks ? id : 0;
   };
@@ -396,10 +412,19 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   };
   // Query fragments (MFMA B operand) of pair (s, kv): head kv g + col, chunks 4c + grp.
   auto load_q = [&](u32x4 (&qf)[NKC], int s, int kv) __attribute__((always_inline)) {
-    const char* qrow = (const char*)p.q + ((size_t)s * p.num_heads + kv * g + col) * ROWB;
+    if constexpr (ROWS) {
+      const int q0 = qsf(s);
+      const bool ok = col < p.rows && row_i < qsf(s + 1) - q0;  // q0 + row_i < total_q
+      const char* qrow = (const char*)p.q + ((size_t)(q0 + row_i) * p.num_heads + kv * g + row_h) * ROWB;
 #pragma unroll
-    for (int c = 0; c < NKC; ++c)
-      qf[c] = col < g ? *reinterpret_cast<const u32x4*>(qrow + (4 * c + grp) * 16) : u32x4{0, 0, 0, 0};
+      for (int c = 0; c < NKC; ++c)
+        qf[c] = ok ? *reinterpret_cast<const u32x4*>(qrow + (4 * c + grp) * 16) : u32x4{0, 0, 0, 0};
+    } else {
+      const char* qrow = (const char*)p.q + ((size_t)s * p.num_heads + kv * g + col) * ROWB;
+#pragma unroll
+      for (int c = 0; c < NKC; ++c)
+        qf[c] = col < g ? *reinterpret_cast<const u32x4*>(qrow + (4 * c + grp) * 16) : u32x4{0, 0, 0, 0};
+    }
   };
 
   struct Tile {
@@ -474,6 +499,14 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
       // is flushed when `cc` finishes a segment.
       TileCursor lc{s0, (int)(off / n0), (int)(off % n0), n0, L0};
       TileCursor cc = lc;
+      // ROWS: tokens this lane's query row sees in the compute cursor's pair (query i of
+      // the pair's n queries sits at position L - n + i); padding rows see them all
+      auto visible = [&](int s, int L) {
+        const int nq = qsf(s + 1) - qsf(s);
+        return row_i < nq ? L - nq + row_i + 1 : L;
+      };
+      int c_vis = 0;
+      if constexpr (ROWS) c_vis = visible(cc.s, cc.L);
 
       // load side: ids of lc's current window (`ids_cur`) and the next one, the
       // first two windows of lc's sequence (for its next KV head) and of the next
@@ -619,36 +652,87 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
       // Matrix-core layout: every row group already holds the full sums of head col
       // for its 4*VE elements, and the reference maximum m is the same in all four
       // groups; only the running sums are added over the groups.
-      auto flush_mpv = [&](int s, int kv, int jb, int je, int L, long long tseg) __attribute__((always_inline)) {
+      // ROWS: store one piece's partial result (running max, sum and unnormalised
+      // accumulator of every row) in its slot.  The slot holds R rows x D floats in 16-byte
+      // chunks: chunk j of lane (grp, col), elements (4 grp + r) VE + i .. + 3 of row col
+      // with j = r VE/4 + i/4, sits at chunk (4 j + grp) R + col, so each store instruction
+      // writes 4 R consecutive chunks (whole cache lines) and the merge reads them back the
+      // same way.  The decode variants keep row-major slots.
+      auto store_piece = [&](size_t slot, const f32x4 (&acc4)[MPV ? VE : 1], float mx, float sum, int R)
+          __attribute__((always_inline)) {
+        f32x4* dst = reinterpret_cast<f32x4*>(p.ws_acc + slot * R * D);
+        const int off0 = grp * R + col, stride = 4 * R;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int i = 0; i < VE; i += 4)
+            dst[off0 + (r * (VE / 4) + i / 4) * stride] =
+                f32x4{acc4[i][r], acc4[i + 1][r], acc4[i + 2][r], acc4[i + 3][r]};
+        if (grp == 0) {
+          float* ml = p.ws_ml + (slot * R + col) * 2;
+          ml[0] = mx;
+          ml[1] = sum;
+        }
+      };
+      // Matrix-core P.V: a chunk's first piece, when the chunk goes on past it, is kept in
+      // registers and stored after the chunk's last tile, so that no load wait inside the
+      // stream also waits for those stores (stores and loads share one counter).
+      // Llama-3-8B decode 389.6 against 394 us; verification 411 against 446.
+      f32x4 def_acc[MPV ? VE : 1];
+      float def_m = 0.f, def_l = 0.f;
+      size_t def_slot = 0;
+      bool has_def = false;
+
+      auto flush_mpv = [&](int s, int kv, int jb, int je, int L, long long tseg, bool chunk_end) __attribute__((always_inline)) {
         float ls = l;
         ls += __shfl_xor(ls, 16);
         ls += __shfl_xor(ls, 32);
         const int n_pair = tiles_of(L);
         const int d0 = 4 * grp * VE;  // first element of this lane's run
-        if (col < g) {
+        const int R = ROWS ? p.rows : g;
+        if (col < R) {
           float o[4 * VE];
           if (jb == 0 && je == n_pair) {
+            size_t orow = (size_t)s * p.num_heads + kv * g + col;
+            bool out_ok = true;
+            if constexpr (ROWS) {
+              const int q0 = qsf(s);
+              out_ok = row_i < qsf(s + 1) - q0;
+              orow = (size_t)(q0 + row_i) * p.num_heads + kv * g + row_h;
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r)
 #pragma unroll
               for (int i = 0; i < VE; ++i) o[r * VE + i] = oacc[i][r] / ls;
-            store_row<DT, 4 * VE>((char*)p.out + ((size_t)s * p.num_heads + kv * g + col) * ROWB + d0 * EB, o);
+            if (out_ok) store_row<DT, 4 * VE>((char*)p.out + orow * ROWB + d0 * EB, o);
           } else {
             const size_t slot = 2 * (size_t)ck + (jb == 0 ? 1 : 0);
-            float* dst = p.ws_acc + (slot * g + col) * D + d0;
+            if (jb != 0 && !chunk_end) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
+              for (int i = 0; i < (MPV ? VE : 1); ++i) def_acc[i] = oacc[i];
+              def_m = m;
+              def_l = ls;
+              def_slot = slot;
+            } else if constexpr (ROWS) {
+              store_piece(slot, oacc, m, ls, R);
+            } else {
+              // row-major slots: row col's elements d0 .. d0 + 4 VE - 1 from this lane
+              float* dst = p.ws_acc + (slot * R + col) * D + d0;
 #pragma unroll
-              for (int i = 0; i < VE; i += 4)
-                *reinterpret_cast<f32x4*>(dst + r * VE + i) =
-                    f32x4{oacc[i][r], oacc[i + 1][r], oacc[i + 2][r], oacc[i + 3][r]};
-            if (grp == 0) {
-              float* ml = p.ws_ml + (slot * g + col) * 2;
-              ml[0] = m;
-              ml[1] = ls;
+              for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int i = 0; i < VE; i += 4)
+                  *reinterpret_cast<f32x4*>(dst + r * VE + i) =
+                      f32x4{oacc[i][r], oacc[i + 1][r], oacc[i + 2][r], oacc[i + 3][r]};
+              if (grp == 0) {
+                float* ml = p.ws_ml + (slot * R + col) * 2;
+                ml[0] = m;
+                ml[1] = ls;
+              }
             }
           }
         }
+        if (jb != 0 && !chunk_end) has_def = true;
         if (!(jb == 0 && je == n_pair)) note_piece(s, kv, jb, n_pair, tseg);
         m = kNegBig;
         l = 0.f;
@@ -657,9 +741,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
       };
 
       // Normalise or store the finished segment [jb, je) of pair (s, kv).
-      auto flush = [&](int s, int kv, int jb, int je, int L, long long tseg) __attribute__((always_inline)) {
+      auto flush = [&](int s, int kv, int jb, int je, int L, long long tseg, bool chunk_end) __attribute__((always_inline)) {
         if constexpr (MPV) {
-          flush_mpv(s, kv, jb, je, L, tseg);
+          flush_mpv(s, kv, jb, je, L, tseg, chunk_end);
         } else {
           // Merge the four per-group streams of every head.
           float M = fmaxf(m, __shfl_xor(m, 16));
@@ -745,7 +829,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
           }
         }
         // online softmax, stream (grp, head col); tokens past the end get -inf
-        const int lim = cc.L - kTileTokens * cc.j - 4 * grp;
+        const int lim = (ROWS ? c_vis : cc.L) - kTileTokens * cc.j - 4 * grp;
         float sv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) sv[r] = r < lim ? sc[r] * sl2 : -__builtin_inff();
@@ -835,9 +919,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
         TileCursor nx = cc;  // as for lc, the step succeeds whenever a tile is left
         const bool last_tile = c_count + 1 == nt || !nx.next(N, Hkv, lenf);
         if (last_tile || cc.j + 1 == cc.n) {
-          flush(cc.s, cc.kv, seg_jb, cc.j + 1, cc.L, seg_t);
+          flush(cc.s, cc.kv, seg_jb, cc.j + 1, cc.L, seg_t, last_tile);
           if (!last_tile) {  // on to the next pair
             cc = nx;
+            if constexpr (ROWS) c_vis = visible(cc.s, cc.L);
             ++c_count;
             ++c_pair;
             seg_jb = 0;
@@ -873,6 +958,24 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
           __builtin_amdgcn_sched_barrier(0);
         });
       }
+      if constexpr (ROWS) {
+        if (has_def && col < p.rows) store_piece(def_slot, def_acc, def_m, def_l, p.rows);
+      } else if constexpr (MPV) {
+        if (has_def && col < g) {
+          float* dst = p.ws_acc + (def_slot * g + col) * D + 4 * grp * VE;
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int i = 0; i < VE; i += 4)
+              *reinterpret_cast<f32x4*>(dst + r * VE + i) =
+                  f32x4{def_acc[i][r], def_acc[i + 1][r], def_acc[i + 2][r], def_acc[i + 3][r]};
+          if (grp == 0) {
+            float* ml = p.ws_ml + (def_slot * g + col) * 2;
+            ml[0] = def_m;
+            ml[1] = def_l;
+          }
+        }
+      }
     }
     // Every chunk states whether it owns a split pair (parts >= 2) and whether it
     // left a first piece of one in slot 2c.
@@ -896,11 +999,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
 // For pa_decode_append the workgroups from merge_blocks on store each sequence's
 // newest K and V rows (read from new_k/new_v by the decode kernel, which has
 // finished) into the slot of position L - 1, 16 bytes per lane, alongside the merges.
-template <int DT, int D, int GP>
+template <int DT, int D, int GP, bool ROWS>
 __global__ __launch_bounds__(256) void reduce_kernel(DecodeParams p) {
   constexpr int LPH = 64 / GP;   // lanes per head
   constexpr int EPL = D / LPH;   // accumulator elements per lane
   constexpr int EB = Elem<DT>::bytes;
+  static_assert(!ROWS || (kMatrixPV<DT, GP> && EPL % 4 == 0), "chunked slots hold 4-element runs");
   if ((int)blockIdx.x >= p.merge_blocks) {
     constexpr int PPR = D * EB / 16;  // 16-byte pieces per row
     const long long x = (long long)(blockIdx.x - p.merge_blocks) * 256 + threadIdx.x;
@@ -942,9 +1046,10 @@ __global__ __launch_bounds__(256) void reduce_kernel(DecodeParams p) {
   const int kv = meta[1];
   if (s < 0 || s >= p.num_seqs || kv < 0 || kv >= p.num_kv_heads) return;
   const int g = p.group;
+  const int R = p.rows;          // rows of a pair: the group's heads, or (query, head) rows
   const int h = lane / LPH;
   const int sub = lane % LPH;
-  const int hr = h < g ? h : 0;  // lanes of padding heads read head 0 and store nothing
+  const int hr = h < R ? h : 0;  // lanes of padding rows read row 0 and store nothing
 
   float m = kNegBig, l = 0.f;
   float acc[EPL];
@@ -974,12 +1079,29 @@ __global__ __launch_bounds__(256) void reduce_kernel(DecodeParams p) {
       for (int k = 0; k < kBatch; ++k) {
         if (!ok[k]) continue;
         const size_t sl = bi[k] == 0 ? 2 * (size_t)c + 1 : 2 * ((size_t)c + bi[k]);
-        const size_t r = sl * g + hr;
+        const size_t r = sl * R + hr;
         mi[k] = p.ws_ml[2 * r];
         li[k] = p.ws_ml[2 * r + 1];
-        const float* a = p.ws_acc + r * D + sub * EPL;
+        if constexpr (ROWS) {
+          // the rows mode's chunked slot layout (store_piece): element e = (4 grp + r) VE + i
+          // of row hr is in chunk (4 (r VE/4 + i/4) + grp) R + hr
+          constexpr int VE = D / 16;
+          const f32x4* a = reinterpret_cast<const f32x4*>(p.ws_acc + sl * R * D);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) av[k][e] = a[e];
+          for (int e4 = 0; e4 < EPL; e4 += 4) {
+            const int e = sub * EPL + e4;
+            const int grp = e / (4 * VE), rr = (e / VE) % 4, i = e % VE;
+            const f32x4 x = a[(4 * (rr * (VE / 4) + i / 4) + grp) * R + hr];
+            av[k][e4] = x[0];
+            av[k][e4 + 1] = x[1];
+            av[k][e4 + 2] = x[2];
+            av[k][e4 + 3] = x[3];
+          }
+        } else {
+          const float* a = p.ws_acc + r * D + sub * EPL;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) av[k][e] = a[e];
+        }
       }
 #pragma unroll
       for (int k = 0; k < kBatch; ++k) {
@@ -994,26 +1116,43 @@ __global__ __launch_bounds__(256) void reduce_kernel(DecodeParams p) {
       }
     }
   }
-  if (h < g) {
+  size_t orow = (size_t)s * p.num_heads + kv * g + h;
+  bool ok = h < R;
+  if constexpr (ROWS) {  // row h is query h / g, head h % g
+    const int q0 = min(max(p.q_start[s], 0), p.total_q);
+    const int i = h / g;
+    ok = ok && i < min(max(p.q_start[s + 1], 0), p.total_q) - q0;
+    orow = (size_t)(q0 + i) * p.num_heads + kv * g + (h - i * g);
+  }
+  if (ok) {
     float o[EPL];
 #pragma unroll
     for (int e = 0; e < EPL; ++e) o[e] = acc[e] / l;
-    store_row<DT, EPL>((char*)p.out + ((size_t)s * p.num_heads + kv * g + h) * (D * EB) + sub * (EPL * EB), o);
+    store_row<DT, EPL>((char*)p.out + orow * (D * EB) + sub * (EPL * EB), o);
   }
 }
 
-// The decode and merge kernels of one shape (nullptr if not compiled).
-// Three decode variants: streaming K/V loads (pa_decode), the same with the append
-// (pa_decode_append), and default-policy loads (pa_decode_cached).
+// The decode and merge kernels of one shape (false if not compiled).  Four decode
+// variants: streaming K/V loads (pa_decode), the same with the append
+// (pa_decode_append), default-policy loads (pa_decode_cached), and the multi-query rows
+// (pa_multi_query with at most 16 rows per (sequence, KV head), 16-bit types, GP = 16).
 template <int DT, int D, int BS, int GP>
 bool pick(DecodeVariant v, const void** dec, const void** red) {
   switch (v) {
-    case DecodeVariant::kStream: *dec = reinterpret_cast<const void*>(&decode_kernel<DT, D, BS, GP, false, true>); break;
-    case DecodeVariant::kAppend: *dec = reinterpret_cast<const void*>(&decode_kernel<DT, D, BS, GP, true, true>); break;
-    case DecodeVariant::kCached: *dec = reinterpret_cast<const void*>(&decode_kernel<DT, D, BS, GP, false, false>); break;
+    case DecodeVariant::kStream: *dec = reinterpret_cast<const void*>(&decode_kernel<DT, D, BS, GP, false, true, false>); break;
+    case DecodeVariant::kAppend: *dec = reinterpret_cast<const void*>(&decode_kernel<DT, D, BS, GP, true, true, false>); break;
+    case DecodeVariant::kCached: *dec = reinterpret_cast<const void*>(&decode_kernel<DT, D, BS, GP, false, false, false>); break;
+    case DecodeVariant::kRows:
+      if constexpr (GP == 16 && DT != kF32) {
+        *dec = reinterpret_cast<const void*>(&decode_kernel<DT, D, BS, GP, false, true, true>);
+        break;
+      } else {
+        return false;
+      }
     default: return false;
   }
-  *red = reinterpret_cast<const void*>(&reduce_kernel<DT, D, GP>);
+  *red = v == DecodeVariant::kRows ? reinterpret_cast<const void*>(&reduce_kernel<DT, D, GP, GP == 16 && DT != kF32>)
+                                   : reinterpret_cast<const void*>(&reduce_kernel<DT, D, GP, false>);
   return true;
 }
 

@@ -3,8 +3,14 @@
 #pragma once
 
 #include "common.h"
+#include "pagedkv.h"
 
 namespace pagedkv {
+
+// Batches of at most this many sequences keep every sequence's length and tile
+// prefix sum in LDS (each wave its own copy), so locating a chunk and stepping to
+// the next sequence read LDS instead of global memory.
+constexpr int kLdsSeqs = 2048;
 
 // Everything one pa_decode launch needs, already validated by the host code.
 struct DecodeParams {
@@ -40,12 +46,20 @@ struct DecodeParams {
   const void* new_v;
   int merge_blocks;    // workgroups of the merge kernel that merge (one wave per chunk)
   int append_blocks;   // workgroups after them that store the newest rows (0 = none)
+  // pa_multi_query on the decode kernels (null otherwise): query rows of sequence s are
+  // q_start[s] .. q_start[s+1] - 1 of q and out, and row r of pair (s, kv) is query
+  // r / group, head r % group, seeing the tokens up to its own position.
+  const int32_t* q_start;
+  int rows;            // rows of one (sequence, KV head) pair: group, or the multi-query
+                       // rows (max_q_len * group, at most 16)
+  int total_q;         // rows mode: query rows of q and out (q_start values are clamped
+                       // to [0, total_q], so no access leaves them)
 };
 
 // Decode kernel variants: K/V loads with the non-temporal hint (pa_decode), the same
 // with the append of the newest tokens (pa_decode_append), and K/V loads with the
 // default cache policy (pa_decode_cached).
-enum class DecodeVariant { kStream, kAppend, kCached };
+enum class DecodeVariant { kStream, kAppend, kCached, kRows };
 
 // The decode and merge kernels for one shape, one translation unit per element
 // type; false for a shape outside the compiled set.  `gp` is the padded group.
@@ -55,6 +69,28 @@ bool decode_kernels_f16(int head_dim, int block_size, int gp, DecodeVariant vari
                         const void** dec, const void** red);
 bool decode_kernels_bf16(int head_dim, int block_size, int gp, DecodeVariant variant,
                          const void** dec, const void** red);
+
+// pa_multi_query on the decode kernels ("rows mode"): when every (sequence, KV head)
+// pair has at most 16 (query, head) rows, the batch's tables fit the decode kernel's
+// LDS (at most kLdsSeqs sequences, tile prefix sums below 2^31) and the decode kernels
+// cover the shape, each
+// pair's rows take the 16 columns of the decode kernel's score tile, every row with its
+// own causal limit, and the work is split evenly over the waves as for pa_decode.
+// `multi_query_rows_apply` says whether the mode covers the shape; the workspace it
+// needs is `multi_query_rows_workspace` bytes (any 16-byte aligned buffer: the call
+// clears the part it counts on).  Launches a header clear, the decode kernel and the
+// merge kernel on `st`.
+bool multi_query_rows_apply(pa_dtype dtype, int num_seqs, int num_heads, int num_kv_heads,
+                            int head_dim, int block_size, int max_q_len, int max_seq_len);
+size_t multi_query_rows_workspace(int num_seqs, int num_kv_heads, int head_dim, int max_seq_len,
+                                  int rows);
+pa_status multi_query_rows(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_tables, const int32_t* seq_lens,
+                           const int32_t* q_start, int num_seqs, int total_q, int num_heads,
+                           int num_kv_heads, int head_dim, int block_size, int num_blocks,
+                           int max_blocks_per_seq, int max_q_len, int max_seq_len, float scale,
+                           pa_dtype dtype, void* out,
+                           void* workspace, size_t workspace_bytes, hipStream_t st);
 
 // Smallest group size of the compiled decode variants that can hold `group`
 // query heads (1, 2, 4, 8, 16), or 0 if none can.

@@ -2,6 +2,9 @@
 // dispatch of the kernels in multi_query.hip.
 #include <vector>
 
+#include <algorithm>
+
+#include "decode_params.h"
 #include "host_util.h"
 #include "multi_query.h"
 #include "pagedkv.h"
@@ -57,6 +60,13 @@ MQPlan mq_plan(int num_seqs, int total_q, int num_heads, int num_kv_heads, int h
   return pl;
 }
 
+// PA_MULTI_QUERY_ROWS=0 keeps pa_multi_query on its own kernels for every shape (for
+// comparisons); the rows mode is on by default.
+bool multi_query_rows_enabled() {
+  static const int v = env_int("PA_MULTI_QUERY_ROWS", 1);
+  return v != 0;
+}
+
 bool mq_shapes_ok(int num_seqs, int total_q, int num_heads, int num_kv_heads, int head_dim,
                   int max_q_len, int max_seq_len) {
   return num_seqs >= 0 && total_q >= 0 && num_heads > 0 && num_kv_heads > 0 && head_dim > 0 &&
@@ -71,8 +81,13 @@ size_t pa_multi_query_workspace_size(int num_seqs, int total_q, int num_heads, i
   if (!mq_shapes_ok(num_seqs, total_q, num_heads, num_kv_heads, head_dim, max_q_len, max_seq_len))
     return 0;
   // the workspace does not depend on the element type (the split variant has one
-  // query block whenever it applies, like the other)
-  return mq_plan(num_seqs, total_q, num_heads, num_kv_heads, head_dim, max_q_len, max_seq_len, PA_BF16).total;
+  // query block whenever it applies, like the other); where the rows mode may apply
+  // (16-bit types, at most 16 rows per pair), it covers that mode's too
+  size_t n = mq_plan(num_seqs, total_q, num_heads, num_kv_heads, head_dim, max_q_len, max_seq_len, PA_BF16).total;
+  const long long rows = (long long)max_q_len * (num_heads / num_kv_heads);
+  if (rows >= 1 && rows <= 16 && (head_dim == 64 || head_dim == 128))
+    n = std::max(n, multi_query_rows_workspace(num_seqs, num_kv_heads, head_dim, max_seq_len, (int)rows));
+  return n;
 }
 
 pa_status pa_multi_query(const void* q, const void* k_cache, const void* v_cache,
@@ -156,6 +171,16 @@ pa_status pa_multi_query(const void* q, const void* k_cache, const void* v_cache
       }
     }
   }
+  // At most 16 rows per (sequence, KV head) pair (verification of a few drafted tokens):
+  // the decode kernels, whose even split of the step over the waves streams the cache
+  // faster than one work item per workgroup
+  if (multi_query_rows_enabled() &&
+      multi_query_rows_apply(dtype, num_seqs, num_heads, num_kv_heads, head_dim, block_size, max_q_len,
+                             max_seq_len))
+    return multi_query_rows(q, k_cache, v_cache, block_tables, seq_lens, q_start, num_seqs, total_q,
+                            num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                            max_blocks_per_seq, max_q_len, max_seq_len, scale, dtype, out, workspace,
+                            workspace_bytes, st);
   const void* kmain = nullptr;
   const void* kmerge = nullptr;
   if (!multi_query_kernels((int)dtype, head_dim, pl.rows, false, &kmain, &kmerge))

@@ -198,6 +198,15 @@ def test_multi_query_workspace_formula(pk, N, TQ, H, HKV, D, MQ, L):
     want = 0 if parts == 1 else up(TQ * H * parts * 2 * 4) + TQ * H * parts * D * 4
     if N > 0:   # a longest-first order of the sequences
         want += up(4 * N)
+    rows = MQ * g
+    if 1 <= rows <= 16:
+        # the rows mode's workspace (the decode kernels' layout with `rows` rows per pair):
+        # one wave per 8 tiles of the longest batch (at most 2048), five chunks per wave, a
+        # 256-byte header and 16 bytes per chunk, then two partial slots of rows x (D + 2)
+        # floats per chunk; the size covers whichever mode the call takes
+        waves = min(2048, max(1, -(-(N * HKV * math.ceil(L / 16)) // 8)))
+        chunks = 5 * waves
+        want = max(want, up(256 + chunks * 16) + up(2 * chunks * rows * 2 * 4) + 2 * chunks * rows * D * 4)
     assert pk.pa_multi_query_workspace_size(N, TQ, H, HKV, D, MQ, L) == want
 
 

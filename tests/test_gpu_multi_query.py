@@ -76,11 +76,17 @@ SWEEP = [  # dtype, D, B, Hq, Hkv, lens, queries
     ("bf16", 128, 5, 64, 8, [77, 200], [9, 8]),
     ("f32", 128, 16, 8, 2, [45, 90], [20, 90]),
     ("bf16", 128, 16, 40, 40, [18, 260], [18, 33]),
-    # at most 16 rows per (sequence, KV head): the four waves split the context
+    # at most 16 rows per (sequence, KV head), block sizes 8/16/32: the decode kernels'
+    # rows mode (each pair's rows in the 16 columns of a score tile)
     ("f16", 64, 16, 16, 8, [5, 300, 33], [5, 8, 1]),
     ("bf16", 128, 8, 16, 1, [40, 1, 77], [1, 1, 1]),
     ("bf16", 64, 32, 4, 4, [700, 16, 90], [16, 16, 2]),
     ("bf16", 128, 16, 32, 8, [31, 64, 65, 200], [4, 4, 3, 4]),
+    ("bf16", 128, 16, 32, 8, [1, 2, 3, 17, 33, 300], [0, 2, 1, 2, 0, 2]),    # 8 rows, no-query sequences
+    ("f16", 128, 8, 12, 4, [5000, 3, 4099], [4, 3, 1]),                      # split pairs, 12 rows
+    # the same row counts with other block sizes: the split variant (four waves split the context)
+    ("bf16", 128, 5, 32, 8, [31, 64, 65, 200], [4, 4, 3, 4]),
+    ("f16", 64, 12, 16, 8, [5, 300, 33], [5, 8, 1]),
 ]
 
 
@@ -137,8 +143,8 @@ def test_negative_and_zero_scale(dtype, scale, queries):
 
 
 def test_long_context_few_queries_uses_partitions():
-    # one sequence, 3 queries, 5000 tokens: few work items, so the context is split
-    # into partitions and merged by the second kernel
+    # one sequence, 3 queries, 5000 tokens: the rows mode cuts its pairs over many waves
+    # and the merge kernel folds the pieces
     b = batch(7, "bf16", [5000], [3], 8, 8, 128, 16)
     m = pk()
     assert m.pa_multi_query_workspace_size(1, 3, 8, 8, 128, 3, 5000) > 0
@@ -196,8 +202,9 @@ def test_many_short_sequences_in_longest_first_order():
 
 
 def test_more_sequences_than_the_ordering_pass_sorts_in_one_sweep():
-    # 2100 short sequences (more than twice the ordering pass's 1024 threads), up to 16
-    # (query, head) rows per KV head (the split variant); some sequences have no queries
+    # 2100 short sequences (more than twice the ordering pass's 1024 threads, and more
+    # than the decode kernels keep in LDS, so the split variant runs), up to 16 (query,
+    # head) rows per KV head; some have no queries
     rng = np.random.default_rng(23)
     lens = rng.integers(1, 61, 2100).tolist()
     qn = [int(min(L, q)) for L, q in zip(lens, rng.integers(0, 5, 2100))]
