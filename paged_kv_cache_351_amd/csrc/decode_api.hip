@@ -412,12 +412,16 @@ pa_status multi_query_rows(const void* q, const void* k_cache, const void* v_cac
   if (!workspace || workspace_bytes < ws.total)
     return fail(PA_ERR_WORKSPACE, "pa_multi_query: workspace of %zu bytes, %zu needed",
                 workspace ? workspace_bytes : (size_t)0, ws.total);
-  // the workspace carries no state between pa_multi_query calls: the counter that hands
-  // out tail parts is cleared first (a kernel, not a memset, so that a capture stays valid)
+  // The workspace carries no state between pa_multi_query calls.  Without tail parts
+  // (the default) nothing reads the counter that hands them out, and the decode kernel
+  // writes the chunk count and every chunk record itself; with them the counter is
+  // cleared first (a kernel, not a memset, so that a capture stays valid).
   char* base = static_cast<char*>(workspace);
-  hipLaunchKernelGGL(clear_header_kernel, dim3(1), dim3(64), 0, st, reinterpret_cast<int*>(base));
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return hip_fail(e, "pa_multi_query: clearing the workspace header");
+  if (p.tail_div > 0) {
+    hipLaunchKernelGGL(clear_header_kernel, dim3(1), dim3(64), 0, st, reinterpret_cast<int*>(base));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "pa_multi_query: clearing the workspace header");
+  }
   return launch_decode(&p, dec, red, base, ws, st);
 }
 
