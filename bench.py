@@ -757,7 +757,11 @@ def main():
             res["value"] = ub / (total / K) / 1e9
             res["pct_of_hbm_peak"] = 100.0 * res["value"] / HBM_PEAK_GBS
             res["logical_kv_gbs"] = kv_bytes / (total / K) / 1e9
-            res["roofline"].update({"kernel": "pa_decode_shared_prefix (multi_query_kernel, shared layout)",
+            split = os.environ.get("PA_SHARED_PREFIX_ROWS") == "0"
+            res["roofline"].update({"kernel": "pa_decode_shared_prefix (multi_query_kernel, shared layout)"
+                                    if split else
+                                    "pa_decode_shared_prefix (decode_kernel rows mode over laid-out group "
+                                    "tables, + shared_layout_kernel and reduce_kernel)",
                                     "achieved": res["roofline"]["achieved_unique"],
                                     "frac": res["roofline"]["achieved_unique"] / HBM_PEAK_GBS,
                                     "algorithmic_bytes_per_launch": ub})
@@ -770,7 +774,10 @@ def main():
         flops = 4.0 * b.causal_pairs() * b.num_heads * b.head_dim
         res["config"]["query_rows"] = int(q.shape[0])
         res["config"]["causal_flops_per_step"] = flops
-        res["roofline"]["kernel"] = "pa_multi_query (multi_query_kernel)"
+        res["roofline"]["kernel"] = ("pa_multi_query (decode_kernel rows mode + reduce_kernel)"
+                                     if args.workload.endswith("spec") and
+                                     os.environ.get("PA_MULTI_QUERY_ROWS") != "0" else
+                                     "pa_multi_query (multi_query_kernel)")
         if args.workload.endswith("chunk"):
             tf = flops / (dec_avg * 1e-3) / 1e12
             res.update({"value": flops / (total / K) / 1e12, "unit": "TFLOP/s"})

@@ -327,12 +327,22 @@ pa_status pa_multi_query(const void* q, const void* k_cache, const void* v_cache
  *                  member's length
  *   max_group_size host bound on every group's size
  *   other arguments as for pa_decode (block_size any positive value here)
- *   workspace      pa_decode_shared_prefix_workspace_size(...) bytes: a
- *                  longest-first order of the groups and, when the context is
- *                  partitioned, partial results; no zero-fill needed
+ *   workspace      pa_decode_shared_prefix_workspace_size(...) bytes, 16-byte
+ *                  aligned, no zero-fill needed (enough for either path below)
  *
  * A group is processed in blocks of 16 / (num_heads / num_kv_heads) members
  * (at most 16 query heads per KV head); each block reads the prefix once.
+ * With block_size 8, 16 or 32, fewer than 2^22 blocks in the pool and at most
+ * 2,048 such member blocks, the call runs on pa_decode's kernels: a layout
+ * kernel writes, for every member block, one table holding the prefix (rounded
+ * down to whole 16-token units, or 32-token blocks) and then each member's own
+ * tokens, each member's part starting on a whole unit; the decode kernel reads
+ * those tables with the members as the rows of each (block, KV head) pair,
+ * every row seeing the prefix and its own part only, the step split evenly
+ * over the waves; the merge kernel folds pairs cut by a wave boundary.
+ * Otherwise a multi-query kernel takes (group block, KV head, context
+ * partition) items, longest group first, with a partition merge when there are
+ * few items.  PA_SHARED_PREFIX_ROWS=0 selects the second path for every call.
  * float16 and bfloat16 only (PA_ERR_UNSUPPORTED for float32).  Index data that
  * breaks the contract is clamped so that no access leaves the arrays, with
  * unspecified results; PA_DEBUG_CHECK=1 rejects it, including tables that do

@@ -47,6 +47,14 @@ int env_int(const char* name, int dflt) {
   return (end && *end == 0 && v > 0 && v < (1L << 30)) ? (int)v : dflt;
 }
 
+bool env_flag(const char* name, bool dflt) {
+  const char* s = getenv(name);
+  if (!s || !*s) return dflt;
+  if (s[0] == '0' && s[1] == 0) return false;
+  if (s[0] == '1' && s[1] == 0) return true;
+  return dflt;
+}
+
 bool debug_checks() {
   static const bool on = env_int("PA_DEBUG_CHECK", 0) == 1;
   return on;

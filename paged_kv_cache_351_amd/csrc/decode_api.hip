@@ -298,6 +298,7 @@ pa_status prepare_decode(DecodeVariant variant, const void* q, const void* k_cac
   p->q_start = nullptr;
   p->rows = group;
   p->total_q = 0;
+  p->shared = 0;
   p->ws_meta = nullptr;
   p->ws_ml = nullptr;
   p->ws_acc = nullptr;
@@ -423,6 +424,210 @@ pa_status multi_query_rows(const void* q, const void* k_cache, const void* v_cac
     if (e != hipSuccess) return hip_fail(e, "pa_multi_query: clearing the workspace header");
   }
   return launch_decode(&p, dec, red, base, ws, st);
+}
+
+namespace {
+
+// pa_decode_shared_prefix on the rows mode.  Group j's members are taken in blocks of
+// `mpb` (at most 16 / group); block v = j * cpg + c holds members
+// group_start[j] + c * mpb ... (none when the group is smaller).  Each block's table is
+// laid out as: the group's prefix, cut down to whole units (a unit is max(block size, 16)
+// tokens, so every region starts on a tile and on a block), read once; then, for each
+// member in order, its tokens past that prefix, padded to whole units.  Member i of the
+// block is row i (with its group's heads); the prefix is everyone's.
+struct SharedRowsLayout {
+  int mpb = 0;          // members per block
+  int cpg = 0;          // blocks per group
+  int vgroups = 0;      // blocks of all groups: the "sequences" the decode kernel sees
+  int unit = 0;         // region alignment in tokens
+  int max_vlen = 0;     // bound on a laid-out length
+  int max_vblocks = 0;  // entries per laid-out table
+  WorkspaceLayout dec{0, 0, 0, 0};
+  size_t table_off = 0, lens_off = 0, qs_off = 0, total = 0;
+  bool ok = false;      // the shapes fit the decode kernel's LDS tables and the length bound
+};
+
+SharedRowsLayout shared_rows_layout(int num_seqs, int num_groups, int num_heads, int num_kv_heads,
+                                    int head_dim, int block_size, int max_group_size, int max_seq_len) {
+  SharedRowsLayout L;
+  if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 || num_groups <= 0 ||
+      max_group_size <= 0 || max_seq_len < 0 || !valid_block_size(block_size))
+    return L;
+  const int group = num_heads / num_kv_heads;
+  if (group > 16) return L;
+  L.mpb = std::min(16 / group, max_group_size);
+  L.cpg = (max_group_size + L.mpb - 1) / L.mpb;
+  const long long vg = (long long)num_groups * L.cpg;
+  L.unit = std::max(block_size, kTileTokens);
+  const long long per = ((long long)max_seq_len + L.unit - 1) / L.unit * L.unit;
+  const long long vlen = std::max<long long>(per * (L.mpb + 1), L.unit);
+  if (vg > kLdsSeqs || vlen > kMaxSeqLen || vg * tiles_of((int)vlen) >= (1LL << 31) - 1) return L;
+  L.vgroups = (int)vg;
+  L.max_vlen = (int)vlen;
+  L.max_vblocks = L.max_vlen / block_size;
+  const long long t_max = (long long)num_seqs * num_kv_heads * tiles_of(max_seq_len);
+  L.dec = layout_for(waves_used(t_max, kMaxWaves), kMaxTailPieces, L.mpb * group, head_dim);
+  L.table_off = align_up(L.dec.total, 256);
+  L.lens_off = L.table_off + align_up((size_t)L.vgroups * L.max_vblocks * sizeof(int32_t), 256);
+  L.qs_off = L.lens_off + align_up((size_t)L.vgroups * sizeof(int32_t), 256);
+  L.total = L.qs_off + ((size_t)L.vgroups + 1) * sizeof(int32_t);
+  L.ok = true;
+  return L;
+}
+
+struct SharedLayoutArgs {
+  const int32_t* block_tables;
+  const int32_t* seq_lens;
+  const int32_t* group_start;
+  const int32_t* prefix_lens;
+  int32_t* vtable;
+  int32_t* vlens;
+  int32_t* vqs;
+  char* out;
+  int num_seqs, cpg, mpb, vgroups, block_size, unit;
+  int max_blocks_per_seq, max_seq_len, num_blocks, max_vblocks;
+  int out_row_bytes;  // one sequence's output rows (all heads)
+};
+
+// One wave per laid-out block of members: its table, length and first member row, and
+// zeros for the output of every empty member (which sees no token).  Index data outside
+// the contract is clamped so that every read stays in its array.
+__global__ __launch_bounds__(64) void shared_layout_kernel(SharedLayoutArgs a) {
+  __shared__ int s_len[16], s_start[16], s_tail[16];
+  const int v = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int j = v / a.cpg, c = v - j * a.cpg;
+  const int ga = min(max(a.group_start[j], 0), a.num_seqs);
+  const int gb = min(max(a.group_start[j + 1], ga), a.num_seqs);
+  const int m0 = (int)min((long long)ga + (long long)c * a.mpb, (long long)gb);
+  const int nq = min(m0 + a.mpb, gb) - m0;
+  const int B = a.block_size, U = a.unit;
+  int P = nq > 0 ? min(max(a.prefix_lens[j], 0), a.max_seq_len) : 0;
+  P = P / U * U;
+  if (lane < nq) s_len[lane] = min(max(a.seq_lens[m0 + lane], 0), a.max_seq_len);
+  __syncthreads();
+  if (lane == 0) {
+    int S = P;
+    for (int i = 0; i < nq; ++i) {
+      const int t = max(s_len[i] - P, 0);
+      s_start[i] = S;
+      s_tail[i] = t;
+      S += (t + U - 1) / U * U;
+    }
+    a.vqs[v] = m0;
+    if (v == a.vgroups - 1) a.vqs[a.vgroups] = a.num_seqs;
+    a.vlens[v] = nq > 0 ? s_start[nq - 1] + s_tail[nq - 1] : 0;
+  }
+  __syncthreads();
+  const int Lv = nq > 0 ? s_start[nq - 1] + s_tail[nq - 1] : 0;
+  const int nvb = (Lv + B - 1) / B;
+  for (int k = lane; k < nvb; k += 64) {
+    const int x = k * B;
+    int own = kSharedAll, m = m0, idx = k, e = min(P - x, 32);
+    if (x >= P) {
+      own = 0;
+      for (int i = 0; i < nq; ++i)
+        if (x >= s_start[i] && x - s_start[i] < (s_tail[i] + U - 1) / U * U) own = i;
+      m = m0 + own;
+      const int mb = max((s_len[own] + B - 1) / B, 1);
+      idx = min(P / B + (x - s_start[own]) / B, mb - 1);
+      e = s_start[own] + s_tail[own] - x;
+    }
+    e = min(max(e, 1), 32);
+    int id = a.block_tables[(size_t)m * a.max_blocks_per_seq + idx];
+    id = (unsigned)id < (unsigned)a.num_blocks ? id : 0;
+    a.vtable[(size_t)v * a.max_vblocks + k] =
+        (int)((unsigned)id | ((unsigned)(e - 1) << kSharedEndShift) | ((unsigned)own << kSharedOwnerShift));
+  }
+  for (int i = 0; i < nq; ++i) {
+    if (s_len[i] != 0) continue;
+    uint4* o = reinterpret_cast<uint4*>(a.out + (size_t)(m0 + i) * a.out_row_bytes);
+    for (int x = lane; x < a.out_row_bytes / 16; x += 64) o[x] = make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+}  // namespace
+
+bool shared_rows_apply(pa_dtype dtype, int num_groups, int num_heads, int num_kv_heads,
+                       int head_dim, int block_size, int num_blocks, int max_group_size,
+                       int max_seq_len) {
+  if (dtype == PA_F32 || (head_dim != 64 && head_dim != 128) || !valid_block_size(block_size) ||
+      num_blocks <= 0 || (unsigned)num_blocks > kSharedIdMask + 1u)
+    return false;
+  return shared_rows_layout(0, num_groups, num_heads, num_kv_heads, head_dim, block_size,
+                            max_group_size, max_seq_len).ok;
+}
+
+size_t shared_rows_workspace(int num_seqs, int num_groups, int num_heads, int num_kv_heads,
+                             int head_dim, int block_size, int max_group_size, int max_seq_len) {
+  const SharedRowsLayout L = shared_rows_layout(num_seqs, num_groups, num_heads, num_kv_heads,
+                                                head_dim, block_size, max_group_size, max_seq_len);
+  return L.ok ? L.total : 0;
+}
+
+pa_status shared_rows(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* seq_lens,
+                      const int32_t* group_start, const int32_t* prefix_lens, int num_seqs,
+                      int num_groups, int num_heads, int num_kv_heads, int head_dim,
+                      int block_size, int num_blocks, int max_blocks_per_seq, int max_group_size,
+                      int max_seq_len, float scale, pa_dtype dtype, void* out, void* workspace,
+                      size_t workspace_bytes, hipStream_t st) {
+  const char* who = "pa_decode_shared_prefix";
+  const SharedRowsLayout L = shared_rows_layout(num_seqs, num_groups, num_heads, num_kv_heads,
+                                                head_dim, block_size, max_group_size, max_seq_len);
+  if (!L.ok) return fail(PA_ERR_UNSUPPORTED, "%s: shapes outside the rows path", who);
+  if (!workspace || workspace_bytes < L.total || !aligned16(workspace))
+    return fail(PA_ERR_WORKSPACE, "%s: workspace of %zu bytes, %zu needed (16-byte aligned)", who,
+                workspace ? workspace_bytes : (size_t)0, L.total);
+  DecodeParams p;
+  const void* dec = nullptr;
+  const void* red = nullptr;
+  bool skip = false;
+  pa_status r = prepare_decode(DecodeVariant::kRows, q, k_cache, v_cache, nullptr, nullptr,
+                               block_tables, seq_lens, num_seqs, num_heads, num_kv_heads, head_dim,
+                               block_size, num_blocks, max_blocks_per_seq, max_seq_len, scale, dtype,
+                               out, st, who, nullptr, 0, false, &p, &dec, &red, &skip);
+  if (r != PA_OK || skip) return r;
+  char* base = static_cast<char*>(workspace);
+  SharedLayoutArgs la;
+  la.block_tables = block_tables;
+  la.seq_lens = seq_lens;
+  la.group_start = group_start;
+  la.prefix_lens = prefix_lens;
+  la.vtable = reinterpret_cast<int32_t*>(base + L.table_off);
+  la.vlens = reinterpret_cast<int32_t*>(base + L.lens_off);
+  la.vqs = reinterpret_cast<int32_t*>(base + L.qs_off);
+  la.out = static_cast<char*>(out);
+  la.num_seqs = num_seqs;
+  la.cpg = L.cpg;
+  la.mpb = L.mpb;
+  la.vgroups = L.vgroups;
+  la.block_size = block_size;
+  la.unit = L.unit;
+  la.max_blocks_per_seq = max_blocks_per_seq;
+  la.max_seq_len = max_seq_len;
+  la.num_blocks = num_blocks;
+  la.max_vblocks = L.max_vblocks;
+  la.out_row_bytes = num_heads * head_dim * (dtype == PA_F32 ? 4 : 2);
+  hipLaunchKernelGGL(shared_layout_kernel, dim3((unsigned)L.vgroups), dim3(64), 0, st, la);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "pa_decode_shared_prefix layout launch");
+  p.block_tables = la.vtable;
+  p.seq_lens = la.vlens;
+  p.num_seqs = L.vgroups;
+  p.max_blocks_per_seq = L.max_vblocks;
+  p.max_seq_len = L.max_vlen;
+  p.q_start = la.vqs;
+  p.rows = L.mpb * (num_heads / num_kv_heads);
+  p.total_q = num_seqs;
+  p.shared = 1;
+  p.tail_div = rows_tail_divisor();
+  if (p.tail_div > 0) {
+    hipLaunchKernelGGL(clear_header_kernel, dim3(1), dim3(64), 0, st, reinterpret_cast<int*>(base));
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "pa_decode_shared_prefix: clearing the workspace header");
+  }
+  return launch_decode(&p, dec, red, base, L.dec, st);
 }
 
 }  // namespace pagedkv

@@ -396,6 +396,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   auto valid_id = [&](int id) __attribute__((always_inline)) {
     return (unsigned)id < (unsigned)p.num_blocks ? id : 0;
   };
+  // rows mode: shared-prefix table entries carry more than the block id
+  const int id_mask = ROWS && p.shared ? (int)kSharedIdMask : -1;
   // Raw ids of blocks 64 wi + lane of sequence s, which has nblk blocks.  They
   // are range-checked only where a tile uses them, so a prefetch never stalls on
   // its data; an id outside the pool is a contract violation and becomes 0, so no
@@ -430,6 +432,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   struct Tile {
     u32x4 k[NKC];
     uint32_t v[4][VW];
+    int vis;  // rows mode over shared-prefix groups: the table entry of the tile's block
   };
 
   // The wave's own head chunk first, then tail parts while any are left.
@@ -501,8 +504,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
       TileCursor cc = lc;
       // ROWS: tokens this lane's query row sees in the compute cursor's pair (query i of
       // the pair's n queries sits at position L - n + i); padding rows see them all
+      // Shared-prefix groups: the owner index this lane's row answers to (its member
+      // row; padding rows answer to the prefix owner and so see every tile).
       auto visible = [&](int s, int L) {
         const int nq = qsf(s + 1) - qsf(s);
+        if (p.shared) return row_i < nq ? row_i : kSharedAll;
         return row_i < nq ? L - nq + row_i + 1 : L;
       };
       int c_vis = 0;
@@ -559,7 +565,15 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
           ids_nxt = fetch_ids(l_seq, l_nblk, lw + 1);
         }
         const int a = kTileTokens * lc.j;
-        const int last = lc.L - 1;
+        int last = lc.L - 1;
+        const int raw0 = __builtin_amdgcn_readlane(ids_cur, blk & 63);
+        if constexpr (ROWS) {
+          // shared-prefix tables: tokens past the end of the tile's region (a member's
+          // padding, whose slots need not hold finite values) read its last token instead
+          Tl.vis = raw0;
+          if (p.shared)
+            last = min(last, blk * BS + (int)(((unsigned)raw0 >> kSharedEndShift) & 31u));
+        }
         const int tk = min(a + col, last);
         int tv[4];
 #pragma unroll
@@ -567,13 +581,14 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
         int pk, pv[4];
         if constexpr (BS == 8) {
           // a tile spans two blocks; it starts on a multiple of 16 tokens
-          const int ida = valid_id(__builtin_amdgcn_readlane(ids_cur, blk & 63));
-          const int idb = valid_id(__builtin_amdgcn_readlane(ids_cur, (blk & 63) + 1));
+          const int ida = valid_id(ROWS ? raw0 & id_mask : raw0);
+          const int idb = valid_id(ROWS ? __builtin_amdgcn_readlane(ids_cur, (blk & 63) + 1) & id_mask
+                                        : __builtin_amdgcn_readlane(ids_cur, (blk & 63) + 1));
           pk = (tk & 8) ? idb : ida;
 #pragma unroll
           for (int j = 0; j < 4; ++j) pv[j] = (tv[j] & 8) ? idb : ida;
         } else {
-          const int id = valid_id(__builtin_amdgcn_readlane(ids_cur, blk & 63));
+          const int id = valid_id(ROWS ? raw0 & id_mask : raw0);
           pk = id;
 #pragma unroll
           for (int j = 0; j < 4; ++j) pv[j] = id;
@@ -696,8 +711,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
             size_t orow = (size_t)s * p.num_heads + kv * g + col;
             bool out_ok = true;
             if constexpr (ROWS) {
+              // (a row that saw no token, an empty member of a shared-prefix group, keeps
+              // the zeros the layout kernel wrote)
               const int q0 = qsf(s);
-              out_ok = row_i < qsf(s + 1) - q0;
+              out_ok = row_i < qsf(s + 1) - q0 && ls != 0.f;
               orow = (size_t)(q0 + row_i) * p.num_heads + kv * g + row_h;
             }
 #pragma unroll
@@ -829,7 +846,20 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
           }
         }
         // online softmax, stream (grp, head col); tokens past the end get -inf
-        const int lim = (ROWS ? c_vis : cc.L) - kTileTokens * cc.j - 4 * grp;
+        int lim;
+        if constexpr (ROWS) {
+          if (p.shared) {
+            // the tile's owner and the tokens of its region from the tile's start
+            const unsigned u = (unsigned)Tl.vis;
+            const int own = (int)(u >> kSharedOwnerShift);
+            const int cnt = (int)((u >> kSharedEndShift) & 31u) + 1 - (kTileTokens * cc.j) % BS;
+            lim = own == kSharedAll || own == c_vis ? cnt - 4 * grp : 0;
+          } else {
+            lim = c_vis - kTileTokens * cc.j - 4 * grp;
+          }
+        } else {
+          lim = cc.L - kTileTokens * cc.j - 4 * grp;
+        }
         float sv[4];
 #pragma unroll
         for (int r = 0; r < 4; ++r) sv[r] = r < lim ? sc[r] * sl2 : -__builtin_inff();
@@ -1121,7 +1151,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(DecodeParams p) {
   if constexpr (ROWS) {  // row h is query h / g, head h % g
     const int q0 = min(max(p.q_start[s], 0), p.total_q);
     const int i = h / g;
-    ok = ok && i < min(max(p.q_start[s + 1], 0), p.total_q) - q0;
+    ok = ok && i < min(max(p.q_start[s + 1], 0), p.total_q) - q0 && l != 0.f;
     orow = (size_t)(q0 + i) * p.num_heads + kv * g + (h - i * g);
   }
   if (ok) {

@@ -54,7 +54,22 @@ struct DecodeParams {
                        // rows (max_q_len * group, at most 16)
   int total_q;         // rows mode: query rows of q and out (q_start values are clamped
                        // to [0, total_q], so no access leaves them)
+  // Rows mode over shared-prefix groups (0 otherwise): a "sequence" is a block of one
+  // group's members and its block table is the group's laid-out table (shared_rows): the
+  // prefix once, then each member's own tokens, each region starting on a tile.  Every
+  // entry is a block id (bits 0..21) with the owner of its tokens (bits 27..31: the
+  // member's row index, kSharedAll for the prefix) and, less one, how many of the
+  // region's tokens lie at or after the block's start, at most 32 (bits 22..26).  Row r
+  // sees the prefix and its own region only.
+  int shared;
 };
+
+// Bits of a laid-out shared-prefix table entry.
+constexpr int kSharedIdBits = 22;
+constexpr unsigned kSharedIdMask = (1u << kSharedIdBits) - 1u;
+constexpr int kSharedEndShift = 22;     // 5 bits: tokens of the region from the block start, - 1
+constexpr int kSharedOwnerShift = 27;   // 5 bits: member row index 0..15, or kSharedAll
+constexpr int kSharedAll = 16;   // owner of the prefix blocks: every row
 
 // Decode kernel variants: K/V loads with the non-temporal hint (pa_decode), the same
 // with the append of the newest tokens (pa_decode_append), and K/V loads with the
@@ -91,6 +106,26 @@ pa_status multi_query_rows(const void* q, const void* k_cache, const void* v_cac
                            int max_blocks_per_seq, int max_q_len, int max_seq_len, float scale,
                            pa_dtype dtype, void* out,
                            void* workspace, size_t workspace_bytes, hipStream_t st);
+
+// pa_decode_shared_prefix on the decode kernels: each group's members are taken in
+// blocks of at most 16 / group; for every block a layout kernel writes one table whose
+// first entries are the group's prefix blocks (once) followed by each member's own
+// blocks, every member's region starting on a whole tile (16 tokens, or a 32-token
+// block), and the rows mode runs over those tables with the members as its rows.
+// `shared_rows_apply` says whether the path covers the call; it needs
+// `shared_rows_workspace` bytes (16-byte aligned, no zero-fill) for the given block size.
+bool shared_rows_apply(pa_dtype dtype, int num_groups, int num_heads, int num_kv_heads,
+                       int head_dim, int block_size, int num_blocks, int max_group_size,
+                       int max_seq_len);
+size_t shared_rows_workspace(int num_seqs, int num_groups, int num_heads, int num_kv_heads,
+                             int head_dim, int block_size, int max_group_size, int max_seq_len);
+pa_status shared_rows(const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* seq_lens,
+                      const int32_t* group_start, const int32_t* prefix_lens, int num_seqs,
+                      int num_groups, int num_heads, int num_kv_heads, int head_dim,
+                      int block_size, int num_blocks, int max_blocks_per_seq, int max_group_size,
+                      int max_seq_len, float scale, pa_dtype dtype, void* out, void* workspace,
+                      size_t workspace_bytes, hipStream_t st);
 
 // Smallest group size of the compiled decode variants that can hold `group`
 // query heads (1, 2, 4, 8, 16), or 0 if none can.

@@ -21,6 +21,9 @@ pa_status hip_fail(hipError_t e, const char* what);
 // Positive integer value of an environment variable, else dflt.
 int env_int(const char* name, int dflt);
 
+// Environment switch: "0" is false, "1" true, anything else (or unset) dflt.
+bool env_flag(const char* name, bool dflt);
+
 // PA_DEBUG_CHECK=1: validate device-resident index data on the host before launching.
 bool debug_checks();
 

@@ -63,8 +63,8 @@ MQPlan mq_plan(int num_seqs, int total_q, int num_heads, int num_kv_heads, int h
 // PA_MULTI_QUERY_ROWS=0 keeps pa_multi_query on its own kernels for every shape (for
 // comparisons); the rows mode is on by default.
 bool multi_query_rows_enabled() {
-  static const int v = env_int("PA_MULTI_QUERY_ROWS", 1);
-  return v != 0;
+  static const bool v = env_flag("PA_MULTI_QUERY_ROWS", true);
+  return v;
 }
 
 bool mq_shapes_ok(int num_seqs, int total_q, int num_heads, int num_kv_heads, int head_dim,
@@ -272,8 +272,18 @@ size_t pa_decode_shared_prefix_workspace_size(int num_seqs, int num_groups, int 
       num_heads % num_kv_heads != 0 || num_heads / num_kv_heads > 16 || max_group_size < 0 ||
       max_seq_len < 0 || max_seq_len > kMaxSeqLen)
     return 0;
-  return sp_plan(num_seqs, num_groups, num_heads, num_kv_heads, head_dim, max_group_size, max_seq_len).total;
+  // the larger of the split kernel's plan and the rows path's (whose tables are largest
+  // for 8-token blocks), so that either path fits
+  const size_t split = sp_plan(num_seqs, num_groups, num_heads, num_kv_heads, head_dim, max_group_size,
+                               max_seq_len).total;
+  const size_t rows = shared_rows_workspace(num_seqs, num_groups, num_heads, num_kv_heads, head_dim, 8,
+                                            max_group_size, max_seq_len);
+  return split > rows ? split : rows;
 }
+
+// PA_SHARED_PREFIX_ROWS=0 keeps pa_decode_shared_prefix on the split multi-query kernel
+// (for comparisons); read at every call.
+static bool shared_prefix_rows_enabled() { return env_flag("PA_SHARED_PREFIX_ROWS", true); }
 
 pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void* v_cache,
                                   const int32_t* block_tables, const int32_t* seq_lens,
@@ -362,6 +372,18 @@ pa_status pa_decode_shared_prefix(const void* q, const void* k_cache, const void
       }
     }
   }
+  // The decode kernels' rows mode: the step split evenly over one wave per SIMD (the
+  // split kernel runs one work item per workgroup and pays a start per item).
+  if (shared_prefix_rows_enabled() &&
+      shared_rows_apply(dtype, num_groups, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                        max_group_size, max_seq_len) &&
+      workspace && aligned16(workspace) &&
+      workspace_bytes >= shared_rows_workspace(num_seqs, num_groups, num_heads, num_kv_heads, head_dim,
+                                               block_size, max_group_size, max_seq_len))
+    return shared_rows(q, k_cache, v_cache, block_tables, seq_lens, group_start, prefix_lens, num_seqs,
+                       num_groups, num_heads, num_kv_heads, head_dim, block_size, num_blocks,
+                       max_blocks_per_seq, max_group_size, max_seq_len, scale, dtype, out, workspace,
+                       workspace_bytes, st);
   const void* kmain = nullptr;
   const void* kmerge = nullptr;
   if (!multi_query_kernels((int)dtype, head_dim, 16, true, &kmain, &kmerge))

@@ -259,6 +259,20 @@ def test_shared_prefix_workspace_formula(pk, N, G, H, HKV, D, MG, L):
     parts = max(1, min(-(-1024 // items), -(-L // 256), 64)) if items and L else 1
     up = lambda x: -(-x // 256) * 256
     want = up(4 * G) + (0 if parts == 1 else up(N * H * parts * 2 * 4) + N * H * parts * D * 4)
+    # the rows path (decode kernels): members in blocks of mpb = min(16 / group, MG), each
+    # block a laid-out table of at most (mpb + 1) x L tokens rounded to 16-token units and
+    # read as 8-token blocks (the largest table); then the block lengths and first rows,
+    # after the decode kernels' workspace for mpb x group rows per pair
+    mpb = min(16 // g, MG)
+    vg = G * (-(-MG // mpb))
+    vlen = max(-(-L // 16) * 16 * (mpb + 1), 16)
+    if vg <= 2048 and vlen <= 1 << 24:
+        rows = mpb * g
+        waves = min(2048, max(1, -(-(N * HKV * math.ceil(L / 16)) // 8)))
+        chunks = 5 * waves
+        dec = up(256 + chunks * 16) + up(2 * chunks * rows * 2 * 4) + 2 * chunks * rows * D * 4
+        total = up(dec) + up(vg * (vlen // 8) * 4) + up(vg * 4) + (vg + 1) * 4
+        want = max(want, total)
     assert pk.pa_decode_shared_prefix_workspace_size(N, G, H, HKV, D, MG, L) == want
 
 

@@ -120,6 +120,53 @@ def test_groups_match_the_decode_oracle(case):
     assert_close(out.float().cpu().double().numpy(), oracle_out(b), dt, f"case {case}")
 
 
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_split_kernel_matches_the_decode_oracle(case, monkeypatch):
+    # the same groups on the split multi-query kernel (the path for block sizes outside
+    # {8, 16, 32}, batches beyond the decode kernels' tables and ids of 2^22 blocks or more)
+    monkeypatch.setenv("PA_SHARED_PREFIX_ROWS", "0")
+    dt, Hq, Hkv, D, B, groups = CASES[case]
+    b = grouped_batch(40 + case, dt, groups, Hq, Hkv, D, B)
+    log(f"shared prefix case {case} on the split kernel")
+    out, _ = run(b)
+    assert_close(out.float().cpu().double().numpy(), oracle_out(b), dt, f"split, case {case}")
+
+
+# Groups for the decode kernels' rows path: each block of members gets a laid-out table
+# (the prefix rounded down to whole 16-token units, or 32-token blocks, then every member's
+# own tokens padded to whole units), member i of a block is row i.
+ROWS_CASES = [  # dtype, Hq, Hkv, D, B, groups
+    ("f16", 8, 8, 128, 16, [(0, [0, 5, 0, 16, 1]), (0, [0])]),   # empty members: zeros
+    ("bf16", 8, 8, 64, 16, [(40, list(range(20)))]),             # 20 members, g=1: rows 0..15, then 4
+    ("bf16", 32, 8, 128, 32, [(64, [5, 40, 17]), (96, [0, 33])]),  # 32-token blocks: half-block tiles
+    ("f16", 16, 4, 128, 8, [(24, [3, 8, 9, 0]), (8, [1, 15])]),  # prefix 24 in 8-token blocks: 16 shared
+    ("bf16", 64, 8, 128, 16, [(100, [1, 2]), (17, [30]), (250, [0, 0])]),  # g=8: 2 members per block
+]
+
+
+@pytest.mark.parametrize("case", range(len(ROWS_CASES)))
+def test_rows_path_groups(case):
+    dt, Hq, Hkv, D, B, groups = ROWS_CASES[case]
+    b = grouped_batch(70 + case, dt, groups, Hq, Hkv, D, B)
+    log(f"shared prefix rows case {case}: {ROWS_CASES[case]}, prefixes {b.prefix_lens.tolist()}")
+    out, d = run(b)
+    got = out.float().cpu().double().numpy()
+    assert_close(got, oracle_out(b), dt, f"rows case {case}")
+    empty = (b.seq_lens == 0).numpy()
+    assert (got[empty] == 0).all(), "empty members must get zeros"
+    out2, _ = run(b, d=d)
+    assert torch.equal(bits(out.cpu()), bits(out2.cpu())), "reruns differ"
+
+
+def test_rows_path_long_prefix_split_over_waves():
+    # 2 groups x 8 KV heads, each pair thousands of tokens: pairs are cut over many waves
+    # and merged; members' own tokens sit after the prefix in the laid-out table
+    b = grouped_batch(81, "bf16", [(4000, [1, 300, 0, 77, 16, 5]), (2500, [640, 2])], 32, 8, 128, 16)
+    log("shared prefix rows: long prefixes")
+    out, _ = run(b)
+    assert_close(out.float().cpu().double().numpy(), oracle_out(b), "bf16", "long prefixes")
+
+
 @pytest.mark.parametrize("scale", [-0.11, 0.0])
 def test_negative_and_zero_scale(scale):
     b = grouped_batch(61, "bf16", [(64, [0, 5, 17, 40]), (33, [1, 0, 2])], 32, 8, 128, 16)
