@@ -489,13 +489,17 @@ struct SharedLayoutArgs {
   int out_row_bytes;  // one sequence's output rows (all heads)
 };
 
-// One wave per laid-out block of members: its table, length and first member row, and
-// zeros for the output of every empty member (which sees no token).  Index data outside
-// the contract is clamped so that every read stays in its array.
-__global__ __launch_bounds__(64) void shared_layout_kernel(SharedLayoutArgs a) {
+// Workgroup (v, y) writes entries 256 y .. 256 y + 255 of member block v's table;
+// workgroup (v, 0) also its length and first member row, and zeros for the output of
+// every empty member (which sees no token).  Each workgroup works out the block's regions
+// itself, so the table takes three dependent rounds of loads (group bounds, member
+// lengths, block ids).  Index data outside the contract is clamped so that every read
+// stays in its array.
+__global__ __launch_bounds__(256) void shared_layout_kernel(SharedLayoutArgs a) {
   __shared__ int s_len[16], s_start[16], s_tail[16];
   const int v = blockIdx.x;
   const int lane = threadIdx.x;
+  const bool first = blockIdx.y == 0;
   const int j = v / a.cpg, c = v - j * a.cpg;
   const int ga = min(max(a.group_start[j], 0), a.num_seqs);
   const int gb = min(max(a.group_start[j + 1], ga), a.num_seqs);
@@ -514,14 +518,16 @@ __global__ __launch_bounds__(64) void shared_layout_kernel(SharedLayoutArgs a) {
       s_tail[i] = t;
       S += (t + U - 1) / U * U;
     }
-    a.vqs[v] = m0;
-    if (v == a.vgroups - 1) a.vqs[a.vgroups] = a.num_seqs;
-    a.vlens[v] = nq > 0 ? s_start[nq - 1] + s_tail[nq - 1] : 0;
+    if (first) {
+      a.vqs[v] = m0;
+      if (v == a.vgroups - 1) a.vqs[a.vgroups] = a.num_seqs;
+      a.vlens[v] = nq > 0 ? s_start[nq - 1] + s_tail[nq - 1] : 0;
+    }
   }
   __syncthreads();
   const int Lv = nq > 0 ? s_start[nq - 1] + s_tail[nq - 1] : 0;
   const int nvb = (Lv + B - 1) / B;
-  for (int k = lane; k < nvb; k += 64) {
+  for (int k = blockIdx.y * 256 + lane; k < nvb; k += 256 * gridDim.y) {
     const int x = k * B;
     int own = kSharedAll, m = m0, idx = k, e = min(P - x, 32);
     if (x >= P) {
@@ -539,10 +545,10 @@ __global__ __launch_bounds__(64) void shared_layout_kernel(SharedLayoutArgs a) {
     a.vtable[(size_t)v * a.max_vblocks + k] =
         (int)((unsigned)id | ((unsigned)(e - 1) << kSharedEndShift) | ((unsigned)own << kSharedOwnerShift));
   }
-  for (int i = 0; i < nq; ++i) {
+  for (int i = 0; i < nq && first; ++i) {
     if (s_len[i] != 0) continue;
     uint4* o = reinterpret_cast<uint4*>(a.out + (size_t)(m0 + i) * a.out_row_bytes);
-    for (int x = lane; x < a.out_row_bytes / 16; x += 64) o[x] = make_uint4(0u, 0u, 0u, 0u);
+    for (int x = lane; x < a.out_row_bytes / 16; x += 256) o[x] = make_uint4(0u, 0u, 0u, 0u);
   }
 }
 
@@ -609,7 +615,8 @@ pa_status shared_rows(const void* q, const void* k_cache, const void* v_cache,
   la.num_blocks = num_blocks;
   la.max_vblocks = L.max_vblocks;
   la.out_row_bytes = num_heads * head_dim * (dtype == PA_F32 ? 4 : 2);
-  hipLaunchKernelGGL(shared_layout_kernel, dim3((unsigned)L.vgroups), dim3(64), 0, st, la);
+  const unsigned parts = (unsigned)std::min((L.max_vblocks + 255) / 256, 65535);
+  hipLaunchKernelGGL(shared_layout_kernel, dim3((unsigned)L.vgroups, parts), dim3(256), 0, st, la);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "pa_decode_shared_prefix layout launch");
   p.block_tables = la.vtable;
