@@ -332,8 +332,10 @@ pa_status pa_multi_query(const void* q, const void* k_cache, const void* v_cache
  *
  * A group is processed in blocks of 16 / (num_heads / num_kv_heads) members
  * (at most 16 query heads per KV head); each block reads the prefix once.
- * With block_size 8, 16 or 32, fewer than 2^22 blocks in the pool and at most
- * 2,048 such member blocks, the call runs on pa_decode's kernels: a layout
+ * With block_size 8, 16 or 32, fewer than 2^22 blocks in the pool, at most
+ * 2,048 such member blocks and laid-out tables of at most 256 MiB (bounded by
+ * member blocks x (members per block + 1) x max_seq_len / block_size entries),
+ * the call runs on pa_decode's kernels: a layout
  * kernel writes, for every member block, one table holding the prefix (rounded
  * down to whole 16-token units, or 32-token blocks) and then each member's own
  * tokens, each member's part starting on a whole unit; the decode kernel reads

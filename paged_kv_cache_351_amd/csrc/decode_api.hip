@@ -435,6 +435,8 @@ namespace {
 // tokens, so every region starts on a tile and on a block), read once; then, for each
 // member in order, its tokens past that prefix, padded to whole units.  Member i of the
 // block is row i (with its group's heads); the prefix is everyone's.
+constexpr long long kSharedTableBytes = 256LL << 20;
+
 struct SharedRowsLayout {
   int mpb = 0;          // members per block
   int cpg = 0;          // blocks per group
@@ -461,7 +463,11 @@ SharedRowsLayout shared_rows_layout(int num_seqs, int num_groups, int num_heads,
   L.unit = std::max(block_size, kTileTokens);
   const long long per = ((long long)max_seq_len + L.unit - 1) / L.unit * L.unit;
   const long long vlen = std::max<long long>(per * (L.mpb + 1), L.unit);
-  if (vg > kLdsSeqs || vlen > kMaxSeqLen || vg * tiles_of((int)vlen) >= (1LL << 31) - 1) return L;
+  // (tables of more than kSharedTableBytes, from long sequences in many large groups, are
+  // left to the split kernel rather than held in the workspace)
+  if (vg > kLdsSeqs || vlen > kMaxSeqLen || vg * tiles_of((int)vlen) >= (1LL << 31) - 1 ||
+      vg * (vlen / block_size) * (long long)sizeof(int32_t) > kSharedTableBytes)
+    return L;
   L.vgroups = (int)vg;
   L.max_vlen = (int)vlen;
   L.max_vblocks = L.max_vlen / block_size;

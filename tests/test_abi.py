@@ -249,7 +249,8 @@ def test_multi_query_with_no_queries_is_a_no_op(pk):
 
 
 @pytest.mark.parametrize("N,G,H,HKV,D,MG,L", [(256, 32, 40, 40, 128, 8, 1280), (4, 1, 8, 8, 128, 4, 3200),
-                                             (8, 2, 32, 8, 128, 6, 150), (3, 3, 16, 1, 64, 1, 40)])
+                                             (8, 2, 32, 8, 128, 6, 150), (3, 3, 16, 1, 64, 1, 40),
+                                             (4096, 1024, 8, 8, 128, 32, 32768)])   # tables past 256 MiB
 def test_shared_prefix_workspace_formula(pk, N, G, H, HKV, D, MG, L):
     # blocks of 16 / group members per item, about 1024 items wanted, partitions of >= 256
     # tokens, at most 64; a longest-first order of the groups, then (with partitions) the
@@ -266,7 +267,7 @@ def test_shared_prefix_workspace_formula(pk, N, G, H, HKV, D, MG, L):
     mpb = min(16 // g, MG)
     vg = G * (-(-MG // mpb))
     vlen = max(-(-L // 16) * 16 * (mpb + 1), 16)
-    if vg <= 2048 and vlen <= 1 << 24:
+    if vg <= 2048 and vlen <= 1 << 24 and vg * (vlen // 8) * 4 <= 256 << 20:
         rows = mpb * g
         waves = min(2048, max(1, -(-(N * HKV * math.ceil(L / 16)) // 8)))
         chunks = 5 * waves
