@@ -1,8 +1,9 @@
 """Benchmark: paged decode attention on one MI355X, Llama-3-8B-shaped GQA layer.
 
-One step = pa_write_kv of 256 new tokens (one per sequence) followed by pa_decode
-over all 256 sequences (decode kernel + merge kernel), on one stream, with every
-input already resident in HBM; ``--fused`` runs the two as one pa_decode_append call.
+One step = the append of 256 new tokens (one per sequence, its newest) and the decode
+over all 256 sequences, on one stream, with every input already resident in HBM: one
+pa_decode_append call (decode kernel + merge kernel, whose last workgroups store the new
+rows); ``--two-call`` runs it as pa_write_kv followed by pa_decode instead (bit-identical).
 Workload: 256 sequences, 32 query / 8 KV heads, head_dim 128, bf16 KV and q, fp32
 accumulation, block size 16, lengths uniform in [512, 4096] (seed 0), 70,000-block
 pool with random block placement.
@@ -21,7 +22,7 @@ new tokens) and pa_copy_blocks (224 copy-on-write pairs of OPT-13B-shaped blocks
 same way.  ``cpu_baseline`` times the float64 CPU oracle on the host.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload NAME [--block-size B]]
-    python bench.py --fused              # the step as one pa_decode_append
+    python bench.py --two-call           # the step as pa_write_kv + pa_decode
     python bench.py --workload opt13b_shared --shared-prefix   # shared-prefix decode
     python bench.py --workload llama3_8b_spec                  # multi-query (also llama3_8b_chunk)
     python bench.py --swap               # pa_swap_blocks HBM <-> pinned host throughput
@@ -540,9 +541,11 @@ def main():
     ap.add_argument("--block-size", type=int, default=16, choices=[8, 16, 32],
                     help="block size of the llama2_70b workload")
     ap.add_argument("--fused", action="store_true",
-                    help="run the step's write and decode as one pa_decode_append instead of "
-                         "two calls (pa_write_kv, pa_decode); the write must store each "
-                         "sequence's newest token")
+                    help="run the step's write and decode as one pa_decode_append (the default "
+                         "wherever the write stores each sequence's newest token and the batch "
+                         "shares no blocks); an error where it cannot")
+    ap.add_argument("--two-call", action="store_true",
+                    help="run the step's write and decode as two calls, pa_write_kv then pa_decode")
     ap.add_argument("--graph", action="store_true",
                     help="time the step as replays of a HIP graph captured once (the roofline "
                          "still times the eager decode call)")
@@ -615,13 +618,16 @@ def main():
             pk.pa_decode_append(q, nk, nv, kc, vc, bt, lens, b.num_kv_heads, b.scale, out,
                                 max_seq_len=max_len, workspace=ws)
         attend = decode
-    # --fused: a step whose write stores exactly each sequence's newest token (position
-    # L - 1) runs write and decode as one pa_decode_append
-    fused = args.fused
+    # A step whose write stores exactly each sequence's newest token (position L - 1), in a
+    # batch that shares no blocks, runs write and decode as one pa_decode_append unless
+    # --two-call asks for pa_write_kv + pa_decode.
+    can_fuse = (not multi and not shared and has_write and b.group_start is None
+                and write_is_newest(b))
+    if args.fused and (args.two_call or not can_fuse):
+        raise SystemExit("--fused needs a decode workload whose write stores each sequence's "
+                         "newest token, in a batch that shares no blocks (and no --two-call)")
+    fused = can_fuse and not args.two_call
     if fused:
-        if multi or shared or not has_write or not write_is_newest(b):
-            raise SystemExit("--fused needs a decode workload whose write stores each sequence's "
-                             "newest token")
         attend = decode_append
 
     def step(ev0=None, ev1=None):
